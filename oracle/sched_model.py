@@ -1,0 +1,198 @@
+"""Model of the four tile schedulers: which workgroup (program) computes which
+output tile, and in which order.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+Notation: T tiles, G programs (the persistent grid), X XCDs, tile grid
+num_pid_m x num_pid_n.  A virtual tile id v in [0, T) is decoded into
+(pid_m, pid_n).
+
+Sources:
+* Blocked ranges, stride-by-grid and the plain decode: "Implement persistent
+  kernels" (Helion PR #238), example output, PERSISTENT BLOCKED KERNEL and
+  PERSISTENT INTERLEAVED KERNEL.  A program p with block size cdiv(T, G)
+  takes [p*bs, min(p*bs + bs, T)); interleaved takes p, p+G, p+2G, ...;
+  decode puts dimension 0 fastest: pid_m = v mod num_pid_m.
+* Grouped decode: the same page, PERSISTENT BLOCKED WITH L2 GROUPING (group
+  of 8 rows of tiles there; group_size here), with the last group shortened
+  by the min().
+* Grouped scheduler = stride-by-grid over the grouped order, the persistent
+  loop plus swizzle of "[Feature] Introduce tile scheduler" (TileLang PR
+  #2441), scheduler with swizzle_size / group_size.
+* Work stealing: "Work Stealing Scheduler Kernel" (tritonBLAS PR #65),
+  overview and review of the kernel: one int32 counter per XCD, program p
+  uses counter p mod X, counters zeroed before each launch, programs claim
+  their XCD's tiles until none are left.  Reading taken where the page is
+  silent: XCD x owns the contiguous range [floor(x*T/X), floor((x+1)*T/X))
+  of the grouped order; a claim is fetch_add(counter, chunk) and a program
+  stops at its first claim that starts at or beyond the range's length.
+"""
+from __future__ import annotations
+
+import random
+from typing import Dict, List, Sequence, Tuple
+
+BLOCKED = "blocked"
+INTERLEAVED = "interleaved"
+GROUPED = "grouped"
+WORK_STEALING = "work_stealing"
+BLOCKED_GROUPED = "blocked_grouped"
+STATIC_KINDS = (BLOCKED, INTERLEAVED, GROUPED, BLOCKED_GROUPED)
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plain_decode(v: int, num_pid_m: int) -> Tuple[int, int]:
+    return v % num_pid_m, v // num_pid_m
+
+
+def grouped_decode(v: int, num_pid_m: int, num_pid_n: int, gs: int) -> Tuple[int, int]:
+    num_pid_in_group = gs * num_pid_n
+    group_id = v // num_pid_in_group
+    first_pid_m = group_id * gs
+    group_size_m = min(num_pid_m - first_pid_m, gs)
+    pid_m = first_pid_m + (v % num_pid_in_group) % group_size_m
+    pid_n = (v % num_pid_in_group) // group_size_m
+    return pid_m, pid_n
+
+
+def blocked_vpids(p: int, T: int, G: int) -> List[int]:
+    bs = cdiv(T, G)
+    start = p * bs
+    end = min(start + bs, T)
+    return list(range(start, end))
+
+
+def interleaved_vpids(p: int, T: int, G: int) -> List[int]:
+    return list(range(p, T, G))
+
+
+def decode(kind: str, v: int, num_pid_m: int, num_pid_n: int, gs: int) -> Tuple[int, int]:
+    if kind in (BLOCKED, INTERLEAVED):
+        return plain_decode(v, num_pid_m)
+    return grouped_decode(v, num_pid_m, num_pid_n, gs)
+
+
+def static_schedule(kind: str, num_pid_m: int, num_pid_n: int, G: int,
+                    gs: int = 8) -> List[List[Tuple[int, int, int]]]:
+    """Per program p, the ordered list of (v, pid_m, pid_n) it computes."""
+    T = num_pid_m * num_pid_n
+    out = []
+    for p in range(G):
+        if kind in (BLOCKED, BLOCKED_GROUPED):
+            vs = blocked_vpids(p, T, G)
+        elif kind in (INTERLEAVED, GROUPED):
+            vs = interleaved_vpids(p, T, G)
+        else:
+            raise ValueError(kind)
+        out.append([(v,) + decode(kind, v, num_pid_m, num_pid_n, gs) for v in vs])
+    return out
+
+
+def ws_ranges(T: int, X: int) -> List[Tuple[int, int]]:
+    return [((x * T) // X, ((x + 1) * T) // X) for x in range(X)]
+
+
+def ws_programs_per_xcd(G: int, X: int) -> List[int]:
+    return [sum(1 for p in range(G) if p % X == x) for x in range(X)]
+
+
+def ws_final_counters(T: int, G: int, X: int, chunk: int = 1) -> List[int]:
+    """Counter values after a complete launch: every successful claim and
+    exactly one failing claim per program each added ``chunk``."""
+    out = []
+    for (s, e), w in zip(ws_ranges(T, X), ws_programs_per_xcd(G, X)):
+        n = e - s
+        out.append(chunk * (cdiv(n, chunk) + w))
+    return out
+
+
+def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
+                chunk: int = 1, seed: int = 0, speeds: Sequence[float] = None):
+    """One possible work-stealing execution.
+
+    Programs run concurrently; the interleaving is drawn at random (or, with
+    ``speeds``, the program with the earliest finish time claims next).
+    Returns (per-program list of (v, pid_m, pid_n), final counters)."""
+    T = num_pid_m * num_pid_n
+    if G < X:
+        raise ValueError("work stealing needs at least one program per XCD")
+    ranges = ws_ranges(T, X)
+    cnt = [0] * X
+    seqs: List[List[Tuple[int, int, int]]] = [[] for _ in range(G)]
+    active = list(range(G))
+    clock = [0.0] * G
+    r = random.Random(seed)
+    while active:
+        if speeds is None:
+            p = r.choice(active)
+        else:
+            p = min(active, key=lambda q: (clock[q], q))
+        x = p % X
+        s, e = ranges[x]
+        i = cnt[x]
+        cnt[x] += chunk
+        if i >= e - s:
+            active.remove(p)
+            continue
+        for v in range(s + i, min(s + i + chunk, e)):
+            seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
+        if speeds is not None:
+            clock[p] += speeds[p] * (min(i + chunk, e - s) - i)
+    return seqs, cnt
+
+
+def check_partition(seqs: Sequence[Sequence[Tuple[int, int, int]]],
+                    num_pid_m: int, num_pid_n: int) -> None:
+    """Every tile id in [0, T) and every (pid_m, pid_n) appears exactly once."""
+    T = num_pid_m * num_pid_n
+    seen_v: Dict[int, int] = {}
+    seen_mn: Dict[Tuple[int, int], int] = {}
+    for p, seq in enumerate(seqs):
+        for v, pm, pn in seq:
+            if not (0 <= v < T):
+                raise AssertionError(f"program {p}: tile id {v} outside [0, {T})")
+            if not (0 <= pm < num_pid_m and 0 <= pn < num_pid_n):
+                raise AssertionError(f"program {p}: tile ({pm},{pn}) outside the grid")
+            if v in seen_v:
+                raise AssertionError(f"tile id {v} computed by {seen_v[v]} and {p}")
+            if (pm, pn) in seen_mn:
+                raise AssertionError(f"tile {(pm, pn)} computed twice")
+            seen_v[v] = p
+            seen_mn[(pm, pn)] = p
+    if len(seen_v) != T or len(seen_mn) != T:
+        raise AssertionError(f"{T - len(seen_mn)} tiles never computed")
+
+
+def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
+                       local_order: Sequence[int], counters: Sequence[int],
+                       T: int, G: int, X: int, chunk: int = 1) -> None:
+    """Invariants every correct work-stealing launch satisfies (the exact
+    assignment depends on timing).  Arrays are indexed by tile id v:
+    visits[v] = times computed, owner[v] = program, local_order[v] = its
+    position in that program's sequence."""
+    ranges = ws_ranges(T, X)
+    for v in range(T):
+        if visits[v] != 1:
+            raise AssertionError(f"tile {v} visited {visits[v]} times")
+    for x, (s, e) in enumerate(ranges):
+        for v in range(s, e):
+            if owner[v] % X != x or not (0 <= owner[v] < G):
+                raise AssertionError(f"tile {v} of XCD {x} computed by program {owner[v]}")
+    # claims of one program come from one counter, so its tiles rise with its order
+    by_prog: Dict[int, List[Tuple[int, int]]] = {}
+    for v in range(T):
+        by_prog.setdefault(owner[v], []).append((local_order[v], v))
+    for p, lst in by_prog.items():
+        lst.sort()
+        orders = [o for o, _ in lst]
+        if orders != list(range(len(lst))):
+            raise AssertionError(f"program {p}: local order {orders} not 0..n-1")
+        vs = [v for _, v in lst]
+        if any(b <= a for a, b in zip(vs, vs[1:])):
+            raise AssertionError(f"program {p}: tiles not increasing {vs}")
+    want = ws_final_counters(T, G, X, chunk)
+    if list(counters[:X]) != want:
+        raise AssertionError(f"final counters {list(counters[:X])} != {want}")

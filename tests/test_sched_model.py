@@ -1,0 +1,143 @@
+"""Pins for the schedule model: hand-derived fixtures, the partition
+property over many sizes, special cases that reduce to textbook orders, the
+work-stealing invariants under random interleavings, and planted mistakes."""
+import itertools
+
+import pytest
+
+from oracle import sched_model as sm
+
+
+def _prog_table(rows):
+    out = {}
+    for r in rows:
+        p, _, rest = r.partition(":")
+        out[int(p)] = [int(v) for v in rest.split()]
+    return out
+
+
+@pytest.mark.parametrize("name,kind,T,G", [
+    ("sched_blocked_T10_G4.txt", "blocked", 10, 4),
+    ("sched_blocked_T3_G8.txt", "blocked", 3, 8),
+    ("sched_interleaved_T10_G4.txt", "interleaved", 10, 4),
+])
+def test_static_golden(golden, name, kind, T, G):
+    want = _prog_table(golden(name))
+    f = sm.blocked_vpids if kind == "blocked" else sm.interleaved_vpids
+    for p in range(G):
+        assert f(p, T, G) == want[p]
+
+
+def test_plain_decode_golden(golden):
+    for r in golden("decode_plain_m5_n2.txt"):
+        v, m, n = map(int, r.split())
+        assert sm.plain_decode(v, 5) == (m, n)
+
+
+def test_grouped_decode_golden(golden):
+    for r in golden("decode_grouped_m10_n3_g4.txt"):
+        v, m, n = map(int, r.split())
+        assert sm.grouped_decode(v, 10, 3, 4) == (m, n)
+
+
+def test_ws_golden(golden):
+    rows = [tuple(map(int, r.split())) for r in golden("ws_T10_X4_G8.txt")]
+    assert sm.ws_ranges(10, 4) == [(s, e) for _, s, e, _ in rows]
+    assert sm.ws_final_counters(10, 8, 4) == [c for *_, c in rows]
+    seqs, cnt = sm.ws_simulate(5, 2, 8, 4, gs=8, seed=1)
+    assert cnt == [c for *_, c in rows]
+
+
+SIZES = [(1, 1), (1, 7), (7, 1), (3, 5), (16, 16), (13, 23), (10, 30), (32, 4), (17, 17)]
+
+
+@pytest.mark.parametrize("kind", sm.STATIC_KINDS)
+@pytest.mark.parametrize("G", [1, 7, 8, 256])
+def test_static_partition(kind, G):
+    for (pm, pn), gs in itertools.product(SIZES, [1, 3, 8, 16]):
+        sm.check_partition(sm.static_schedule(kind, pm, pn, G, gs), pm, pn)
+
+
+def test_grouped_special_cases():
+    for pm, pn in SIZES:
+        for v in range(pm * pn):
+            # group_size 1: row-major (pid_n fastest)
+            assert sm.grouped_decode(v, pm, pn, 1) == (v // pn, v % pn)
+            # group_size >= num_pid_m: the plain decode
+            assert sm.grouped_decode(v, pm, pn, pm) == sm.plain_decode(v, pm)
+            assert sm.grouped_decode(v, pm, pn, pm + 5) == sm.plain_decode(v, pm)
+
+
+def test_blocked_fewer_tiles_than_programs():
+    s = sm.static_schedule("blocked", 4, 4, 256)
+    assert [len(x) for x in s[:16]] == [1] * 16 and all(len(x) == 0 for x in s[16:])
+    s = sm.static_schedule("blocked", 20, 20, 256)          # T = 400: bs = 2
+    assert all(len(x) == 2 for x in s[:200]) and all(len(x) == 0 for x in s[200:])
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [
+    (5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (20, 20, 256, 8, 1), (19, 32, 256, 8, 1),
+    (12, 28, 256, 8, 1), (2, 2, 256, 8, 1), (1, 1, 8, 8, 1), (9, 7, 11, 8, 1),
+    (256, 8, 256, 8, 8), (33, 5, 16, 8, 4),
+])
+def test_ws_simulated_invariants(pm, pn, G, X, chunk):
+    T = pm * pn
+    for seed in range(3):
+        seqs, cnt = sm.ws_simulate(pm, pn, G, X, gs=8, chunk=chunk, seed=seed)
+        sm.check_partition(seqs, pm, pn)
+        visits, owner, order = [0] * T, [-1] * T, [-1] * T
+        for p, seq in enumerate(seqs):
+            for i, (v, _, _) in enumerate(seq):
+                visits[v] += 1
+                owner[v] = p
+                order[v] = i
+        sm.check_ws_execution(visits, owner, order, cnt, T, G, X, chunk)
+
+
+def test_ws_rebalances_straggler():
+    # program 0 is 10x slower: its XCD peers take over its share
+    G, X = 16, 8
+    speeds = [10.0] + [1.0] * (G - 1)
+    seqs, _ = sm.ws_simulate(8, 8, G, X, speeds=speeds)
+    assert len(seqs[0]) < len(seqs[8])
+    sm.check_partition(seqs, 8, 8)
+
+
+def test_ws_rejects_grid_below_xcds():
+    with pytest.raises(ValueError):
+        sm.ws_simulate(4, 4, 7, 8)
+
+
+def _witness(seqs, T):
+    visits, owner, order = [0] * T, [-1] * T, [-1] * T
+    for p, seq in enumerate(seqs):
+        for i, (v, _, _) in enumerate(seq):
+            visits[v] += 1
+            owner[v] = p
+            order[v] = i
+    return visits, owner, order
+
+
+def test_checkers_catch_planted_mistakes():
+    seqs = sm.static_schedule("interleaved", 4, 4, 3)
+    bad = [list(s) for s in seqs]
+    bad[0].append(bad[1][0])                                # a tile twice
+    with pytest.raises(AssertionError):
+        sm.check_partition(bad, 4, 4)
+    bad = [list(s) for s in seqs]
+    bad[2].pop()                                            # a tile dropped
+    with pytest.raises(AssertionError):
+        sm.check_partition(bad, 4, 4)
+    seqs, cnt = sm.ws_simulate(4, 4, 8, 4, seed=2)
+    T = 16
+    v, o, r = _witness(seqs, T)
+    with pytest.raises(AssertionError):                      # wrong final counter
+        sm.check_ws_execution(v, o, r, [c + 1 for c in cnt], T, 8, 4)
+    o2 = list(o)
+    o2[0] = (o2[0] + 1) % 8                                 # owner on another XCD
+    with pytest.raises(AssertionError):
+        sm.check_ws_execution(v, o2, r, cnt, T, 8, 4)
+    v2 = list(v)
+    v2[5] = 2
+    with pytest.raises(AssertionError):
+        sm.check_ws_execution(v2, o, r, cnt, T, 8, 4)
