@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Benchmark of the persistent tiled GEMM (8192^3 bf16, bf16 C) per tile
+scheduler, plus the persistent fp32 add, on one MI355X.
+
+Prints ONE JSON line.  `value` is the GEMM throughput (TFLOP/s) of the
+work-stealing scheduler on the 8192^3 workload; every scheduler's figure, the
+add's GB/s, the roofline of the dominant kernel and the CPU oracle baseline
+are reported in the same line.
+
+Timed region: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize() on both sides; inputs are resident in HBM before the
+timed region starts.  A step is one pgemm_run call (counter reset + persistent
+GEMM launch) on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+M = N = K = 8192
+SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
+          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8)]
+HEADLINE = ("work_stealing", 8)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of schedulers to time (profiling runs)")
+    p.add_argument("--skip-add", action="store_true")
+    return p.parse_args()
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Wall time of `steps` calls plus per-call HIP-event durations on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return wall * 1e3 / steps, float(np.mean(durs)), float(np.min(durs))
+
+
+def cpu_baseline(a_bits, b_bits):
+    """The oracle on a bounded sample: 16 full rows of C (16 x 8192 outputs, K = 8192)."""
+    from oracle import gemm as og
+    from oracle.codecs import bf16_to_f64
+    rows = np.arange(0, M, M // 16)[:16]
+    A = bf16_to_f64(a_bits[rows])
+    B = bf16_to_f64(b_bits)
+    t0 = time.perf_counter()
+    og.gemm_f64(A, B)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": og.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} full rows of C (16x8192 outputs, K=8192, fp64 with |A||B|) in {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+                                   "(the sharding plan is described, not run)"}))
+        sys.exit(2)
+    import torch
+    import tile_scheduling_persistent_amd as pg
+    from synthetic import bf16_bits_normal, f32_normal
+
+    cfg = pg.Config(0)
+    stream = torch.cuda.current_stream()
+    a_bits = bf16_bits_normal((M, K), 1030)
+    b_bits = bf16_bits_normal((K, N), 1031)
+    A = torch.from_numpy(a_bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    B = torch.from_numpy(b_bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    flops = 2.0 * M * N * K
+
+    only = set(s for s in args.only.split(",") if s)
+    per = {}
+    for sched, gs in SCHEDS:
+        if only and sched not in only:
+            continue
+        a = pg.make_args(tile=(256, 256, 64), group_size=gs)
+        fn = lambda: pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)  # noqa: E731
+        ms, ev_mean, ev_min = time_calls(fn, args.steps, args.warmup, stream)
+        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped") else "")
+        per[key] = {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "event_ms_mean": ev_mean,
+                    "event_ms_min": ev_min,
+                    "frac_peak": flops / (ev_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        print(f"# {key}: {ms:.4f} ms/step, {per[key]['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    add = {}
+    if not args.skip_add:
+        R = Cc = 8192
+        X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
+        Y = torch.from_numpy(f32_normal((R, Cc), 2002)).to("cuda:0")
+        Z = torch.empty_like(X)
+        nbytes = 3 * R * Cc * 4
+        for tile in [(32, 16), (128, 128)]:
+            for sched in ["blocked", "interleaved", "grouped", "work_stealing"]:
+                fn = lambda: pg.padd_run(cfg, X, Y, Z, R, Cc, tile[0], tile[1], sched)  # noqa: E731
+                ms, ev_mean, _ = time_calls(fn, max(args.steps, 20), args.warmup, stream)
+                add[f"{tile[0]}x{tile[1]}_{sched}"] = {"gbs": nbytes / (ev_mean * 1e-3) / 1e9,
+                                                       "event_ms_mean": ev_mean}
+                print(f"# add {tile} {sched}: {nbytes / (ev_mean * 1e-3) / 1e9:.0f} GB/s",
+                      file=sys.stderr, flush=True)
+
+    head_key = f"{HEADLINE[0]}_g{HEADLINE[1]}"
+    if head_key not in per:
+        head_key = next(iter(per))
+    h = per[head_key]
+    line = {
+        "metric": "GEMM TFLOP/s & % MFMA peak per scheduler (8192^3 bf16); add GB/s",
+        "value": round(h["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: A, B iid normal(0,1) rounded to bf16 (PCG64 seeds 1030/1031)",
+        "config": {"workload": "bf16 GEMM M=N=K=8192, fp32 accumulate, bf16 C, 256x256x64 tiles, "
+                               f"persistent grid = {cfg.info['num_cus']} CUs, scheduler {head_key}",
+                   "M": M, "N": N, "K": K, "scheduler": head_key},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),
+                              "event_ms_mean": round(v["event_ms_mean"], 5)} for k, v in per.items()},
+        "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}
+                for k, v in add.items()},
+        "device": cfg.info,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a_bits, b_bits)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * pgemm.h -- persistent tiled GEMM and persistent 2-D add with tile
+ * schedulers, for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point is extern "C", takes plain host or device pointers and
+ * sizes, returns a pgemm_status and never throws.  Argument errors are
+ * reported before anything is enqueued.  Compute calls are asynchronous on
+ * the HIP stream passed in (a hipStream_t given as void*; NULL is the null
+ * stream); device faults surface at the caller's next synchronisation.
+ *
+ * Sources for the operations (page title, section):
+ *  - "Work Stealing Scheduler Kernel" (tritonBLAS PR #65): overview (an
+ *    opt-in per-XCD work-stealing persistent GEMM with preallocated reusable
+ *    buffers), review of the matmul wrapper (config object with the CU count
+ *    and an int32 tile-counter array sized by max_xcds, counters reset before
+ *    every launch, grid = number of CUs, kernel arguments A, B, C, a_scale,
+ *    b_scale, tile_counter, M, N, K), review of the kernel (masked edge
+ *    tiles, no index wrapping; counter index bounded by the array size).
+ *  - "Implement persistent kernels" (Helion PR #238), example output:
+ *    persistent blocked, interleaved and L2-grouped schedules of a 2-D add.
+ *  - "[Feature] Introduce tile scheduler" (TileLang PR #2441): persistent
+ *    scheduler object with a swizzle / group size, block-scaled fp8 GEMM with
+ *    scale shape (1, 1, 128) and K-group-major scale arrays.
+ */
+#ifndef PGEMM_H
+#define PGEMM_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PGEMM_API __attribute__((visibility("default")))
+#else
+#define PGEMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PGEMM_OK = 0,
+  PGEMM_ERR_INVALID = 1,     /* bad argument or state; nothing was enqueued */
+  PGEMM_ERR_UNSUPPORTED = 2, /* device is not gfx950, or no kernel built for the request */
+  PGEMM_ERR_DEVICE = 3,      /* a HIP runtime call failed */
+  PGEMM_ERR_OOM = 4,         /* a device allocation failed */
+  PGEMM_ERR_LAUNCH = 5       /* the kernel launch was rejected */
+} pgemm_status;
+
+/* Operand / result formats. */
+typedef enum {
+  /* A, B bf16; fp32 accumulate; C fp32. */
+  PGEMM_BF16_OUT_F32 = 0,
+  /* A, B bf16; fp32 accumulate; C bf16 (round to nearest even). */
+  PGEMM_BF16_OUT_BF16 = 1,
+  /* A, B OCP e4m3 bytes with one e8m0 scale byte per 128 consecutive K
+   * elements per row of A (a_scale[K/128][M]) and per column of B
+   * (b_scale[K/128][N]); value = e4m3(q) * 2^(scale - 127); fp32
+   * accumulate; C bf16.  K must be a multiple of 128. */
+  PGEMM_FP8E4M3_B128_OUT_BF16 = 2
+} pgemm_dtype;
+
+/* Tile schedulers.  T = number of output tiles, G = grid (programs), X = XCDs.
+ * v is a tile id in [0, T); it is decoded into (pid_m, pid_n).
+ *  BLOCKED          program p takes [p*ceil(T/G), min((p+1)*ceil(T/G), T)),
+ *                   plain decode (pid_m = v mod num_pid_m fastest).
+ *  INTERLEAVED      program p takes p, p+G, p+2G, ...; plain decode.
+ *  GROUPED          stride-by-grid over the grouped order: group_size rows of
+ *                   tiles per group, the last group shortened.
+ *  WORK_STEALING    one int32 counter per XCD; program p claims from counter
+ *                   p mod X the tiles of the contiguous range
+ *                   [floor(x*T/X), floor((x+1)*T/X)) of the grouped order
+ *                   until a claim falls past its end.  Needs G >= X.
+ *  BLOCKED_GROUPED  blocked ranges over the grouped order. */
+typedef enum {
+  PGEMM_SCHED_BLOCKED = 0,
+  PGEMM_SCHED_INTERLEAVED = 1,
+  PGEMM_SCHED_GROUPED = 2,
+  PGEMM_SCHED_WORK_STEALING = 3,
+  PGEMM_SCHED_BLOCKED_GROUPED = 4
+} pgemm_sched;
+
+/* debug_flags (tests and measurement only). */
+#define PGEMM_DEBUG_WITNESS 0x1u    /* record per-tile visits / owner / order and per-program
+                                       timing into the witness buffers (see pgemm_witness_enable) */
+#define PGEMM_DEBUG_SKIP_RESET 0x2u /* do not zero the work-stealing counters before the launch */
+#define PGEMM_DEBUG_STRAGGLER 0x4u  /* program straggler_program waits straggler_ns before each tile */
+
+/* Optional per-call arguments; pass NULL for all defaults. */
+typedef struct {
+  int tile_m, tile_n, tile_k; /* 0 => default: bf16 256x256x64, fp8 256x256x128 */
+  int group_size;             /* grouped order rows per group; 0 => 8 */
+  int grid;                   /* programs; 0 => number of CUs */
+  int claim_chunk;            /* add only: tiles per work-stealing claim; 0 => default */
+  const uint8_t* a_scale;     /* fp8: device, e8m0 [K/128][M] */
+  const uint8_t* b_scale;     /* fp8: device, e8m0 [K/128][N] */
+  unsigned debug_flags;       /* PGEMM_DEBUG_* */
+  int straggler_program;      /* with PGEMM_DEBUG_STRAGGLER */
+  int straggler_ns;           /* with PGEMM_DEBUG_STRAGGLER */
+} pgemm_args;
+
+typedef struct pgemm_config pgemm_config; /* opaque */
+
+typedef struct {
+  int num_cus;           /* compute units (grid size of a default launch) */
+  int num_xcds;          /* XCDs = number of work-stealing counters in use */
+  int counter_capacity;  /* length of the int32 counter array */
+  int wall_clock_khz;    /* tick rate of the witness timestamps */
+  int clock_khz;         /* peak engine clock */
+  int lds_bytes_per_cu;  /* LDS per compute unit */
+  char arch[64];         /* gcnArchName */
+} pgemm_info;
+
+/* Create a configuration for HIP device `device`: reads the CU count and the
+ * XCD count, allocates and zeroes an int32 work-stealing counter array of
+ * max_xcds entries (0 => 16).  Fails with PGEMM_ERR_INVALID if the device has more XCDs than max_xcds
+ * (the counter index p mod X would run past the array), with
+ * PGEMM_ERR_UNSUPPORTED if the device is not gfx950.  *out receives the new
+ * config, owned by the caller until pgemm_config_destroy. */
+PGEMM_API pgemm_status pgemm_config_create(int device, int max_xcds, pgemm_config** out);
+
+/* Device facts read at creation. */
+PGEMM_API pgemm_status pgemm_config_query(const pgemm_config* cfg, pgemm_info* info);
+
+/* Free the counters and witness buffers (after the caller has synchronised
+ * the streams that used them).  NULL is a no-op. */
+PGEMM_API pgemm_status pgemm_config_destroy(pgemm_config* cfg);
+
+/* C[M][N] = A[M][K] . B[K][N], all dense row-major on device `cfg`'s GPU.
+ * A, B, C: device pointers owned by the caller; C must not alias A or B.
+ * Elements of C outside [0, M) x [0, N) are never written.  With
+ * PGEMM_SCHED_WORK_STEALING the counters are zeroed on `hip_stream` first.
+ * A config holds one counter array: calls with the same config on different
+ * streams must not overlap.  Errors: NULL pointer, M, N or K < 1,
+ * group_size < 1, grid < 1 (or < X for work stealing), fp8 without scales or
+ * with K % 128 != 0 => PGEMM_ERR_INVALID; tile shape not built =>
+ * PGEMM_ERR_UNSUPPORTED. */
+PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
+                       int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
+                       pgemm_sched sched, const pgemm_args* args, void* hip_stream);
+
+/* C[rows][cols] = X + Y (fp32, one IEEE add per element, round to nearest
+ * even), persistent over tile_rows x tile_cols tiles with the same
+ * schedulers (tile rows are dimension 0 of the decode).  Built tiles: 32x16,
+ * 64x64, 128x128.  Same ownership, error and stream rules as pgemm_run.
+ * C may alias X or Y exactly (in place), not partially. */
+PGEMM_API pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* C,
+                      int64_t rows, int64_t cols, int tile_rows, int tile_cols,
+                      pgemm_sched sched, const pgemm_args* args, void* hip_stream);
+
+/* Witness buffers for PGEMM_DEBUG_WITNESS launches: per tile (up to
+ * max_tiles) visit count, owner program and position in the owner's
+ * sequence; per program (up to max_programs) start / end wall-clock ticks,
+ * hardware id and tile count.  Allocated on device by this call and owned by
+ * the config. */
+PGEMM_API pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_programs);
+
+typedef struct {      /* host arrays supplied by the caller */
+  int32_t* visits;    /* [tiles] */
+  int32_t* owner;     /* [tiles] */
+  int32_t* order;     /* [tiles] */
+  int64_t tiles;      /* entries to copy */
+  int64_t* t_start;   /* [programs] wall-clock ticks */
+  int64_t* t_end;     /* [programs] */
+  int32_t* hw_id;     /* [programs] bits 0-15: HW_ID register low half; bits 16-19: XCC id */
+  int32_t* n_tiles;   /* [programs] */
+  int32_t programs;   /* entries to copy */
+  int32_t* counters;  /* [counter_capacity] work-stealing counters after the launch */
+} pgemm_witness;
+
+/* Synchronise `hip_stream` and copy the witness of the last launch into the
+ * caller's host arrays (any array may be NULL to skip it). */
+PGEMM_API pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip_stream);
+
+/* Static string for a status code. */
+PGEMM_API const char* pgemm_status_str(pgemm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGEMM_H */

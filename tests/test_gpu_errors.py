@@ -1,0 +1,127 @@
+"""Argument checking of the C ABI on a GPU, and failure detection forced from
+the host (stale counters, a straggling program).  Every kernel launched here
+exits normally."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import tile_scheduling_persistent_amd as pg
+from tile_scheduling_persistent_amd import _abi
+from synthetic import bf16_bits_uniform
+from tests.gpu_util import config, dev_bf16, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _status(fn, *a):
+    return fn(*a)
+
+
+def test_config_rejects_small_counter_array():
+    h = ctypes.c_void_p()
+    X = config().info["num_xcds"]
+    assert _abi.lib().pgemm_config_create(0, X - 1, ctypes.byref(h)) == _abi.ERR_INVALID
+    assert _abi.lib().pgemm_config_create(99, 0, ctypes.byref(h)) == _abi.ERR_INVALID
+    assert _abi.lib().pgemm_config_create(0, 0, None) == _abi.ERR_INVALID
+    with pg.Config(0, X) as c:
+        assert c.info["counter_capacity"] == X
+
+
+def test_device_facts():
+    info = config().info
+    assert info["arch"].startswith("gfx950")
+    assert info["num_cus"] >= info["num_xcds"] >= 1
+    note(f"device facts {info}")
+
+
+def test_invalid_arguments_enqueue_nothing():
+    cfg = config()
+    L = _abi.lib()
+    A = torch.zeros(64 * 64, dtype=torch.bfloat16, device="cuda:0")
+    B = torch.zeros(64 * 64, dtype=torch.bfloat16, device="cuda:0")
+    C = torch.full((64 * 64,), 7.0, dtype=torch.float32, device="cuda:0")
+    s = torch.cuda.current_stream().cuda_stream
+    a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    run = lambda *x: L.pgemm_run(cfg.handle, *x)  # noqa: E731
+    assert run(None, b, c, 64, 64, 64, 0, 0, None, s) == _abi.ERR_INVALID
+    assert run(a, b, c, 0, 64, 64, 0, 0, None, s) == _abi.ERR_INVALID
+    assert run(a, b, c, 64, -1, 64, 0, 0, None, s) == _abi.ERR_INVALID
+    assert run(a, b, c, 64, 64, 64, 9, 0, None, s) == _abi.ERR_INVALID          # dtype
+    assert run(a, b, c, 64, 64, 64, 0, 17, None, s) == _abi.ERR_INVALID         # sched
+    assert run(a, b, a, 64, 64, 64, 1, 0, None, s) == _abi.ERR_INVALID          # C aliases A
+    host = np.zeros(64 * 64, np.float32)
+    assert run(a, b, host.ctypes.data, 64, 64, 64, 0, 0, None, s) == _abi.ERR_INVALID
+    args = pg.make_args(tile=(64, 32, 16))
+    assert run(a, b, c, 64, 64, 64, 0, 0, ctypes.byref(args), s) == _abi.ERR_UNSUPPORTED
+    args = pg.make_args(group_size=-1)
+    assert run(a, b, c, 64, 64, 64, 0, 2, ctypes.byref(args), s) == _abi.ERR_INVALID
+    args = pg.make_args(grid=cfg.info["num_xcds"] - 1)
+    assert run(a, b, c, 64, 64, 64, 0, 3, ctypes.byref(args), s) == _abi.ERR_INVALID
+    # fp8 without scales, or K not a multiple of 128
+    assert run(a, b, c, 64, 64, 128, 2, 0, None, s) == _abi.ERR_INVALID
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+    X = torch.zeros(100, dtype=torch.float32, device="cuda:0")
+    assert L.padd_run(cfg.handle, X.data_ptr(), X.data_ptr(), X.data_ptr(), 10, 10, 7, 7, 0,
+                      None, s) == _abi.ERR_UNSUPPORTED
+    assert L.padd_run(cfg.handle, X.data_ptr(), X.data_ptr(), X.data_ptr() + 4, 10, 9, 32, 16, 0,
+                      None, s) == _abi.ERR_INVALID                              # partial overlap
+
+
+def test_stale_counters_are_detected():
+    """Skipping the counter reset leaves the counters at their final values:
+    every claim fails, no tile is computed, and the witness shows it."""
+    cfg = config()
+    M = N = 1024
+    K = 128
+    a, b = bf16_bits_uniform((M, K), 1), bf16_bits_uniform((K, N), 2)
+    A, B = dev_bf16(a), dev_bf16(b)
+    T = 16
+    cfg.witness_enable(T, cfg.info["num_cus"])
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+    flags = _abi.DEBUG_WITNESS
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing", pg.make_args(debug_flags=flags))
+    w1 = cfg.witness_read(T, cfg.info["num_cus"])
+    assert np.all(w1["visits"] == 1)
+    C.fill_(-5.0)
+    note("work stealing with the reset skipped")
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing",
+                 pg.make_args(debug_flags=flags | _abi.DEBUG_SKIP_RESET))
+    w2 = cfg.witness_read(T, cfg.info["num_cus"])
+    torch.cuda.synchronize()
+    assert np.all(w2["visits"] == 0)
+    assert torch.all(C == -5.0)
+    # the normal path resets and recovers
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing", pg.make_args(debug_flags=flags))
+    w3 = cfg.witness_read(T, cfg.info["num_cus"])
+    assert np.all(w3["visits"] == 1)
+
+
+def test_straggler_rebalanced_by_work_stealing():
+    """Program 0 waits 200 us before each tile: under work stealing its XCD
+    peers take its share; under blocked ranges it keeps its full share."""
+    cfg = config()
+    G, X = cfg.info["num_cus"], cfg.info["num_xcds"]
+    M = N = 4096
+    K = 256
+    tile = (128, 128, 64)
+    T = (M // 128) * (N // 128)            # 1024 tiles: 4 per program on average
+    a, b = bf16_bits_uniform((M, K), 1), bf16_bits_uniform((K, N), 2)
+    A, B = dev_bf16(a), dev_bf16(b)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    cfg.witness_enable(T, G)
+    flags = _abi.DEBUG_WITNESS | _abi.DEBUG_STRAGGLER
+    res = {}
+    for sched in ["blocked", "work_stealing"]:
+        note(f"straggler {sched}")
+        pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", sched,
+                     pg.make_args(tile=tile, debug_flags=flags, straggler_program=0,
+                                  straggler_ns=200_000))
+        w = cfg.witness_read(T, G)
+        assert np.all(w["visits"] == 1)
+        res[sched] = int(w["n_tiles"][0])
+    assert res["blocked"] == T // G
+    peers = [p for p in range(G) if p % X == 0]
+    assert res["work_stealing"] < T // G, res

@@ -1,0 +1,94 @@
+"""GPU schedule witness: every tile computed exactly once under every scheduler;
+static schedules equal the oracle's model tile for tile; work-stealing runs
+satisfy the model's invariants (owner on the right XCD, increasing claims,
+final counters)."""
+import numpy as np
+import pytest
+import torch
+
+import tile_scheduling_persistent_amd as pg
+from oracle import sched_model as sm
+from synthetic import bf16_bits_uniform, f32_normal
+from tests.gpu_util import config, dev_bf16, dev_f32, note
+
+pytestmark = pytest.mark.gpu
+
+STATIC = ["blocked", "interleaved", "grouped", "blocked_grouped"]
+
+
+def _check(w, kind, pm, pn, G, X, gs, chunk=1):
+    T = pm * pn
+    visits, owner, order = w["visits"][:T], w["owner"][:T], w["order"][:T]
+    assert np.all(visits == 1), f"{kind}: tiles visited {np.unique(visits)} times"
+    assert int(w["n_tiles"][:G].sum()) == T
+    if kind in STATIC:
+        model = sm.static_schedule(kind, pm, pn, G, gs)
+        for p, seq in enumerate(model):
+            for i, (v, _, _) in enumerate(seq):
+                assert owner[v] == p and order[v] == i, (kind, v, owner[v], p, order[v], i)
+            assert w["n_tiles"][p] == len(seq)
+    else:
+        sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(),
+                              w["counters"].tolist(), T, G, X, chunk)
+
+
+def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
+    cfg = config()
+    G = grid or cfg.info["num_cus"]
+    pm, pn = -(-M // tile[0]), -(-N // tile[1])
+    cfg.witness_enable(pm * pn, G)
+    a = bf16_bits_uniform((M, K), 1)
+    b = bf16_bits_uniform((K, N), 2)
+    A, B = dev_bf16(a), dev_bf16(b)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    note(f"witness gemm {M}x{N}x{K} tile={tile} {sched} gs={gs} grid={G}")
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched,
+                 pg.make_args(tile=tile, group_size=gs, grid=grid, debug_flags=pg._abi.DEBUG_WITNESS))
+    w = cfg.witness_read(pm * pn, G)
+    # the witness build computes the same bits as the timed build
+    C2 = torch.empty_like(C)
+    pg.pgemm_run(cfg, A, B, C2, M, N, K, "bf16_out_bf16", sched,
+                 pg.make_args(tile=tile, group_size=gs, grid=grid))
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    return w, pm, pn, G, cfg.info["num_xcds"]
+
+
+@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("shape,tile", [
+    ((512, 512, 512), (128, 128, 64)),
+    ((5120, 5120, 256), (256, 256, 64)),
+    ((3000, 7000, 128), (256, 256, 64)),
+    ((8192, 8192, 64), (256, 256, 64)),
+])
+def test_gemm_schedule_exactly_once(sched, shape, tile):
+    M, N, K = shape
+    w, pm, pn, G, X = _gemm_witness(M, N, K, tile, sched)
+    _check(w, sched, pm, pn, G, X, 8)
+
+
+@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("grid", [1, 7, 8, 13, 300])
+def test_gemm_schedule_grid_override(sched, grid):
+    if sched == "work_stealing" and grid < config().info["num_xcds"]:
+        pytest.skip("work stealing needs at least one program per XCD")
+    w, pm, pn, G, X = _gemm_witness(1100, 900, 64, (128, 128, 64), sched, gs=3, grid=grid)
+    _check(w, sched, pm, pn, G, X, 3)
+
+
+@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("tile", [(32, 16), (128, 128)])
+def test_add_schedule_exactly_once(sched, tile):
+    cfg = config()
+    rows, cols = 2048, 3000
+    pm, pn = -(-rows // tile[0]), -(-cols // tile[1])
+    G = cfg.info["num_cus"]
+    cfg.witness_enable(pm * pn, G)
+    X, Y = dev_f32(f32_normal((rows, cols), 1)), dev_f32(f32_normal((rows, cols), 2))
+    C = torch.empty_like(X)
+    note(f"witness add {rows}x{cols} tile={tile} {sched}")
+    pg.padd_run(cfg, X, Y, C, rows, cols, tile[0], tile[1], sched,
+                pg.make_args(debug_flags=pg._abi.DEBUG_WITNESS))
+    w = cfg.witness_read(pm * pn, G)
+    chunk = {(32, 16): 16, (64, 64): 2, (128, 128): 1}[tile]
+    _check(w, sched, pm, pn, G, cfg.info["num_xcds"], 8, chunk)

@@ -1,0 +1,163 @@
+"""Persistent tiled GEMM and persistent 2-D add with tile schedulers, for
+AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of libpgemm.so (include/pgemm.h): the
+functions keep the C names, marshal torch device tensors (or raw device
+pointers) and the current HIP stream, and raise PgemmError on a non-zero
+status.  Every step of the hot path runs in the library's HIP kernels;
+PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _abi
+from ._abi import PgemmError, status_str  # noqa: F401
+
+SCHEDULERS = {
+    "blocked": _abi.SCHED_BLOCKED,
+    "interleaved": _abi.SCHED_INTERLEAVED,
+    "grouped": _abi.SCHED_GROUPED,
+    "work_stealing": _abi.SCHED_WORK_STEALING,
+    "blocked_grouped": _abi.SCHED_BLOCKED_GROUPED,
+}
+DTYPES = {
+    "bf16_out_f32": _abi.BF16_OUT_F32,
+    "bf16_out_bf16": _abi.BF16_OUT_BF16,
+    "fp8_b128_out_bf16": _abi.FP8E4M3_B128_OUT_BF16,
+}
+
+__all__ = ["Config", "pgemm_run", "padd_run", "SCHEDULERS", "DTYPES", "PgemmError", "status_str",
+           "make_args"]
+
+
+def _check(where, code):
+    if code != _abi.OK:
+        raise PgemmError(where, code)
+
+
+def _ptr(x, what, dtype=None):
+    """Device pointer of a torch tensor (contiguous, on a GPU) or a raw int pointer."""
+    if isinstance(x, int):
+        return x
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor or an int device pointer")
+    if not x.is_cuda:
+        raise ValueError(f"{what}: tensor must live on the GPU")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous (row-major)")
+    if dtype is not None and x.dtype not in dtype:
+        raise ValueError(f"{what}: dtype {x.dtype} not in {dtype}")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _sched(s):
+    return SCHEDULERS[s] if isinstance(s, str) else int(s)
+
+
+def _dtype(d):
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_scale=None,
+              debug_flags=0, straggler_program=-1, straggler_ns=0):
+    a = _abi.pgemm_args()
+    if tile is not None:
+        a.tile_m, a.tile_n, a.tile_k = (tuple(tile) + (0,))[:3]
+    a.group_size = group_size
+    a.grid = grid
+    a.claim_chunk = claim_chunk
+    a.a_scale = _ptr(a_scale, "a_scale") if a_scale is not None else None
+    a.b_scale = _ptr(b_scale, "b_scale") if b_scale is not None else None
+    a.debug_flags = debug_flags
+    a.straggler_program = straggler_program
+    a.straggler_ns = straggler_ns
+    return a
+
+
+class Config:
+    """pgemm_config: device facts plus the reusable per-XCD counters."""
+
+    def __init__(self, device: int = 0, max_xcds: int = 0):
+        h = ctypes.c_void_p()
+        _check("pgemm_config_create", _abi.lib().pgemm_config_create(int(device), int(max_xcds),
+                                                                      ctypes.byref(h)))
+        self.handle = h
+        self.device = int(device)
+        info = _abi.pgemm_info()
+        _check("pgemm_config_query", _abi.lib().pgemm_config_query(h, ctypes.byref(info)))
+        self.info = {
+            "num_cus": info.num_cus, "num_xcds": info.num_xcds,
+            "counter_capacity": info.counter_capacity, "wall_clock_khz": info.wall_clock_khz,
+            "clock_khz": info.clock_khz, "lds_bytes_per_cu": info.lds_bytes_per_cu,
+            "arch": info.arch.decode(),
+        }
+
+    def close(self):
+        if self.handle is not None:
+            _abi.lib().pgemm_config_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def witness_enable(self, max_tiles: int, max_programs: int):
+        _check("pgemm_witness_enable",
+               _abi.lib().pgemm_witness_enable(self.handle, int(max_tiles), int(max_programs)))
+
+    def witness_read(self, tiles: int, programs: int, stream=None):
+        out = {
+            "visits": np.zeros(tiles, np.int32), "owner": np.zeros(tiles, np.int32),
+            "order": np.zeros(tiles, np.int32), "t_start": np.zeros(programs, np.int64),
+            "t_end": np.zeros(programs, np.int64), "hw_id": np.zeros(programs, np.int32),
+            "n_tiles": np.zeros(programs, np.int32),
+            "counters": np.zeros(self.info["counter_capacity"], np.int32),
+        }
+        w = _abi.pgemm_witness()
+        for k in ("visits", "owner", "order", "t_start", "t_end", "hw_id", "n_tiles", "counters"):
+            setattr(w, k, out[k].ctypes.data)
+        w.tiles = tiles
+        w.programs = programs
+        _check("pgemm_witness_read",
+               _abi.lib().pgemm_witness_read(self.handle, ctypes.byref(w), _stream(stream)))
+        return out
+
+
+def pgemm_run(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=None,
+              stream=None):
+    """C[M][N] = A[M][K] . B[K][N] on the GPU (asynchronous on `stream`)."""
+    a = args if args is not None else None
+    code = _abi.lib().pgemm_run(cfg.handle, _ptr(A, "A"), _ptr(B, "B"), _ptr(C, "C"),
+                                int(M), int(N), int(K), _dtype(dtype), _sched(sched),
+                                ctypes.byref(a) if a is not None else None, _stream(stream))
+    _check("pgemm_run", code)
+
+
+def padd_run(cfg: Config, X, Y, C, rows: int, cols: int, tile_rows: int, tile_cols: int, sched,
+             args=None, stream=None):
+    """C = X + Y (fp32) over tile_rows x tile_cols tiles (asynchronous on `stream`)."""
+    code = _abi.lib().padd_run(cfg.handle, _ptr(X, "X"), _ptr(Y, "Y"), _ptr(C, "C"),
+                               int(rows), int(cols), int(tile_rows), int(tile_cols), _sched(sched),
+                               ctypes.byref(args) if args is not None else None, _stream(stream))
+    _check("padd_run", code)

@@ -1,0 +1,146 @@
+// Shared definitions of the HIP library: kernel parameter blocks, launcher
+// declarations and the device-side tile walker used by every persistent
+// kernel (GEMM bf16, GEMM block-scaled fp8, 2-D add).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sched.hpp"
+
+namespace pgk {
+
+// Optional instrumentation buffers (all NULL unless the witness is on).
+struct Witness {
+  int* visits;        // [T] times tile v was computed
+  int* owner;         // [T] program that computed tile v
+  int* order;         // [T] position of tile v in its owner's sequence
+  long long* t_start; // [G] wall clock at program start
+  long long* t_end;   // [G] wall clock at program end
+  int* hw_id;         // [G] hardware placement of the program
+  int* n_tiles;       // [G] tiles the program computed
+};
+
+struct SchedParams {
+  int kind;           // pgs::Kind
+  int T;              // tiles
+  int G;              // programs (grid)
+  int X;              // XCDs = counters in use (work stealing)
+  int gs;             // group size of the grouped order
+  int num_pid_m;      // tiles along dimension 0 (rows)
+  int num_pid_n;      // tiles along dimension 1 (columns)
+  int* counters;      // work-stealing counters, zero at launch
+  int chunk;          // tiles per work-stealing claim
+  int straggler_program;  // -1: off
+  int straggler_ns;
+  int wall_khz;       // wall-clock tick rate (straggler wait)
+};
+
+struct GemmParams {
+  const void* A;      // [M][K]
+  const void* B;      // [K][N]
+  void* C;            // [M][N]
+  const uint8_t* sa;  // fp8: [K/128][M]
+  const uint8_t* sb;  // fp8: [K/128][N]
+  int M, N, K;
+  SchedParams s;
+  Witness w;
+};
+
+struct AddParams {
+  const float* X;
+  const float* Y;
+  float* C;
+  int rows, cols;
+  SchedParams s;
+  Witness w;
+};
+
+// Launchers: return hipErrorInvalidValue when no kernel is built for the
+// requested tile shape.
+hipError_t launch_gemm_bf16(const GemmParams& p, int bm, int bn, int bk, bool out_bf16,
+                            bool vec, bool witness, hipStream_t stream);
+hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec,
+                           bool witness, hipStream_t stream);
+hipError_t launch_padd(const AddParams& p, int tr, int tc, bool vec, bool witness,
+                       hipStream_t stream);
+hipError_t launch_zero_i32(int* ptr, int n, hipStream_t stream);
+hipError_t launch_fill_i32(int* ptr, int n, int value, hipStream_t stream);
+bool gemm_bf16_tile_supported(int bm, int bn, int bk);
+bool gemm_bf16_vec_fits(int bm, int bk, long long N, long long K);
+bool gemm_fp8_tile_supported(int bm, int bn, int bk);
+bool padd_tile_supported(int tr, int tc);
+int padd_tiles_per_step(int tr, int tc);
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+// Wall clock (constant rate, see hipDeviceAttributeWallClockRate).
+__device__ __forceinline__ long long wall_ticks() { return (long long)wall_clock64(); }
+
+// Placement of the calling wave: HW_ID low half (CU, SH, SE fields) and the
+// XCC id in bits 16-19.
+__device__ __forceinline__ int hw_placement() {
+  const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID, 32 bits
+  const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, 4 bits
+  return (int)((hw & 0xffffu) | ((xcc & 0xfu) << 16));
+}
+
+// Bounded wait used by the straggler debug flag: returns after `ns`.
+__device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
+  const long long t0 = wall_ticks();
+  const long long ticks = ((long long)ns * wall_khz) / 1000000LL;
+  while (wall_ticks() - t0 < ticks) __builtin_amdgcn_s_sleep(2);
+}
+
+// Per-program view of the scheduler.  Static kinds walk arithmetically; the
+// work-stealing kind claims from counter p mod X.  first()/next() return a
+// tile id or -1 when the program is done.  For work stealing only one
+// thread of the workgroup may call them (each call is one claim).
+struct Walker {
+  SchedParams s;
+  int p;
+  int end;       // static: end of the walk
+  int x;         // work stealing: XCD / counter index
+  int begin, n;  // work stealing: the XCD's range [begin, begin + n)
+
+  __device__ __forceinline__ Walker(const SchedParams& sp, int prog) : s(sp), p(prog) {
+    end = 0;
+    x = prog % (sp.X > 0 ? sp.X : 1);
+    begin = pgs::ws_range_begin(x, sp.T, sp.X > 0 ? sp.X : 1);
+    n = pgs::ws_range_begin(x + 1, sp.T, sp.X > 0 ? sp.X : 1) - begin;
+  }
+
+  // One claim of s.chunk tiles; returns the first claimed id or -1.
+  __device__ __forceinline__ int claim() {
+    const int i = __hip_atomic_fetch_add(s.counters + x, s.chunk, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return (i >= 0 && i < n) ? begin + i : -1;
+  }
+
+  // End (exclusive) of the chunk that starts at v (work stealing).
+  __device__ __forceinline__ int claim_end(int v) const {
+    const int e = v + s.chunk;
+    return e < begin + n ? e : begin + n;
+  }
+
+  __device__ __forceinline__ int first() {
+    if (s.kind == pgs::kWorkStealing) return claim();
+    int v;
+    pgs::static_first(s.kind, p, s.T, s.G, v, end);
+    return v < end ? v : -1;
+  }
+
+  __device__ __forceinline__ int next(int v) {
+    if (s.kind == pgs::kWorkStealing) return claim();
+    const int nv = pgs::static_next(s.kind, v, s.G, end);
+    return nv < end ? nv : -1;
+  }
+
+  __device__ __forceinline__ void tile_coords(int v, int& pid_m, int& pid_n) const {
+    pgs::decode(s.kind, v, s.num_pid_m, s.num_pid_n, s.gs, pid_m, pid_n);
+  }
+};
+
+#endif
+
+}  // namespace pgk

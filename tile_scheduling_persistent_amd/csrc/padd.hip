@@ -1,0 +1,215 @@
+// Persistent element-wise 2-D add for gfx950: C = X + Y in fp32.
+//
+// "Implement persistent kernels" (Helion PR #238), example output: a grid of
+// one program per compute unit walks tiles of TR rows x TC columns (blocked,
+// interleaved, or L2-grouped order), decodes each tile id with rows of tiles
+// fastest, and does a masked load of x and y, one add, a masked store.  The
+// per-XCD work-stealing walk of "Work Stealing Scheduler Kernel" (tritonBLAS
+// PR #65) applies unchanged.
+//
+// The add is bound by HBM bandwidth, so a workgroup keeps U tiles of its
+// sequence in flight at once: every thread issues all its 16-byte loads of X
+// and Y for the U tiles before any add, which gives each compute unit about
+// 64 KiB of outstanding reads.  The tiles of a step are the next U tiles the
+// scheduler gives the program (for work stealing: one claim of U tiles, and
+// the claim for the following step is issued before the current step's
+// loads so its latency is hidden).
+#include "common.hpp"
+
+namespace pgk {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+template <int TR, int TC>
+struct AddShape {
+  static constexpr int F4 = TR * TC / 4;  // float4 per tile
+  // tiles per step: ~8 float4 per thread per operand
+  static constexpr int U = (8 * kThreads) / F4 > 0 ? (8 * kThreads) / F4 : 1;
+  static constexpr int SLOTS = (U * F4 + kThreads - 1) / kThreads;
+  static_assert(TC % 4 == 0, "tile columns must be a multiple of 4");
+};
+
+template <int TR, int TC, bool VEC, bool WITNESS>
+__global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
+  using S = AddShape<TR, TC>;
+  __shared__ int s_claim[2];
+  const int tid = threadIdx.x;
+  const int prog = blockIdx.x;
+  const int rows = P.rows, cols = P.cols;
+  const bool ws = P.s.kind == pgs::kWorkStealing;
+  Walker walker(P.s, prog);
+  long long t_start = 0;
+  if (WITNESS && tid == 0) t_start = wall_ticks();
+
+  // Static kinds: every thread walks the same sequence itself.  Work
+  // stealing: thread 0 claims, the result is shared through LDS.
+  int v0;
+  if (ws) {
+    if (tid == 0) s_claim[0] = walker.claim();
+    __syncthreads();
+    v0 = s_claim[0];
+  } else {
+    v0 = walker.first();
+  }
+  int done = 0;  // tiles computed so far by this program
+  int step = 0;
+  while (v0 >= 0) {
+    // tile ids of this step
+    int vt[S::U];
+    int next_v0 = -1;
+    if (ws) {
+      if (tid == 0) s_claim[(step + 1) & 1] = walker.claim();
+      const int e = walker.claim_end(v0);
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) vt[u] = (v0 + u < e) ? v0 + u : -1;
+    } else {
+      int v = v0;
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) {
+        vt[u] = v;
+        if (v >= 0) v = walker.next(v);
+      }
+      next_v0 = v;
+    }
+    if (WITNESS && tid == 0) {
+#pragma unroll
+      for (int u = 0; u < S::U; ++u)
+        if (vt[u] >= 0) {
+          atomicAdd(P.w.visits + vt[u], 1);
+          P.w.owner[vt[u]] = prog;
+          P.w.order[vt[u]] = done + u;
+        }
+    }
+    if (tid == 0 && P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
+
+    f32x4 xa[S::SLOTS], ya[S::SLOTS];
+    long long off[S::SLOTS];
+    int cnt[S::SLOTS];
+#pragma unroll
+    for (int j = 0; j < S::SLOTS; ++j) {
+      const int idx = j * kThreads + tid;
+      const int u = idx / S::F4;
+      const int e = idx % S::F4;
+      cnt[j] = 0;
+      off[j] = 0;
+      if (u < S::U && vt[u] >= 0) {
+        int pm, pn;
+        walker.tile_coords(vt[u], pm, pn);
+        const int r = pm * TR + e / (TC / 4);
+        const int c = pn * TC + (e % (TC / 4)) * 4;
+        if (r < rows && c < cols) {
+          off[j] = (long long)r * cols + c;
+          cnt[j] = cols - c < 4 ? cols - c : 4;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S::SLOTS; ++j) {
+      if (VEC) {
+        if (cnt[j] > 0) {
+          xa[j] = *reinterpret_cast<const f32x4*>(P.X + off[j]);
+          ya[j] = *reinterpret_cast<const f32x4*>(P.Y + off[j]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xa[j][q] = q < cnt[j] ? P.X[off[j] + q] : 0.0f;
+          ya[j][q] = q < cnt[j] ? P.Y[off[j] + q] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S::SLOTS; ++j) {
+      if (cnt[j] <= 0) continue;
+      const f32x4 z = xa[j] + ya[j];
+      if (VEC) {
+        *reinterpret_cast<f32x4*>(P.C + off[j]) = z;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < cnt[j]) P.C[off[j] + q] = z[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) done += vt[u] >= 0 ? 1 : 0;
+
+    if (ws) {
+      __syncthreads();
+      v0 = s_claim[(step + 1) & 1];
+    } else {
+      v0 = next_v0;
+    }
+    ++step;
+  }
+
+  if (WITNESS && tid == 0) {
+    P.w.t_start[prog] = t_start;
+    P.w.t_end[prog] = wall_ticks();
+    P.w.hw_id[prog] = hw_placement();
+    P.w.n_tiles[prog] = done;
+  }
+}
+
+template <int TR, int TC>
+hipError_t launch_tile(const AddParams& p, bool vec, bool witness, hipStream_t stream) {
+  if (vec) {
+    if (witness)
+      hipLaunchKernelGGL((padd_kernel<TR, TC, true, true>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((padd_kernel<TR, TC, true, false>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+  } else {
+    if (witness)
+      hipLaunchKernelGGL((padd_kernel<TR, TC, false, true>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((padd_kernel<TR, TC, false, false>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+__global__ void zero_i32_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+__global__ void fill_i32_kernel(int* p, int n, int value) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+}  // namespace
+
+int padd_tiles_per_step(int tr, int tc) {
+  if (tr == 32 && tc == 16) return AddShape<32, 16>::U;
+  if (tr == 64 && tc == 64) return AddShape<64, 64>::U;
+  if (tr == 128 && tc == 128) return AddShape<128, 128>::U;
+  return 1;
+}
+
+bool padd_tile_supported(int tr, int tc) {
+  return (tr == 32 && tc == 16) || (tr == 64 && tc == 64) || (tr == 128 && tc == 128);
+}
+
+hipError_t launch_padd(const AddParams& p, int tr, int tc, bool vec, bool witness,
+                       hipStream_t stream) {
+  if (tr == 32 && tc == 16) return launch_tile<32, 16>(p, vec, witness, stream);
+  if (tr == 64 && tc == 64) return launch_tile<64, 64>(p, vec, witness, stream);
+  if (tr == 128 && tc == 128) return launch_tile<128, 128>(p, vec, witness, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_i32(int* ptr, int n, int value, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, stream, ptr, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int* ptr, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, ptr, n);
+  return hipGetLastError();
+}
+
+}  // namespace pgk

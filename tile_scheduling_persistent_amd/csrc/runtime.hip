@@ -1,0 +1,408 @@
+// C ABI of the library (include/pgemm.h): configuration, argument checks,
+// stream-ordered counter reset and kernel launch.
+//
+// The configuration object follows the matmul wrapper reviewed in "Work
+// Stealing Scheduler Kernel" (tritonBLAS PR #65): it reads the CU count of
+// the device once, preallocates the int32 per-XCD tile counters (max_xcds
+// entries, 16 by default) for reuse across calls, and the counters are reset
+// before every work-stealing launch.  The reviewed defects become checks
+// here: the device is an int ordinal; the XCD count may not exceed the
+// counter array; only device pointers are accepted.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/pgemm.h"
+#include "common.hpp"
+
+struct pgemm_config {
+  int device;
+  int num_cus;
+  int num_xcds;
+  int capacity;
+  int wall_khz;
+  int clock_khz;
+  int lds_per_cu;
+  char arch[64];
+  int* counters;  // device, [capacity]
+  // witness buffers (device)
+  int64_t w_tiles;
+  int w_programs;
+  int* w_visits;
+  int* w_owner;
+  int* w_order;
+  long long* w_t_start;
+  long long* w_t_end;
+  int* w_hw_id;
+  int* w_n_tiles;
+};
+
+namespace {
+
+constexpr int kDefaultMaxXcds = 16;
+constexpr int kDefaultGroup = 8;
+
+pgemm_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return PGEMM_OK;
+  if (e == hipErrorOutOfMemory) return PGEMM_ERR_OOM;
+  return PGEMM_ERR_DEVICE;
+}
+
+// Is p a device (or managed) allocation of device `dev`?
+bool is_device_ptr(const void* p, int dev) {
+  if (p == nullptr) return false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return false;
+  return attr.device == dev;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+void free_witness(pgemm_config* c) {
+  void* ptrs[] = {c->w_visits, c->w_owner, c->w_order, c->w_t_start,
+                  c->w_t_end, c->w_hw_id, c->w_n_tiles};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  c->w_visits = c->w_owner = c->w_order = c->w_hw_id = c->w_n_tiles = nullptr;
+  c->w_t_start = c->w_t_end = nullptr;
+  c->w_tiles = 0;
+  c->w_programs = 0;
+}
+
+// Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
+pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
+                        int num_pid_m, int num_pid_n, pgk::SchedParams& s) {
+  if ((int)sched < 0 || (int)sched > 4) return PGEMM_ERR_INVALID;
+  const int64_t T = (int64_t)num_pid_m * num_pid_n;
+  if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  s.kind = (int)sched;
+  s.T = (int)T;
+  s.G = (args && args->grid) ? args->grid : cfg->num_cus;
+  s.X = cfg->num_xcds;
+  s.gs = (args && args->group_size) ? args->group_size : kDefaultGroup;
+  s.num_pid_m = num_pid_m;
+  s.num_pid_n = num_pid_n;
+  s.counters = cfg->counters;
+  s.chunk = 1;
+  s.straggler_program = -1;
+  s.straggler_ns = 0;
+  s.wall_khz = cfg->wall_khz;
+  if (s.G < 1 || s.gs < 1) return PGEMM_ERR_INVALID;
+  if (s.kind == pgs::kWorkStealing && s.G < s.X) return PGEMM_ERR_INVALID;
+  if (s.X < 1 || s.X > cfg->capacity) return PGEMM_ERR_INVALID;
+  if (args && (args->debug_flags & PGEMM_DEBUG_STRAGGLER)) {
+    if (args->straggler_ns < 0 || args->straggler_ns > 1000000000) return PGEMM_ERR_INVALID;
+    s.straggler_program = args->straggler_program;
+    s.straggler_ns = args->straggler_ns;
+  }
+  return PGEMM_OK;
+}
+
+pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
+                          pgk::Witness& w, bool& on, hipStream_t stream) {
+  memset(&w, 0, sizeof(w));
+  on = args && (args->debug_flags & PGEMM_DEBUG_WITNESS);
+  if (!on) return PGEMM_OK;
+  if (cfg->w_visits == nullptr || s.T > cfg->w_tiles || s.G > cfg->w_programs)
+    return PGEMM_ERR_INVALID;
+  w.visits = cfg->w_visits;
+  w.owner = cfg->w_owner;
+  w.order = cfg->w_order;
+  w.t_start = cfg->w_t_start;
+  w.t_end = cfg->w_t_end;
+  w.hw_id = cfg->w_hw_id;
+  w.n_tiles = cfg->w_n_tiles;
+  // visits start at 0, owner / order at -1 (fill kernels, no memset nodes)
+  hipError_t e = pgk::launch_fill_i32(w.visits, s.T, 0, stream);
+  if (e == hipSuccess) e = pgk::launch_fill_i32(w.owner, s.T, -1, stream);
+  if (e == hipSuccess) e = pgk::launch_fill_i32(w.order, s.T, -1, stream);
+  if (e == hipSuccess) e = pgk::launch_fill_i32(w.n_tiles, s.G, 0, stream);
+  return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
+pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
+                            hipStream_t stream) {
+  if (s.kind != pgs::kWorkStealing) return PGEMM_OK;
+  if (args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET)) return PGEMM_OK;
+  // a fill kernel rather than a memset node, so that the call may be captured
+  return pgk::launch_zero_i32(cfg->counters, cfg->capacity, stream) == hipSuccess
+             ? PGEMM_OK
+             : PGEMM_ERR_LAUNCH;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pgemm_status_str(pgemm_status s) {
+  switch (s) {
+    case PGEMM_OK: return "ok";
+    case PGEMM_ERR_INVALID: return "invalid argument";
+    case PGEMM_ERR_UNSUPPORTED: return "unsupported device or kernel variant";
+    case PGEMM_ERR_DEVICE: return "HIP runtime error";
+    case PGEMM_ERR_OOM: return "device out of memory";
+    case PGEMM_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+pgemm_status pgemm_config_create(int device, int max_xcds, pgemm_config** out) {
+  if (out == nullptr) return PGEMM_ERR_INVALID;
+  *out = nullptr;
+  if (max_xcds < 0 || max_xcds > 1024) return PGEMM_ERR_INVALID;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return PGEMM_ERR_DEVICE;
+  if (device < 0 || device >= ndev) return PGEMM_ERR_INVALID;
+  DeviceGuard g(device);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return PGEMM_ERR_DEVICE;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PGEMM_ERR_UNSUPPORTED;
+  int xcc = 0, wall = 0;
+  if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || xcc < 1)
+    return PGEMM_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, device) != hipSuccess)
+    wall = 100000;
+  const int cap = max_xcds ? max_xcds : kDefaultMaxXcds;
+  if (xcc > cap) return PGEMM_ERR_INVALID;
+
+  pgemm_config* c = new (std::nothrow) pgemm_config();
+  if (!c) return PGEMM_ERR_OOM;
+  memset(c, 0, sizeof(*c));
+  c->device = device;
+  c->num_cus = prop.multiProcessorCount;
+  c->num_xcds = xcc;
+  c->capacity = cap;
+  c->wall_khz = wall > 0 ? wall : 100000;
+  c->clock_khz = prop.clockRate;
+  c->lds_per_cu = (int)prop.maxSharedMemoryPerMultiProcessor;
+  strncpy(c->arch, prop.gcnArchName, sizeof(c->arch) - 1);
+  hipError_t e = hipMalloc((void**)&c->counters, sizeof(int) * cap);
+  if (e == hipSuccess) e = hipMemset(c->counters, 0, sizeof(int) * cap);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    if (c->counters) (void)hipFree(c->counters);
+    delete c;
+    return from_hip(e);
+  }
+  *out = c;
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_config_query(const pgemm_config* cfg, pgemm_info* info) {
+  if (!cfg || !info) return PGEMM_ERR_INVALID;
+  memset(info, 0, sizeof(*info));
+  info->num_cus = cfg->num_cus;
+  info->num_xcds = cfg->num_xcds;
+  info->counter_capacity = cfg->capacity;
+  info->wall_clock_khz = cfg->wall_khz;
+  info->clock_khz = cfg->clock_khz;
+  info->lds_bytes_per_cu = cfg->lds_per_cu;
+  strncpy(info->arch, cfg->arch, sizeof(info->arch) - 1);
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_config_destroy(pgemm_config* cfg) {
+  if (!cfg) return PGEMM_OK;
+  DeviceGuard g(cfg->device);
+  free_witness(cfg);
+  if (cfg->counters) (void)hipFree(cfg->counters);
+  delete cfg;
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_programs) {
+  if (!cfg || max_tiles < 1 || max_tiles > (1LL << 30) || max_programs < 1 ||
+      max_programs > (1 << 20))
+    return PGEMM_ERR_INVALID;
+  DeviceGuard g(cfg->device);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess) return PGEMM_ERR_DEVICE;
+  free_witness(cfg);
+  hipError_t e = hipSuccess;
+  const size_t t = (size_t)max_tiles, p = (size_t)max_programs;
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_visits, sizeof(int) * t);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_owner, sizeof(int) * t);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_order, sizeof(int) * t);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_t_start, sizeof(long long) * p);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_t_end, sizeof(long long) * p);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_hw_id, sizeof(int) * p);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_n_tiles, sizeof(int) * p);
+  if (e != hipSuccess) {
+    free_witness(cfg);
+    return from_hip(e);
+  }
+  cfg->w_tiles = max_tiles;
+  cfg->w_programs = max_programs;
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip_stream) {
+  if (!cfg || !out) return PGEMM_ERR_INVALID;
+  if (cfg->w_visits == nullptr) return PGEMM_ERR_INVALID;
+  if (out->tiles < 0 || out->tiles > cfg->w_tiles || out->programs < 0 ||
+      out->programs > cfg->w_programs)
+    return PGEMM_ERR_INVALID;
+  DeviceGuard g(cfg->device);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  hipStream_t st = (hipStream_t)hip_stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return PGEMM_ERR_DEVICE;
+  struct Copy { void* dst; const void* src; size_t bytes; };
+  const size_t t = (size_t)out->tiles, p = (size_t)out->programs;
+  Copy cps[] = {
+      {out->visits, cfg->w_visits, 4 * t},      {out->owner, cfg->w_owner, 4 * t},
+      {out->order, cfg->w_order, 4 * t},        {out->t_start, cfg->w_t_start, 8 * p},
+      {out->t_end, cfg->w_t_end, 8 * p},        {out->hw_id, cfg->w_hw_id, 4 * p},
+      {out->n_tiles, cfg->w_n_tiles, 4 * p},    {out->counters, cfg->counters, 4 * (size_t)cfg->capacity},
+  };
+  for (const Copy& c : cps) {
+    if (!c.dst || c.bytes == 0) continue;
+    if (hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyDeviceToHost) != hipSuccess)
+      return PGEMM_ERR_DEVICE;
+  }
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M,
+                       int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
+                       const pgemm_args* args, void* hip_stream) {
+  if (!cfg || !A || !B || !C) return PGEMM_ERR_INVALID;
+  if (M < 1 || N < 1 || K < 1 || M > 0x7fffffffLL || N > 0x7fffffffLL || K > 0x7fffffffLL)
+    return PGEMM_ERR_INVALID;
+  const bool fp8 = dtype == PGEMM_FP8E4M3_B128_OUT_BF16;
+  if (!fp8 && dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16)
+    return PGEMM_ERR_INVALID;
+  int bm = 256, bn = 256, bk = fp8 ? 128 : 64;
+  if (args && (args->tile_m || args->tile_n || args->tile_k)) {
+    bm = args->tile_m;
+    bn = args->tile_n;
+    bk = args->tile_k;
+  }
+  if (bm < 1 || bn < 1 || bk < 1) return PGEMM_ERR_INVALID;
+  if (fp8) {
+    if (!args || !args->a_scale || !args->b_scale) return PGEMM_ERR_INVALID;
+    if (K % 128 != 0) return PGEMM_ERR_INVALID;
+    if (!pgk::gemm_fp8_tile_supported(bm, bn, bk)) return PGEMM_ERR_UNSUPPORTED;
+  } else if (!pgk::gemm_bf16_tile_supported(bm, bn, bk)) {
+    return PGEMM_ERR_UNSUPPORTED;
+  }
+  const int dev = cfg->device;
+  if (!is_device_ptr(A, dev) || !is_device_ptr(B, dev) || !is_device_ptr(C, dev))
+    return PGEMM_ERR_INVALID;
+  if (fp8 && (!is_device_ptr(args->a_scale, dev) || !is_device_ptr(args->b_scale, dev)))
+    return PGEMM_ERR_INVALID;
+  const size_t esz = fp8 ? 1 : 2;
+  const size_t csz = dtype == PGEMM_BF16_OUT_F32 ? 4 : 2;
+  // C must not overlap A or B
+  {
+    const char* c0 = (const char*)C;
+    const char* c1 = c0 + (size_t)M * N * csz;
+    const char* a0 = (const char*)A;
+    const char* a1 = a0 + (size_t)M * K * esz;
+    const char* b0 = (const char*)B;
+    const char* b1 = b0 + (size_t)K * N * esz;
+    if ((c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1)) return PGEMM_ERR_INVALID;
+  }
+
+  pgk::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.sa = fp8 ? args->a_scale : nullptr;
+  p.sb = fp8 ? args->b_scale : nullptr;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  const int64_t npm = (M + bm - 1) / bm, npn = (N + bn - 1) / bn;
+  if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, p.s);
+  if (st != PGEMM_OK) return st;
+
+  DeviceGuard g(dev);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  bool witness = false;
+  st = make_witness(cfg, args, p.s, p.w, witness, stream);
+  if (st != PGEMM_OK) return st;
+  st = reset_counters(cfg, args, p.s, stream);
+  if (st != PGEMM_OK) return st;
+
+  hipError_t e;
+  if (fp8) {
+    const bool vec = (N % 16 == 0) && aligned(A, 16) && aligned(B, 16) && aligned(C, 8);
+    e = pgk::launch_gemm_fp8(p, bm, bn, bk, vec, witness, stream);
+  } else {
+    const bool vec = (K % 8 == 0) && (N % 8 == 0) && aligned(A, 16) && aligned(B, 16) &&
+                     aligned(C, 16) && pgk::gemm_bf16_vec_fits(bm, bk, N, K);
+    e = pgk::launch_gemm_bf16(p, bm, bn, bk, dtype == PGEMM_BF16_OUT_BF16, vec, witness, stream);
+  }
+  if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
+pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* C, int64_t rows,
+                      int64_t cols, int tile_rows, int tile_cols, pgemm_sched sched,
+                      const pgemm_args* args, void* hip_stream) {
+  if (!cfg || !X || !Y || !C) return PGEMM_ERR_INVALID;
+  if (rows < 1 || cols < 1 || rows > 0x7fffffffLL || cols > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  if (tile_rows < 1 || tile_cols < 1) return PGEMM_ERR_INVALID;
+  if (!pgk::padd_tile_supported(tile_rows, tile_cols)) return PGEMM_ERR_UNSUPPORTED;
+  const int dev = cfg->device;
+  if (!is_device_ptr(X, dev) || !is_device_ptr(Y, dev) || !is_device_ptr(C, dev))
+    return PGEMM_ERR_INVALID;
+  const size_t bytes = (size_t)rows * cols * 4;
+  {
+    const char* c0 = (const char*)C;
+    const char* xs[2] = {(const char*)X, (const char*)Y};
+    for (const char* x0 : xs)
+      if (x0 != c0 && c0 < x0 + bytes && x0 < c0 + bytes) return PGEMM_ERR_INVALID;
+  }
+  pgk::AddParams p;
+  memset(&p, 0, sizeof(p));
+  p.X = X;
+  p.Y = Y;
+  p.C = C;
+  p.rows = (int)rows;
+  p.cols = (int)cols;
+  const int64_t npm = (rows + tile_rows - 1) / tile_rows, npn = (cols + tile_cols - 1) / tile_cols;
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, p.s);
+  if (st != PGEMM_OK) return st;
+  const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
+  p.s.chunk = step;
+  if (args && args->claim_chunk) {
+    if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
+    p.s.chunk = args->claim_chunk;
+  }
+  DeviceGuard g(dev);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  bool witness = false;
+  st = make_witness(cfg, args, p.s, p.w, witness, stream);
+  if (st != PGEMM_OK) return st;
+  st = reset_counters(cfg, args, p.s, stream);
+  if (st != PGEMM_OK) return st;
+  const bool vec = (cols % 4 == 0) && aligned(X, 16) && aligned(Y, 16) && aligned(C, 16);
+  hipError_t e = pgk::launch_padd(p, tile_rows, tile_cols, vec, witness, stream);
+  if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
+}  // extern "C"
