@@ -1,0 +1,56 @@
+"""The library's scheduler header, built for the host with g++, against the
+oracle's schedule model: static walks tile for tile, and the work-stealing
+claim loop on real threads with std::atomic counters against the model's
+invariants."""
+import itertools
+import os
+import subprocess
+
+import pytest
+
+from oracle import sched_model as sm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KINDS = {"blocked": 0, "interleaved": 1, "grouped": 2, "blocked_grouped": 4}
+
+
+@pytest.fixture(scope="module")
+def harness(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("sched") / "sched_host")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-pthread",
+                    os.path.join(ROOT, "tests", "host", "sched_host.cpp"), "-o", exe], check=True)
+    return exe
+
+
+def _static(exe, kind, pm, pn, G, gs):
+    out = subprocess.run([exe, "static", str(KINDS[kind]), str(pm), str(pn), str(G), str(gs)],
+                         check=True, capture_output=True, text=True).stdout
+    seqs = []
+    for line in out.strip().splitlines():
+        _, _, rest = line.partition(":")
+        seqs.append([tuple(map(int, t.split(","))) for t in rest.split()])
+    return seqs
+
+
+@pytest.mark.parametrize("kind", list(KINDS))
+def test_static_walk_matches_model(harness, kind):
+    for (pm, pn), G, gs in itertools.product([(1, 1), (5, 2), (13, 23), (32, 32), (20, 20), (19, 32)],
+                                             [1, 7, 8, 256], [1, 3, 8, 16]):
+        got = _static(harness, kind, pm, pn, G, gs)
+        assert got == sm.static_schedule(kind, pm, pn, G, gs), (kind, pm, pn, G, gs)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1),
+                                             (19, 32, 256, 8, 1), (33, 7, 64, 8, 4),
+                                             (1, 1, 16, 8, 1)])
+def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
+    out = subprocess.run([harness, "ws", str(pm), str(pn), str(G), str(X), "8", str(chunk)],
+                         check=True, capture_output=True, text=True).stdout.strip().splitlines()
+    counters = list(map(int, out[0].split(":")[1].split()))
+    T = pm * pn
+    rows = [tuple(map(int, l.split())) for l in out[1:]]
+    assert len(rows) == T
+    visits = [r[1] for r in rows]
+    owner = [r[2] for r in rows]
+    order = [r[3] for r in rows]
+    sm.check_ws_execution(visits, owner, order, counters, T, G, X, chunk)
