@@ -32,6 +32,7 @@ M = N = K = 8192
 SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
           ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8)]
 HEADLINE = ("work_stealing", 8)
+CPU_ROWS = 4096
 
 
 def parse():
@@ -42,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of schedulers to time (profiling runs)")
     p.add_argument("--skip-add", action="store_true")
+    p.add_argument("--skip-extra", action="store_true", help="only the 8192^3 bf16 GEMM and the add")
     return p.parse_args()
 
 
@@ -65,10 +67,10 @@ def time_calls(fn, steps, warmup, stream):
 
 
 def cpu_baseline(a_bits, b_bits):
-    """The oracle on a bounded sample: 16 full rows of C (16 x 8192 outputs, K = 8192)."""
+    """The oracle on a bounded sample: CPU_ROWS full rows of C (K = 8192)."""
     from oracle import gemm as og
     from oracle.codecs import bf16_to_f64
-    rows = np.arange(0, M, M // 16)[:16]
+    rows = np.arange(CPU_ROWS) * (M // CPU_ROWS)
     A = bf16_to_f64(a_bits[rows])
     B = bf16_to_f64(b_bits)
     t0 = time.perf_counter()
@@ -77,7 +79,8 @@ def cpu_baseline(a_bits, b_bits):
     flops = 2.0 * len(rows) * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": og.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} full rows of C (16x8192 outputs, K=8192, fp64 with |A||B|) in {dt:.2f} s"}
+            "sample": f"{len(rows)} full rows of C ({len(rows)}x{N} outputs, K={K}; fp64 sum and |A||B| "
+                      f"bound in one pass) in {dt:.2f} s"}
 
 
 def main():
@@ -112,6 +115,50 @@ def main():
                     "event_ms_min": ev_min,
                     "frac_peak": flops / (ev_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         print(f"# {key}: {ms:.4f} ms/step, {per[key]['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # ragged, wave-quantised shapes (workload 4): every scheduler
+    ragged = {}
+    if not args.skip_extra:
+        from synthetic import bf16_bits_uniform
+        for (m, n, k) in [(5120, 5120, 4096), (4864, 8000, 8192), (3000, 7000, 2048)]:
+            ra = torch.from_numpy(bf16_bits_uniform((m, k), 1040 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            rb = torch.from_numpy(bf16_bits_uniform((k, n), 1041 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+            f = 2.0 * m * n * k
+            row = {}
+            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]:
+                a = pg.make_args(tile=(256, 256, 64))
+                fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
+                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+                row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
+            ragged[f"{m}x{n}x{k}"] = row
+            print(f"# ragged {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
+                  file=sys.stderr, flush=True)
+            del ra, rb, rc
+
+    # block-scaled fp8 (workload 5): work stealing vs grouped
+    fp8 = {}
+    if not args.skip_extra:
+        from synthetic import fp8_blockscaled
+        for (m, n, k, tile) in [(256, 28672, 8192, (128, 128, 128)), (8192, 8192, 8192, (256, 256, 128))]:
+            qa, sa = fp8_blockscaled(m, k, 1050, 1052, k_major=True)
+            qb, sb = fp8_blockscaled(n, k, 1051, 1053, k_major=False)
+            dA, dB = torch.from_numpy(qa).to("cuda:0"), torch.from_numpy(qb).to("cuda:0")
+            dSA, dSB = torch.from_numpy(sa).to("cuda:0"), torch.from_numpy(sb).to("cuda:0")
+            dC = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+            f = 2.0 * m * n * k
+            nbytes = m * k + k * n + (m + n) * (k // 128) + 2 * m * n
+            row = {}
+            for sched in ["grouped", "work_stealing"]:
+                a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
+                fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
+                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+                row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2),
+                              "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1),
+                              "event_ms_mean": round(ev_mean, 5)}
+            fp8[f"{m}x{n}x{k}"] = row
+            print(f"# fp8 {m}x{n}x{k}: {row}", file=sys.stderr, flush=True)
+            del dA, dB, dC, qa, qb
 
     add = {}
     if not args.skip_add:
@@ -157,6 +204,8 @@ def main():
                               "event_ms_mean": round(v["event_ms_mean"], 5)} for k, v in per.items()},
         "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                 for k, v in add.items()},
+        "ragged": ragged,
+        "fp8": fp8,
         "device": cfg.info,
     }
     if not args.no_cpu_baseline:

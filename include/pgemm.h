@@ -55,7 +55,8 @@ typedef enum {
   /* A, B OCP e4m3 bytes with one e8m0 scale byte per 128 consecutive K
    * elements per row of A (a_scale[K/128][M]) and per column of B
    * (b_scale[K/128][N]); value = e4m3(q) * 2^(scale - 127); fp32
-   * accumulate; C bf16.  K must be a multiple of 128. */
+   * accumulate; C bf16.  K must be a multiple of 128, N a multiple of 16,
+   * and A, B, C 16-byte aligned (otherwise PGEMM_ERR_UNSUPPORTED). */
   PGEMM_FP8E4M3_B128_OUT_BF16 = 2
 } pgemm_dtype;
 
@@ -84,6 +85,9 @@ typedef enum {
                                        timing into the witness buffers (see pgemm_witness_enable) */
 #define PGEMM_DEBUG_SKIP_RESET 0x2u /* do not zero the work-stealing counters before the launch */
 #define PGEMM_DEBUG_STRAGGLER 0x4u  /* program straggler_program waits straggler_ns before each tile */
+#define PGEMM_DEBUG_REGISTER_STAGED 0x8u /* bf16: use the register-staged kernel (the path taken
+                                            for unaligned shapes) even where the direct-to-LDS
+                                            kernel applies */
 
 /* Optional per-call arguments; pass NULL for all defaults. */
 typedef struct {

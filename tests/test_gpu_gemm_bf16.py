@@ -41,15 +41,17 @@ def run_gemm(a_bits, b_bits, M, N, K, out, sched, tile, **kw):
     return C
 
 
+@pytest.mark.parametrize("staged", [False, True], ids=["lds_dma", "register_staged"])
 @pytest.mark.parametrize("tile", [(128, 128, 64), (256, 256, 64)])
 @pytest.mark.parametrize("out", ["bf16_out_f32", "bf16_out_bf16"])
-def test_brute_force_shapes(tile, out):
+def test_brute_force_shapes(tile, out, staged):
+    flags = pg._abi.DEBUG_REGISTER_STAGED if staged else 0
     for si, (M, N, K) in enumerate(_shapes()):
         a = bf16_bits_uniform((M, K), 7 + si)
         b = bf16_bits_uniform((K, N), 8 + si)
         Cref, Abs = og.gemm_bf16(a, b)
         for sched in SCHEDS:
-            C = run_gemm(a, b, M, N, K, out, sched, tile)
+            C = run_gemm(a, b, M, N, K, out, sched, tile, debug_flags=flags)
             assert C.guards_intact(), (M, N, K, sched)
             assert_within(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL,
                           out == "bf16_out_bf16", f"{(M, N, K)} {sched} {tile} {out}")
@@ -152,9 +154,11 @@ def test_8192_all_schedulers():
     b = bf16_bits_normal((K, N), 1031)
     rows = _edge_rows(M, 256, np.random.default_rng(3), k=8)[:24]
     ref_bits = None
-    for sched, gs in [("blocked", 0), ("interleaved", 0), ("grouped", 8), ("grouped", 16),
-                      ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8)]:
-        C = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, (256, 256, 64), group_size=gs)
+    for sched, gs, fl in [("blocked", 0, 0), ("interleaved", 0, 0), ("grouped", 8, 0), ("grouped", 16, 0),
+                          ("work_stealing", 8, 0), ("work_stealing", 16, 0), ("blocked_grouped", 8, 0),
+                          ("work_stealing", 8, pg._abi.DEBUG_REGISTER_STAGED)]:
+        C = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, (256, 256, 64), group_size=gs,
+                     debug_flags=fl)
         assert C.guards_intact()
         bits = C.body_bits()
         if ref_bits is None:

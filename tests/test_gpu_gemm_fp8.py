@@ -1,0 +1,114 @@
+"""GPU parity of the persistent block-scaled fp8 (e4m3, e8m0 per 128 K) GEMM
+against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import tile_scheduling_persistent_amd as pg
+from oracle import gemm as og
+from oracle.codecs import dequant_fp8_a, dequant_fp8_b
+from synthetic import fp8_blockscaled
+from tests.gpu_util import FP8_TOL, Guarded, assert_north_star, assert_within, config, dev_u8, note
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]
+
+
+def make_inputs(M, N, K, seed):
+    qa, sa = fp8_blockscaled(M, K, seed, seed + 2, k_major=True)
+    qb, sb = fp8_blockscaled(N, K, seed + 1, seed + 3, k_major=False)
+    return qa, sa, qb, sb
+
+
+def run_fp8(qa, sa, qb, sb, M, N, K, sched, tile, **kw):
+    cfg = config()
+    A, B, SA, SB = dev_u8(qa), dev_u8(qb), dev_u8(sa), dev_u8(sb)
+    C = Guarded(M * N, "bf16")
+    note(f"pgemm_run fp8 M={M} N={N} K={K} sched={sched} tile={tile} {kw}")
+    pg.pgemm_run(cfg, A, B, C.view, M, N, K, "fp8_b128_out_bf16", sched,
+                 pg.make_args(tile=tile, a_scale=SA, b_scale=SB, **kw))
+    torch.cuda.synchronize()
+    return C
+
+
+def test_closed_form_scales():
+    # q = 1.0 everywhere; SA[g][i] = 127 + (g + i) % 5 - 2, SB[g][j] = 127 - (j % 3):
+    # C[i][j] = 128 * sum_g 2**(SA - 127) * 2**(SB - 127), exact in bf16 here.
+    M, N, K = 300, 272, 512
+    qa = np.full((M, K), 0x38, np.uint8)
+    qb = np.full((K, N), 0x38, np.uint8)
+    G = K // 128
+    sa = np.array([[127 + (g + i) % 5 - 2 for i in range(M)] for g in range(G)], np.uint8)
+    sb = np.array([[127 - (j % 3) for j in range(N)] for g in range(G)], np.uint8)
+    want = np.zeros((M, N))
+    for g in range(G):
+        want += 128.0 * np.outer(2.0 ** (sa[g].astype(float) - 127), 2.0 ** (sb[g].astype(float) - 127))
+    for tile in [(128, 128, 128), (256, 256, 128)]:
+        for sched in SCHEDS:
+            C = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile)
+            assert C.guards_intact()
+            assert np.array_equal(C.as_f64().reshape(M, N), want), (tile, sched)
+
+
+@pytest.mark.parametrize("tile", [(128, 128, 128), (256, 256, 128)])
+def test_small_shapes(tile):
+    shapes = [(1, 16, 128), (100, 112, 256), (129, 128, 384), (256, 272, 128), (300, 400, 256),
+              (257, 16, 640), (64, 1024, 128)]
+    for i, (M, N, K) in enumerate(shapes):
+        qa, sa, qb, sb = make_inputs(M, N, K, 50 + i)
+        Cref, Abs = og.gemm_fp8_b128(qa, sa, qb, sb)
+        for sched in SCHEDS:
+            C = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile)
+            assert C.guards_intact(), (M, N, K, sched)
+            assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"{(M, N, K)} {sched} {tile}")
+
+
+def test_unsupported_shapes_are_rejected():
+    cfg = config()
+    qa, sa, qb, sb = make_inputs(64, 24, 128, 3)
+    A, B, SA, SB = dev_u8(qa), dev_u8(qb), dev_u8(sa), dev_u8(sb)
+    C = torch.empty(64 * 24, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_run(cfg, A, B, C, 64, 24, 128, "fp8_b128_out_bf16", "blocked",
+                     pg.make_args(tile=(128, 128, 128), a_scale=SA, b_scale=SB))
+    assert e.value.code == pg._abi.ERR_UNSUPPORTED
+
+
+def _sampled(qa, sa, qb, sb, C, M, N, rows, what):
+    A = dequant_fp8_a(qa[rows], sa[:, rows])
+    B = dequant_fp8_b(qb, sb)
+    Cref, Abs = og.gemm_f64(A, B)
+    assert_north_star(C.as_f64().reshape(M, N)[rows], Cref, Abs, FP8_TOL, what)
+
+
+def test_skinny_256x28672x8192():
+    """Workload 5a: M=256, N=28672, K=8192, 128x128x128 tiles, work stealing vs grouped."""
+    M, N, K = 256, 28672, 8192
+    qa, sa, qb, sb = make_inputs(M, N, K, 1050)
+    rows = np.array([0, 1, 31, 64, 127, 128, 200, 255])
+    ref = None
+    for sched in ["work_stealing", "grouped", "blocked", "interleaved"]:
+        C = run_fp8(qa, sa, qb, sb, M, N, K, sched, (128, 128, 128))
+        assert C.guards_intact()
+        if ref is None:
+            _sampled(qa, sa, qb, sb, C, M, N, rows, f"5a {sched}")
+            ref = C.body_bits()
+        else:
+            assert np.array_equal(C.body_bits(), ref), sched
+
+
+def test_square_8192():
+    """Workload 5b: 8192^3, 256x256x128 tiles, work stealing vs grouped."""
+    M = N = K = 8192
+    qa, sa, qb, sb = make_inputs(M, N, K, 1050)
+    rows = np.array([0, 255, 256, 4100, 8191])
+    ref = None
+    for sched in ["work_stealing", "grouped"]:
+        C = run_fp8(qa, sa, qb, sb, M, N, K, sched, (256, 256, 128))
+        assert C.guards_intact()
+        if ref is None:
+            _sampled(qa, sa, qb, sb, C, M, N, rows, f"5b {sched}")
+            ref = C.body_bits()
+        else:
+            assert np.array_equal(C.body_bits(), ref), sched

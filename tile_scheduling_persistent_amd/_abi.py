@@ -17,7 +17,7 @@ BF16_OUT_F32, BF16_OUT_BF16, FP8E4M3_B128_OUT_BF16 = range(3)
 # pgemm_sched
 SCHED_BLOCKED, SCHED_INTERLEAVED, SCHED_GROUPED, SCHED_WORK_STEALING, SCHED_BLOCKED_GROUPED = range(5)
 # debug flags
-DEBUG_WITNESS, DEBUG_SKIP_RESET, DEBUG_STRAGGLER = 0x1, 0x2, 0x4
+DEBUG_WITNESS, DEBUG_SKIP_RESET, DEBUG_STRAGGLER, DEBUG_REGISTER_STAGED = 0x1, 0x2, 0x4, 0x8
 
 
 class pgemm_args(ctypes.Structure):

@@ -68,7 +68,11 @@ hipError_t launch_zero_i32(int* ptr, int n, hipStream_t stream);
 hipError_t launch_fill_i32(int* ptr, int n, int value, hipStream_t stream);
 bool gemm_bf16_tile_supported(int bm, int bn, int bk);
 bool gemm_bf16_vec_fits(int bm, int bk, long long N, long long K);
+bool gemm_bf16_lds_eligible(int bm, int bn, int bk, long long N, long long K);
+hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
+                                hipStream_t stream);
 bool gemm_fp8_tile_supported(int bm, int bn, int bk);
+bool gemm_fp8_eligible(int bm, long long N, long long K);
 bool padd_tile_supported(int tr, int tc);
 int padd_tiles_per_step(int tr, int tc);
 

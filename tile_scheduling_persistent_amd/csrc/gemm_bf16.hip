@@ -64,8 +64,15 @@ struct Shape {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// Buffer resource over [base, base + bytes).  base and bytes are uniform
+// across the wave; readfirstlane states that, so the resource lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           kRsrcWord3);
 }
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, unsigned off) {
@@ -304,7 +311,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
   const int nk = (K + BK - 1) / BK;
   if (tid == 0) s_tile[0] = walker.first();
   __syncthreads();
-  int tile = s_tile[0];
+  int tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
   int stage = 0;
   int it = 0;
   if (tile >= 0) {
@@ -349,7 +356,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
     // last slab: fetch the first slab of the next tile (if known already)
     int next = -1;
     if (nk >= 2) {
-      next = s_tile[slot];
+      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
       if (next >= 0) {
         int qm, qn;
         walker.tile_coords(next, qm, qn);
@@ -362,7 +369,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
     stage ^= 1;
     epilogue(m0, n0);
     if (nk == 1) {
-      next = s_tile[slot];
+      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
       if (next >= 0) {
         int qm, qn;
         walker.tile_coords(next, qm, qn);

@@ -1,0 +1,348 @@
+// Persistent bf16 GEMM for gfx950, fast path (K and N multiples of 8,
+// 16-byte aligned operands): C[M][N] = A[M][K] . B[K][N], fp32 accumulate.
+//
+// Same persistent tile loop and schedulers as gemm_bf16.hip ("Work Stealing
+// Scheduler Kernel", tritonBLAS PR #65; "Implement persistent kernels",
+// Helion PR #238; the pipeline phase that runs on across tiles of
+// "[Feature] Introduce tile scheduler", TileLang PR #2441).  What differs is
+// how operands reach the matrix cores:
+//  * Global -> LDS with buffer_load ... lds (16 bytes per lane, 1 KiB per
+//    wave instruction): no staging registers, no VALU work.  The LDS side of
+//    such a load is linear, so the bank swizzle is applied on the global side
+//    (each lane fetches the chunk that belongs at its LDS position).
+//  * A stays [m][k] in LDS (128-byte rows, 16-byte chunk c stored at
+//    c ^ (m & 7)); MFMA operand reads are ds_read_b128.
+//  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
+//    c ^ 2*(k & 3)); the k-contiguous operand the MFMA needs is produced by
+//    ds_read_b64_tr_b16: within each 16-lane group, lane i points at row
+//    K0 + i/4, columns N0 + 4*(i%4) .. +3, and lane j receives rows
+//    K0 .. K0+3 of column N0 + j.  Two such reads give a lane its 8 k-values.
+//  * Rows past M (A) and past K (B) read as zero through the buffer range
+//    check; the K tail and columns past N are masked per lane, only on the
+//    slabs / tiles that need it.
+#include "common.hpp"
+
+namespace pgk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kThreads = 256;
+constexpr int BK = 64;
+constexpr unsigned kOob = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int BM, int BN>
+struct Shape {
+  static constexpr int WM = 2, WN = 2;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int SM = TM / 32, SN = TN / 32;
+  static constexpr int A_BYTES = BM * BK * 2;       // one stage of A
+  static constexpr int B_BYTES = BK * BN * 2;       // one stage of B
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE + 16;
+  static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per stage
+  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int B_ROW = BN * 2;                // bytes per LDS row of B
+  static constexpr int B_ROWS_PER_INSTR = 1024 / B_ROW;
+  static constexpr int B_CPR = BN / 8;                // 16-byte chunks per row of B
+  static_assert(B_ROWS_PER_INSTR >= 1 && 1024 % B_ROW == 0, "B row must divide 1 KiB");
+};
+
+// Buffer resource over [base, base + bytes).  base and bytes are uniform
+// across the wave; readfirstlane states that, so the resource lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_dst,
+                                           unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// vmcnt(0): this wave's buffer loads, including the ones into LDS, have landed.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int BM, int BN, bool OUT_BF16, bool WITNESS>
+__global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
+  using S = Shape<BM, BN>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  int* s_tile = reinterpret_cast<int*>(smem + 2 * S::STAGE);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / S::WN;
+  const int wn = wave % S::WN;
+  const int prog = blockIdx.x;
+  const int M = P.M, N = P.N, K = P.K;
+  const unsigned short* __restrict__ A = static_cast<const unsigned short*>(P.A);
+  const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);
+
+  Walker walker(P.s, prog);
+  long long t_start = 0;
+  if (WITNESS && tid == 0) t_start = wall_ticks();
+
+  // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
+  // A: wave instruction q covers rows 8q .. 8q+7; lane p -> row 8q + p/8,
+  // LDS chunk p%8, global chunk (p%8) ^ (p/8).
+  const int a_c = (lane & 7) ^ (lane >> 3);
+  const unsigned a_lane = (unsigned)(lane >> 3) * (unsigned)K * 2u + (unsigned)a_c * 16u;
+  const unsigned a_qstep = 8u * (unsigned)K * 2u;
+  // B: wave instruction q covers rows R*q .. ; lane p -> row R*q + p/CPR,
+  // LDS chunk p%CPR, global chunk (p%CPR) ^ 2*(row & 3).
+  auto b_row = [&](int q) { return q * S::B_ROWS_PER_INSTR + lane / S::B_CPR; };
+  auto b_chunk = [&](int q) { return (lane % S::B_CPR) ^ (2 * (b_row(q) & 3)); };
+
+  // ---- LDS read offsets ----
+  const int l32 = lane & 31;
+  unsigned rd_a[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int row = wm * S::TM + l32;
+    const int c = (kk * 2 + (lane >> 5)) ^ (lane & 7);
+    rd_a[kk] = (unsigned)(row * 128 + c * 16);
+  }
+  // B^T through the transpose read: lane i of a 16-lane group g points at
+  // row K0 + i/4, column N0 + 4*(i%4).
+  unsigned rd_b[S::SN];
+  {
+    const int g = lane >> 4, i16 = lane & 15, a = i16 & 3, e = i16 >> 2;
+    const int krow = (g >> 1) * 8 + e;  // + kk*16 + h*4 (multiples of 4: swizzle unchanged)
+#pragma unroll
+    for (int sn = 0; sn < S::SN; ++sn) {
+      const int n = wn * S::TN + sn * 32 + (g & 1) * 16 + 4 * a;
+      const int c = (n >> 3) ^ (2 * e);
+      rd_b[sn] = (unsigned)(S::A_BYTES + krow * S::B_ROW + c * 16 + 8 * (a & 1));
+    }
+  }
+
+  // Issue the loads of slab (m0, n0, k0) into LDS stage `st`.
+  auto gload = [&](int st, int m0, int n0, int k0) {
+    unsigned char* sbase = smem + st * S::STAGE;
+    const int rows = (M - m0) < BM ? (M - m0) : BM;
+    const auto rA = rsrc(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0) * 2u);
+    const int krows = (K - k0) < BK ? (K - k0) : BK;
+    const auto rB = rsrc(B + (size_t)k0 * N + n0, (unsigned)(krows * N - n0) * 2u);
+    const bool a_full = k0 + BK <= K;
+    const bool b_full = n0 + BN <= N;
+#pragma unroll
+    for (int i = 0; i < S::A_INSTR; ++i) {
+      const int q = wave * S::A_INSTR + i;
+      unsigned off = a_lane + (unsigned)q * a_qstep;
+      if (!a_full && k0 + a_c * 8 >= K) off = kOob;
+      load_lds16(rA, sbase + q * 1024, off);
+    }
+#pragma unroll
+    for (int i = 0; i < S::B_INSTR; ++i) {
+      const int q = wave * S::B_INSTR + i;
+      const int c = b_chunk(q);
+      unsigned off = (unsigned)b_row(q) * (unsigned)N * 2u + (unsigned)c * 16u;
+      if (!b_full && n0 + c * 8 >= N) off = kOob;
+      load_lds16(rB, sbase + S::A_BYTES + q * 1024, off);
+    }
+  };
+
+  f32x16 acc[S::SN][S::SM];
+
+  auto compute = [&](int st) {
+    const unsigned char* sbase = smem + st * S::STAGE;
+    bf16x8 bf[2][S::SN], af[2][S::SM];
+    auto frag = [&](int kk, int slot) {
+#pragma unroll
+      for (int sn = 0; sn < S::SN; ++sn) {
+        const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * S::B_ROW));
+        bf[slot][sn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int sm = 0; sm < S::SM; ++sm)
+        af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * 128);
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) frag(kk + 1, cur ^ 1);
+#pragma unroll
+      for (int sn = 0; sn < S::SN; ++sn)
+#pragma unroll
+        for (int sm = 0; sm < S::SM; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][sn], af[cur][sm],
+                                                                acc[sn][sm], 0, 0, 0);
+    }
+  };
+
+  auto epilogue = [&](int m0, int n0) {
+    constexpr unsigned esz = OUT_BF16 ? 2u : 4u;
+    const int rows = (M - m0) < BM ? (M - m0) : BM;
+    const auto rC = rsrc(static_cast<unsigned char*>(P.C) + ((size_t)m0 * N + n0) * esz,
+                         (unsigned)((size_t)rows * N - n0) * esz);
+    const int r0 = wm * S::TM + l32;
+    const int c0 = wn * S::TN + 4 * (lane >> 5);
+    const unsigned eb = (unsigned)(r0 * N + c0) * esz;
+    const unsigned rstep = 32u * (unsigned)N * esz;
+    const int ncols = N - n0;
+#pragma unroll
+    for (int sm = 0; sm < S::SM; ++sm) {
+#pragma unroll
+      for (int sn = 0; sn < S::SN; ++sn) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cc = sn * 32 + 8 * g;
+          const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
+          const f32x16& a = acc[sn][sm];
+          if (OUT_BF16) {
+            const u32x2 v = u32x2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                                  pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
+          } else {
+            const f32x4 v = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  if (tid == 0) s_tile[0] = walker.first();
+  __syncthreads();
+  int tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  int stage = 0;
+  int it = 0;
+  if (tile >= 0) {
+    int pm, pn;
+    walker.tile_coords(tile, pm, pn);
+    gload(0, pm * BM, pn * BN, 0);
+  }
+  wait_vm0();
+  __syncthreads();
+
+  while (tile >= 0) {
+    int pm, pn;
+    walker.tile_coords(tile, pm, pn);
+    const int m0 = pm * BM, n0 = pn * BN;
+    if (tid == 0) {
+      if (WITNESS) {
+        atomicAdd(P.w.visits + tile, 1);
+        P.w.owner[tile] = prog;
+        P.w.order[tile] = it;
+      }
+      if (P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
+    }
+#pragma unroll
+    for (int sn = 0; sn < S::SN; ++sn)
+#pragma unroll
+      for (int sm = 0; sm < S::SM; ++sm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
+
+    const int slot = (it + 1) & 1;
+    if (nk == 1 && tid == 0) s_tile[slot] = walker.next(tile);
+    for (int kb = 0; kb + 1 < nk; ++kb) {
+      if (kb == nk - 2 && tid == 0) s_tile[slot] = walker.next(tile);
+      gload(stage ^ 1, m0, n0, (kb + 1) * BK);
+      compute(stage);
+      wait_vm0();
+      __syncthreads();
+      stage ^= 1;
+    }
+    int next = -1;
+    if (nk >= 2) {
+      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
+      if (next >= 0) {
+        int qm, qn;
+        walker.tile_coords(next, qm, qn);
+        gload(stage ^ 1, qm * BM, qn * BN, 0);
+      }
+    }
+    compute(stage);
+    wait_vm0();
+    __syncthreads();
+    stage ^= 1;
+    epilogue(m0, n0);
+    if (nk == 1) {
+      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
+      if (next >= 0) {
+        int qm, qn;
+        walker.tile_coords(next, qm, qn);
+        gload(stage, qm * BM, qn * BN, 0);
+      }
+      wait_vm0();
+      __syncthreads();
+    }
+    tile = next;
+    ++it;
+  }
+
+  if (WITNESS && tid == 0) {
+    P.w.t_start[prog] = t_start;
+    P.w.t_end[prog] = wall_ticks();
+    P.w.hw_id[prog] = hw_placement();
+    P.w.n_tiles[prog] = it;
+  }
+}
+
+template <int BM, int BN, bool OUT_BF16, bool WITNESS>
+hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
+  using S = Shape<BM, BN>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, OUT_BF16, WITNESS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.s.G), dim3(kThreads), S::LDS_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const GemmParams& p, bool out_bf16, bool witness, hipStream_t stream) {
+  if (out_bf16)
+    return witness ? launch_one<BM, BN, true, true>(p, stream) : launch_one<BM, BN, true, false>(p, stream);
+  return witness ? launch_one<BM, BN, false, true>(p, stream) : launch_one<BM, BN, false, false>(p, stream);
+}
+
+}  // namespace
+
+// The direct-to-LDS path: needs 16-byte aligned rows of A, B and C, and the
+// 32-bit buffer offsets of one tile panel / slab to stay in range.
+bool gemm_bf16_lds_eligible(int bm, int bn, int bk, long long N, long long K) {
+  if (bk != 64) return false;
+  if (!((bm == 256 && bn == 256) || (bm == 128 && bn == 128))) return false;
+  if (K % 8 != 0 || N % 8 != 0) return false;
+  return (long long)bm * K * 2 < (1LL << 31) && 64LL * N * 2 < (1LL << 31) &&
+         (long long)bm * N * 4 < (1LL << 31);
+}
+
+hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
+                                hipStream_t stream) {
+  if (bm == 256 && bn == 256) return launch_tile<256, 256>(p, out_bf16, witness, stream);
+  if (bm == 128 && bn == 128) return launch_tile<128, 128>(p, out_bf16, witness, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pgk

@@ -300,6 +300,9 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
     if (!args || !args->a_scale || !args->b_scale) return PGEMM_ERR_INVALID;
     if (K % 128 != 0) return PGEMM_ERR_INVALID;
     if (!pgk::gemm_fp8_tile_supported(bm, bn, bk)) return PGEMM_ERR_UNSUPPORTED;
+    // the fp8 kernel moves 16-byte chunks of B rows and of C
+    if (!pgk::gemm_fp8_eligible(bm, N, K) || !aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
+      return PGEMM_ERR_UNSUPPORTED;
   } else if (!pgk::gemm_bf16_tile_supported(bm, bn, bk)) {
     return PGEMM_ERR_UNSUPPORTED;
   }
@@ -347,12 +350,18 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
 
   hipError_t e;
   if (fp8) {
-    const bool vec = (N % 16 == 0) && aligned(A, 16) && aligned(B, 16) && aligned(C, 8);
-    e = pgk::launch_gemm_fp8(p, bm, bn, bk, vec, witness, stream);
+    e = pgk::launch_gemm_fp8(p, bm, bn, bk, true, witness, stream);
   } else {
-    const bool vec = (K % 8 == 0) && (N % 8 == 0) && aligned(A, 16) && aligned(B, 16) &&
-                     aligned(C, 16) && pgk::gemm_bf16_vec_fits(bm, bk, N, K);
-    e = pgk::launch_gemm_bf16(p, bm, bn, bk, dtype == PGEMM_BF16_OUT_BF16, vec, witness, stream);
+    const bool out_bf16 = dtype == PGEMM_BF16_OUT_BF16;
+    const bool staged = args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED);
+    if (!staged && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) &&
+        pgk::gemm_bf16_lds_eligible(bm, bn, bk, N, K)) {
+      e = pgk::launch_gemm_bf16_lds(p, bm, bn, out_bf16, witness, stream);
+    } else {
+      const bool vec = (K % 8 == 0) && (N % 8 == 0) && aligned(A, 16) && aligned(B, 16) &&
+                       aligned(C, 16) && pgk::gemm_bf16_vec_fits(bm, bk, N, K);
+      e = pgk::launch_gemm_bf16(p, bm, bn, bk, out_bf16, vec, witness, stream);
+    }
   }
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
