@@ -3,23 +3,36 @@
 //
 // Same persistent tile loop and schedulers as gemm_bf16.hip ("Work Stealing
 // Scheduler Kernel", tritonBLAS PR #65; "Implement persistent kernels",
-// Helion PR #238; the pipeline phase that runs on across tiles of
-// "[Feature] Introduce tile scheduler", TileLang PR #2441).  What differs is
-// how operands reach the matrix cores:
+// Helion PR #238).  What differs is how operands reach the matrix cores:
 //  * Global -> LDS with buffer_load ... lds (16 bytes per lane, 1 KiB per
 //    wave instruction): no staging registers, no VALU work.  The LDS side of
 //    such a load is linear, so the bank swizzle is applied on the global side
 //    (each lane fetches the chunk that belongs at its LDS position).
-//  * A stays [m][k] in LDS (128-byte rows, 16-byte chunk c stored at
-//    c ^ (m & 7)); MFMA operand reads are ds_read_b128.
+//  * NST LDS stages of BK-deep slabs form a ring; the loader runs NST-1
+//    slabs ahead of the matrix cores and walks straight on into the next
+//    tile of the schedule (the pipeline phase runs on across tiles, like the
+//    scheduler's iteration counter of "[Feature] Introduce tile scheduler",
+//    TileLang PR #2441).  The next tile is claimed when the loader issues
+//    the last slab of the current one, so a work-stealing claim happens
+//    NST-1 slabs before the tile is needed.  One barrier per slab; each wave
+//    waits only for the slab it is about to consume (vmcnt counts the
+//    younger slabs still in flight).
+//  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
+//    (row & 7 for 128-byte rows, (row >> 1) & 3 for 64-byte rows) so that the
+//    ds_read_b128 operand reads of 8 consecutive rows hit distinct banks.
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
 //    c ^ 2*(k & 3)); the k-contiguous operand the MFMA needs is produced by
 //    ds_read_b64_tr_b16: within each 16-lane group, lane i points at row
 //    K0 + i/4, columns N0 + 4*(i%4) .. +3, and lane j receives rows
 //    K0 .. K0+3 of column N0 + j.  Two such reads give a lane its 8 k-values.
+//  * Each wave owns a (BM/2) x (BN/2) sub-tile as 32x32 MFMA blocks
+//    (v_mfma_f32_32x32x16_bf16) with the B^T block as the first operand, so
+//    a lane's 4 consecutive accumulators are 4 consecutive columns of C.
 //  * Rows past M (A) and past K (B) read as zero through the buffer range
 //    check; the K tail and columns past N are masked per lane, only on the
-//    slabs / tiles that need it.
+//    slabs / tiles that need it; C stores outside the matrix are dropped by
+//    the range check or masked (no index wrapping; review of the
+//    work-stealing kernel in tritonBLAS PR #65).
 #include "common.hpp"
 
 namespace pgk {
@@ -38,29 +51,41 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;
 constexpr unsigned kOob = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NST>
 struct Shape {
   static constexpr int WM = 2, WN = 2;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int SM = TM / 32, SN = TN / 32;
-  static constexpr int A_BYTES = BM * BK * 2;       // one stage of A
-  static constexpr int B_BYTES = BK * BN * 2;       // one stage of B
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE + 16;
-  static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per stage
-  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int KK = BK / 16;                  // MFMA k-steps per slab
+  static constexpr int A_ROW = BK * 2;                // bytes per LDS row of A
+  static constexpr int A_BYTES = BM * A_ROW;          // one stage of A
   static constexpr int B_ROW = BN * 2;                // bytes per LDS row of B
-  static constexpr int B_ROWS_PER_INSTR = 1024 / B_ROW;
-  static constexpr int B_CPR = BN / 8;                // 16-byte chunks per row of B
-  static_assert(B_ROWS_PER_INSTR >= 1 && 1024 % B_ROW == 0, "B row must divide 1 KiB");
+  static constexpr int B_BYTES = BK * B_ROW;          // one stage of B
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = NST * STAGE + 32;
+  static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per slab
+  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int LOADS = A_INSTR + B_INSTR;     // vmcnt units per slab
+  static constexpr int A_RPI = 1024 / A_ROW;          // A rows per load instruction
+  static constexpr int A_CPR = A_ROW / 16;            // 16-byte chunks per A row
+  static constexpr int B_RPI = 1024 / B_ROW;
+  static constexpr int B_CPR = B_ROW / 16;
+  static_assert(BK == 32 || BK == 64, "slab depth");
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1 && 1024 % B_ROW == 0, "slab splits into 1 KiB loads");
+  static_assert(NST >= 2 && NST <= 4 && (NST - 1) * LOADS <= 63, "vmcnt range");
 };
 
-// Buffer resource over [base, base + bytes).  base and bytes are uniform
-// across the wave; readfirstlane states that, so the resource lives in SGPRs.
+// Physical chunk of logical chunk c in row `row` of A.
+template <int BK>
+__device__ __forceinline__ int swz_a(int row, int c) {
+  return BK == 64 ? (c ^ (row & 7)) : (c ^ ((row >> 1) & 3));
+}
+
+// Buffer resource over [base, base + bytes); base and bytes are uniform
+// across the wave and readfirstlane says so, so the resource lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
   const unsigned long long b = reinterpret_cast<unsigned long long>(base);
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
@@ -79,14 +104,38 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// vmcnt(0): this wave's buffer loads, including the ones into LDS, have landed.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Copy one accumulator out of its AGPR.  Spelling the read out keeps the
+// register allocator from moving all accumulators to VGPRs (the conversion
+// to bf16 is a VALU instruction and cannot read AGPRs).
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
 
-template <int BM, int BN, bool OUT_BF16, bool WITNESS>
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `ahead` younger slabs of loads (LOADS instructions
+// each) are still in flight.
+template <int LOADS, int NST>
+__device__ __forceinline__ void wait_slabs(int ahead) {
+  if (NST > 3 && ahead >= 3) wait_vm<3 * LOADS>();
+  else if (NST > 2 && ahead == 2) wait_vm<2 * LOADS>();
+  else if (ahead == 1) wait_vm<LOADS>();
+  else wait_vm<0>();
+}
+
+template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
-  using S = Shape<BM, BN>;
+  using S = Shape<BM, BN, BK, NST>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  int* s_tile = reinterpret_cast<int*>(smem + 2 * S::STAGE);
+  int* s_first = reinterpret_cast<int*>(smem + NST * S::STAGE);
+  int* s_next = s_first + 1;  // [2]: the loader's next tile, double-buffered by claim parity
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,27 +152,26 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   if (WITNESS && tid == 0) t_start = wall_ticks();
 
   // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
-  // A: wave instruction q covers rows 8q .. 8q+7; lane p -> row 8q + p/8,
-  // LDS chunk p%8, global chunk (p%8) ^ (p/8).
-  const int a_c = (lane & 7) ^ (lane >> 3);
-  const unsigned a_lane = (unsigned)(lane >> 3) * (unsigned)K * 2u + (unsigned)a_c * 16u;
-  const unsigned a_qstep = 8u * (unsigned)K * 2u;
-  // B: wave instruction q covers rows R*q .. ; lane p -> row R*q + p/CPR,
-  // LDS chunk p%CPR, global chunk (p%CPR) ^ 2*(row & 3).
-  auto b_row = [&](int q) { return q * S::B_ROWS_PER_INSTR + lane / S::B_CPR; };
+  // A: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
+  // chunk p%CPR, global chunk swz_a(row, p%CPR) (the swizzle is an involution
+  // and does not depend on q).
+  const int a_r = lane / S::A_CPR;
+  const int a_c = swz_a<BK>(a_r, lane % S::A_CPR);
+  const unsigned a_lane = (unsigned)a_r * (unsigned)K * 2u + (unsigned)a_c * 16u;
+  const unsigned a_qstep = (unsigned)S::A_RPI * (unsigned)K * 2u;
+  // B: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
+  // chunk p%CPR, global chunk (p%CPR) ^ 2*(row & 3).
+  auto b_row = [&](int q) { return q * S::B_RPI + lane / S::B_CPR; };
   auto b_chunk = [&](int q) { return (lane % S::B_CPR) ^ (2 * (b_row(q) & 3)); };
 
   // ---- LDS read offsets ----
   const int l32 = lane & 31;
-  unsigned rd_a[BK / 16];
+  unsigned rd_a[S::KK];
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
+  for (int kk = 0; kk < S::KK; ++kk) {
     const int row = wm * S::TM + l32;
-    const int c = (kk * 2 + (lane >> 5)) ^ (lane & 7);
-    rd_a[kk] = (unsigned)(row * 128 + c * 16);
+    rd_a[kk] = (unsigned)(row * S::A_ROW + swz_a<BK>(row, kk * 2 + (lane >> 5)) * 16);
   }
-  // B^T through the transpose read: lane i of a 16-lane group g points at
-  // row K0 + i/4, column N0 + 4*(i%4).
   unsigned rd_b[S::SN];
   {
     const int g = lane >> 4, i16 = lane & 15, a = i16 & 3, e = i16 >> 2;
@@ -177,13 +225,13 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       }
 #pragma unroll
       for (int sm = 0; sm < S::SM; ++sm)
-        af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * 128);
+        af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * S::A_ROW);
     };
     frag(0, 0);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < S::KK; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < BK / 16) frag(kk + 1, cur ^ 1);
+      if (kk + 1 < S::KK) frag(kk + 1, cur ^ 1);
 #pragma unroll
       for (int sn = 0; sn < S::SN; ++sn)
 #pragma unroll
@@ -213,8 +261,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
           const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
           const f32x16& a = acc[sn][sm];
           if (OUT_BF16) {
-            const u32x2 v = u32x2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
-                                  pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            const u32x2 v = u32x2{pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1])),
+                                  pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]))};
             __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
           } else {
             const f32x4 v = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
@@ -225,29 +273,43 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
-  if (tid == 0) s_tile[0] = walker.first();
-  __syncthreads();
-  int tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  int stage = 0;
-  int it = 0;
-  if (tile >= 0) {
+  auto coords = [&](int v, int& m0, int& n0) {
     int pm, pn;
-    walker.tile_coords(tile, pm, pn);
-    gload(0, pm * BM, pn * BN, 0);
-  }
-  wait_vm0();
-  __syncthreads();
+    walker.tile_coords(v, pm, pn);
+    m0 = pm * BM;
+    n0 = pn * BN;
+  };
 
-  while (tile >= 0) {
-    int pm, pn;
-    walker.tile_coords(tile, pm, pn);
-    const int m0 = pm * BM, n0 = pn * BN;
+  const int nk = (K + BK - 1) / BK;
+  const int dist = nk < NST - 1 ? nk : NST - 1;  // slabs the loader runs ahead
+
+  if (tid == 0) s_first[0] = walker.first();
+  __syncthreads();
+  int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
+  int lt = ct, lk = 0;                                   // loader: tile, next slab
+  int pend = -1;                                         // tile the loader moved on to
+  int issued = 0;                                        // slabs issued so far
+  int claims = 0;                                        // loader tile changes so far
+  int g = 0;                                             // slabs computed so far
+  int lm0 = 0, ln0 = 0;                                  // loader tile origin
+  int it = 0;                                            // tiles finished
+  if (lt >= 0) {
+    coords(lt, lm0, ln0);
+    for (int i = 0; i < dist; ++i) {
+      gload(issued % NST, lm0, ln0, lk * BK);
+      ++issued;
+      ++lk;
+    }
+    if (lk == nk && tid == 0) s_next[0] = walker.next(lt);
+  }
+
+  int m0 = lm0, n0 = ln0;
+  while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
-        atomicAdd(P.w.visits + tile, 1);
-        P.w.owner[tile] = prog;
-        P.w.order[tile] = it;
+        atomicAdd(P.w.visits + ct, 1);
+        P.w.owner[ct] = prog;
+        P.w.order[ct] = it;
       }
       if (P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
     }
@@ -257,43 +319,36 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
-
-    const int slot = (it + 1) & 1;
-    if (nk == 1 && tid == 0) s_tile[slot] = walker.next(tile);
-    for (int kb = 0; kb + 1 < nk; ++kb) {
-      if (kb == nk - 2 && tid == 0) s_tile[slot] = walker.next(tile);
-      gload(stage ^ 1, m0, n0, (kb + 1) * BK);
-      compute(stage);
-      wait_vm0();
+    for (int ck = 0; ck < nk; ++ck) {
+      wait_slabs<S::LOADS, NST>(issued - g - 1);
       __syncthreads();
-      stage ^= 1;
-    }
-    int next = -1;
-    if (nk >= 2) {
-      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
-      if (next >= 0) {
-        int qm, qn;
-        walker.tile_coords(next, qm, qn);
-        gload(stage ^ 1, qm * BM, qn * BN, 0);
+      // loader: one slab, moving on to the next tile when this one is issued
+      if (lt >= 0) {
+        if (lk == nk) {
+          lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+          ++claims;
+          lk = 0;
+          if (lt >= 0) {
+            pend = lt;
+            coords(lt, lm0, ln0);
+          }
+        }
+        if (lt >= 0) {
+          gload(issued % NST, lm0, ln0, lk * BK);
+          ++issued;
+          ++lk;
+          if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+        }
       }
+      // matrix cores: one slab of the current tile
+      compute(g % NST);
+      ++g;
     }
-    compute(stage);
-    wait_vm0();
-    __syncthreads();
-    stage ^= 1;
     epilogue(m0, n0);
-    if (nk == 1) {
-      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
-      if (next >= 0) {
-        int qm, qn;
-        walker.tile_coords(next, qm, qn);
-        gload(stage, qm * BM, qn * BN, 0);
-      }
-      wait_vm0();
-      __syncthreads();
-    }
-    tile = next;
     ++it;
+    ct = pend;
+    pend = -1;
+    if (ct >= 0) coords(ct, m0, n0);
   }
 
   if (WITNESS && tid == 0) {
@@ -304,10 +359,13 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   }
 }
 
+constexpr int kBK = 32;
+constexpr int kNST = 4;
+
 template <int BM, int BN, bool OUT_BF16, bool WITNESS>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
-  using S = Shape<BM, BN>;
-  auto kern = gemm_bf16_lds_kernel<BM, BN, OUT_BF16, WITNESS>;
+  using S = Shape<BM, BN, kBK, kNST>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, WITNESS>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
