@@ -90,5 +90,5 @@ def test_add_schedule_exactly_once(sched, tile):
     pg.padd_run(cfg, X, Y, C, rows, cols, tile[0], tile[1], sched,
                 pg.make_args(debug_flags=pg._abi.DEBUG_WITNESS))
     w = cfg.witness_read(pm * pn, G)
-    chunk = {(32, 16): 16, (64, 64): 2, (128, 128): 1}[tile]
+    chunk = {(32, 16): 32, (64, 64): 4, (128, 128): 1}[tile]
     _check(w, sched, pm, pn, G, cfg.info["num_xcds"], 8, chunk)

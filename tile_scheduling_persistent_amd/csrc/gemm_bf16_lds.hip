@@ -18,10 +18,9 @@
 //    waits only for the slab it is about to consume (vmcnt counts the
 //    younger slabs still in flight).
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
-//    (row & 7 for 128-byte rows, (row >> 1) & 3 for 64-byte rows) so that the
-//    ds_read_b128 operand reads of 8 consecutive rows hit distinct banks.
+//    so that the ds_read_b128 operand reads hit distinct banks (see swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
-//    c ^ 2*(k & 3)); the k-contiguous operand the MFMA needs is produced by
+//    c ^ 4*(k & 3)); the k-contiguous operand the MFMA needs is produced by
 //    ds_read_b64_tr_b16: within each 16-lane group, lane i points at row
 //    K0 + i/4, columns N0 + 4*(i%4) .. +3, and lane j receives rows
 //    K0 .. K0+3 of column N0 + j.  Two such reads give a lane its 8 k-values.
@@ -76,13 +75,27 @@ struct Shape {
   static_assert(BK == 32 || BK == 64, "slab depth");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && 1024 % B_ROW == 0, "slab splits into 1 KiB loads");
   static_assert(NST >= 2 && NST <= 4 && (NST - 1) * LOADS <= 63, "vmcnt range");
+  static_assert(KK % 2 == 0, "the next slab's first k-step lands in fragment slot 0");
 };
 
-// Physical chunk of logical chunk c in row `row` of A.
+// LDS banks: 64 x 4 bytes.  A ds_read_b128 is served 16 lanes at a time and
+// a ds_read_b64 (also the transposing form) 32 lanes at a time, so a read is
+// conflict-free when those lanes hit distinct 16- (8-) byte slots of a
+// 256-byte window.
+//
+// Physical chunk of logical chunk c in row `row` of A: the MFMA operand read
+// touches 16 consecutive rows at one logical chunk; the XOR spreads them
+// over the 16 slots (128-byte rows: 2 rows per window x 8 chunks; 64-byte
+// rows: 4 rows x 4 chunks).
 template <int BK>
 __device__ __forceinline__ int swz_a(int row, int c) {
-  return BK == 64 ? (c ^ (row & 7)) : (c ^ ((row >> 1) & 3));
+  return BK == 64 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
 }
+
+// Physical chunk of logical chunk c in row k of B: a transposing read of 32
+// lanes touches 4 consecutive rows x 4 consecutive chunks; XOR-ing chunk
+// bits 2-3 with the row moves the 4 rows to different quarter windows.
+__device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
 
 // Buffer resource over [base, base + bytes); base and bytes are uniform
 // across the wave and readfirstlane says so, so the resource lives in SGPRs.
@@ -153,16 +166,14 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 
   // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
   // A: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
-  // chunk p%CPR, global chunk swz_a(row, p%CPR) (the swizzle is an involution
-  // and does not depend on q).
-  const int a_r = lane / S::A_CPR;
-  const int a_c = swz_a<BK>(a_r, lane % S::A_CPR);
-  const unsigned a_lane = (unsigned)a_r * (unsigned)K * 2u + (unsigned)a_c * 16u;
-  const unsigned a_qstep = (unsigned)S::A_RPI * (unsigned)K * 2u;
+  // chunk p%CPR, global chunk swz_a(row, p%CPR) (the swizzle is an
+  // involution).
+  auto a_row = [&](int q) { return q * S::A_RPI + lane / S::A_CPR; };
+  auto a_chunk = [&](int q) { return swz_a<BK>(a_row(q), lane % S::A_CPR); };
   // B: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
-  // chunk p%CPR, global chunk (p%CPR) ^ 2*(row & 3).
+  // chunk p%CPR, global chunk swz_b(row, p%CPR).
   auto b_row = [&](int q) { return q * S::B_RPI + lane / S::B_CPR; };
-  auto b_chunk = [&](int q) { return (lane % S::B_CPR) ^ (2 * (b_row(q) & 3)); };
+  auto b_chunk = [&](int q) { return swz_b(b_row(q), lane % S::B_CPR); };
 
   // ---- LDS read offsets ----
   const int l32 = lane & 31;
@@ -179,7 +190,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
     for (int sn = 0; sn < S::SN; ++sn) {
       const int n = wn * S::TN + sn * 32 + (g & 1) * 16 + 4 * a;
-      const int c = (n >> 3) ^ (2 * e);
+      const int c = swz_b(krow, n >> 3);
       rd_b[sn] = (unsigned)(S::A_BYTES + krow * S::B_ROW + c * 16 + 8 * (a & 1));
     }
   }
@@ -196,8 +207,9 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
       const int q = wave * S::A_INSTR + i;
-      unsigned off = a_lane + (unsigned)q * a_qstep;
-      if (!a_full && k0 + a_c * 8 >= K) off = kOob;
+      const int c = a_chunk(q);
+      unsigned off = (unsigned)a_row(q) * (unsigned)K * 2u + (unsigned)c * 16u;
+      if (!a_full && k0 + c * 8 >= K) off = kOob;
       load_lds16(rA, sbase + q * 1024, off);
     }
 #pragma unroll
@@ -211,34 +223,31 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   };
 
   f32x16 acc[S::SN][S::SM];
+  // MFMA operand fragments, double-buffered by k-step; slot 0 of a slab's
+  // first k-step is filled during the previous slab (across the barrier).
+  bf16x8 bf[2][S::SN], af[2][S::SM];
 
-  auto compute = [&](int st) {
+  auto frag = [&](int st, int kk, int slot) {
     const unsigned char* sbase = smem + st * S::STAGE;
-    bf16x8 bf[2][S::SN], af[2][S::SM];
-    auto frag = [&](int kk, int slot) {
 #pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn) {
-        const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * S::B_ROW));
-        bf[slot][sn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+    for (int sn = 0; sn < S::SN; ++sn) {
+      const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * S::B_ROW));
+      bf[slot][sn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int sm = 0; sm < S::SM; ++sm)
+      af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * S::A_ROW);
+  };
+
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int sn = 0; sn < S::SN; ++sn)
 #pragma unroll
       for (int sm = 0; sm < S::SM; ++sm)
-        af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * S::A_ROW);
-    };
-    frag(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < S::KK; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < S::KK) frag(kk + 1, cur ^ 1);
-#pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn)
-#pragma unroll
-        for (int sm = 0; sm < S::SM; ++sm)
-          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][sn], af[cur][sm],
-                                                                acc[sn][sm], 0, 0, 0);
-    }
+        acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[slot][sn], af[slot][sm],
+                                                              acc[sn][sm], 0, 0, 0);
   };
 
   auto epilogue = [&](int m0, int n0) {
@@ -303,7 +312,25 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     if (lk == nk && tid == 0) s_next[0] = walker.next(lt);
   }
 
+  // loader: one slab, moving on to the next tile once this one is issued
+  auto loader_step = [&]() {
+    if (lt < 0) return;
+    if (lk == nk) {
+      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+      ++claims;
+      lk = 0;
+      if (lt < 0) return;
+      pend = lt;
+      coords(lt, lm0, ln0);
+    }
+    gload(issued % NST, lm0, ln0, lk * BK);
+    ++issued;
+    ++lk;
+    if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+  };
+
   int m0 = lm0, n0 = ln0;
+  bool pre = false;  // slot 0 already holds the first k-step of slab g
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -320,28 +347,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
     for (int ck = 0; ck < nk; ++ck) {
-      wait_slabs<S::LOADS, NST>(issued - g - 1);
+      // Slab g landed during an earlier wait.  If slab g+1 was issued before
+      // this point, wait for it too, so that its first fragments can be read
+      // at the end of this slab; the barrier also frees the stage of slab g-1
+      // for the loader.
+      const bool next_ready = issued > g + 1;
+      wait_slabs<S::LOADS, NST>(issued - (next_ready ? g + 2 : g + 1));
       __syncthreads();
-      // loader: one slab, moving on to the next tile when this one is issued
-      if (lt >= 0) {
-        if (lk == nk) {
-          lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
-          ++claims;
-          lk = 0;
-          if (lt >= 0) {
-            pend = lt;
-            coords(lt, lm0, ln0);
-          }
-        }
-        if (lt >= 0) {
-          gload(issued % NST, lm0, ln0, lk * BK);
-          ++issued;
-          ++lk;
-          if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
-        }
+      const int st = g % NST;
+      if (!pre) frag(st, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < S::KK; ++kk) {
+        const int slot = kk & 1;
+        if (kk + 1 < S::KK) frag(st, kk + 1, slot ^ 1);
+        else if (next_ready) frag((g + 1) % NST, 0, slot ^ 1);
+        mfmas(slot);
+        if (kk == 0) loader_step();
       }
-      // matrix cores: one slab of the current tile
-      compute(g % NST);
+      pre = next_ready;
       ++g;
     }
     epilogue(m0, n0);
@@ -359,8 +382,14 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   }
 }
 
-constexpr int kBK = 32;
-constexpr int kNST = 4;
+#ifndef PGK_LDS_BK
+#define PGK_LDS_BK 64
+#endif
+#ifndef PGK_LDS_NST
+#define PGK_LDS_NST 2
+#endif
+constexpr int kBK = PGK_LDS_BK;    // slab depth
+constexpr int kNST = PGK_LDS_NST;  // LDS stages
 
 template <int BM, int BN, bool OUT_BF16, bool WITNESS>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {

@@ -15,8 +15,8 @@
 // positions to MFMA blocks does not matter.
 //
 // Data movement as in gemm_bf16_lds.hip: buffer_load ... lds for A ([m][k],
-// 128-byte rows, chunk c at c ^ (m & 7)) and B ([k][n], chunk c of row k at
-// c ^ (k & 7)); A operands by ds_read_b128, B^T operands by
+// 128-byte rows) and B ([k][n]), both chunk-swizzled against LDS bank
+// conflicts (swz_a, swz_b); A operands by ds_read_b128, B^T operands by
 // ds_read_b64_tr_b8 (within a 16-lane group, lane i points at row
 // K0 + i/2, columns N0 + 8*(i%2) .. +7, and lane j receives rows K0 .. K0+7
 // of column N0 + j).  Lane l of the MFMA owns logical K positions
@@ -79,6 +79,18 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// LDS banks: 64 x 4 bytes; ds_read_b128 is served 16 lanes at a time,
+// ds_read_b64 (and its transposing form) 32 lanes at a time.
+// A rows are 128 bytes: the operand read touches 16 consecutive rows at one
+// chunk, spread over 16 slots of a 256-byte window by XOR-ing (row >> 1).
+__device__ __forceinline__ int swz_a(int row, int c) { return c ^ ((row >> 1) & 7); }
+// B rows are BN bytes: a transposing read of 32 lanes touches 8 consecutive
+// rows x 2 adjacent chunks.
+template <int BN>
+__device__ __forceinline__ int swz_b(int k, int c) {
+  return BN >= 256 ? (c ^ (2 * (k & 7))) : (c ^ (k & 6));
+}
+
 template <int OPSEL_A, int OPSEL_B>
 __device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtE4M3, kFmtE4M3, OPSEL_A, sa,
@@ -106,14 +118,13 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   if (WITNESS && tid == 0) t_start = wall_ticks();
 
   // A: instruction q covers rows 8q .. 8q+7; lane p -> row 8q + p/8, LDS
-  // chunk p%8, global chunk (p%8) ^ (p/8).
-  const int a_c = (lane & 7) ^ (lane >> 3);
-  const unsigned a_lane = (unsigned)(lane >> 3) * (unsigned)K + (unsigned)a_c * 16u;
-  const unsigned a_qstep = 8u * (unsigned)K;
+  // chunk p%8, global chunk swz_a(row, p%8).
+  auto a_row = [&](int q) { return q * 8 + (lane >> 3); };
+  auto a_chunk = [&](int q) { return swz_a(a_row(q), lane & 7); };
   // B: instruction q covers rows R*q ..; lane p -> row R*q + p/CPR, LDS chunk
-  // p%CPR, global chunk (p%CPR) ^ (row & 7).
+  // p%CPR, global chunk swz_b(row, p%CPR).
   auto b_row = [&](int q) { return q * S::B_ROWS_PER_INSTR + lane / S::B_CPR; };
-  auto b_chunk = [&](int q) { return (lane % S::B_CPR) ^ (b_row(q) & 7); };
+  auto b_chunk = [&](int q) { return swz_b<BN>(b_row(q), lane % S::B_CPR); };
 
   // LDS read offsets.  A: lane l, sub-tile sm, step ks reads row
   // wm*TM + sm*32 + l%32, bytes ks*64 + (l/32)*32 .. +31 (two chunks).
@@ -125,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = wm * S::TM + l32;
-      const int c = (ks * 4 + hi * 2 + h) ^ (lane & 7);
+      const int c = swz_a(row, ks * 4 + hi * 2 + h);
       rd_a[ks][h] = (unsigned)(row * BK + c * 16);
     }
   // B^T: 16-lane group g, lane i -> row K0 + i/2, columns N0 + 8*(i%2);
@@ -137,7 +148,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     for (int sn = 0; sn < S::SN; ++sn) {
       const int n = wn * S::TN + sn * 32 + (g & 1) * 16 + 8 * h;
       const int krow = hi * 32 + e;  // + ks*64 + 8r: multiples of 8 keep (row & 7) = e
-      const int c = (n >> 4) ^ e;
+      const int c = swz_b<BN>(krow, n >> 4);
       rd_b[sn] = (unsigned)(S::A_BYTES + krow * BN + c * 16 + (n & 15));
     }
   }
@@ -173,7 +184,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
       const int q = wave * S::A_INSTR + i;
-      load_lds16(rA, sbase + q * 1024, a_lane + (unsigned)q * a_qstep);
+      load_lds16(rA, sbase + q * 1024, (unsigned)a_row(q) * (unsigned)K + (unsigned)a_chunk(q) * 16u);
     }
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i) {

@@ -7,10 +7,11 @@
 // per-XCD work-stealing walk of "Work Stealing Scheduler Kernel" (tritonBLAS
 // PR #65) applies unchanged.
 //
-// The add is bound by HBM bandwidth, so a workgroup keeps U tiles of its
-// sequence in flight at once: every thread issues all its 16-byte loads of X
-// and Y for the U tiles before any add, which gives each compute unit about
-// 64 KiB of outstanding reads.  The tiles of a step are the next U tiles the
+// The add is bound by HBM bandwidth, so a workgroup of 1024 threads keeps U
+// tiles of its sequence in flight at once: every thread issues all its
+// 16-byte loads of X and Y for the U tiles before any add, which gives each
+// compute unit about 128 KiB of outstanding reads.  Stores stream past the
+// caches (nontemporal).  The tiles of a step are the next U tiles the
 // scheduler gives the program (for work stealing: one claim of U tiles, and
 // the claim for the following step is issued before the current step's
 // loads so its latency is hidden).
@@ -21,14 +22,20 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+// 16 waves per compute unit: enough loads in flight to cover HBM latency
+// with one program per CU.
+constexpr int kThreads = 1024;
 
 template <int TR, int TC>
 struct AddShape {
   static constexpr int F4 = TR * TC / 4;  // float4 per tile
-  // tiles per step: ~8 float4 per thread per operand
-  static constexpr int U = (8 * kThreads) / F4 > 0 ? (8 * kThreads) / F4 : 1;
+  // tiles per step: ~4 float4 per thread per operand
+  static constexpr int U = (4 * kThreads) / F4 > 0 ? (4 * kThreads) / F4 : 1;
   static constexpr int SLOTS = (U * F4 + kThreads - 1) / kThreads;
+  // Streaming (nontemporal) loads pay off when a tile row covers whole
+  // 128-byte lines; 16-column tiles share lines between neighbouring tiles,
+  // which a later step of the same program may still find in cache.
+  static constexpr bool NT_LOAD = TC * 4 >= 128;
   static_assert(TC % 4 == 0, "tile columns must be a multiple of 4");
 };
 
@@ -110,8 +117,15 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     for (int j = 0; j < S::SLOTS; ++j) {
       if (VEC) {
         if (cnt[j] > 0) {
-          xa[j] = *reinterpret_cast<const f32x4*>(P.X + off[j]);
-          ya[j] = *reinterpret_cast<const f32x4*>(P.Y + off[j]);
+          const f32x4* px = reinterpret_cast<const f32x4*>(P.X + off[j]);
+          const f32x4* py = reinterpret_cast<const f32x4*>(P.Y + off[j]);
+          if (S::NT_LOAD) {
+            xa[j] = __builtin_nontemporal_load(px);
+            ya[j] = __builtin_nontemporal_load(py);
+          } else {
+            xa[j] = *px;
+            ya[j] = *py;
+          }
         }
       } else {
 #pragma unroll
@@ -126,7 +140,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
       if (cnt[j] <= 0) continue;
       const f32x4 z = xa[j] + ya[j];
       if (VEC) {
-        *reinterpret_cast<f32x4*>(P.C + off[j]) = z;
+        __builtin_nontemporal_store(z, reinterpret_cast<f32x4*>(P.C + off[j]));
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
