@@ -41,10 +41,28 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", default="", help="comma list of schedulers to time (profiling runs)")
+    p.add_argument("--only", default="", help="comma list of schedulers (or keys such as work_stealing_g8) to time (profiling runs)")
     p.add_argument("--skip-add", action="store_true")
     p.add_argument("--skip-extra", action="store_true", help="only the 8192^3 bf16 GEMM and the add")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only time a plain 256 MiB device-to-device copy (the reference kernel for "
+                        "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(steps, warmup):
+    """A plain copy of a 256 MiB fp32 buffer: reads 256 MiB and writes 256 MiB
+    per launch, so a counter pass over it gives the factor between what the
+    counter reports and the bytes actually moved."""
+    import torch
+    n = 64 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ms, ev_mean, _ = time_calls(lambda: dst.copy_(src), steps, warmup, stream)
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
+                                           "event_ms_mean": round(ev_mean, 5),
+                                           "gbs": round(8 * n / (ev_mean * 1e-3) / 1e9, 1)}}), flush=True)
 
 
 def time_calls(fn, steps, warmup, stream):
@@ -89,6 +107,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
                                    "(the sharding plan is described, not run)"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps, args.warmup)
+        return
     import torch
     import tile_scheduling_persistent_amd as pg
     from synthetic import bf16_bits_normal, f32_normal
@@ -105,12 +126,12 @@ def main():
     only = set(s for s in args.only.split(",") if s)
     per = {}
     for sched, gs in SCHEDS:
-        if only and sched not in only:
+        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped") else "")
+        if only and sched not in only and key not in only:
             continue
         a = pg.make_args(tile=(256, 256, 64), group_size=gs)
         fn = lambda: pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)  # noqa: E731
         ms, ev_mean, ev_min = time_calls(fn, args.steps, args.warmup, stream)
-        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped") else "")
         per[key] = {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "event_ms_mean": ev_mean,
                     "event_ms_min": ev_min,
                     "frac_peak": flops / (ev_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}

@@ -16,7 +16,12 @@
 //    the last slab of the current one, so a work-stealing claim happens
 //    NST-1 slabs before the tile is needed.  One barrier per slab; each wave
 //    waits only for the slab it is about to consume (vmcnt counts the
-//    younger slabs still in flight).
+//    younger slabs still in flight).  The loads are issued by hand and the
+//    barrier carries no memory fence (lds_dma.hpp), so the compiler adds no
+//    wait for the slab in flight before the LDS reads of the current one.
+//  * Within a k-step the fragment reads of the next k-step are spread over
+//    the matrix instructions (one LDS read after each MFMA), so their issue
+//    and latency hide behind the MFMA pipeline.
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
 //    so that the ds_read_b128 operand reads hit distinct banks (see swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
@@ -33,6 +38,7 @@
 //    the range check or masked (no index wrapping; review of the
 //    work-stealing kernel in tritonBLAS PR #65).
 #include "common.hpp"
+#include "lds_dma.hpp"
 
 namespace pgk {
 namespace {
@@ -46,12 +52,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr unsigned kOob = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;
 
 template <int BM, int BN, int BK, int NST>
 struct Shape {
@@ -97,22 +100,6 @@ __device__ __forceinline__ int swz_a(int row, int c) {
 // bits 2-3 with the row moves the 4 rows to different quarter windows.
 __device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
 
-// Buffer resource over [base, base + bytes); base and bytes are uniform
-// across the wave and readfirstlane says so, so the resource lives in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           kRsrcWord3);
-}
-
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_dst,
-                                           unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
-}
-
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
@@ -124,13 +111,6 @@ __device__ __forceinline__ float acc_read(float x) {
   float r;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
   return r;
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // Wait until at most `ahead` younger slabs of loads (LOADS instructions
@@ -199,9 +179,9 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   auto gload = [&](int st, int m0, int n0, int k0) {
     unsigned char* sbase = smem + st * S::STAGE;
     const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const auto rA = rsrc(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0) * 2u);
+    const rsrc_words_t rA = rsrc_words(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0) * 2u);
     const int krows = (K - k0) < BK ? (K - k0) : BK;
-    const auto rB = rsrc(B + (size_t)k0 * N + n0, (unsigned)(krows * N - n0) * 2u);
+    const rsrc_words_t rB = rsrc_words(B + (size_t)k0 * N + n0, (unsigned)(krows * N - n0) * 2u);
     const bool a_full = k0 + BK <= K;
     const bool b_full = n0 + BN <= N;
 #pragma unroll
@@ -353,15 +333,30 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       // for the loader.
       const bool next_ready = issued > g + 1;
       wait_slabs<S::LOADS, NST>(issued - (next_ready ? g + 2 : g + 1));
-      __syncthreads();
+      slab_barrier();
       const int st = g % NST;
       if (!pre) frag(st, 0, 0);
+      const int st1 = (g + 1) % NST;
 #pragma unroll
       for (int kk = 0; kk < S::KK; ++kk) {
         const int slot = kk & 1;
+        // Fragments of the next k-step (for the last k-step: the first one of
+        // the next slab, when a third stage lets it land early; read
+        // unconditionally, used only if next_ready).
+        constexpr int kReads = S::SN * 2 + S::SM;
+        const bool reads = kk + 1 < S::KK || NST > 2;
         if (kk + 1 < S::KK) frag(st, kk + 1, slot ^ 1);
-        else if (next_ready) frag((g + 1) % NST, 0, slot ^ 1);
+        else if (NST > 2) frag(st1, 0, slot ^ 1);
         mfmas(slot);
+        // Spread the LDS reads over the matrix instructions of this k-step.
+        if (reads) {
+#pragma unroll
+          for (int i = 0; i < kReads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, S::SN * S::SM - kReads, 0);
+        }
         if (kk == 0) loader_step();
       }
       pre = next_ready;

@@ -14,7 +14,9 @@
 // lane passes its row's scale for the slab's group and the assignment of K
 // positions to MFMA blocks does not matter.
 //
-// Data movement as in gemm_bf16_lds.hip: buffer_load ... lds for A ([m][k],
+// Data movement as in gemm_bf16_lds.hip: hand-issued buffer_load ... lds
+// (lds_dma.hpp; the next slab's loads stay in flight while the current
+// slab is read) for A ([m][k],
 // 128-byte rows) and B ([k][n]), both chunk-swizzled against LDS bank
 // conflicts (swz_a, swz_b); A operands by ds_read_b128, B^T operands by
 // ds_read_b64_tr_b8 (within a 16-lane group, lane i points at row
@@ -22,6 +24,7 @@
 // of column N0 + j).  Lane l of the MFMA owns logical K positions
 // 32*(l/32) .. +31 of each 64-deep step on both operands.
 #include "common.hpp"
+#include "lds_dma.hpp"
 
 namespace pgk {
 namespace {
@@ -34,13 +37,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kThreads = 256;
 constexpr int BK = 128;          // bytes of K per slab = one scale group
-constexpr unsigned kOob = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kFmtE4M3 = 0;      // f8f6f4 operand format code of e4m3
 
 template <int BM, int BN>
@@ -58,20 +58,6 @@ struct Shape {
   static constexpr int B_CPR = BN / 16;
   static_assert(SM <= 4 && SN <= 4, "scale bytes of at most 4 sub-tiles per register");
 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           kRsrcWord3);
-}
-
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_dst,
-                                           unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
-}
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -178,8 +164,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   auto gload = [&](int st, int m0, int n0, int k0) {
     unsigned char* sbase = smem + st * S::STAGE;
     const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const auto rA = rsrc(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0));
-    const auto rB = rsrc(B + (size_t)k0 * N + n0, (unsigned)(BK * N - n0));
+    const rsrc_words_t rA = rsrc_words(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0));
+    const rsrc_words_t rB = rsrc_words(B + (size_t)k0 * N + n0, (unsigned)(BK * N - n0));
     const bool b_full = n0 + BN <= N;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
@@ -272,7 +258,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     sload(pm * BM, pn * BN, 0, sa_nxt, sb_nxt);
   }
   wait_vm0();
-  __syncthreads();
+  slab_barrier();
 
   while (tile >= 0) {
     int pm, pn;
@@ -303,7 +289,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       sload(m0, n0, (kb + 1) * BK, sa_nxt, sb_nxt);
       compute(stage);
       wait_vm0();
-      __syncthreads();
+      slab_barrier();
       stage ^= 1;
     }
     sa_reg = sa_nxt;
@@ -320,7 +306,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     }
     compute(stage);
     wait_vm0();
-    __syncthreads();
+    slab_barrier();
     stage ^= 1;
     epilogue(m0, n0);
     if (nk == 1) {
@@ -332,7 +318,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
         sload(qm * BM, qn * BN, 0, sa_nxt, sb_nxt);
       }
       wait_vm0();
-      __syncthreads();
+      slab_barrier();
     }
     tile = next;
     ++it;

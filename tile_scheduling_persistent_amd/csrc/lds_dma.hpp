@@ -1,0 +1,68 @@
+// Global -> LDS movement shared by the direct-to-LDS GEMM kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace pgk {
+
+// A buffer offset past every range: the load returns zeros, a store is dropped.
+constexpr unsigned kOob = 0x80000000u;
+// Buffer resource word 3 for raw (unformatted, unswizzled) byte buffers.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Buffer resource over [base, base + bytes); base and bytes are uniform
+// across the wave and readfirstlane says so, so the resource lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           kRsrcWord3);
+}
+
+typedef unsigned rsrc_words_t __attribute__((ext_vector_type(4)));
+
+// The same resource as four SGPR words, for the hand-issued loads below.
+__device__ __forceinline__ rsrc_words_t rsrc_words(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  return rsrc_words_t{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)b),
+                      (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) & 0xffffu,
+                      (unsigned)__builtin_amdgcn_readfirstlane(bytes), (unsigned)kRsrcWord3};
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(unsigned long)((const __attribute__((address_space(3))) void*)p);
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset voff of
+// the buffer into LDS at lds_dst + 16 * lane (lds_dst uniform).  Issued by
+// hand: the compiler would treat the intrinsic form as an LDS store of
+// unknown extent and wait for every such load still in flight (vmcnt(0))
+// before each later LDS read, which serialises the slab pipeline.  The
+// kernels track completion themselves: s_waitcnt vmcnt on the issuing wave,
+// then a workgroup barrier, before any wave reads the slab.
+__device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned char* lds_dst, unsigned voff) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(r) : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// half waits for every outstanding global access): the caller has already
+// waited (vmcnt) for the LDS loads the other waves will read; this waits for
+// the wave's own LDS reads and writes, then meets the other waves.
+__device__ __forceinline__ void slab_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace pgk
