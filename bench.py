@@ -34,6 +34,17 @@ SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
 HEADLINE = ("work_stealing", 8)
 CPU_ROWS = 4096
 
+# HBM traffic of one 8192^3 launch of the bf16 GEMM kernel, from two
+# rocprofv3 counter passes over `bench.py --only work_stealing_g8` (FETCH_SIZE,
+# WRITE_SIZE; KiB per dispatch, mean of 4 dispatches), each scaled by what
+# the same counter reads for a plain 256 MiB device copy (`bench.py
+# --copy-calibration`: FETCH_SIZE x2.000, WRITE_SIZE x1.000).  Valid only for
+# the kernel sources it was measured on (hash below); otherwise reported as
+# null.
+TRAFFIC_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
+TRAFFIC_MEASURED = {"sources_sha256_16": "c0f2235eab7839f4",
+                    "fetch_bytes": 1705020618, "write_bytes": 190757344}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -82,6 +93,18 @@ def time_calls(fn, steps, warmup, stream):
     wall = time.perf_counter() - t0
     durs = [e0.elapsed_time(e1) for e0, e1 in evs]
     return wall * 1e3 / steps, float(np.mean(durs)), float(np.min(durs))
+
+
+def measured_traffic():
+    """Counter-derived HBM bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "tile_scheduling_persistent_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != TRAFFIC_MEASURED["sources_sha256_16"]:
+        return None
+    return TRAFFIC_MEASURED["fetch_bytes"] + TRAFFIC_MEASURED["write_bytes"]
 
 
 def cpu_baseline(a_bits, b_bits):
@@ -220,7 +243,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (counter passes, copy-calibrated)",
+                     "algorithmic_bytes": 2 * (M * K + K * N + M * N)},
         "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),
                               "event_ms_mean": round(v["event_ms_mean"], 5)} for k, v in per.items()},
         "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}

@@ -8,20 +8,23 @@
 //    wave instruction): no staging registers, no VALU work.  The LDS side of
 //    such a load is linear, so the bank swizzle is applied on the global side
 //    (each lane fetches the chunk that belongs at its LDS position).
-//  * NST LDS stages of BK-deep slabs form a ring; the loader runs NST-1
-//    slabs ahead of the matrix cores and walks straight on into the next
-//    tile of the schedule (the pipeline phase runs on across tiles, like the
-//    scheduler's iteration counter of "[Feature] Introduce tile scheduler",
-//    TileLang PR #2441).  The next tile is claimed when the loader issues
-//    the last slab of the current one, so a work-stealing claim happens
-//    NST-1 slabs before the tile is needed.  One barrier per slab; each wave
-//    waits only for the slab it is about to consume (vmcnt counts the
-//    younger slabs still in flight).  The loads are issued by hand and the
-//    barrier carries no memory fence (lds_dma.hpp), so the compiler adds no
+//  * Two LDS stages of 64-deep slabs: while the matrix cores work on slab g
+//    the loads of slab g+1 fill the other stage, and the loader walks
+//    straight on into the next tile of the schedule (the pipeline phase runs
+//    on across tiles, like the scheduler's iteration counter of "[Feature]
+//    Introduce tile scheduler", TileLang PR #2441).  The next tile is
+//    claimed when the loader sets up the last slab of the current one, one
+//    slab before it is needed.  One barrier per slab, after each wave has
+//    waited for its own loads (vmcnt).  The loads are issued by hand and the
+//    barrier carries no memory fence (gemm_device.hpp), so the compiler adds no
 //    wait for the slab in flight before the LDS reads of the current one.
-//  * Within a k-step the fragment reads of the next k-step are spread over
-//    the matrix instructions (one LDS read after each MFMA), so their issue
-//    and latency hide behind the MFMA pipeline.
+//  * The issue order inside a slab is fixed by hand (scheduling barriers):
+//    after each MFMA come its share of the next k-step's fragment reads and,
+//    in the first k-steps, one load of the next slab, so LDS reads, global
+//    loads and their latencies hide behind the MFMA pipeline instead of
+//    stalling the wave in bursts.  The loader's bookkeeping (tile switch,
+//    claim, buffer resources) runs right after the barrier, under the
+//    latency of the slab's first fragment reads.
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
 //    so that the ds_read_b128 operand reads hit distinct banks (see swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
@@ -38,23 +41,22 @@
 //    the range check or masked (no index wrapping; review of the
 //    work-stealing kernel in tritonBLAS PR #65).
 #include "common.hpp"
-#include "lds_dma.hpp"
+#include "gemm_device.hpp"
 
 namespace pgk {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
+constexpr int kLoadSpread = 2;  // k-steps of a slab that carry the next slab's loads
 
 template <int BM, int BN, int BK, int NST>
 struct Shape {
@@ -70,15 +72,12 @@ struct Shape {
   static constexpr int LDS_BYTES = NST * STAGE + 32;
   static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per slab
   static constexpr int B_INSTR = B_BYTES / 1024 / 4;
-  static constexpr int LOADS = A_INSTR + B_INSTR;     // vmcnt units per slab
   static constexpr int A_RPI = 1024 / A_ROW;          // A rows per load instruction
   static constexpr int A_CPR = A_ROW / 16;            // 16-byte chunks per A row
   static constexpr int B_RPI = 1024 / B_ROW;
   static constexpr int B_CPR = B_ROW / 16;
   static_assert(BK == 32 || BK == 64, "slab depth");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && 1024 % B_ROW == 0, "slab splits into 1 KiB loads");
-  static_assert(NST >= 2 && NST <= 4 && (NST - 1) * LOADS <= 63, "vmcnt range");
-  static_assert(KK % 2 == 0, "the next slab's first k-step lands in fragment slot 0");
 };
 
 // LDS banks: 64 x 4 bytes.  A ds_read_b128 is served 16 lanes at a time and
@@ -100,32 +99,20 @@ __device__ __forceinline__ int swz_a(int row, int c) {
 // bits 2-3 with the row moves the 4 rows to different quarter windows.
 __device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
 
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-// Copy one accumulator out of its AGPR.  Spelling the read out keeps the
-// register allocator from moving all accumulators to VGPRs (the conversion
-// to bf16 is a VALU instruction and cannot read AGPRs).
-__device__ __forceinline__ float acc_read(float x) {
-  float r;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
-  return r;
-}
-
-// Wait until at most `ahead` younger slabs of loads (LOADS instructions
-// each) are still in flight.
-template <int LOADS, int NST>
-__device__ __forceinline__ void wait_slabs(int ahead) {
-  if (NST > 3 && ahead >= 3) wait_vm<3 * LOADS>();
-  else if (NST > 2 && ahead == 2) wait_vm<2 * LOADS>();
-  else if (ahead == 1) wait_vm<LOADS>();
-  else wait_vm<0>();
-}
-
 template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   using S = Shape<BM, BN, BK, NST>;
+  static_assert(NST == 2, "two LDS stages: the loads of slab g+1 run during slab g");
+  constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NL = NA + NB;  // loads per wave per slab
+  constexpr int NMF = S::SN * S::SM;                             // MFMAs per k-step
+  constexpr int NRD = 2 * S::SN + S::SM;                         // LDS reads per k-step
+  // The slab's loads are spread over the MFMAs of its first kLoadSpread
+  // k-steps: load d is issued after MFMA number d*DSTEP + DSTEP-1 of the
+  // slab, so the texture unit takes them one at a time instead of stalling
+  // the wave on a burst of 16.
+  constexpr int DSTEP = (kLoadSpread * NMF) / NL > 1 ? (kLoadSpread * NMF) / NL : 1;
+  static_assert(NL * DSTEP <= (S::KK - 1) * NMF, "room for the loads among the MFMAs");
+
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* s_first = reinterpret_cast<int*>(smem + NST * S::STAGE);
   int* s_next = s_first + 1;  // [2]: the loader's next tile, double-buffered by claim parity
@@ -147,13 +134,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
   // A: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
   // chunk p%CPR, global chunk swz_a(row, p%CPR) (the swizzle is an
-  // involution).
-  auto a_row = [&](int q) { return q * S::A_RPI + lane / S::A_CPR; };
-  auto a_chunk = [&](int q) { return swz_a<BK>(a_row(q), lane % S::A_CPR); };
-  // B: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
-  // chunk p%CPR, global chunk swz_b(row, p%CPR).
-  auto b_row = [&](int q) { return q * S::B_RPI + lane / S::B_CPR; };
-  auto b_chunk = [&](int q) { return swz_b(b_row(q), lane % S::B_CPR); };
+  // involution).  B likewise with swz_b.
+  unsigned aoff[NA], boff[NB];
+  int achk[NA], bchk[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int q = wave * NA + i;
+    const int row = q * S::A_RPI + lane / S::A_CPR;
+    achk[i] = swz_a<BK>(row, lane % S::A_CPR);
+    aoff[i] = (unsigned)row * (unsigned)K * 2u + (unsigned)achk[i] * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int q = wave * NB + i;
+    const int row = q * S::B_RPI + lane / S::B_CPR;
+    bchk[i] = swz_b(row, lane % S::B_CPR);
+    boff[i] = (unsigned)row * (unsigned)N * 2u + (unsigned)bchk[i] * 16u;
+  }
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   // ---- LDS read offsets ----
   const int l32 = lane & 31;
@@ -175,59 +173,90 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     }
   }
 
-  // Issue the loads of slab (m0, n0, k0) into LDS stage `st`.
-  auto gload = [&](int st, int m0, int n0, int k0) {
-    unsigned char* sbase = smem + st * S::STAGE;
-    const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const rsrc_words_t rA = rsrc_words(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0) * 2u);
+  auto coords = [&](int v, int& m0, int& n0) {
+    int pm, pn;
+    walker.tile_coords(v, pm, pn);
+    m0 = pm * BM;
+    n0 = pn * BN;
+  };
+
+  const int nk = (K + BK - 1) / BK;
+
+  // ---- loader state ----
+  int lt = -1, lk = 0;      // loader: tile, next slab
+  int pend = -1;            // tile the loader moved on to
+  int claims = 0;           // loader tile changes so far
+  int lm0 = 0, ln0 = 0;     // loader tile origin
+  rsrc_words_t rA, rB;      // resources of the slab being loaded
+  unsigned ao[NA], bo[NB];  // its per-lane offsets (edge chunks pushed out of range)
+
+  // Pick the next slab for the loader (moving on to the next tile once the
+  // current one is issued) and set up its resources; without one the
+  // resources are empty, so the loads read zeros into a stage no one reads.
+  auto prep = [&]() {
+    bool load = false;
+    if (lt >= 0 && lk == nk) {
+      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+      ++claims;
+      lk = 0;
+      if (lt >= 0) {
+        pend = lt;
+        coords(lt, lm0, ln0);
+      }
+    }
+    const int k0 = lk * BK;
+    if (lt >= 0) {
+      load = true;
+      ++lk;
+      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+    }
+    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
     const int krows = (K - k0) < BK ? (K - k0) : BK;
-    const rsrc_words_t rB = rsrc_words(B + (size_t)k0 * N + n0, (unsigned)(krows * N - n0) * 2u);
+    rA = rsrc_words(A + (size_t)lm0 * K + k0, load ? (unsigned)(rows * K - k0) * 2u : 0u);
+    rB = rsrc_words(B + (size_t)k0 * N + ln0, load ? (unsigned)(krows * N - ln0) * 2u : 0u);
     const bool a_full = k0 + BK <= K;
-    const bool b_full = n0 + BN <= N;
+    const bool b_full = ln0 + BN <= N;
 #pragma unroll
-    for (int i = 0; i < S::A_INSTR; ++i) {
-      const int q = wave * S::A_INSTR + i;
-      const int c = a_chunk(q);
-      unsigned off = (unsigned)a_row(q) * (unsigned)K * 2u + (unsigned)c * 16u;
-      if (!a_full && k0 + c * 8 >= K) off = kOob;
-      load_lds16(rA, sbase + q * 1024, off);
-    }
+    for (int i = 0; i < NA; ++i) ao[i] = (a_full || k0 + achk[i] * 8 < K) ? aoff[i] : kOob;
 #pragma unroll
-    for (int i = 0; i < S::B_INSTR; ++i) {
-      const int q = wave * S::B_INSTR + i;
-      const int c = b_chunk(q);
-      unsigned off = (unsigned)b_row(q) * (unsigned)N * 2u + (unsigned)c * 16u;
-      if (!b_full && n0 + c * 8 >= N) off = kOob;
-      load_lds16(rB, sbase + S::A_BYTES + q * 1024, off);
-    }
+    for (int i = 0; i < NB; ++i) bo[i] = (b_full || ln0 + bchk[i] * 8 < N) ? boff[i] : kOob;
+  };
+
+  // Load d of the prepared slab into stage st.
+  auto dma = [&](int st, int d) {
+    const unsigned sb = lds0 + (unsigned)(st * S::STAGE);
+    if (d < NA)
+      load_lds16(rA, sb + (unsigned)((wave * NA + d) * 1024), ao[d]);
+    else
+      load_lds16(rB, sb + (unsigned)(S::A_BYTES + (wave * NB + d - NA) * 1024), bo[d - NA]);
   };
 
   f32x16 acc[S::SN][S::SM];
-  // MFMA operand fragments, double-buffered by k-step; slot 0 of a slab's
-  // first k-step is filled during the previous slab (across the barrier).
-  bf16x8 bf[2][S::SN], af[2][S::SM];
+  // MFMA operand fragments, double-buffered by k-step; B^T fragments arrive
+  // as two halves (4 k-values each).
+  i16x4 bh[2][S::SN][2];
+  bf16x8 af[2][S::SM];
 
-  auto frag = [&](int st, int kk, int slot) {
+  // LDS read r of k-step kk into slot: B^T block 0 first, then the A
+  // blocks, then the other B^T blocks (the order the MFMAs consume them).
+  auto read = [&](int st, int kk, int slot, int r) {
     const unsigned char* sbase = smem + st * S::STAGE;
-#pragma unroll
-    for (int sn = 0; sn < S::SN; ++sn) {
-      const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * S::B_ROW));
-      bf[slot][sn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int sm = 0; sm < S::SM; ++sm)
+    if (r >= 2 && r < 2 + S::SM) {
+      const int sm = r - 2;
       af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * S::A_ROW);
+    } else {
+      const int b = r < 2 ? r : r - S::SM;
+      const int sn = b >> 1, h = b & 1;
+      const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW + h * 4 * S::B_ROW;
+      bh[slot][sn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    }
   };
 
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int sn = 0; sn < S::SN; ++sn)
-#pragma unroll
-      for (int sm = 0; sm < S::SM; ++sm)
-        acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[slot][sn], af[slot][sm],
-                                                              acc[sn][sm], 0, 0, 0);
+  auto mfma = [&](int slot, int j) {
+    const int sn = j / S::SM, sm = j % S::SM;
+    const bf16x8 b = __builtin_bit_cast(
+        bf16x8, __builtin_shufflevector(bh[slot][sn][0], bh[slot][sn][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, af[slot][sm], acc[sn][sm], 0, 0, 0);
   };
 
   auto epilogue = [&](int m0, int n0) {
@@ -262,55 +291,20 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     }
   };
 
-  auto coords = [&](int v, int& m0, int& n0) {
-    int pm, pn;
-    walker.tile_coords(v, pm, pn);
-    m0 = pm * BM;
-    n0 = pn * BN;
-  };
-
-  const int nk = (K + BK - 1) / BK;
-  const int dist = nk < NST - 1 ? nk : NST - 1;  // slabs the loader runs ahead
-
   if (tid == 0) s_first[0] = walker.first();
   __syncthreads();
   int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
-  int lt = ct, lk = 0;                                   // loader: tile, next slab
-  int pend = -1;                                         // tile the loader moved on to
-  int issued = 0;                                        // slabs issued so far
-  int claims = 0;                                        // loader tile changes so far
-  int g = 0;                                             // slabs computed so far
-  int lm0 = 0, ln0 = 0;                                  // loader tile origin
-  int it = 0;                                            // tiles finished
+  lt = ct;
   if (lt >= 0) {
     coords(lt, lm0, ln0);
-    for (int i = 0; i < dist; ++i) {
-      gload(issued % NST, lm0, ln0, lk * BK);
-      ++issued;
-      ++lk;
-    }
-    if (lk == nk && tid == 0) s_next[0] = walker.next(lt);
+    prep();
+#pragma unroll
+    for (int d = 0; d < NL; ++d) dma(0, d);
   }
 
-  // loader: one slab, moving on to the next tile once this one is issued
-  auto loader_step = [&]() {
-    if (lt < 0) return;
-    if (lk == nk) {
-      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
-      ++claims;
-      lk = 0;
-      if (lt < 0) return;
-      pend = lt;
-      coords(lt, lm0, ln0);
-    }
-    gload(issued % NST, lm0, ln0, lk * BK);
-    ++issued;
-    ++lk;
-    if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
-  };
-
+  int g = 0;   // slabs computed so far
+  int it = 0;  // tiles finished
   int m0 = lm0, n0 = ln0;
-  bool pre = false;  // slot 0 already holds the first k-step of slab g
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -327,39 +321,32 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
     for (int ck = 0; ck < nk; ++ck) {
-      // Slab g landed during an earlier wait.  If slab g+1 was issued before
-      // this point, wait for it too, so that its first fragments can be read
-      // at the end of this slab; the barrier also frees the stage of slab g-1
-      // for the loader.
-      const bool next_ready = issued > g + 1;
-      wait_slabs<S::LOADS, NST>(issued - (next_ready ? g + 2 : g + 1));
+      // Slab g is in LDS once this wave's loads have landed and every wave
+      // has passed the barrier, which also frees the other stage.
+      wait_vm<0>();
       slab_barrier();
-      const int st = g % NST;
-      if (!pre) frag(st, 0, 0);
-      const int st1 = (g + 1) % NST;
+      const int st = g & 1;
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
+      prep();  // overlaps the latency of the first reads
+      __builtin_amdgcn_sched_barrier(0);
+      // Fixed issue order: MFMA, then its share of the next k-step's LDS
+      // reads, then (first KK-1 k-steps) a load of slab g+1.
 #pragma unroll
       for (int kk = 0; kk < S::KK; ++kk) {
         const int slot = kk & 1;
-        // Fragments of the next k-step (for the last k-step: the first one of
-        // the next slab, when a third stage lets it land early; read
-        // unconditionally, used only if next_ready).
-        constexpr int kReads = S::SN * 2 + S::SM;
-        const bool reads = kk + 1 < S::KK || NST > 2;
-        if (kk + 1 < S::KK) frag(st, kk + 1, slot ^ 1);
-        else if (NST > 2) frag(st1, 0, slot ^ 1);
-        mfmas(slot);
-        // Spread the LDS reads over the matrix instructions of this k-step.
-        if (reads) {
 #pragma unroll
-          for (int i = 0; i < kReads; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int j = 0; j < NMF; ++j) {
+          mfma(slot, j);
+          if (kk + 1 < S::KK) {
+#pragma unroll
+            for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, kk + 1, slot ^ 1, r);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, S::SN * S::SM - kReads, 0);
+          const int p = kk * NMF + j;
+          if (p % DSTEP == DSTEP - 1 && p / DSTEP < NL) dma(st ^ 1, p / DSTEP);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (kk == 0) loader_step();
       }
-      pre = next_ready;
       ++g;
     }
     epilogue(m0, n0);
@@ -377,14 +364,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   }
 }
 
-#ifndef PGK_LDS_BK
-#define PGK_LDS_BK 64
-#endif
-#ifndef PGK_LDS_NST
-#define PGK_LDS_NST 2
-#endif
-constexpr int kBK = PGK_LDS_BK;    // slab depth
-constexpr int kNST = PGK_LDS_NST;  // LDS stages
+constexpr int kBK = 64;   // slab depth
+constexpr int kNST = 2;   // LDS stages
 
 template <int BM, int BN, bool OUT_BF16, bool WITNESS>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {

@@ -1,4 +1,6 @@
-// Global -> LDS movement shared by the direct-to-LDS GEMM kernels (gfx950).
+// Device helpers shared by the direct-to-LDS MFMA GEMM kernels (gfx950):
+// buffer resources, global -> LDS loads, waits and barriers, accumulator
+// reads and bf16 packing.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,10 +45,13 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // before each later LDS read, which serialises the slab pipeline.  The
 // kernels track completion themselves: s_waitcnt vmcnt on the issuing wave,
 // then a workgroup barrier, before any wave reads the slab.
-__device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned char* lds_dst, unsigned voff) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(lds_dst));
+__device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned lds_address, unsigned voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m), "v"(voff), "s"(r) : "memory");
+               :: "s"(lds_address), "v"(voff), "s"(r) : "memory");
+}
+
+__device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned char* lds_dst, unsigned voff) {
+  load_lds16(r, __builtin_amdgcn_readfirstlane(lds_addr(lds_dst)), voff);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
@@ -63,6 +68,23 @@ __device__ __forceinline__ void wait_vm() {
 // the wave's own LDS reads and writes, then meets the other waves.
 __device__ __forceinline__ void slab_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Copy one accumulator out of its AGPR.  Spelling the read out keeps the
+// register allocator from moving all accumulators to VGPRs (the conversion
+// to bf16 is a VALU instruction and cannot read AGPRs).
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
+// Two floats rounded to bf16 (nearest even) and packed, the first in the
+// low half.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 }  // namespace pgk

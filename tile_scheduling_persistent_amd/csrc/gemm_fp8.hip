@@ -14,17 +14,19 @@
 // lane passes its row's scale for the slab's group and the assignment of K
 // positions to MFMA blocks does not matter.
 //
-// Data movement as in gemm_bf16_lds.hip: hand-issued buffer_load ... lds
-// (lds_dma.hpp; the next slab's loads stay in flight while the current
-// slab is read) for A ([m][k],
-// 128-byte rows) and B ([k][n]), both chunk-swizzled against LDS bank
-// conflicts (swz_a, swz_b); A operands by ds_read_b128, B^T operands by
+// Data movement and issue order as in gemm_bf16_lds.hip: two LDS stages of
+// 128-deep slabs filled by hand-issued buffer_load ... lds (gemm_device.hpp),
+// the next slab's loads spread over the MFMAs of the current one, the next
+// step's fragment reads after each MFMA, the loader's bookkeeping and the
+// next slab's scale bytes right after the barrier.  A ([m][k], 128-byte
+// rows) and B ([k][n]) are chunk-swizzled against LDS bank conflicts
+// (swz_a, swz_b); A operands by ds_read_b128, B^T operands by
 // ds_read_b64_tr_b8 (within a 16-lane group, lane i points at row
 // K0 + i/2, columns N0 + 8*(i%2) .. +7, and lane j receives rows K0 .. K0+7
 // of column N0 + j).  Lane l of the MFMA owns logical K positions
 // 32*(l/32) .. +31 of each 64-deep step on both operands.
 #include "common.hpp"
-#include "lds_dma.hpp"
+#include "gemm_device.hpp"
 
 namespace pgk {
 namespace {
@@ -32,9 +34,7 @@ namespace {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
@@ -51,19 +51,13 @@ struct Shape {
   static constexpr int A_BYTES = BM * BK;
   static constexpr int B_BYTES = BK * BN;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE + 16;
+  static constexpr int LDS_BYTES = 2 * STAGE + 16;  // + first tile, next tile [2]
   static constexpr int A_INSTR = A_BYTES / 1024 / 4;
   static constexpr int B_INSTR = B_BYTES / 1024 / 4;
   static constexpr int B_ROWS_PER_INSTR = 1024 / BN;
   static constexpr int B_CPR = BN / 16;
   static_assert(SM <= 4 && SN <= 4, "scale bytes of at most 4 sub-tiles per register");
 };
-
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS banks: 64 x 4 bytes; ds_read_b128 is served 16 lanes at a time,
 // ds_read_b64 (and its transposing form) 32 lanes at a time.
@@ -86,8 +80,18 @@ __device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa
 template <int BM, int BN, bool WITNESS>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   using S = Shape<BM, BN>;
+  constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NL = NA + NB;  // loads per wave per slab
+  constexpr int NMF = S::SN * S::SM;                             // MFMAs per 64-deep step
+  constexpr int NRD = 4 * S::SN + 2 * S::SM;                     // LDS reads per step
+  // The next slab's loads are spread over the first SPREAD MFMAs of the
+  // slab (load d after MFMA d*SPREAD/NL), one at a time rather than a burst.
+  constexpr int SPREAD_W = 3 * NMF / 2 > NL ? 3 * NMF / 2 : NL;
+  constexpr int SPREAD = SPREAD_W < 2 * NMF ? SPREAD_W : 2 * NMF;
+  static_assert(SPREAD >= NL, "one load per MFMA at most");
+
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  int* s_tile = reinterpret_cast<int*>(smem + 2 * S::STAGE);
+  int* s_first = reinterpret_cast<int*>(smem + 2 * S::STAGE);
+  int* s_next = s_first + 1;  // [2]: the loader's next tile, double-buffered by claim parity
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,14 +107,24 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   long long t_start = 0;
   if (WITNESS && tid == 0) t_start = wall_ticks();
 
-  // A: instruction q covers rows 8q .. 8q+7; lane p -> row 8q + p/8, LDS
-  // chunk p%8, global chunk swz_a(row, p%8).
-  auto a_row = [&](int q) { return q * 8 + (lane >> 3); };
-  auto a_chunk = [&](int q) { return swz_a(a_row(q), lane & 7); };
-  // B: instruction q covers rows R*q ..; lane p -> row R*q + p/CPR, LDS chunk
+  // Global -> LDS offsets.  A: instruction q covers rows 8q .. 8q+7; lane p
+  // -> row 8q + p/8, LDS chunk p%8, global chunk swz_a(row, p%8).  B:
+  // instruction q covers rows R*q ..; lane p -> row R*q + p/CPR, LDS chunk
   // p%CPR, global chunk swz_b(row, p%CPR).
-  auto b_row = [&](int q) { return q * S::B_ROWS_PER_INSTR + lane / S::B_CPR; };
-  auto b_chunk = [&](int q) { return swz_b<BN>(b_row(q), lane % S::B_CPR); };
+  unsigned aoff[NA], boff[NB];
+  int bchk[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = (wave * NA + i) * 8 + (lane >> 3);
+    aoff[i] = (unsigned)row * (unsigned)K + (unsigned)swz_a(row, lane & 7) * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * S::B_ROWS_PER_INSTR + lane / S::B_CPR;
+    bchk[i] = swz_b<BN>(row, lane % S::B_CPR);
+    boff[i] = (unsigned)row * (unsigned)N + (unsigned)bchk[i] * 16u;
+  }
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   // LDS read offsets.  A: lane l, sub-tile sm, step ks reads row
   // wm*TM + sm*32 + l%32, bytes ks*64 + (l/32)*32 .. +31 (two chunks).
@@ -139,86 +153,113 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     }
   }
 
-  // Scales of the slab: lane bytes for its sub-tile rows (opsel picks one).
-  int sa_reg = 0, sb_reg = 0;      // current slab
-  int sa_nxt = 0, sb_nxt = 0;      // prefetched for the next slab
-  auto sload = [&](int m0, int n0, int k0, int& sa_out, int& sb_out) {
+  auto coords = [&](int v, int& m0, int& n0) {
+    int pm, pn;
+    walker.tile_coords(v, pm, pn);
+    m0 = pm * BM;
+    n0 = pn * BN;
+  };
+
+  const int nk = K / BK;
+
+  // ---- loader state ----
+  int lt = -1, lk = 0;      // loader: tile, next slab
+  int pend = -1;            // tile the loader moved on to
+  int claims = 0;           // loader tile changes so far
+  int lm0 = 0, ln0 = 0;     // loader tile origin
+  rsrc_words_t rA, rB;      // resources of the slab being loaded
+  unsigned bo[NB];          // B offsets (column chunks past N pushed out of range)
+  // Scale bytes of the slab being loaded, one per sub-tile row of the lane
+  // (kept apart until the slab is consumed, so nothing waits for them early).
+  int sab[S::SM], sbb[S::SN];
+
+  // Pick the next slab for the loader (moving on to the next tile once the
+  // current one is issued), set up its resources and load its scales;
+  // without one the resources are empty and the loads read zeros into a
+  // stage no one reads.
+  auto prep = [&]() {
+    bool load = false;
+    if (lt >= 0 && lk == nk) {
+      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+      ++claims;
+      lk = 0;
+      if (lt >= 0) {
+        pend = lt;
+        coords(lt, lm0, ln0);
+      }
+    }
+    const int k0 = lk * BK;
+    if (lt >= 0) {
+      load = true;
+      ++lk;
+      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+    }
+    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
+    rA = rsrc_words(A + (size_t)lm0 * K + k0, load ? (unsigned)(rows * K - k0) : 0u);
+    rB = rsrc_words(B + (size_t)k0 * N + ln0, load ? (unsigned)(BK * N - ln0) : 0u);
+    const bool b_full = ln0 + BN <= N;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) bo[i] = (b_full || ln0 + bchk[i] * 16 < N) ? boff[i] : kOob;
     const int grp = k0 / BK;
-    const auto rSA = rsrc(P.sa + (size_t)grp * M, (unsigned)M);
-    const auto rSB = rsrc(P.sb + (size_t)grp * N, (unsigned)N);
-    unsigned va = 0, vb = 0;
+    const auto rSA = rsrc(P.sa + (size_t)grp * M, load ? (unsigned)M : 0u);
+    const auto rSB = rsrc(P.sb + (size_t)grp * N, load ? (unsigned)N : 0u);
 #pragma unroll
     for (int s = 0; s < S::SM; ++s) {
-      const int m = m0 + wm * S::TM + s * 32 + l32;
-      va |= (unsigned)__builtin_amdgcn_raw_buffer_load_b8(rSA, m < M ? (unsigned)m : kOob, 0, 0) << (8 * s);
+      const int m = lm0 + wm * S::TM + s * 32 + l32;
+      sab[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSA, m < M ? (unsigned)m : kOob, 0, 0);
     }
 #pragma unroll
     for (int s = 0; s < S::SN; ++s) {
-      const int n = n0 + wn * S::TN + s * 32 + l32;
-      vb |= (unsigned)__builtin_amdgcn_raw_buffer_load_b8(rSB, n < N ? (unsigned)n : kOob, 0, 0) << (8 * s);
+      const int n = ln0 + wn * S::TN + s * 32 + l32;
+      sbb[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSB, n < N ? (unsigned)n : kOob, 0, 0);
     }
-    sa_out = (int)va;
-    sb_out = (int)vb;
   };
 
-  auto gload = [&](int st, int m0, int n0, int k0) {
-    unsigned char* sbase = smem + st * S::STAGE;
-    const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const rsrc_words_t rA = rsrc_words(A + (size_t)m0 * K + k0, (unsigned)(rows * K - k0));
-    const rsrc_words_t rB = rsrc_words(B + (size_t)k0 * N + n0, (unsigned)(BK * N - n0));
-    const bool b_full = n0 + BN <= N;
-#pragma unroll
-    for (int i = 0; i < S::A_INSTR; ++i) {
-      const int q = wave * S::A_INSTR + i;
-      load_lds16(rA, sbase + q * 1024, (unsigned)a_row(q) * (unsigned)K + (unsigned)a_chunk(q) * 16u);
-    }
-#pragma unroll
-    for (int i = 0; i < S::B_INSTR; ++i) {
-      const int q = wave * S::B_INSTR + i;
-      const int c = b_chunk(q);
-      unsigned off = (unsigned)b_row(q) * (unsigned)N + (unsigned)c * 16u;
-      if (!b_full && n0 + c * 16 >= N) off = kOob;
-      load_lds16(rB, sbase + S::A_BYTES + q * 1024, off);
-    }
+  // Load d of the prepared slab into stage st.
+  auto dma = [&](int st, int d) {
+    const unsigned sb = lds0 + (unsigned)(st * S::STAGE);
+    if (d < NA)
+      load_lds16(rA, sb + (unsigned)((wave * NA + d) * 1024), aoff[d]);
+    else
+      load_lds16(rB, sb + (unsigned)(S::A_BYTES + (wave * NB + d - NA) * 1024), bo[d - NA]);
   };
 
   f32x16 acc[S::SN][S::SM];
+  // Operand fragments, double-buffered by step: B^T blocks as four 8-byte
+  // transposed pieces, A blocks as two 16-byte pieces.
+  i32x2 bq[2][S::SN][4];
+  i32x4 aq[2][S::SM][2];
+  int sa_reg = 0, sb_reg = 0;  // scales of the slab on the matrix cores
 
-  auto compute = [&](int st) {
+  // LDS read r of step ks into slot: B^T block 0 first, then the A blocks,
+  // then the other B^T blocks (the order the MFMAs consume them).
+  auto read = [&](int st, int ks, int slot, int r) {
     const unsigned char* sbase = smem + st * S::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x8 bf[S::SN], af[S::SM];
-#pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn) {
-        const unsigned char* p = sbase + rd_b[sn] + ks * 64 * BN;
-        i32x2 r[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + q * 8 * BN));
-        bf[sn] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-      }
-#pragma unroll
-      for (int sm = 0; sm < S::SM; ++sm) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(sbase + rd_a[ks][0] + sm * 32 * BK);
-        const i32x4 hh = *reinterpret_cast<const i32x4*>(sbase + rd_a[ks][1] + sm * 32 * BK);
-        af[sm] = i32x8{lo[0], lo[1], lo[2], lo[3], hh[0], hh[1], hh[2], hh[3]};
-      }
-#pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn) {
-#pragma unroll
-        for (int sm = 0; sm < S::SM; ++sm) {
-          // opsel selects the scale byte of sub-tile sn (B^T rows) / sm (A rows)
-#define PGK_MFMA_CASE(a_, b_) \
-  if (sn == a_ && sm == b_) acc[sn][sm] = mfma_scaled<a_, b_>(bf[sn], af[sm], acc[sn][sm], sb_reg, sa_reg);
-          PGK_MFMA_CASE(0, 0) PGK_MFMA_CASE(0, 1) PGK_MFMA_CASE(0, 2) PGK_MFMA_CASE(0, 3)
-          PGK_MFMA_CASE(1, 0) PGK_MFMA_CASE(1, 1) PGK_MFMA_CASE(1, 2) PGK_MFMA_CASE(1, 3)
-          PGK_MFMA_CASE(2, 0) PGK_MFMA_CASE(2, 1) PGK_MFMA_CASE(2, 2) PGK_MFMA_CASE(2, 3)
-          PGK_MFMA_CASE(3, 0) PGK_MFMA_CASE(3, 1) PGK_MFMA_CASE(3, 2) PGK_MFMA_CASE(3, 3)
-#undef PGK_MFMA_CASE
-        }
-      }
+    if (r >= 4 && r < 4 + 2 * S::SM) {
+      const int sm = (r - 4) >> 1, h = (r - 4) & 1;
+      aq[slot][sm][h] = *reinterpret_cast<const i32x4*>(sbase + rd_a[ks][h] + sm * 32 * BK);
+    } else {
+      const int b = r < 4 ? r : r - 2 * S::SM;
+      const int sn = b >> 2, q = b & 3;
+      const unsigned char* p = sbase + rd_b[sn] + ks * 64 * BN + q * 8 * BN;
+      bq[slot][sn][q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
     }
+  };
+
+  auto mfma = [&](int slot, int j) {
+    const int sn = j / S::SM, sm = j % S::SM;
+    const i32x2* b4 = bq[slot][sn];
+    const i32x8 bf = i32x8{b4[0][0], b4[0][1], b4[1][0], b4[1][1], b4[2][0], b4[2][1], b4[3][0], b4[3][1]};
+    const i32x4* a2 = aq[slot][sm];
+    const i32x8 af = i32x8{a2[0][0], a2[0][1], a2[0][2], a2[0][3], a2[1][0], a2[1][1], a2[1][2], a2[1][3]};
+    // opsel selects the scale byte of sub-tile sn (B^T rows) / sm (A rows)
+#define PGK_MFMA_CASE(a_, b_) \
+    if (sn == a_ && sm == b_) acc[sn][sm] = mfma_scaled<a_, b_>(bf, af, acc[sn][sm], sb_reg, sa_reg);
+    PGK_MFMA_CASE(0, 0) PGK_MFMA_CASE(0, 1) PGK_MFMA_CASE(0, 2) PGK_MFMA_CASE(0, 3)
+    PGK_MFMA_CASE(1, 0) PGK_MFMA_CASE(1, 1) PGK_MFMA_CASE(1, 2) PGK_MFMA_CASE(1, 3)
+    PGK_MFMA_CASE(2, 0) PGK_MFMA_CASE(2, 1) PGK_MFMA_CASE(2, 2) PGK_MFMA_CASE(2, 3)
+    PGK_MFMA_CASE(3, 0) PGK_MFMA_CASE(3, 1) PGK_MFMA_CASE(3, 2) PGK_MFMA_CASE(3, 3)
+#undef PGK_MFMA_CASE
   };
 
   auto epilogue = [&](int m0, int n0) {
@@ -239,36 +280,32 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
           const int cc = sn * 32 + 8 * g;
           const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * 2u : kOob;
           const f32x16& a = acc[sn][sm];
-          const u32x2 v = u32x2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
-                                pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+          const u32x2 v = u32x2{pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1])),
+                                pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]))};
           __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
         }
   };
 
-  const int nk = K / BK;
-  if (tid == 0) s_tile[0] = walker.first();
+  if (tid == 0) s_first[0] = walker.first();
   __syncthreads();
-  int tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  int stage = 0;
-  int it = 0;
-  if (tile >= 0) {
-    int pm, pn;
-    walker.tile_coords(tile, pm, pn);
-    gload(0, pm * BM, pn * BN, 0);
-    sload(pm * BM, pn * BN, 0, sa_nxt, sb_nxt);
+  int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
+  lt = ct;
+  if (lt >= 0) {
+    coords(lt, lm0, ln0);
+    prep();
+#pragma unroll
+    for (int d = 0; d < NL; ++d) dma(0, d);
   }
-  wait_vm0();
-  slab_barrier();
 
-  while (tile >= 0) {
-    int pm, pn;
-    walker.tile_coords(tile, pm, pn);
-    const int m0 = pm * BM, n0 = pn * BN;
+  int g = 0;   // slabs computed so far
+  int it = 0;  // tiles finished
+  int m0 = lm0, n0 = ln0;
+  while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
-        atomicAdd(P.w.visits + tile, 1);
-        P.w.owner[tile] = prog;
-        P.w.order[tile] = it;
+        atomicAdd(P.w.visits + ct, 1);
+        P.w.owner[ct] = prog;
+        P.w.order[ct] = it;
       }
       if (P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
     }
@@ -278,50 +315,51 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
-
-    const int slot = (it + 1) & 1;
-    if (nk == 1 && tid == 0) s_tile[slot] = walker.next(tile);
-    for (int kb = 0; kb + 1 < nk; ++kb) {
-      if (kb == nk - 2 && tid == 0) s_tile[slot] = walker.next(tile);
-      sa_reg = sa_nxt;
-      sb_reg = sb_nxt;
-      gload(stage ^ 1, m0, n0, (kb + 1) * BK);
-      sload(m0, n0, (kb + 1) * BK, sa_nxt, sb_nxt);
-      compute(stage);
-      wait_vm0();
+    for (int ck = 0; ck < nk; ++ck) {
+      // Slab g (and its scale bytes) landed once this wave's loads are done
+      // and every wave has passed the barrier, which also frees the other
+      // stage for the loads of slab g+1.
+      wait_vm<0>();
       slab_barrier();
-      stage ^= 1;
-    }
-    sa_reg = sa_nxt;
-    sb_reg = sb_nxt;
-    int next = -1;
-    if (nk >= 2) {
-      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
-      if (next >= 0) {
-        int qm, qn;
-        walker.tile_coords(next, qm, qn);
-        gload(stage ^ 1, qm * BM, qn * BN, 0);
-        sload(qm * BM, qn * BN, 0, sa_nxt, sb_nxt);
+      const int st = g & 1;
+      {
+        unsigned va = 0, vb = 0;
+#pragma unroll
+        for (int s = 0; s < S::SM; ++s) va |= (unsigned)sab[s] << (8 * s);
+#pragma unroll
+        for (int s = 0; s < S::SN; ++s) vb |= (unsigned)sbb[s] << (8 * s);
+        sa_reg = (int)va;
+        sb_reg = (int)vb;
       }
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
+      prep();  // overlaps the latency of the first reads
+      __builtin_amdgcn_sched_barrier(0);
+      // Fixed issue order: MFMA, then its share of the next step's LDS reads,
+      // then (first SPREAD MFMAs) a load of slab g+1.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+          mfma(ks, j);
+          if (ks == 0) {
+#pragma unroll
+            for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, 1, 1, r);
+          }
+          const int p = ks * NMF + j;
+#pragma unroll
+          for (int d = 0; d < NL; ++d)
+            if (d * SPREAD / NL == p) dma(st ^ 1, d);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      ++g;
     }
-    compute(stage);
-    wait_vm0();
-    slab_barrier();
-    stage ^= 1;
     epilogue(m0, n0);
-    if (nk == 1) {
-      next = __builtin_amdgcn_readfirstlane(s_tile[slot]);
-      if (next >= 0) {
-        int qm, qn;
-        walker.tile_coords(next, qm, qn);
-        gload(stage, qm * BM, qn * BN, 0);
-        sload(qm * BM, qn * BN, 0, sa_nxt, sb_nxt);
-      }
-      wait_vm0();
-      slab_barrier();
-    }
-    tile = next;
     ++it;
+    ct = pend;
+    pend = -1;
+    if (ct >= 0) coords(ct, m0, n0);
   }
 
   if (WITNESS && tid == 0) {
