@@ -188,38 +188,59 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   int claims = 0;           // loader tile changes so far
   int lm0 = 0, ln0 = 0;     // loader tile origin
   rsrc_words_t rA, rB;      // resources of the slab being loaded
-  unsigned ao[NA], bo[NB];  // its per-lane offsets (edge chunks pushed out of range)
+  unsigned long long a_ptr = 0, b_ptr = 0;  // the loader tile's A rows / B columns at k = 0
+  unsigned a_rec = 0;                       // bytes of A from a_ptr to the tile's last row
+  unsigned ao[NA], bo[NB];  // per-lane offsets (edge chunks pushed out of range)
+  bool masked = true;       // ao / bo hold masked offsets
 
   // Pick the next slab for the loader (moving on to the next tile once the
   // current one is issued) and set up its resources; without one the
   // resources are empty, so the loads read zeros into a stage no one reads.
+  // The loader moves on to tile t (t >= 0).
+  auto begin_tile = [&](int t) {
+    lt = t;
+    lk = 0;
+    coords(t, lm0, ln0);
+    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
+    a_ptr = reinterpret_cast<unsigned long long>(A + (size_t)lm0 * K);
+    a_rec = (unsigned)(rows * K) * 2u;
+    b_ptr = reinterpret_cast<unsigned long long>(B + ln0);
+  };
+
   auto prep = [&]() {
-    bool load = false;
     if (lt >= 0 && lk == nk) {
-      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+      const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
       ++claims;
-      lk = 0;
-      if (lt >= 0) {
-        pend = lt;
-        coords(lt, lm0, ln0);
+      lt = -1;
+      if (t >= 0) {
+        pend = t;
+        begin_tile(t);
       }
     }
     const int k0 = lk * BK;
-    if (lt >= 0) {
-      load = true;
+    const bool load = lt >= 0;
+    if (load) {
       ++lk;
       if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
     }
-    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
+    // Slab k0 of the tile: A from column k0 (the range shrinks with it), B
+    // from row k0 (the range ends with the slab's last row, so rows past K
+    // read zero).
     const int krows = (K - k0) < BK ? (K - k0) : BK;
-    rA = rsrc_words(A + (size_t)lm0 * K + k0, load ? (unsigned)(rows * K - k0) * 2u : 0u);
-    rB = rsrc_words(B + (size_t)k0 * N + ln0, load ? (unsigned)(krows * N - ln0) * 2u : 0u);
-    const bool a_full = k0 + BK <= K;
-    const bool b_full = ln0 + BN <= N;
+    const unsigned long long pa = a_ptr + (unsigned long long)k0 * 2u;
+    const unsigned long long pb = b_ptr + (unsigned long long)k0 * (unsigned long long)N * 2u;
+    rA = rsrc_words_u64(pa, load ? a_rec - (unsigned)k0 * 2u : 0u);
+    rB = rsrc_words_u64(pb, load ? (unsigned)(krows * N - ln0) * 2u : 0u);
+    // Per-lane offsets: the plain ones, except on a K-tail slab or an N-edge
+    // tile (and the slab after one), where edge chunks are pushed out of range.
+    const bool edge = k0 + BK > K || ln0 + BN > N;
+    if (edge || masked) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ao[i] = (a_full || k0 + achk[i] * 8 < K) ? aoff[i] : kOob;
+      for (int i = 0; i < NA; ++i) ao[i] = (k0 + achk[i] * 8 < K) ? aoff[i] : kOob;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) bo[i] = (b_full || ln0 + bchk[i] * 8 < N) ? boff[i] : kOob;
+      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 8 < N) ? boff[i] : kOob;
+      masked = edge;
+    }
   };
 
   // Load d of the prepared slab into stage st.
@@ -294,9 +315,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   if (tid == 0) s_first[0] = walker.first();
   __syncthreads();
   int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
-  lt = ct;
-  if (lt >= 0) {
-    coords(lt, lm0, ln0);
+  if (ct >= 0) {
+    begin_tile(ct);
     prep();
 #pragma unroll
     for (int d = 0; d < NL; ++d) dma(0, d);

@@ -33,6 +33,12 @@ __device__ __forceinline__ rsrc_words_t rsrc_words(const void* base, unsigned by
                       (unsigned)__builtin_amdgcn_readfirstlane(bytes), (unsigned)kRsrcWord3};
 }
 
+__device__ __forceinline__ rsrc_words_t rsrc_words_u64(unsigned long long base, unsigned bytes) {
+  return rsrc_words_t{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)base),
+                      (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(base >> 32)) & 0xffffu,
+                      (unsigned)__builtin_amdgcn_readfirstlane(bytes), (unsigned)kRsrcWord3};
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(unsigned long)((const __attribute__((address_space(3))) void*)p);

@@ -168,7 +168,11 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   int claims = 0;           // loader tile changes so far
   int lm0 = 0, ln0 = 0;     // loader tile origin
   rsrc_words_t rA, rB;      // resources of the slab being loaded
+  unsigned long long a_ptr = 0, b_ptr = 0;  // the loader tile's A rows / B columns at k = 0
+  unsigned a_rec = 0;                       // bytes of A from a_ptr to the tile's last row
   unsigned bo[NB];          // B offsets (column chunks past N pushed out of range)
+  bool masked = true;       // bo holds masked offsets
+  unsigned soa[S::SM], sob[S::SN];  // scale byte offsets of the lane's rows / columns
   // Scale bytes of the slab being loaded, one per sub-tile row of the lane
   // (kept apart until the slab is consumed, so nothing waits for them early).
   int sab[S::SM], sbb[S::SN];
@@ -177,42 +181,60 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   // current one is issued), set up its resources and load its scales;
   // without one the resources are empty and the loads read zeros into a
   // stage no one reads.
-  auto prep = [&]() {
-    bool load = false;
-    if (lt >= 0 && lk == nk) {
-      lt = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
-      ++claims;
-      lk = 0;
-      if (lt >= 0) {
-        pend = lt;
-        coords(lt, lm0, ln0);
-      }
-    }
-    const int k0 = lk * BK;
-    if (lt >= 0) {
-      load = true;
-      ++lk;
-      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
-    }
+  // The loader moves on to tile t (t >= 0): per-tile bases, B offsets with
+  // column chunks past N pushed out of range, scale byte offsets.
+  auto begin_tile = [&](int t) {
+    lt = t;
+    lk = 0;
+    coords(t, lm0, ln0);
     const int rows = (M - lm0) < BM ? (M - lm0) : BM;
-    rA = rsrc_words(A + (size_t)lm0 * K + k0, load ? (unsigned)(rows * K - k0) : 0u);
-    rB = rsrc_words(B + (size_t)k0 * N + ln0, load ? (unsigned)(BK * N - ln0) : 0u);
-    const bool b_full = ln0 + BN <= N;
+    a_ptr = reinterpret_cast<unsigned long long>(A + (size_t)lm0 * K);
+    a_rec = (unsigned)(rows * K);
+    b_ptr = reinterpret_cast<unsigned long long>(B + ln0);
+    const bool edge = ln0 + BN > N;
+    if (edge || masked) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) bo[i] = (b_full || ln0 + bchk[i] * 16 < N) ? boff[i] : kOob;
-    const int grp = k0 / BK;
-    const auto rSA = rsrc(P.sa + (size_t)grp * M, load ? (unsigned)M : 0u);
-    const auto rSB = rsrc(P.sb + (size_t)grp * N, load ? (unsigned)N : 0u);
+      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 16 < N) ? boff[i] : kOob;
+      masked = edge;
+    }
 #pragma unroll
     for (int s = 0; s < S::SM; ++s) {
       const int m = lm0 + wm * S::TM + s * 32 + l32;
-      sab[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSA, m < M ? (unsigned)m : kOob, 0, 0);
+      soa[s] = m < M ? (unsigned)m : kOob;
     }
 #pragma unroll
     for (int s = 0; s < S::SN; ++s) {
       const int n = ln0 + wn * S::TN + s * 32 + l32;
-      sbb[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSB, n < N ? (unsigned)n : kOob, 0, 0);
+      sob[s] = n < N ? (unsigned)n : kOob;
     }
+  };
+
+  auto prep = [&]() {
+    if (lt >= 0 && lk == nk) {
+      const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+      ++claims;
+      lt = -1;
+      if (t >= 0) {
+        pend = t;
+        begin_tile(t);
+      }
+    }
+    const int k0 = lk * BK;
+    const bool load = lt >= 0;
+    if (load) {
+      ++lk;
+      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+    }
+    rA = rsrc_words_u64(a_ptr + (unsigned long long)k0, load ? a_rec - (unsigned)k0 : 0u);
+    rB = rsrc_words_u64(b_ptr + (unsigned long long)k0 * (unsigned long long)N,
+                        load ? (unsigned)(BK * N - ln0) : 0u);
+    const int grp = k0 / BK;
+    const auto rSA = rsrc(P.sa + (size_t)grp * M, load ? (unsigned)M : 0u);
+    const auto rSB = rsrc(P.sb + (size_t)grp * N, load ? (unsigned)N : 0u);
+#pragma unroll
+    for (int s = 0; s < S::SM; ++s) sab[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSA, soa[s], 0, 0);
+#pragma unroll
+    for (int s = 0; s < S::SN; ++s) sbb[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSB, sob[s], 0, 0);
   };
 
   // Load d of the prepared slab into stage st.
@@ -289,9 +311,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   if (tid == 0) s_first[0] = walker.first();
   __syncthreads();
   int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
-  lt = ct;
-  if (lt >= 0) {
-    coords(lt, lm0, ln0);
+  if (ct >= 0) {
+    begin_tile(ct);
     prep();
 #pragma unroll
     for (int d = 0; d < NL; ++d) dma(0, d);
