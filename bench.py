@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4          # engine clock the dense peak is quoted at
 M = N = K = 8192
 SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
           ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8)]
@@ -42,8 +43,8 @@ CPU_ROWS = 4096
 # the kernel sources it was measured on (hash below); otherwise reported as
 # null.
 TRAFFIC_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
-TRAFFIC_MEASURED = {"sources_sha256_16": "78b82c8f5f393bac",
-                    "fetch_bytes": 1792673627, "write_bytes": 183416464}
+TRAFFIC_MEASURED = {"sources_sha256_16": "46a94442bf71fdfa",
+                    "fetch_bytes": 1671307635, "write_bytes": 188111705}
 
 
 def parse():
@@ -93,6 +94,23 @@ def time_calls(fn, steps, warmup, stream):
     wall = time.perf_counter() - t0
     durs = [e0.elapsed_time(e1) for e0, e1 in evs]
     return wall * 1e3 / steps, float(np.mean(durs)), float(np.min(durs))
+
+
+def measured_clock(pg, cfg, A, B, C, key):
+    """Engine clock (GHz) the headline launch runs at: one witness launch after
+    the timed steps; median over programs of shader cycles / wall time."""
+    import torch
+    sched, gs = key.rsplit("_g", 1) if "_g" in key else (key, "8")
+    G = cfg.info["num_cus"]
+    T = (M // 256) * (N // 256)
+    cfg.witness_enable(T, G)
+    a = pg.make_args(tile=(256, 256, 64), group_size=int(gs), debug_flags=pg._abi.DEBUG_WITNESS)
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)
+    torch.cuda.synchronize()
+    w = cfg.witness_read(T, G)
+    dt = (w["t_end"] - w["t_start"]) / (cfg.info["wall_clock_khz"] * 1e3)
+    ok = dt > 0
+    return round(float(np.median(w["cycles"][ok] / dt[ok])) / 1e9, 3)
 
 
 def measured_traffic():
@@ -224,6 +242,7 @@ def main():
     if head_key not in per:
         head_key = next(iter(per))
     h = per[head_key]
+    clock_ghz = measured_clock(pg, cfg, A, B, C, head_key)
     line = {
         "metric": "GEMM TFLOP/s & % MFMA peak per scheduler (8192^3 bf16); add GB/s",
         "value": round(h["tflops"], 2),
@@ -244,6 +263,10 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
+                     "clock_ghz_measured": clock_ghz,
+                     "peak_at_measured_clock": round(PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ, 1),
+                     "frac_at_measured_clock": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12
+                                                     / (PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ), 4),
                      "traffic_unit": "HBM bytes per launch (counter passes, copy-calibrated)",
                      "algorithmic_bytes": 2 * (M * K + K * N + M * N)},
         "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),

@@ -67,6 +67,18 @@ def test_gemm_schedule_exactly_once(sched, shape, tile):
     _check(w, sched, pm, pn, G, X, 8)
 
 
+def test_gemm_witness_clock():
+    """Per-program shader cycles over wall time give a plausible engine clock."""
+    w, pm, pn, G, X = _gemm_witness(5120, 5120, 2048, (256, 256, 64), "work_stealing")
+    khz = config().info["wall_clock_khz"]
+    dt = (w["t_end"][:G] - w["t_start"][:G]) / (khz * 1e3)   # seconds
+    busy = dt > 2e-6
+    assert busy.sum() >= G // 2
+    ghz = w["cycles"][:G][busy] / dt[busy] / 1e9
+    note(f"clock GHz min {ghz.min():.3f} median {np.median(ghz):.3f} max {ghz.max():.3f}")
+    assert np.all((ghz > 0.3) & (ghz < 3.0)), ghz
+
+
 @pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
 @pytest.mark.parametrize("grid", [1, 7, 8, 13, 300])
 def test_gemm_schedule_grid_override(sched, grid):

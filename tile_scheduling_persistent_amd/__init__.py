@@ -133,9 +133,11 @@ class Config:
             "t_end": np.zeros(programs, np.int64), "hw_id": np.zeros(programs, np.int32),
             "n_tiles": np.zeros(programs, np.int32),
             "counters": np.zeros(self.info["counter_capacity"], np.int32),
+            "cycles": np.zeros(programs, np.int64),
         }
         w = _abi.pgemm_witness()
-        for k in ("visits", "owner", "order", "t_start", "t_end", "hw_id", "n_tiles", "counters"):
+        for k in ("visits", "owner", "order", "t_start", "t_end", "hw_id", "n_tiles", "counters",
+                  "cycles"):
             setattr(w, k, out[k].ctypes.data)
         w.tiles = tiles
         w.programs = programs

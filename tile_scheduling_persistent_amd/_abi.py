@@ -45,6 +45,7 @@ class pgemm_witness(ctypes.Structure):
         ("t_start", ctypes.c_void_p), ("t_end", ctypes.c_void_p),
         ("hw_id", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("programs", ctypes.c_int32), ("counters", ctypes.c_void_p),
+        ("cycles", ctypes.c_void_p),
     ]
 
 

@@ -17,6 +17,7 @@ struct Witness {
   int* order;         // [T] position of tile v in its owner's sequence
   long long* t_start; // [G] wall clock at program start
   long long* t_end;   // [G] wall clock at program end
+  long long* cycles;  // [G] shader clock cycles from program start to end
   int* hw_id;         // [G] hardware placement of the program
   int* n_tiles;       // [G] tiles the program computed
 };
@@ -80,6 +81,10 @@ int padd_tiles_per_step(int tr, int tc);
 
 // Wall clock (constant rate, see hipDeviceAttributeWallClockRate).
 __device__ __forceinline__ long long wall_ticks() { return (long long)wall_clock64(); }
+
+// Shader clock cycle counter of the wave (runs at the current engine clock,
+// so cycles / wall time is the clock the program actually ran at).
+__device__ __forceinline__ long long shader_cycles() { return (long long)__builtin_readcyclecounter(); }
 
 // Placement of the calling wave: HW_ID low half (CU, SH, SE fields) and the
 // XCC id in bits 16-19.

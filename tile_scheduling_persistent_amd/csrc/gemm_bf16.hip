@@ -129,8 +129,11 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
   const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);
 
   Walker walker(P.s, prog);
-  long long t_start = 0;
-  if (WITNESS && tid == 0) t_start = wall_ticks();
+  long long t_start = 0, c_start = 0;
+  if (WITNESS && tid == 0) {
+    t_start = wall_ticks();
+    c_start = shader_cycles();
+  }
 
   // ---- per-thread loop invariants -------------------------------------
   // A staging: chunk q = r*256 + tid -> row q/CK, 16-byte chunk q%CK.
@@ -385,6 +388,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
   if (WITNESS && tid == 0) {
     P.w.t_start[prog] = t_start;
     P.w.t_end[prog] = wall_ticks();
+    P.w.cycles[prog] = shader_cycles() - c_start;
     P.w.hw_id[prog] = hw_placement();
     P.w.n_tiles[prog] = it;
   }

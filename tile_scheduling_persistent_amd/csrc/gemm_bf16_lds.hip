@@ -13,18 +13,21 @@
 //    straight on into the next tile of the schedule (the pipeline phase runs
 //    on across tiles, like the scheduler's iteration counter of "[Feature]
 //    Introduce tile scheduler", TileLang PR #2441).  The next tile is
-//    claimed when the loader sets up the last slab of the current one, one
-//    slab before it is needed.  One barrier per slab, after each wave has
-//    waited for its own loads (vmcnt).  The loads are issued by hand and the
-//    barrier carries no memory fence (gemm_device.hpp), so the compiler adds no
-//    wait for the slab in flight before the LDS reads of the current one.
-//  * The issue order inside a slab is fixed by hand (scheduling barriers):
-//    after each MFMA come its share of the next k-step's fragment reads and,
-//    in the first k-steps, one load of the next slab, so LDS reads, global
-//    loads and their latencies hide behind the MFMA pipeline instead of
-//    stalling the wave in bursts.  The loader's bookkeeping (tile switch,
-//    claim, buffer resources) runs right after the barrier, under the
-//    latency of the slab's first fragment reads.
+//    claimed when the loader sets up the last slab of the current one.
+//  * One barrier per slab, after its third k-step: each wave has waited for
+//    its own loads of slab g+1 (vmcnt) and finished every read of slab g, so
+//    after the barrier slab g+1 is complete and slab g's stage is free.  The
+//    last k-step then reads slab g+1's first fragments and starts slab g+2's
+//    loads; the loads are issued by hand and the barrier carries no memory
+//    fence (gemm_device.hpp), so the compiler adds no wait for loads in
+//    flight before LDS reads.
+//  * The issue order inside a k-step is fixed by hand (scheduling
+//    barriers): after each MFMA come its share of the next k-step's fragment
+//    reads and, in k-steps 0 and 3, a load, so LDS reads, global loads and
+//    their latencies hide behind the MFMA pipeline instead of stalling the
+//    wave in bursts; each load has at least two k-steps to land.  The
+//    loader's bookkeeping (tile switch, claim, buffer resources) is scalar
+//    pointer arithmetic except on edge slabs.
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
 //    so that the ds_read_b128 operand reads hit distinct banks (see swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
@@ -56,7 +59,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr int kLoadSpread = 2;  // k-steps of a slab that carry the next slab's loads
 
 template <int BM, int BN, int BK, int NST>
 struct Shape {
@@ -106,12 +108,6 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NL = NA + NB;  // loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per k-step
   constexpr int NRD = 2 * S::SN + S::SM;                         // LDS reads per k-step
-  // The slab's loads are spread over the MFMAs of its first kLoadSpread
-  // k-steps: load d is issued after MFMA number d*DSTEP + DSTEP-1 of the
-  // slab, so the texture unit takes them one at a time instead of stalling
-  // the wave on a burst of 16.
-  constexpr int DSTEP = (kLoadSpread * NMF) / NL > 1 ? (kLoadSpread * NMF) / NL : 1;
-  static_assert(NL * DSTEP <= (S::KK - 1) * NMF, "room for the loads among the MFMAs");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* s_first = reinterpret_cast<int*>(smem + NST * S::STAGE);
@@ -128,8 +124,11 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);
 
   Walker walker(P.s, prog);
-  long long t_start = 0;
-  if (WITNESS && tid == 0) t_start = wall_ticks();
+  long long t_start = 0, c_start = 0;
+  if (WITNESS && tid == 0) {
+    t_start = wall_ticks();
+    c_start = shader_cycles();
+  }
 
   // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
   // A: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
@@ -184,7 +183,9 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
-  int pend = -1;            // tile the loader moved on to
+  // Tiles the loader moved on to that the matrix cores have not reached:
+  // the loader runs two slabs ahead, so with one slab per tile two can wait.
+  int pend0 = -1, pend1 = -1;
   int claims = 0;           // loader tile changes so far
   int lm0 = 0, ln0 = 0;     // loader tile origin
   rsrc_words_t rA, rB;      // resources of the slab being loaded
@@ -213,7 +214,10 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       ++claims;
       lt = -1;
       if (t >= 0) {
-        pend = t;
+        if (pend0 < 0)
+          pend0 = t;
+        else
+          pend1 = t;
         begin_tile(t);
       }
     }
@@ -315,16 +319,54 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   if (tid == 0) s_first[0] = walker.first();
   __syncthreads();
   int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
+  // Issue order per slab g (stage st = g & 1), fixed by scheduling barriers:
+  //   k-step 0: MFMAs; reads of k-step 1; second half of slab g+1's loads
+  //   k-steps 1, 2: MFMAs; reads of the next k-step
+  //   wait for the wave's loads, barrier: slab g+1 is complete in LDS and
+  //   every read of slab g is done, so stage st is free
+  //   loader bookkeeping for slab g+2
+  //   k-step 3: MFMAs; reads of slab g+1's k-step 0; first half of slab g+2's
+  //   loads (into stage st)
+  // so the next slab's first fragments and the loads' latency hide behind
+  // MFMAs, and each load has at least two k-steps to land.
+  constexpr int HALF = NL / 2;
+  static_assert(NL % 2 == 0 && HALF <= NMF, "half a slab's loads per k-step");
+  static_assert(S::KK % 2 == 0, "the next slab's first k-step lands in slot 0");
+  auto kstep = [&](int st_rd, int kk_rd, int slot, int st_dma, int d0) {
+#pragma unroll
+    for (int j = 0; j < NMF; ++j) {
+      mfma(slot, j);
+      if (kk_rd >= 0) {
+#pragma unroll
+        for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st_rd, kk_rd, slot ^ 1, r);
+      }
+      if (d0 >= 0) {
+#pragma unroll
+        for (int d = 0; d < HALF; ++d)
+          if (d * NMF / HALF == j) dma(st_dma, d0 + d);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   if (ct >= 0) {
     begin_tile(ct);
-    prep();
+    prep();  // slab 0
 #pragma unroll
     for (int d = 0; d < NL; ++d) dma(0, d);
+    wait_vm<0>();
+    slab_barrier();
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read(0, 0, 0, r);
+    prep();  // slab 1: its first half now, the second half in slab 0's k-step 0
+#pragma unroll
+    for (int d = 0; d < HALF; ++d) dma(1, d);
   }
 
   int g = 0;   // slabs computed so far
   int it = 0;  // tiles finished
-  int m0 = lm0, n0 = ln0;
+  int m0 = 0, n0 = 0;  // origin of tile ct (the loader may already be past it)
+  if (ct >= 0) coords(ct, m0, n0);
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -341,44 +383,30 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
     for (int ck = 0; ck < nk; ++ck) {
-      // Slab g is in LDS once this wave's loads have landed and every wave
-      // has passed the barrier, which also frees the other stage.
+      const int st = g & 1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < S::KK; ++kk)
+        kstep(st, kk + 1, kk & 1, st ^ 1, kk == 0 ? HALF : -1);
       wait_vm<0>();
       slab_barrier();
-      const int st = g & 1;
-#pragma unroll
-      for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
-      prep();  // overlaps the latency of the first reads
+      prep();  // slab g+2
       __builtin_amdgcn_sched_barrier(0);
-      // Fixed issue order: MFMA, then its share of the next k-step's LDS
-      // reads, then (first KK-1 k-steps) a load of slab g+1.
-#pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) {
-        const int slot = kk & 1;
-#pragma unroll
-        for (int j = 0; j < NMF; ++j) {
-          mfma(slot, j);
-          if (kk + 1 < S::KK) {
-#pragma unroll
-            for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, kk + 1, slot ^ 1, r);
-          }
-          const int p = kk * NMF + j;
-          if (p % DSTEP == DSTEP - 1 && p / DSTEP < NL) dma(st ^ 1, p / DSTEP);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      kstep(st ^ 1, 0, (S::KK - 1) & 1, st, 0);
       ++g;
     }
     epilogue(m0, n0);
     ++it;
-    ct = pend;
-    pend = -1;
+    ct = pend0;
+    pend0 = pend1;
+    pend1 = -1;
     if (ct >= 0) coords(ct, m0, n0);
   }
 
   if (WITNESS && tid == 0) {
     P.w.t_start[prog] = t_start;
     P.w.t_end[prog] = wall_ticks();
+    P.w.cycles[prog] = shader_cycles() - c_start;
     P.w.hw_id[prog] = hw_placement();
     P.w.n_tiles[prog] = it;
   }

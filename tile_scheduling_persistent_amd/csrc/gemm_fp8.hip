@@ -104,8 +104,11 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   const unsigned char* __restrict__ B = static_cast<const unsigned char*>(P.B);
 
   Walker walker(P.s, prog);
-  long long t_start = 0;
-  if (WITNESS && tid == 0) t_start = wall_ticks();
+  long long t_start = 0, c_start = 0;
+  if (WITNESS && tid == 0) {
+    t_start = wall_ticks();
+    c_start = shader_cycles();
+  }
 
   // Global -> LDS offsets.  A: instruction q covers rows 8q .. 8q+7; lane p
   // -> row 8q + p/8, LDS chunk p%8, global chunk swz_a(row, p%8).  B:
@@ -320,7 +323,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 
   int g = 0;   // slabs computed so far
   int it = 0;  // tiles finished
-  int m0 = lm0, n0 = ln0;
+  int m0 = 0, n0 = 0;  // origin of tile ct
+  if (ct >= 0) coords(ct, m0, n0);
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -386,6 +390,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   if (WITNESS && tid == 0) {
     P.w.t_start[prog] = t_start;
     P.w.t_end[prog] = wall_ticks();
+    P.w.cycles[prog] = shader_cycles() - c_start;
     P.w.hw_id[prog] = hw_placement();
     P.w.n_tiles[prog] = it;
   }

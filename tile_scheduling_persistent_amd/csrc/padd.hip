@@ -48,8 +48,11 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   const int rows = P.rows, cols = P.cols;
   const bool ws = P.s.kind == pgs::kWorkStealing;
   Walker walker(P.s, prog);
-  long long t_start = 0;
-  if (WITNESS && tid == 0) t_start = wall_ticks();
+  long long t_start = 0, c_start = 0;
+  if (WITNESS && tid == 0) {
+    t_start = wall_ticks();
+    c_start = shader_cycles();
+  }
 
   // Static kinds: every thread walks the same sequence itself.  Work
   // stealing: thread 0 claims, the result is shared through LDS.
@@ -162,6 +165,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   if (WITNESS && tid == 0) {
     P.w.t_start[prog] = t_start;
     P.w.t_end[prog] = wall_ticks();
+    P.w.cycles[prog] = shader_cycles() - c_start;
     P.w.hw_id[prog] = hw_placement();
     P.w.n_tiles[prog] = done;
   }

@@ -35,6 +35,7 @@ struct pgemm_config {
   int* w_order;
   long long* w_t_start;
   long long* w_t_end;
+  long long* w_cycles;
   int* w_hw_id;
   int* w_n_tiles;
 };
@@ -75,11 +76,11 @@ struct DeviceGuard {
 
 void free_witness(pgemm_config* c) {
   void* ptrs[] = {c->w_visits, c->w_owner, c->w_order, c->w_t_start,
-                  c->w_t_end, c->w_hw_id, c->w_n_tiles};
+                  c->w_t_end, c->w_cycles, c->w_hw_id, c->w_n_tiles};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   c->w_visits = c->w_owner = c->w_order = c->w_hw_id = c->w_n_tiles = nullptr;
-  c->w_t_start = c->w_t_end = nullptr;
+  c->w_t_start = c->w_t_end = c->w_cycles = nullptr;
   c->w_tiles = 0;
   c->w_programs = 0;
 }
@@ -125,6 +126,7 @@ pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::
   w.order = cfg->w_order;
   w.t_start = cfg->w_t_start;
   w.t_end = cfg->w_t_end;
+  w.cycles = cfg->w_cycles;
   w.hw_id = cfg->w_hw_id;
   w.n_tiles = cfg->w_n_tiles;
   // visits start at 0, owner / order at -1 (fill kernels, no memset nodes)
@@ -243,6 +245,7 @@ pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_order, sizeof(int) * t);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_t_start, sizeof(long long) * p);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_t_end, sizeof(long long) * p);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_cycles, sizeof(long long) * p);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_hw_id, sizeof(int) * p);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_n_tiles, sizeof(int) * p);
   if (e != hipSuccess) {
@@ -270,6 +273,7 @@ pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip
       {out->visits, cfg->w_visits, 4 * t},      {out->owner, cfg->w_owner, 4 * t},
       {out->order, cfg->w_order, 4 * t},        {out->t_start, cfg->w_t_start, 8 * p},
       {out->t_end, cfg->w_t_end, 8 * p},        {out->hw_id, cfg->w_hw_id, 4 * p},
+      {out->cycles, cfg->w_cycles, 8 * p},
       {out->n_tiles, cfg->w_n_tiles, 4 * p},    {out->counters, cfg->counters, 4 * (size_t)cfg->capacity},
   };
   for (const Copy& c : cps) {
