@@ -294,20 +294,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     const unsigned eb = (unsigned)(r0 * N + c0) * esz;
     const unsigned rstep = 32u * (unsigned)N * esz;
     const int ncols = N - n0;
+    if (OUT_BF16) {
+      const int hi = lane >> 5;
+      const unsigned eb2 = (unsigned)(r0 * N) * 2u;
 #pragma unroll
-    for (int sm = 0; sm < S::SM; ++sm) {
+      for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn) {
+        for (int sn = 0; sn < S::SN; ++sn)
+          store_block_bf16(acc[sn][sm], rC, eb2 + sm * rstep, wn * S::TN + sn * 32, ncols, hi);
+    } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cc = sn * 32 + 8 * g;
-          const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
-          const f32x16& a = acc[sn][sm];
-          if (OUT_BF16) {
-            const u32x2 v = u32x2{pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1])),
-                                  pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]))};
-            __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
-          } else {
+      for (int sm = 0; sm < S::SM; ++sm) {
+#pragma unroll
+        for (int sn = 0; sn < S::SN; ++sn) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int cc = sn * 32 + 8 * g;
+            const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
+            const f32x16& a = acc[sn][sm];
             const f32x4 v = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off, 0, 0);
           }

@@ -93,4 +93,34 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Store one 32x32 block of fp32 accumulators as bf16.  Layout of
+// v_mfma_f32_32x32 with B^T as the first operand: lane l holds row l % 32,
+// columns 8g + 4*(l/32) .. +3 in registers 4g .. 4g+3 (g = 0..3).  Swapping
+// the g = 2q+1 half of the low 32 lanes with the g = 2q half of the high 32
+// (v_permlane32_swap: r0 = [a.lo | b.lo], r1 = [a.hi | b.hi]) leaves each
+// lane 8 consecutive columns, the low lane those of g = 2q and the high lane
+// those of g = 2q+1, stored as one 16-byte chunk.  row_off: byte offset of
+// the lane's row at column 0 of the block's tile; col0: the block's first
+// column; chunks at or past ncols are dropped (ncols a multiple of 8).
+template <typename Acc>
+__device__ __forceinline__ void store_block_bf16(const Acc& a, __amdgpu_buffer_rsrc_t rC,
+                                                 unsigned row_off, int col0, int ncols, int hi) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  unsigned pk[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    pk[g][0] = pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1]));
+    pk[g][1] = pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]));
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
+    const u32x4_t v = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+    const int col = col0 + 8 * (2 * q + hi);
+    const unsigned off = col < ncols ? row_off + (unsigned)col * 2u : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, 0);
+  }
+}
+
 }  // namespace pgk

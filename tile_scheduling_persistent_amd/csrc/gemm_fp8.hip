@@ -292,23 +292,14 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     const auto rC = rsrc(static_cast<unsigned char*>(P.C) + ((size_t)m0 * N + n0) * 2,
                          (unsigned)((size_t)rows * N - n0) * 2u);
     const int r0 = wm * S::TM + l32;
-    const int c0 = wn * S::TN + 4 * hi;
-    const unsigned eb = (unsigned)(r0 * N + c0) * 2u;
+    const unsigned eb = (unsigned)(r0 * N) * 2u;
     const unsigned rstep = 32u * (unsigned)N * 2u;
     const int ncols = N - n0;
 #pragma unroll
     for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
       for (int sn = 0; sn < S::SN; ++sn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cc = sn * 32 + 8 * g;
-          const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * 2u : kOob;
-          const f32x16& a = acc[sn][sm];
-          const u32x2 v = u32x2{pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1])),
-                                pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]))};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
-        }
+        store_block_bf16(acc[sn][sm], rC, eb + sm * rstep, wn * S::TN + sn * 32, ncols, hi);
   };
 
   if (tid == 0) s_first[0] = walker.first();
