@@ -101,10 +101,10 @@ def measured_clock(pg, cfg, A, B, C, key):
     the timed steps; median over programs of shader cycles / wall time."""
     import torch
     sched, gs = key.rsplit("_g", 1) if "_g" in key else (key, "8")
-    G = cfg.info["num_cus"]
-    T = (M // 256) * (N // 256)
-    cfg.witness_enable(T, G)
     a = pg.make_args(tile=(256, 256, 64), group_size=int(gs), debug_flags=pg._abi.DEBUG_WITNESS)
+    plan = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched, a)
+    G, T = plan["grid"], plan["tiles"]
+    cfg.witness_enable(T, G)
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)
     torch.cuda.synchronize()
     w = cfg.witness_read(T, G)
@@ -217,7 +217,8 @@ def main():
                 _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
                 row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2),
                               "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1),
-                              "event_ms_mean": round(ev_mean, 5)}
+                              "event_ms_mean": round(ev_mean, 5),
+                              "grid": pg.plan_gemm(cfg, m, n, k, "fp8_b128_out_bf16", sched, a)["grid"]}
             fp8[f"{m}x{n}x{k}"] = row
             print(f"# fp8 {m}x{n}x{k}: {row}", file=sys.stderr, flush=True)
             del dA, dB, dC, qa, qb
@@ -243,6 +244,8 @@ def main():
         head_key = next(iter(per))
     h = per[head_key]
     clock_ghz = measured_clock(pg, cfg, A, B, C, head_key)
+    head_plan = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", head_key.rsplit("_g", 1)[0],
+                             pg.make_args(tile=(256, 256, 64)))
     line = {
         "metric": "GEMM TFLOP/s & % MFMA peak per scheduler (8192^3 bf16); add GB/s",
         "value": round(h["tflops"], 2),
@@ -257,7 +260,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: A, B iid normal(0,1) rounded to bf16 (PCG64 seeds 1030/1031)",
         "config": {"workload": "bf16 GEMM M=N=K=8192, fp32 accumulate, bf16 C, 256x256x64 tiles, "
-                               f"persistent grid = {cfg.info['num_cus']} CUs, scheduler {head_key}",
+                               f"persistent grid = {head_plan['grid']} programs ({cfg.info['num_cus']} CUs x "
+                               f"{head_plan['occupancy']}), scheduler {head_key}",
                    "M": M, "N": N, "K": K, "scheduler": head_key},
         "roofline": {"bound": "mfma", "achieved": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

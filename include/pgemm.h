@@ -93,7 +93,8 @@ typedef enum {
 typedef struct {
   int tile_m, tile_n, tile_k; /* 0 => default: bf16 256x256x64, fp8 256x256x128 */
   int group_size;             /* grouped order rows per group; 0 => 8 */
-  int grid;                   /* programs; 0 => number of CUs */
+  int grid;                   /* programs; 0 => number of CUs x workgroups of the selected
+                                 kernel one CU holds at once (see pgemm_plan_gemm) */
   int claim_chunk;            /* add only: tiles per work-stealing claim; 0 => default */
   const uint8_t* a_scale;     /* fp8: device, e8m0 [K/128][M] */
   const uint8_t* b_scale;     /* fp8: device, e8m0 [K/128][N] */
@@ -176,6 +177,41 @@ typedef struct {      /* host arrays supplied by the caller */
 /* Synchronise `hip_stream` and copy the witness of the last launch into the
  * caller's host arrays (any array may be NULL to skip it). */
 PGEMM_API pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip_stream);
+
+/* Which kernel a call runs. */
+typedef enum {
+  PGEMM_KERNEL_BF16_LDS = 0,     /* bf16, direct-to-LDS loads (16-byte aligned, K and N % 8 == 0) */
+  PGEMM_KERNEL_BF16_STAGED = 1,  /* bf16, register-staged (any shape and alignment) */
+  PGEMM_KERNEL_FP8 = 2,          /* block-scaled fp8 */
+  PGEMM_KERNEL_ADD = 3           /* persistent add */
+} pgemm_kernel;
+
+/* Launch a call would make.  A persistent launch runs one program per
+ * resident workgroup slot: grid = number of CUs x occupancy unless
+ * args->grid overrides it (e.g. 128x128 GEMM tiles fit two workgroups per
+ * CU, 256x256 tiles one). */
+typedef struct {
+  int grid;          /* programs */
+  int occupancy;     /* workgroups of the kernel one CU holds at once */
+  int64_t tiles;     /* output tiles T */
+  int tile_m, tile_n, tile_k;  /* tile_k = 0 for the add */
+  int threads;       /* per workgroup */
+  int lds_bytes;     /* dynamic LDS per workgroup */
+  pgemm_kernel kernel;
+} pgemm_plan;
+
+/* The launch pgemm_run would make with the same arguments (no pointer is
+ * dereferenced; NULL pointers count as 16-byte aligned).  Same argument
+ * errors as pgemm_run, except that fp8 scales are not required. */
+PGEMM_API pgemm_status pgemm_plan_gemm(pgemm_config* cfg, const void* A, const void* B, const void* C,
+                             int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
+                             pgemm_sched sched, const pgemm_args* args, pgemm_plan* out);
+
+/* The launch padd_run would make with the same arguments (NULL pointers
+ * count as 16-byte aligned). */
+PGEMM_API pgemm_status pgemm_plan_add(pgemm_config* cfg, const float* X, const float* Y, const float* C,
+                            int64_t rows, int64_t cols, int tile_rows, int tile_cols,
+                            pgemm_sched sched, const pgemm_args* args, pgemm_plan* out);
 
 /* Static string for a status code. */
 PGEMM_API const char* pgemm_status_str(pgemm_status s);

@@ -79,23 +79,24 @@ def test_stale_counters_are_detected():
     a, b = bf16_bits_uniform((M, K), 1), bf16_bits_uniform((K, N), 2)
     A, B = dev_bf16(a), dev_bf16(b)
     T = 16
-    cfg.witness_enable(T, cfg.info["num_cus"])
+    G = pg.plan_gemm(cfg, M, N, K, "bf16_out_f32", "work_stealing")["grid"]
+    cfg.witness_enable(T, G)
     C = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
     flags = _abi.DEBUG_WITNESS
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing", pg.make_args(debug_flags=flags))
-    w1 = cfg.witness_read(T, cfg.info["num_cus"])
+    w1 = cfg.witness_read(T, G)
     assert np.all(w1["visits"] == 1)
     C.fill_(-5.0)
     note("work stealing with the reset skipped")
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing",
                  pg.make_args(debug_flags=flags | _abi.DEBUG_SKIP_RESET))
-    w2 = cfg.witness_read(T, cfg.info["num_cus"])
+    w2 = cfg.witness_read(T, G)
     torch.cuda.synchronize()
     assert np.all(w2["visits"] == 0)
     assert torch.all(C == -5.0)
     # the normal path resets and recovers
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing", pg.make_args(debug_flags=flags))
-    w3 = cfg.witness_read(T, cfg.info["num_cus"])
+    w3 = cfg.witness_read(T, G)
     assert np.all(w3["visits"] == 1)
 
 
@@ -103,11 +104,12 @@ def test_straggler_rebalanced_by_work_stealing():
     """Program 0 waits 200 us before each tile: under work stealing its XCD
     peers take its share; under blocked ranges it keeps its full share."""
     cfg = config()
-    G, X = cfg.info["num_cus"], cfg.info["num_xcds"]
+    X = cfg.info["num_xcds"]
     M = N = 4096
     K = 256
     tile = (128, 128, 64)
-    T = (M // 128) * (N // 128)            # 1024 tiles: 4 per program on average
+    T = (M // 128) * (N // 128)            # 1024 tiles: T / G per program on average
+    G = pg.plan_gemm(cfg, M, N, K, "bf16_out_f32", "blocked", pg.make_args(tile=tile))["grid"]
     a, b = bf16_bits_uniform((M, K), 1), bf16_bits_uniform((K, N), 2)
     A, B = dev_bf16(a), dev_bf16(b)
     C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
@@ -125,3 +127,26 @@ def test_straggler_rebalanced_by_work_stealing():
     assert res["blocked"] == T // G
     peers = [p for p in range(G) if p % X == 0]
     assert res["work_stealing"] < T // G, res
+
+
+def test_plan_matches_launch_shape():
+    """The default persistent grid is CUs x resident workgroups per CU of the
+    selected kernel: two for 128x128 GEMM tiles, one for 256x256."""
+    cfg = config()
+    cus = cfg.info["num_cus"]
+    big = pg.plan_gemm(cfg, 8192, 8192, 8192, "bf16_out_bf16", "work_stealing")
+    small = pg.plan_gemm(cfg, 4096, 4096, 4096, "bf16_out_bf16", "work_stealing",
+                         pg.make_args(tile=(128, 128, 64)))
+    fp8 = pg.plan_gemm(cfg, 256, 28672, 8192, "fp8_b128_out_bf16", "grouped",
+                       pg.make_args(tile=(128, 128, 128)))
+    add = pg.plan_add(cfg, 8192, 8192, 128, 128, "blocked")
+    note(f"plans {big} {small} {fp8} {add}")
+    for pl in (big, small, fp8, add):
+        assert pl["occupancy"] >= 1 and pl["grid"] == cus * pl["occupancy"]
+    assert big["kernel"] == "bf16_lds" and big["tiles"] == 32 * 32 and big["occupancy"] == 1
+    assert small["kernel"] == "bf16_lds" and small["occupancy"] == 2
+    assert fp8["kernel"] == "fp8" and fp8["tiles"] == 2 * 224 and fp8["occupancy"] == 2
+    assert add["kernel"] == "add" and add["tiles"] == 64 * 64
+    assert pg.plan_gemm(cfg, 100, 100, 100, "bf16_out_bf16", "blocked", pg.make_args(grid=7))["grid"] == 7
+    staged = pg.plan_gemm(cfg, 512, 512, 500, "bf16_out_bf16", "blocked")
+    assert staged["kernel"] == "bf16_staged"

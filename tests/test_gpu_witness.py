@@ -34,7 +34,8 @@ def _check(w, kind, pm, pn, G, X, gs, chunk=1):
 
 def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
     cfg = config()
-    G = grid or cfg.info["num_cus"]
+    G = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched,
+                     pg.make_args(tile=tile, group_size=gs, grid=grid))["grid"]
     pm, pn = -(-M // tile[0]), -(-N // tile[1])
     cfg.witness_enable(pm * pn, G)
     a = bf16_bits_uniform((M, K), 1)
@@ -94,7 +95,7 @@ def test_add_schedule_exactly_once(sched, tile):
     cfg = config()
     rows, cols = 2048, 3000
     pm, pn = -(-rows // tile[0]), -(-cols // tile[1])
-    G = cfg.info["num_cus"]
+    G = pg.plan_add(cfg, rows, cols, tile[0], tile[1], sched)["grid"]
     cfg.witness_enable(pm * pn, G)
     X, Y = dev_f32(f32_normal((rows, cols), 1)), dev_f32(f32_normal((rows, cols), 2))
     C = torch.empty_like(X)

@@ -29,7 +29,7 @@ DTYPES = {
     "fp8_b128_out_bf16": _abi.FP8E4M3_B128_OUT_BF16,
 }
 
-__all__ = ["Config", "pgemm_run", "padd_run", "SCHEDULERS", "DTYPES", "PgemmError", "status_str",
+__all__ = ["Config", "pgemm_run", "padd_run", "plan_gemm", "plan_add", "SCHEDULERS", "DTYPES", "PgemmError", "status_str",
            "make_args"]
 
 
@@ -154,6 +154,37 @@ def pgemm_run(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=N
                                 int(M), int(N), int(K), _dtype(dtype), _sched(sched),
                                 ctypes.byref(a) if a is not None else None, _stream(stream))
     _check("pgemm_run", code)
+
+
+def _plan_dict(pl) -> dict:
+    return {"grid": pl.grid, "occupancy": pl.occupancy, "tiles": pl.tiles,
+            "tile": (pl.tile_m, pl.tile_n, pl.tile_k), "threads": pl.threads,
+            "lds_bytes": pl.lds_bytes, "kernel": _abi.KERNEL_NAMES.get(pl.kernel, str(pl.kernel))}
+
+
+def plan_gemm(cfg: Config, M: int, N: int, K: int, dtype, sched, args=None, A=None, B=None,
+              C=None) -> dict:
+    """The launch pgemm_run would make (grid, occupancy, tiles, kernel, ...)."""
+    pl = _abi.pgemm_plan()
+    code = _abi.lib().pgemm_plan_gemm(
+        cfg.handle, A.data_ptr() if A is not None else None, B.data_ptr() if B is not None else None,
+        C.data_ptr() if C is not None else None, int(M), int(N), int(K), _dtype(dtype),
+        _sched(sched), ctypes.byref(args) if args is not None else None, ctypes.byref(pl))
+    _check("pgemm_plan_gemm", code)
+    return _plan_dict(pl)
+
+
+def plan_add(cfg: Config, rows: int, cols: int, tile_rows: int, tile_cols: int, sched, args=None,
+             X=None, Y=None, C=None) -> dict:
+    """The launch padd_run would make."""
+    pl = _abi.pgemm_plan()
+    code = _abi.lib().pgemm_plan_add(
+        cfg.handle, X.data_ptr() if X is not None else None, Y.data_ptr() if Y is not None else None,
+        C.data_ptr() if C is not None else None, int(rows), int(cols), int(tile_rows),
+        int(tile_cols), _sched(sched), ctypes.byref(args) if args is not None else None,
+        ctypes.byref(pl))
+    _check("pgemm_plan_add", code)
+    return _plan_dict(pl)
 
 
 def padd_run(cfg: Config, X, Y, C, rows: int, cols: int, tile_rows: int, tile_cols: int, sched,

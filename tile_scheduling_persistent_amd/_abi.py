@@ -18,6 +18,10 @@ BF16_OUT_F32, BF16_OUT_BF16, FP8E4M3_B128_OUT_BF16 = range(3)
 SCHED_BLOCKED, SCHED_INTERLEAVED, SCHED_GROUPED, SCHED_WORK_STEALING, SCHED_BLOCKED_GROUPED = range(5)
 # debug flags
 DEBUG_WITNESS, DEBUG_SKIP_RESET, DEBUG_STRAGGLER, DEBUG_REGISTER_STAGED = 0x1, 0x2, 0x4, 0x8
+# pgemm_kernel
+KERNEL_BF16_LDS, KERNEL_BF16_STAGED, KERNEL_FP8, KERNEL_ADD = range(4)
+KERNEL_NAMES = {KERNEL_BF16_LDS: "bf16_lds", KERNEL_BF16_STAGED: "bf16_staged", KERNEL_FP8: "fp8",
+                KERNEL_ADD: "add"}
 
 
 class pgemm_args(ctypes.Structure):
@@ -46,6 +50,14 @@ class pgemm_witness(ctypes.Structure):
         ("hw_id", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("programs", ctypes.c_int32), ("counters", ctypes.c_void_p),
         ("cycles", ctypes.c_void_p),
+    ]
+
+
+class pgemm_plan(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int), ("occupancy", ctypes.c_int), ("tiles", ctypes.c_int64),
+        ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
+        ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("kernel", ctypes.c_int),
     ]
 
 
@@ -83,6 +95,14 @@ def lib() -> ctypes.CDLL:
     L.pgemm_witness_enable.restype = st
     L.pgemm_witness_read.argtypes = [_cfg_p, ctypes.POINTER(pgemm_witness), ctypes.c_void_p]
     L.pgemm_witness_read.restype = st
+    L.pgemm_plan_gemm.argtypes = [_cfg_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.POINTER(pgemm_plan)]
+    L.pgemm_plan_gemm.restype = st
+    L.pgemm_plan_add.argtypes = [_cfg_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.POINTER(pgemm_plan)]
+    L.pgemm_plan_add.restype = st
     _lib = L
     return L
 

@@ -77,6 +77,29 @@ bool gemm_fp8_eligible(int bm, long long N, long long K);
 bool padd_tile_supported(int tr, int tc);
 int padd_tiles_per_step(int tr, int tc);
 
+// Launch shape of a kernel instance: threads and dynamic LDS per workgroup,
+// and how many such workgroups one CU holds at once (registers, LDS, waves).
+// A persistent launch runs one program per resident slot: CUs x occupancy.
+struct KernelInfo {
+  int threads;
+  int lds_bytes;
+  int occupancy;
+};
+KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec);
+KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16);
+KernelInfo info_gemm_fp8(int bm, int bn);
+KernelInfo info_padd(int tr, int tc, bool vec);
+
+// Resident workgroups per CU of `kern` (at least 1), after raising its
+// dynamic-LDS limit to `lds` bytes.
+inline int occupancy_of(const void* kern, int threads, int lds) {
+  if (lds > 0) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, (size_t)lds) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 
 // Wall clock (constant rate, see hipDeviceAttributeWallClockRate).

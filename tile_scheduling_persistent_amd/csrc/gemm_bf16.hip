@@ -424,7 +424,29 @@ hipError_t launch_tile(const GemmParams& p, bool out_bf16, bool vec, bool witnes
                  : launch_one<BM, BN, BK, false, false, false>(p, stream);
 }
 
+template <int BM, int BN, int BK, bool OUT_BF16, bool VEC>
+KernelInfo info_one() {
+  using S = Shape<BM, BN, BK>;
+  static const KernelInfo ki = {
+      kThreads, S::LDS_BYTES,
+      occupancy_of(reinterpret_cast<const void*>(gemm_bf16_kernel<BM, BN, BK, OUT_BF16, VEC, false>),
+                   kThreads, S::LDS_BYTES)};
+  return ki;
+}
+
+template <int BM, int BN, int BK>
+KernelInfo info_tile(bool out_bf16, bool vec) {
+  if (out_bf16) return vec ? info_one<BM, BN, BK, true, true>() : info_one<BM, BN, BK, true, false>();
+  return vec ? info_one<BM, BN, BK, false, true>() : info_one<BM, BN, BK, false, false>();
+}
+
 }  // namespace
+
+KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec) {
+  if (bm == 256 && bn == 256 && bk == 64) return info_tile<256, 256, 64>(out_bf16, vec);
+  if (bm == 128 && bn == 128 && bk == 64) return info_tile<128, 128, 64>(out_bf16, vec);
+  return KernelInfo{0, 0, 0};
+}
 
 bool gemm_bf16_tile_supported(int bm, int bn, int bk) {
   return bk == 64 && ((bm == 256 && bn == 256) || (bm == 128 && bn == 128));

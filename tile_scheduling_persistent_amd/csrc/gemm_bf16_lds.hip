@@ -434,6 +434,16 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, bool OUT_BF16>
+KernelInfo info_one() {
+  using S = Shape<BM, BN, kBK, kNST>;
+  static const KernelInfo ki = {
+      kThreads, S::LDS_BYTES,
+      occupancy_of(reinterpret_cast<const void*>(gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, false>),
+                   kThreads, S::LDS_BYTES)};
+  return ki;
+}
+
 template <int BM, int BN>
 hipError_t launch_tile(const GemmParams& p, bool out_bf16, bool witness, hipStream_t stream) {
   if (out_bf16)
@@ -451,6 +461,12 @@ bool gemm_bf16_lds_eligible(int bm, int bn, int bk, long long N, long long K) {
   if (K % 8 != 0 || N % 8 != 0) return false;
   return (long long)bm * K * 2 < (1LL << 31) && 64LL * N * 2 < (1LL << 31) &&
          (long long)bm * N * 4 < (1LL << 31);
+}
+
+KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16) {
+  if (bm == 256 && bn == 256) return out_bf16 ? info_one<256, 256, true>() : info_one<256, 256, false>();
+  if (bm == 128 && bn == 128) return out_bf16 ? info_one<128, 128, true>() : info_one<128, 128, false>();
+  return KernelInfo{0, 0, 0};
 }
 
 hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,

@@ -402,6 +402,16 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BM, int BN>
+KernelInfo info_one() {
+  using S = Shape<BM, BN>;
+  static const KernelInfo ki = {
+      kThreads, S::LDS_BYTES,
+      occupancy_of(reinterpret_cast<const void*>(gemm_fp8_kernel<BM, BN, false>), kThreads,
+                   S::LDS_BYTES)};
+  return ki;
+}
+
 }  // namespace
 
 bool gemm_fp8_tile_supported(int bm, int bn, int bk) {
@@ -413,6 +423,12 @@ bool gemm_fp8_tile_supported(int bm, int bn, int bk) {
 bool gemm_fp8_eligible(int bm, long long N, long long K) {
   return N % 16 == 0 && (long long)bm * K < (1LL << 31) && 128LL * N < (1LL << 31) &&
          (long long)bm * N * 2 < (1LL << 31);
+}
+
+KernelInfo info_gemm_fp8(int bm, int bn) {
+  if (bm == 256 && bn == 256) return info_one<256, 256>();
+  if (bm == 128 && bn == 128) return info_one<128, 128>();
+  return KernelInfo{0, 0, 0};
 }
 
 hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec, bool witness,

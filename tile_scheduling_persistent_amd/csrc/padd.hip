@@ -196,6 +196,17 @@ __global__ void fill_i32_kernel(int* p, int n, int value) {
     p[i] = value;
 }
 
+template <int TR, int TC, bool VEC>
+KernelInfo info_one() {
+  static const KernelInfo ki = {
+      kThreads, 0,
+      occupancy_of(reinterpret_cast<const void*>(padd_kernel<TR, TC, VEC, false>), kThreads, 0)};
+  return ki;
+}
+
+template <int TR, int TC>
+KernelInfo info_tile(bool vec) { return vec ? info_one<TR, TC, true>() : info_one<TR, TC, false>(); }
+
 }  // namespace
 
 int padd_tiles_per_step(int tr, int tc) {
@@ -207,6 +218,13 @@ int padd_tiles_per_step(int tr, int tc) {
 
 bool padd_tile_supported(int tr, int tc) {
   return (tr == 32 && tc == 16) || (tr == 64 && tc == 64) || (tr == 128 && tc == 128);
+}
+
+KernelInfo info_padd(int tr, int tc, bool vec) {
+  if (tr == 32 && tc == 16) return info_tile<32, 16>(vec);
+  if (tr == 64 && tc == 64) return info_tile<64, 64>(vec);
+  if (tr == 128 && tc == 128) return info_tile<128, 128>(vec);
+  return KernelInfo{0, 0, 0};
 }
 
 hipError_t launch_padd(const AddParams& p, int tr, int tc, bool vec, bool witness,

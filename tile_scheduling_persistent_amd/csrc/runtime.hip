@@ -85,15 +85,17 @@ void free_witness(pgemm_config* c) {
   c->w_programs = 0;
 }
 
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
-                        int num_pid_m, int num_pid_n, pgk::SchedParams& s) {
+                        int num_pid_m, int num_pid_n, int default_grid, pgk::SchedParams& s) {
   if ((int)sched < 0 || (int)sched > 4) return PGEMM_ERR_INVALID;
   const int64_t T = (int64_t)num_pid_m * num_pid_n;
   if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
   s.kind = (int)sched;
   s.T = (int)T;
-  s.G = (args && args->grid) ? args->grid : cfg->num_cus;
+  s.G = (args && args->grid) ? args->grid : default_grid;
   s.X = cfg->num_xcds;
   s.gs = (args && args->group_size) ? args->group_size : kDefaultGroup;
   s.num_pid_m = num_pid_m;
@@ -112,6 +114,74 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
     s.straggler_ns = args->straggler_ns;
   }
   return PGEMM_OK;
+}
+
+// Kernel a GEMM call takes, from shapes, formats, tile and pointer alignment
+// (pointers may be null: taken as 16-byte aligned).
+struct GemmChoice {
+  int bm, bn, bk;
+  pgemm_kernel kernel;
+  bool out_bf16;
+  bool vec;  // register-staged kernel: 16-byte vector path
+};
+
+pgemm_status choose_gemm(int64_t M, int64_t N, int64_t K, pgemm_dtype dtype, const pgemm_args* args,
+                         const void* A, const void* B, const void* C, GemmChoice& ch) {
+  if (M < 1 || N < 1 || K < 1 || M > 0x7fffffffLL || N > 0x7fffffffLL || K > 0x7fffffffLL)
+    return PGEMM_ERR_INVALID;
+  const bool fp8 = dtype == PGEMM_FP8E4M3_B128_OUT_BF16;
+  if (!fp8 && dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16)
+    return PGEMM_ERR_INVALID;
+  ch.bm = 256;
+  ch.bn = 256;
+  ch.bk = fp8 ? 128 : 64;
+  if (args && (args->tile_m || args->tile_n || args->tile_k)) {
+    ch.bm = args->tile_m;
+    ch.bn = args->tile_n;
+    ch.bk = args->tile_k;
+  }
+  if (ch.bm < 1 || ch.bn < 1 || ch.bk < 1) return PGEMM_ERR_INVALID;
+  ch.out_bf16 = dtype != PGEMM_BF16_OUT_F32;
+  ch.vec = false;
+  const bool al = (!A || aligned(A, 16)) && (!B || aligned(B, 16)) && (!C || aligned(C, 16));
+  if (fp8) {
+    if (K % 128 != 0) return PGEMM_ERR_INVALID;
+    if (!pgk::gemm_fp8_tile_supported(ch.bm, ch.bn, ch.bk)) return PGEMM_ERR_UNSUPPORTED;
+    // the fp8 kernel moves 16-byte chunks of B rows and of C
+    if (!pgk::gemm_fp8_eligible(ch.bm, N, K) || !al) return PGEMM_ERR_UNSUPPORTED;
+    ch.kernel = PGEMM_KERNEL_FP8;
+    return PGEMM_OK;
+  }
+  if (!pgk::gemm_bf16_tile_supported(ch.bm, ch.bn, ch.bk)) return PGEMM_ERR_UNSUPPORTED;
+  const bool staged = args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED);
+  if (!staged && al && pgk::gemm_bf16_lds_eligible(ch.bm, ch.bn, ch.bk, N, K)) {
+    ch.kernel = PGEMM_KERNEL_BF16_LDS;
+  } else {
+    ch.kernel = PGEMM_KERNEL_BF16_STAGED;
+    ch.vec = (K % 8 == 0) && (N % 8 == 0) && al && pgk::gemm_bf16_vec_fits(ch.bm, ch.bk, N, K);
+  }
+  return PGEMM_OK;
+}
+
+pgk::KernelInfo gemm_info(const GemmChoice& ch) {
+  switch (ch.kernel) {
+    case PGEMM_KERNEL_FP8: return pgk::info_gemm_fp8(ch.bm, ch.bn);
+    case PGEMM_KERNEL_BF16_LDS: return pgk::info_gemm_bf16_lds(ch.bm, ch.bn, ch.out_bf16);
+    default: return pgk::info_gemm_bf16(ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec);
+  }
+}
+
+void fill_plan(const pgk::SchedParams& s, const pgk::KernelInfo& ki, int bm, int bn, int bk,
+               pgemm_kernel kernel, pgemm_plan* out) {
+  out->grid = s.G;
+  out->occupancy = ki.occupancy;
+  out->tiles = s.T;
+  out->tile_m = bm;
+  out->tile_n = bn;
+  out->tile_k = bk;
+  out->threads = ki.threads;
+  out->lds_bytes = ki.lds_bytes;
+  out->kernel = kernel;
 }
 
 pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
@@ -147,7 +217,6 @@ pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk
              : PGEMM_ERR_LAUNCH;
 }
 
-bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
@@ -288,28 +357,12 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
                        int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
                        const pgemm_args* args, void* hip_stream) {
   if (!cfg || !A || !B || !C) return PGEMM_ERR_INVALID;
-  if (M < 1 || N < 1 || K < 1 || M > 0x7fffffffLL || N > 0x7fffffffLL || K > 0x7fffffffLL)
-    return PGEMM_ERR_INVALID;
-  const bool fp8 = dtype == PGEMM_FP8E4M3_B128_OUT_BF16;
-  if (!fp8 && dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16)
-    return PGEMM_ERR_INVALID;
-  int bm = 256, bn = 256, bk = fp8 ? 128 : 64;
-  if (args && (args->tile_m || args->tile_n || args->tile_k)) {
-    bm = args->tile_m;
-    bn = args->tile_n;
-    bk = args->tile_k;
-  }
-  if (bm < 1 || bn < 1 || bk < 1) return PGEMM_ERR_INVALID;
-  if (fp8) {
-    if (!args || !args->a_scale || !args->b_scale) return PGEMM_ERR_INVALID;
-    if (K % 128 != 0) return PGEMM_ERR_INVALID;
-    if (!pgk::gemm_fp8_tile_supported(bm, bn, bk)) return PGEMM_ERR_UNSUPPORTED;
-    // the fp8 kernel moves 16-byte chunks of B rows and of C
-    if (!pgk::gemm_fp8_eligible(bm, N, K) || !aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
-      return PGEMM_ERR_UNSUPPORTED;
-  } else if (!pgk::gemm_bf16_tile_supported(bm, bn, bk)) {
-    return PGEMM_ERR_UNSUPPORTED;
-  }
+  GemmChoice ch;
+  pgemm_status st = choose_gemm(M, N, K, dtype, args, A, B, C, ch);
+  if (st != PGEMM_OK) return st;
+  const bool fp8 = ch.kernel == PGEMM_KERNEL_FP8;
+  if (fp8 && (!args || !args->a_scale || !args->b_scale)) return PGEMM_ERR_INVALID;
+  const int bm = ch.bm, bn = ch.bn;
   const int dev = cfg->device;
   if (!is_device_ptr(A, dev) || !is_device_ptr(B, dev) || !is_device_ptr(C, dev))
     return PGEMM_ERR_INVALID;
@@ -340,11 +393,12 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   p.K = (int)K;
   const int64_t npm = (M + bm - 1) / bm, npn = (N + bn - 1) / bn;
   if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
-  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, p.s);
-  if (st != PGEMM_OK) return st;
-
   DeviceGuard g(dev);
   if (!g.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = gemm_info(ch);
+  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, p.s);
+  if (st != PGEMM_OK) return st;
+
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
@@ -353,20 +407,12 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   if (st != PGEMM_OK) return st;
 
   hipError_t e;
-  if (fp8) {
-    e = pgk::launch_gemm_fp8(p, bm, bn, bk, true, witness, stream);
-  } else {
-    const bool out_bf16 = dtype == PGEMM_BF16_OUT_BF16;
-    const bool staged = args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED);
-    if (!staged && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) &&
-        pgk::gemm_bf16_lds_eligible(bm, bn, bk, N, K)) {
-      e = pgk::launch_gemm_bf16_lds(p, bm, bn, out_bf16, witness, stream);
-    } else {
-      const bool vec = (K % 8 == 0) && (N % 8 == 0) && aligned(A, 16) && aligned(B, 16) &&
-                       aligned(C, 16) && pgk::gemm_bf16_vec_fits(bm, bk, N, K);
-      e = pgk::launch_gemm_bf16(p, bm, bn, bk, out_bf16, vec, witness, stream);
-    }
-  }
+  if (fp8)
+    e = pgk::launch_gemm_fp8(p, ch.bm, ch.bn, ch.bk, true, witness, stream);
+  else if (ch.kernel == PGEMM_KERNEL_BF16_LDS)
+    e = pgk::launch_gemm_bf16_lds(p, ch.bm, ch.bn, ch.out_bf16, witness, stream);
+  else
+    e = pgk::launch_gemm_bf16(p, ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec, witness, stream);
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }
@@ -396,7 +442,12 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
   p.rows = (int)rows;
   p.cols = (int)cols;
   const int64_t npm = (rows + tile_rows - 1) / tile_rows, npn = (cols + tile_cols - 1) / tile_cols;
-  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, p.s);
+  if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  const bool vec = (cols % 4 == 0) && aligned(X, 16) && aligned(Y, 16) && aligned(C, 16);
+  DeviceGuard g(dev);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, p.s);
   if (st != PGEMM_OK) return st;
   const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
   p.s.chunk = step;
@@ -404,18 +455,55 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
     if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
     p.s.chunk = args->claim_chunk;
   }
-  DeviceGuard g(dev);
-  if (!g.ok) return PGEMM_ERR_DEVICE;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
   st = reset_counters(cfg, args, p.s, stream);
   if (st != PGEMM_OK) return st;
-  const bool vec = (cols % 4 == 0) && aligned(X, 16) && aligned(Y, 16) && aligned(C, 16);
   hipError_t e = pgk::launch_padd(p, tile_rows, tile_cols, vec, witness, stream);
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
+pgemm_status pgemm_plan_gemm(pgemm_config* cfg, const void* A, const void* B, const void* C,
+                             int64_t M, int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
+                             const pgemm_args* args, pgemm_plan* out) {
+  if (!cfg || !out) return PGEMM_ERR_INVALID;
+  GemmChoice ch;
+  pgemm_status st = choose_gemm(M, N, K, dtype, args, A, B, C, ch);
+  if (st != PGEMM_OK) return st;
+  const int64_t npm = (M + ch.bm - 1) / ch.bm, npn = (N + ch.bn - 1) / ch.bn;
+  if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  DeviceGuard g(cfg->device);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = gemm_info(ch);
+  pgk::SchedParams s;
+  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, s);
+  if (st != PGEMM_OK) return st;
+  fill_plan(s, ki, ch.bm, ch.bn, ch.bk, ch.kernel, out);
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_plan_add(pgemm_config* cfg, const float* X, const float* Y, const float* C,
+                            int64_t rows, int64_t cols, int tile_rows, int tile_cols,
+                            pgemm_sched sched, const pgemm_args* args, pgemm_plan* out) {
+  if (!cfg || !out) return PGEMM_ERR_INVALID;
+  if (rows < 1 || cols < 1 || rows > 0x7fffffffLL || cols > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  if (tile_rows < 1 || tile_cols < 1) return PGEMM_ERR_INVALID;
+  if (!pgk::padd_tile_supported(tile_rows, tile_cols)) return PGEMM_ERR_UNSUPPORTED;
+  const int64_t npm = (rows + tile_rows - 1) / tile_rows, npn = (cols + tile_cols - 1) / tile_cols;
+  if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  const bool vec = (cols % 4 == 0) && (!X || aligned(X, 16)) && (!Y || aligned(Y, 16)) &&
+                   (!C || aligned(C, 16));
+  DeviceGuard g(cfg->device);
+  if (!g.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
+  pgk::SchedParams s;
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, s);
+  if (st != PGEMM_OK) return st;
+  fill_plan(s, ki, tile_rows, tile_cols, 0, PGEMM_KERNEL_ADD, out);
+  return PGEMM_OK;
 }
 
 }  // extern "C"
