@@ -189,7 +189,7 @@ typedef enum {
 /* Launch a call would make.  A persistent launch runs one program per
  * resident workgroup slot: grid = number of CUs x occupancy unless
  * args->grid overrides it (e.g. 128x128 GEMM tiles fit two workgroups per
- * CU, 256x256 tiles one). */
+ * CU, 256x256 tiles one; the add runs one 1024-thread program per CU). */
 typedef struct {
   int grid;          /* programs */
   int occupancy;     /* workgroups of the kernel one CU holds at once */

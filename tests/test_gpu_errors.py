@@ -146,7 +146,7 @@ def test_plan_matches_launch_shape():
     assert big["kernel"] == "bf16_lds" and big["tiles"] == 32 * 32 and big["occupancy"] == 1
     assert small["kernel"] == "bf16_lds" and small["occupancy"] == 2
     assert fp8["kernel"] == "fp8" and fp8["tiles"] == 2 * 224 and fp8["occupancy"] == 2
-    assert add["kernel"] == "add" and add["tiles"] == 64 * 64
+    assert add["kernel"] == "add" and add["tiles"] == 64 * 64 and add["occupancy"] == 1
     assert pg.plan_gemm(cfg, 100, 100, 100, "bf16_out_bf16", "blocked", pg.make_args(grid=7))["grid"] == 7
     staged = pg.plan_gemm(cfg, 512, 512, 500, "bf16_out_bf16", "blocked")
     assert staged["kernel"] == "bf16_staged"
