@@ -213,6 +213,11 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   };
 
   auto prep = [&]() {
+    // The loader state is the same in every lane; saying so keeps its
+    // branches scalar.
+    lt = __builtin_amdgcn_readfirstlane(lt);
+    lk = __builtin_amdgcn_readfirstlane(lk);
+    claims = __builtin_amdgcn_readfirstlane(claims);
     if (lt >= 0 && lk == nk) {
       const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
       ++claims;
