@@ -1,0 +1,65 @@
+"""A pgemm_run / padd_run call captured in a HIP graph: the work-stealing
+counter reset is a fill kernel on the call's stream (no memset node), so
+every replay starts from zeroed counters.  Each replay is checked bit for
+bit against the eager result, with eager work and synchronisations between
+the replays."""
+import pytest
+import torch
+
+import tile_scheduling_persistent_amd as pg
+from synthetic import bf16_bits_uniform, f32_normal
+from tests.gpu_util import config, dev_bf16, dev_f32, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("sched", ["work_stealing", "grouped"])
+def test_gemm_graph_replays(sched):
+    cfg = config()
+    M, N, K = 1536, 1280, 512
+    A = dev_bf16(bf16_bits_uniform((M, K), 71))
+    B = dev_bf16(bf16_bits_uniform((K, N), 72))
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty_like(ref)
+    args = pg.make_args(tile=(256, 256, 64))
+    note(f"graph gemm {M}x{N}x{K} {sched}")
+    pg.pgemm_run(cfg, A, B, ref, M, N, K, "bf16_out_bf16", sched, args)  # eager, also warms up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pg.pgemm_run(cfg, A, B, out, M, N, K, "bf16_out_bf16", sched, args)
+    torch.cuda.synchronize()
+    junk = torch.zeros(1 << 20, device="cuda:0")
+    for r in range(4):
+        out.fill_(float("nan"))
+        junk.add_(1.0)                      # unrelated eager work between replays
+        pg.pgemm_run(cfg, A, B, ref, M, N, K, "bf16_out_bf16", sched, args)  # eager call in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+
+
+def test_add_graph_replays():
+    cfg = config()
+    rows, cols = 1000, 3000
+    X, Y = dev_f32(f32_normal((rows, cols), 73)), dev_f32(f32_normal((rows, cols), 74))
+    ref = X + Y
+    out = torch.empty_like(X)
+    note("graph add work stealing")
+    pg.padd_run(cfg, X, Y, out, rows, cols, 32, 16, "work_stealing")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pg.padd_run(cfg, X, Y, out, rows, cols, 32, 16, "work_stealing")
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
