@@ -26,6 +26,16 @@ Sources:
   silent: XCD x owns the contiguous range [floor(x*T/X), floor((x+1)*T/X))
   of the grouped order; a claim is fetch_add(counter, chunk) and a program
   stops at its first claim that starts at or beyond the range's length.
+* Stream-K (the comparator "Work Stealing Scheduler Kernel", tritonBLAS PR
+  #65, benchmarks work stealing against; the page names it only).  Reading
+  taken: the data-parallel + stream-K hybrid of the published Stream-K
+  method.  With T tiles of nk K-slabs on G programs: if G divides T every
+  tile is data-parallel; otherwise the first (floor(T/G) - 1)*G tiles (none
+  when T < G) are taken stride-by-grid, whole, and the slabs of the
+  remaining tiles, in order, are split into G contiguous runs of
+  floor(p*W/G) .. floor((p+1)*W/G) (W = their slab count).  A tile whose
+  slabs fall into several runs is summed from the runs' partial results in
+  slab order.
 """
 from __future__ import annotations
 
@@ -37,6 +47,7 @@ INTERLEAVED = "interleaved"
 GROUPED = "grouped"
 WORK_STEALING = "work_stealing"
 BLOCKED_GROUPED = "blocked_grouped"
+STREAM_K = "stream_k"
 STATIC_KINDS = (BLOCKED, INTERLEAVED, GROUPED, BLOCKED_GROUPED)
 
 
@@ -196,3 +207,55 @@ def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
     want = ws_final_counters(T, G, X, chunk)
     if list(counters[:X]) != want:
         raise AssertionError(f"final counters {list(counters[:X])} != {want}")
+
+
+def streamk_dp_tiles(T: int, G: int) -> int:
+    """Tiles taken whole (data-parallel) before the stream-K part."""
+    if T % G == 0:
+        return T
+    return max(0, T // G - 1) * G
+
+
+def streamk_schedule(T: int, nk: int, G: int) -> List[List[Tuple[int, int, int]]]:
+    """Per program, its segments (tile id, first slab, end slab) in order."""
+    dp = streamk_dp_tiles(T, G)
+    W = (T - dp) * nk
+    out: List[List[Tuple[int, int, int]]] = []
+    for p in range(G):
+        segs = [(v, 0, nk) for v in range(p, dp, G)]
+        i, end = dp * nk + (p * W) // G, dp * nk + ((p + 1) * W) // G
+        while i < end:
+            v, kb = divmod(i, nk)
+            ke = min(nk, kb + end - i)
+            segs.append((v, kb, ke))
+            i += ke - kb
+        out.append(segs)
+    return out
+
+
+def streamk_partials(T: int, nk: int, G: int) -> Dict[int, List[Tuple[int, int, int]]]:
+    """Tiles split over several programs: tile -> [(program, first slab, end
+    slab)] in slab order (the order the partial results are summed in)."""
+    parts: Dict[int, List[Tuple[int, int, int]]] = {}
+    for p, segs in enumerate(streamk_schedule(T, nk, G)):
+        for v, kb, ke in segs:
+            if kb != 0 or ke != nk:
+                parts.setdefault(v, []).append((p, kb, ke))
+    for v in parts:
+        parts[v].sort(key=lambda t: t[1])
+    return parts
+
+
+def check_streamk_cover(sched: Sequence[Sequence[Tuple[int, int, int]]], T: int, nk: int) -> None:
+    """Every (tile, slab) pair is computed exactly once."""
+    seen: Dict[Tuple[int, int], int] = {}
+    for p, segs in enumerate(sched):
+        for v, kb, ke in segs:
+            if not (0 <= v < T and 0 <= kb < ke <= nk):
+                raise AssertionError(f"program {p}: bad segment {(v, kb, ke)}")
+            for k in range(kb, ke):
+                if (v, k) in seen:
+                    raise AssertionError(f"tile {v} slab {k} computed by {seen[(v, k)]} and {p}")
+                seen[(v, k)] = p
+    if len(seen) != T * nk:
+        raise AssertionError(f"{T * nk - len(seen)} (tile, slab) pairs never computed")

@@ -141,3 +141,48 @@ def test_checkers_catch_planted_mistakes():
     v2[5] = 2
     with pytest.raises(AssertionError):
         sm.check_ws_execution(v2, o, r, cnt, T, 8, 4)
+
+
+def test_streamk_golden(golden):
+    rows = [tuple(map(int, r.split())) for r in golden("sk_T10_nk4_G4.txt")]
+    want = {}
+    for p, v, kb, ke in rows:
+        want.setdefault(p, []).append((v, kb, ke))
+    got = sm.streamk_schedule(10, 4, 4)
+    assert {p: s for p, s in enumerate(got)} == want
+    assert sm.streamk_partials(10, 4, 4) == {5: [(0, 0, 2), (1, 2, 4)], 8: [(2, 0, 2), (3, 2, 4)]}
+
+
+@pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),
+                                    (400, 64, 256), (448, 64, 512), (1024, 128, 256), (3, 5, 256),
+                                    (300, 2, 7)])
+def test_streamk_cover_and_balance(T, nk, G):
+    sched = sm.streamk_schedule(T, nk, G)
+    sm.check_streamk_cover(sched, T, nk)
+    dp = sm.streamk_dp_tiles(T, G)
+    # data-parallel part: stride by grid, whole tiles
+    for p, segs in enumerate(sched):
+        whole = [v for v, kb, ke in segs if v < dp]
+        assert whole == list(range(p, dp, G))
+    # stream-K part: per-program slab counts differ by at most one
+    sk = [sum(ke - kb for v, kb, ke in segs if v >= dp) for segs in sched]
+    assert max(sk) - min(sk) <= 1 and sum(sk) == (T - dp) * nk
+    # G divides T: nothing is split
+    if T % G == 0:
+        assert dp == T and not sm.streamk_partials(T, nk, G)
+    # a program has at most two partial segments: the first and the last of its run
+    for segs in sched:
+        run = [s for s in segs if s[0] >= dp]
+        part = [i for i, (v, kb, ke) in enumerate(run) if kb != 0 or ke != nk]
+        assert all(i in (0, len(run) - 1) for i in part)
+
+
+def test_streamk_checker_catches_planted_mistakes():
+    sched = [list(s) for s in sm.streamk_schedule(10, 4, 4)]
+    sched[1][1] = (5, 1, 4)                                 # slab 1 of tile 5 twice
+    with pytest.raises(AssertionError):
+        sm.check_streamk_cover(sched, 10, 4)
+    sched = [list(s) for s in sm.streamk_schedule(10, 4, 4)]
+    sched[3].pop()                                          # tile 9 dropped
+    with pytest.raises(AssertionError):
+        sm.check_streamk_cover(sched, 10, 4)
