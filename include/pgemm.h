@@ -71,13 +71,28 @@ typedef enum {
  *                   p mod X the tiles of the contiguous range
  *                   [floor(x*T/X), floor((x+1)*T/X)) of the grouped order
  *                   until a claim falls past its end.  Needs G >= X.
- *  BLOCKED_GROUPED  blocked ranges over the grouped order. */
+ *  BLOCKED_GROUPED  blocked ranges over the grouped order.
+ *  STREAM_K         the comparator named by "Work Stealing Scheduler
+ *                   Kernel" (tritonBLAS PR #65, benchmark harness), taken as
+ *                   the data-parallel + stream-K hybrid: if G divides T all
+ *                   tiles are data-parallel (stride-by-grid over the grouped
+ *                   order); otherwise the first (T/G - 1)*G tiles are, and the
+ *                   K-slabs of the rest are cut into G equal contiguous runs.
+ *                   Tiles split between runs are summed (fp32, slab order)
+ *                   by a fix-up kernel from per-program partial-sum slots in
+ *                   a workspace the config allocates on first use (G x 2
+ *                   tiles of fp32).  bf16 direct-to-LDS kernel only (aligned
+ *                   operands, K and N multiples of 8), no witness; otherwise
+ *                   PGEMM_ERR_UNSUPPORTED.  Results are deterministic but
+ *                   not bitwise equal to the other schedulers on split
+ *                   tiles (different summation order). */
 typedef enum {
   PGEMM_SCHED_BLOCKED = 0,
   PGEMM_SCHED_INTERLEAVED = 1,
   PGEMM_SCHED_GROUPED = 2,
   PGEMM_SCHED_WORK_STEALING = 3,
-  PGEMM_SCHED_BLOCKED_GROUPED = 4
+  PGEMM_SCHED_BLOCKED_GROUPED = 4,
+  PGEMM_SCHED_STREAM_K = 5
 } pgemm_sched;
 
 /* debug_flags (tests and measurement only). */
@@ -138,7 +153,9 @@ PGEMM_API pgemm_status pgemm_config_destroy(pgemm_config* cfg);
  * streams must not overlap.  Errors: NULL pointer, M, N or K < 1,
  * group_size < 1, grid < 1 (or < X for work stealing), fp8 without scales or
  * with K % 128 != 0 => PGEMM_ERR_INVALID; tile shape not built =>
- * PGEMM_ERR_UNSUPPORTED. */
+ * PGEMM_ERR_UNSUPPORTED.  PGEMM_SCHED_STREAM_K may allocate (or grow, after
+ * a device synchronisation) the config's workspace: PGEMM_ERR_OOM if that
+ * fails. */
 PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
                        int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
                        pgemm_sched sched, const pgemm_args* args, void* hip_stream);

@@ -63,6 +63,32 @@ static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
   return 0;
 }
 
+// Stream-K: every program's segments (tile, first slab, end slab, slot), then
+// for every split tile its contributors with the slots they wrote.
+static int sk_walk(int T, int nk, int G) {
+  for (int p = 0; p < G; ++p) {
+    pgs::SkWalker w;
+    w.init(p, T, G, nk);
+    std::printf("%d:", p);
+    int v, kb, ke, slot;
+    while (w.next(v, kb, ke, slot)) std::printf(" %d,%d,%d,%d", v, kb, ke, slot);
+    std::printf("\n");
+  }
+  const int dp = pgs::sk_dp_tiles(T, G);
+  const int64_t W = (int64_t)(T - dp) * nk;
+  for (int v = dp; v < T; ++v) {
+    const int64_t j0 = (int64_t)(v - dp) * nk;
+    const int q0 = pgs::sk_owner(j0, W, G), q1 = pgs::sk_owner(j0 + nk - 1, W, G);
+    if (q0 == q1) continue;
+    std::printf("split %d:", v);
+    for (int q = q0; q <= q1; ++q)
+      if (pgs::sk_run_begin(q, W, G) < pgs::sk_run_begin(q + 1, W, G))  // empty runs add nothing
+        std::printf(" %d,%d", q, pgs::sk_slot(q, v, dp, nk, W, G));
+    std::printf("\n");
+  }
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc < 2) return 2;
   const std::string mode = argv[1];
@@ -72,5 +98,7 @@ int main(int argc, char** argv) {
   if (mode == "ws" && argc == 8)
     return ws_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                       std::atoi(argv[6]), std::atoi(argv[7]));
+  if (mode == "sk" && argc == 5)
+    return sk_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   return 2;
 }

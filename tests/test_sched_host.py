@@ -54,3 +54,32 @@ def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     owner = [r[2] for r in rows]
     order = [r[3] for r in rows]
     sm.check_ws_execution(visits, owner, order, counters, T, G, X, chunk)
+
+
+@pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),
+                                    (400, 64, 256), (448, 64, 512), (3, 5, 256), (300, 2, 7),
+                                    (1024, 128, 256)])
+def test_streamk_walk_matches_model(harness, T, nk, G):
+    out = subprocess.run([harness, "sk", str(T), str(nk), str(G)], check=True, capture_output=True,
+                         text=True).stdout.strip().splitlines()
+    segs = [l for l in out if not l.startswith("split")]
+    got = []
+    slots = {}
+    for p, line in enumerate(segs):
+        _, _, rest = line.partition(":")
+        lst = [tuple(map(int, t.split(","))) for t in rest.split()]
+        got.append([(v, kb, ke) for v, kb, ke, _ in lst])
+        for v, kb, ke, slot in lst:
+            assert (slot >= 0) == (kb != 0 or ke != nk)
+            if slot >= 0:
+                slots[(p, v)] = slot
+    assert got == sm.streamk_schedule(T, nk, G)
+    # the split tiles and, for each, its contributors in slab order with the
+    # slot each one wrote its partial sum to
+    want = {v: [(q, slots[(q, v)]) for q, _, _ in parts]
+            for v, parts in sm.streamk_partials(T, nk, G).items()}
+    split = {}
+    for line in (l for l in out if l.startswith("split")):
+        head, _, rest = line.partition(":")
+        split[int(head.split()[1])] = [tuple(map(int, t.split(","))) for t in rest.split()]
+    assert split == want

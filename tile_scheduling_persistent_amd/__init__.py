@@ -22,6 +22,7 @@ SCHEDULERS = {
     "grouped": _abi.SCHED_GROUPED,
     "work_stealing": _abi.SCHED_WORK_STEALING,
     "blocked_grouped": _abi.SCHED_BLOCKED_GROUPED,
+    "stream_k": _abi.SCHED_STREAM_K,
 }
 DTYPES = {
     "bf16_out_f32": _abi.BF16_OUT_F32,

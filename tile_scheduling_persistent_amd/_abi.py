@@ -15,7 +15,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE, ERR_OOM, ERR_LAUNCH = range(6)
 # pgemm_dtype
 BF16_OUT_F32, BF16_OUT_BF16, FP8E4M3_B128_OUT_BF16 = range(3)
 # pgemm_sched
-SCHED_BLOCKED, SCHED_INTERLEAVED, SCHED_GROUPED, SCHED_WORK_STEALING, SCHED_BLOCKED_GROUPED = range(5)
+(SCHED_BLOCKED, SCHED_INTERLEAVED, SCHED_GROUPED, SCHED_WORK_STEALING, SCHED_BLOCKED_GROUPED,
+ SCHED_STREAM_K) = range(6)
 # debug flags
 DEBUG_WITNESS, DEBUG_SKIP_RESET, DEBUG_STRAGGLER, DEBUG_REGISTER_STAGED = 0x1, 0x2, 0x4, 0x8
 # pgemm_kernel

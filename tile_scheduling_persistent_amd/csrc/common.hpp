@@ -43,9 +43,21 @@ struct GemmParams {
   void* C;            // [M][N]
   const uint8_t* sa;  // fp8: [K/128][M]
   const uint8_t* sb;  // fp8: [K/128][N]
+  float* ws;          // stream-K: partial-sum slots [G][2][BM*BN] (fp32, tile-row-major)
   int M, N, K;
   SchedParams s;
   Witness w;
+};
+
+// Stream-K fix-up: the tiles whose slabs several programs shared are summed
+// from the programs' partial-sum slots in slab order and written to C.
+struct SkFixParams {
+  const float* ws;
+  void* C;
+  int M, N;
+  int T, nk, G, dp;
+  long long W;
+  int num_pid_m, num_pid_n, gs;
 };
 
 struct AddParams {
@@ -85,6 +97,9 @@ struct KernelInfo {
   int lds_bytes;
   int occupancy;
 };
+hipError_t launch_gemm_bf16_lds_sk(const GemmParams& p, int bm, int bn, bool out_bf16,
+                                   hipStream_t stream);
+hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, hipStream_t stream);
 KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec);
 KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16);
 KernelInfo info_gemm_fp8(int bm, int bn);

@@ -101,7 +101,11 @@ __device__ __forceinline__ int swz_a(int row, int c) {
 // bits 2-3 with the row moves the 4 rows to different quarter windows.
 __device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
 
-template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS>
+// SK: stream-K.  The program walks segments (tile, first slab, end slab)
+// of its own stream-K run instead of whole tiles; a segment that does not
+// cover its tile leaves fp32 partial sums in the program's workspace slot,
+// summed and stored by the fix-up kernel after this launch.
+template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS, bool SK>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   using S = Shape<BM, BN, BK, NST>;
   static_assert(NST == 2, "two LDS stages: the loads of slab g+1 run during slab g");
@@ -183,6 +187,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
+  int lke = nk;             // loader: end slab of its segment
   // Tiles the loader moved on to that the matrix cores have not reached:
   // the loader runs two slabs ahead, so with one slab per tile two can wait.
   int pend0 = -1, pend1 = -1;
@@ -194,13 +199,19 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   unsigned ao[NA], bo[NB];  // per-lane offsets (edge chunks pushed out of range)
   bool masked = true;       // ao / bo hold masked offsets
 
-  // Pick the next slab for the loader (moving on to the next tile once the
-  // current one is issued) and set up its resources; without one the
-  // resources are empty, so the loads read zeros into a stage no one reads.
-  // The loader moves on to tile t (t >= 0).
-  auto begin_tile = [&](int t) {
+  // Stream-K segment walkers of this program: one for the loader, one for
+  // the matrix cores (the same sequence, read at different times).
+  pgs::SkWalker lw, cw;
+  if (SK) {
+    lw.init(prog, P.s.T, P.s.G, nk);
+    cw.init(prog, P.s.T, P.s.G, nk);
+  }
+
+  // The loader moves on to slabs [kb, ke) of tile t (t >= 0).
+  auto begin_tile = [&](int t, int kb, int ke) {
     lt = t;
-    lk = 0;
+    lk = kb;
+    lke = ke;
     coords(t, lm0, ln0);
     const int rows = (M - lm0) < BM ? (M - lm0) : BM;
     a_ptr = reinterpret_cast<unsigned long long>(A + (size_t)lm0 * K);
@@ -208,29 +219,39 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     b_ptr = reinterpret_cast<unsigned long long>(B + ln0);
   };
 
+  // Pick the next slab for the loader (moving on to the next tile or
+  // segment once the current one is issued) and set up its resources;
+  // without one the resources are empty, so the loads read zeros into a
+  // stage no one reads.
   auto prep = [&]() {
     // The loader state is the same in every lane; saying so keeps its
     // branches scalar.
     lt = __builtin_amdgcn_readfirstlane(lt);
     lk = __builtin_amdgcn_readfirstlane(lk);
+    lke = __builtin_amdgcn_readfirstlane(lke);
     claims = __builtin_amdgcn_readfirstlane(claims);
-    if (lt >= 0 && lk == nk) {
-      const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
-      ++claims;
+    if (lt >= 0 && lk == lke) {
       lt = -1;
-      if (t >= 0) {
-        if (pend0 < 0)
-          pend0 = t;
-        else
-          pend1 = t;
-        begin_tile(t);
+      if (SK) {
+        int v, kb, ke, slot;
+        if (lw.next(v, kb, ke, slot)) begin_tile(v, kb, ke);
+      } else {
+        const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+        ++claims;
+        if (t >= 0) {
+          if (pend0 < 0)
+            pend0 = t;
+          else
+            pend1 = t;
+          begin_tile(t, 0, nk);
+        }
       }
     }
     const int k0 = lk * BK;
     const bool load = lt >= 0;
     if (load) {
       ++lk;
-      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+      if (!SK && lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
     }
     // Slab k0 of the tile: A from column k0 (the range shrinks with it), B
     // from row k0 (the range ends with the slab's last row, so rows past K
@@ -325,9 +346,34 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     }
   };
 
-  if (tid == 0) s_first[0] = walker.first();
-  __syncthreads();
-  int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
+  // Stream-K: the accumulators of a partial segment, fp32, into slot `slot`
+  // of this program's workspace ([BM][BN], tile-relative).
+  auto store_partial = [&](int slot) {
+    float* wsb = P.ws + ((size_t)prog * 2 + slot) * (size_t)(BM * BN);
+    const int r0 = wm * S::TM + l32;
+    const int c0 = wn * S::TN + 4 * (lane >> 5);
+#pragma unroll
+    for (int sm = 0; sm < S::SM; ++sm)
+#pragma unroll
+      for (int sn = 0; sn < S::SN; ++sn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[sn][sm];
+          *reinterpret_cast<f32x4*>(wsb + (r0 + sm * 32) * BN + c0 + sn * 32 + 8 * g) =
+              f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        }
+  };
+
+  int ct = -1;               // tile on the matrix cores
+  int cnsl = nk, cslot = -1;  // its slab count and partial-sum slot (stream-K)
+  if (SK) {
+    int kb, ke;
+    if (cw.next(ct, kb, ke, cslot)) cnsl = ke - kb;
+  } else {
+    if (tid == 0) s_first[0] = walker.first();
+    __syncthreads();
+    ct = __builtin_amdgcn_readfirstlane(s_first[0]);
+  }
   // Issue order per slab g (stage st = g & 1), fixed by scheduling barriers:
   //   k-step 0: MFMAs; reads of k-step 1; second half of slab g+1's loads
   //   k-steps 1, 2: MFMAs; reads of the next k-step
@@ -359,7 +405,13 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   };
 
   if (ct >= 0) {
-    begin_tile(ct);
+    if (SK) {
+      int v, kb, ke, slot;
+      lw.next(v, kb, ke, slot);
+      begin_tile(v, kb, ke);
+    } else {
+      begin_tile(ct, 0, nk);
+    }
     prep();  // slab 0
 #pragma unroll
     for (int d = 0; d < NL; ++d) dma(0, d);
@@ -391,7 +443,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
-    for (int ck = 0; ck < nk; ++ck) {
+    for (int ck = 0; ck < cnsl; ++ck) {
       const int st = g & 1;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -404,11 +456,20 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       kstep(st ^ 1, 0, (S::KK - 1) & 1, st, 0);
       ++g;
     }
-    epilogue(m0, n0);
+    if (SK && cslot >= 0)
+      store_partial(cslot);
+    else
+      epilogue(m0, n0);
     ++it;
-    ct = pend0;
-    pend0 = pend1;
-    pend1 = -1;
+    if (SK) {
+      int kb, ke;
+      ct = -1;
+      if (cw.next(ct, kb, ke, cslot)) cnsl = ke - kb;
+    } else {
+      ct = pend0;
+      pend0 = pend1;
+      pend1 = -1;
+    }
     if (ct >= 0) coords(ct, m0, n0);
   }
 
@@ -424,10 +485,10 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 constexpr int kBK = 64;   // slab depth
 constexpr int kNST = 2;   // LDS stages
 
-template <int BM, int BN, bool OUT_BF16, bool WITNESS>
+template <int BM, int BN, bool OUT_BF16, bool WITNESS, bool SK = false>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   using S = Shape<BM, BN, kBK, kNST>;
-  auto kern = gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, WITNESS>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, WITNESS, SK>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -444,9 +505,43 @@ KernelInfo info_one() {
   using S = Shape<BM, BN, kBK, kNST>;
   static const KernelInfo ki = {
       kThreads, S::LDS_BYTES,
-      occupancy_of(reinterpret_cast<const void*>(gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, false>),
+      occupancy_of(reinterpret_cast<const void*>(gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, false, false>),
                    kThreads, S::LDS_BYTES)};
   return ki;
+}
+
+// Stream-K fix-up: block v - dp sums tile v from the partial-sum slots of
+// the programs whose runs share it, in slab order, and stores it (rows past
+// M and columns past N dropped).  Tiles one program computed whole were
+// stored by that program.
+template <int BM, int BN, bool OUT_BF16>
+__global__ void __launch_bounds__(256) sk_fixup_kernel(SkFixParams F) {
+  const int v = F.dp + blockIdx.x;
+  if (v >= F.T) return;
+  const long long j0 = (long long)(v - F.dp) * F.nk;
+  const int q0 = pgs::sk_owner(j0, F.W, F.G), q1 = pgs::sk_owner(j0 + F.nk - 1, F.W, F.G);
+  if (q0 == q1) return;
+  int pm, pn;
+  pgs::decode(pgs::kStreamK, v, F.num_pid_m, F.num_pid_n, F.gs, pm, pn);
+  const int m0 = pm * BM, n0 = pn * BN;
+  for (int e = threadIdx.x * 4; e < BM * BN; e += 256 * 4) {
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = q0; q <= q1; ++q) {
+      if (pgs::sk_run_begin(q, F.W, F.G) == pgs::sk_run_begin(q + 1, F.W, F.G)) continue;
+      const int slot = pgs::sk_slot(q, v, F.dp, F.nk, F.W, F.G);
+      sum += *reinterpret_cast<const f32x4*>(F.ws + ((size_t)q * 2 + slot) * (size_t)(BM * BN) + e);
+    }
+    const int r = m0 + e / BN, c = n0 + e % BN;
+    if (r >= F.M || c >= F.N) continue;  // N % 8 == 0: the 4 columns are all in or all out
+    if (OUT_BF16) {
+      unsigned short* C = static_cast<unsigned short*>(F.C);
+      *reinterpret_cast<u32x2*>(C + (size_t)r * F.N + c) =
+          u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+    } else {
+      float* C = static_cast<float*>(F.C);
+      *reinterpret_cast<f32x4*>(C + (size_t)r * F.N + c) = sum;
+    }
+  }
 }
 
 template <int BM, int BN>
@@ -472,6 +567,36 @@ KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16) {
   if (bm == 256 && bn == 256) return out_bf16 ? info_one<256, 256, true>() : info_one<256, 256, false>();
   if (bm == 128 && bn == 128) return out_bf16 ? info_one<128, 128, true>() : info_one<128, 128, false>();
   return KernelInfo{0, 0, 0};
+}
+
+hipError_t launch_gemm_bf16_lds_sk(const GemmParams& p, int bm, int bn, bool out_bf16,
+                                   hipStream_t stream) {
+  if (bm == 256 && bn == 256)
+    return out_bf16 ? launch_one<256, 256, true, false, true>(p, stream)
+                    : launch_one<256, 256, false, false, true>(p, stream);
+  if (bm == 128 && bn == 128)
+    return out_bf16 ? launch_one<128, 128, true, false, true>(p, stream)
+                    : launch_one<128, 128, false, false, true>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, hipStream_t stream) {
+  const int blocks = f.T - f.dp;
+  if (blocks <= 0) return hipSuccess;
+  if (bm == 256 && bn == 256) {
+    if (out_bf16)
+      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, true>), dim3(blocks), dim3(256), 0, stream, f);
+    else
+      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, false>), dim3(blocks), dim3(256), 0, stream, f);
+  } else if (bm == 128 && bn == 128) {
+    if (out_bf16)
+      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, true>), dim3(blocks), dim3(256), 0, stream, f);
+    else
+      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, false>), dim3(blocks), dim3(256), 0, stream, f);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,

@@ -27,6 +27,8 @@ struct pgemm_config {
   int lds_per_cu;
   char arch[64];
   int* counters;  // device, [capacity]
+  float* ws;          // stream-K partial-sum workspace (device), grown on demand
+  size_t ws_bytes;
   // witness buffers (device)
   int64_t w_tiles;
   int w_programs;
@@ -90,7 +92,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
                         int num_pid_m, int num_pid_n, int default_grid, pgk::SchedParams& s) {
-  if ((int)sched < 0 || (int)sched > 4) return PGEMM_ERR_INVALID;
+  if ((int)sched < 0 || (int)sched > 5) return PGEMM_ERR_INVALID;
   const int64_t T = (int64_t)num_pid_m * num_pid_n;
   if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
   s.kind = (int)sched;
@@ -218,6 +220,25 @@ pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk
 }
 
 
+// Stream-K workspace of at least `bytes`: two partial-sum slots per program.
+// Grown with hipFree / hipMalloc after synchronising the device, so no
+// launch still uses the old buffer.
+pgemm_status ensure_workspace(pgemm_config* cfg, size_t bytes) {
+  if (cfg->ws_bytes >= bytes) return PGEMM_OK;
+  if (cfg->ws) {
+    if (hipDeviceSynchronize() != hipSuccess) return PGEMM_ERR_DEVICE;
+    (void)hipFree(cfg->ws);
+    cfg->ws = nullptr;
+    cfg->ws_bytes = 0;
+  }
+  if (hipMalloc((void**)&cfg->ws, bytes) != hipSuccess) {
+    cfg->ws = nullptr;
+    return PGEMM_ERR_OOM;
+  }
+  cfg->ws_bytes = bytes;
+  return PGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +316,7 @@ pgemm_status pgemm_config_destroy(pgemm_config* cfg) {
   DeviceGuard g(cfg->device);
   free_witness(cfg);
   if (cfg->counters) (void)hipFree(cfg->counters);
+  if (cfg->ws) (void)hipFree(cfg->ws);
   delete cfg;
   return PGEMM_OK;
 }
@@ -398,6 +420,15 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   const pgk::KernelInfo ki = gemm_info(ch);
   st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, p.s);
   if (st != PGEMM_OK) return st;
+  const bool sk = sched == PGEMM_SCHED_STREAM_K;
+  if (sk) {
+    // stream-K runs on the direct-to-LDS bf16 kernel, without the witness
+    if (ch.kernel != PGEMM_KERNEL_BF16_LDS) return PGEMM_ERR_UNSUPPORTED;
+    if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
+    st = ensure_workspace(cfg, (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float));
+    if (st != PGEMM_OK) return st;
+    p.ws = cfg->ws;
+  }
 
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
@@ -409,10 +440,28 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   hipError_t e;
   if (fp8)
     e = pgk::launch_gemm_fp8(p, ch.bm, ch.bn, ch.bk, true, witness, stream);
+  else if (sk)
+    e = pgk::launch_gemm_bf16_lds_sk(p, ch.bm, ch.bn, ch.out_bf16, stream);
   else if (ch.kernel == PGEMM_KERNEL_BF16_LDS)
     e = pgk::launch_gemm_bf16_lds(p, ch.bm, ch.bn, ch.out_bf16, witness, stream);
   else
     e = pgk::launch_gemm_bf16(p, ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec, witness, stream);
+  if (e == hipSuccess && sk) {
+    pgk::SkFixParams f;
+    f.ws = cfg->ws;
+    f.C = C;
+    f.M = (int)M;
+    f.N = (int)N;
+    f.T = p.s.T;
+    f.nk = (int)((K + ch.bk - 1) / ch.bk);
+    f.G = p.s.G;
+    f.dp = pgs::sk_dp_tiles(p.s.T, p.s.G);
+    f.W = (long long)(f.T - f.dp) * f.nk;
+    f.num_pid_m = p.s.num_pid_m;
+    f.num_pid_n = p.s.num_pid_n;
+    f.gs = p.s.gs;
+    e = pgk::launch_sk_fixup(f, ch.bm, ch.bn, ch.out_bf16, stream);
+  }
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }

@@ -11,7 +11,9 @@
 //    scheduler object with init / valid / next and a swizzle (group) size;
 //    its loop walks tile ids with a stride of the grid.
 //  - "Work Stealing Scheduler Kernel" (tritonBLAS PR #65): one counter per
-//    XCD, chosen by program id modulo the XCD count.
+//    XCD, chosen by program id modulo the XCD count; stream-K is the
+//    comparator its benchmark names (taken here as the data-parallel +
+//    stream-K hybrid of the published Stream-K method).
 #pragma once
 
 #if defined(__HIPCC__)
@@ -31,12 +33,13 @@ enum Kind : int {
   kGrouped = 2,
   kWorkStealing = 3,
   kBlockedGrouped = 4,
+  kStreamK = 5,
 };
 
 PGS_FN int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 PGS_FN bool grouped_order(int kind) {
-  return kind == kGrouped || kind == kWorkStealing || kind == kBlockedGrouped;
+  return kind == kGrouped || kind == kWorkStealing || kind == kBlockedGrouped || kind == kStreamK;
 }
 
 // Tile id -> (pid_m, pid_n), dimension 0 (rows of tiles) fastest.
@@ -94,5 +97,79 @@ PGS_FN int static_next(int kind, int v, int G, int end) {
   const int64_t n = (int64_t)v + static_step(kind, G);
   return n < end ? (int)n : end;
 }
+
+// Stream-K.  T tiles of nk K-slabs on G programs.  If G divides T every
+// tile is data-parallel; otherwise the first (T/G - 1)*G tiles (none when
+// T < G) are taken whole, stride-by-grid, and the W = (T - dp)*nk slabs of
+// the rest are cut into G contiguous runs: program p takes slab indices
+// [floor(p*W/G), floor((p+1)*W/G)) counted from tile dp.  A tile whose slabs
+// fall into several runs is finished from the runs' partial sums.
+PGS_FN int sk_dp_tiles(int T, int G) {
+  if (T % G == 0) return T;
+  const int w = T / G - 1;
+  return (w > 0 ? w : 0) * G;
+}
+
+PGS_FN int64_t sk_run_begin(int p, int64_t W, int G) { return ((int64_t)p * W) / G; }
+
+// Program whose run holds stream-K slab index j (0 <= j < W).
+PGS_FN int sk_owner(int64_t j, int64_t W, int G) {
+  return (int)(((j + 1) * (int64_t)G + W - 1) / W) - 1;
+}
+
+// Partial-sum slot of program q for tile v (v in the stream-K part, split):
+// 0 for the first tile of q's run, 1 for any later one (only its last can
+// be split).
+PGS_FN int sk_slot(int q, int v, int dp, int nk, int64_t W, int G) {
+  return (dp + (int)(sk_run_begin(q, W, G) / nk)) == v ? 0 : 1;
+}
+
+// The segments (tile, first slab, end slab) of one program, in order: its
+// data-parallel tiles, then the pieces of its slab run.  slot is the
+// partial-sum slot of a segment that does not cover its whole tile, -1
+// otherwise.
+struct SkWalker {
+  int G, dp, nk;
+  int64_t W;
+  int v_dp;          // next data-parallel tile
+  int64_t j, j_end;  // stream-K run cursor and end
+  bool first;        // the next stream-K segment is the run's first
+
+  PGS_FN void init(int p, int T, int G_, int nk_) {
+    G = G_;
+    nk = nk_;
+    dp = sk_dp_tiles(T, G);
+    W = (int64_t)(T - dp) * nk;
+    v_dp = p;
+    j = sk_run_begin(p, W, G);
+    j_end = sk_run_begin(p + 1, W, G);
+    first = true;
+  }
+
+  PGS_FN bool next(int& v, int& kb, int& ke, int& slot) {
+    if (v_dp < dp) {
+      v = v_dp;
+      v_dp += G;
+      kb = 0;
+      ke = nk;
+      slot = -1;
+      return true;
+    }
+    if (j < j_end) {
+      v = dp + (int)(j / nk);
+      kb = (int)(j % nk);
+      const int64_t left = j_end - j;
+      ke = (int64_t)(nk - kb) < left ? nk : kb + (int)left;
+      slot = (kb != 0 || ke != nk) ? (first ? 0 : 1) : -1;
+      first = false;
+      j += ke - kb;
+      return true;
+    }
+    v = -1;
+    kb = ke = 0;
+    slot = -1;
+    return false;
+  }
+};
 
 }  // namespace pgs
