@@ -28,14 +28,14 @@ Sources:
   stops at its first claim that starts at or beyond the range's length.
 * Stream-K (the comparator "Work Stealing Scheduler Kernel", tritonBLAS PR
   #65, benchmarks work stealing against; the page names it only).  Reading
-  taken: the data-parallel + stream-K hybrid of the published Stream-K
-  method.  With T tiles of nk K-slabs on G programs: if G divides T every
-  tile is data-parallel; otherwise the first (floor(T/G) - 1)*G tiles (none
-  when T < G) are taken stride-by-grid, whole, and the slabs of the
-  remaining tiles, in order, are split into G contiguous runs of
-  floor(p*W/G) .. floor((p+1)*W/G) (W = their slab count).  A tile whose
-  slabs fall into several runs is summed from the runs' partial results in
-  slab order.
+  taken: a data-parallel + stream-K hybrid in the spirit of the published
+  Stream-K method, with only the partial wave split.  With T tiles of nk
+  K-slabs on G programs, the first floor(T/G)*G tiles (all of them when G
+  divides T, none when T < G) are taken stride-by-grid, whole, and the
+  slabs of the remaining T mod G tiles, in order, are split into G
+  contiguous runs of floor(p*W/G) .. floor((p+1)*W/G) (W = their slab
+  count), so every run is shorter than one tile.  A tile whose slabs fall
+  into several runs is summed from the runs' partial results in slab order.
 """
 from __future__ import annotations
 
@@ -210,10 +210,9 @@ def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
 
 
 def streamk_dp_tiles(T: int, G: int) -> int:
-    """Tiles taken whole (data-parallel) before the stream-K part."""
-    if T % G == 0:
-        return T
-    return max(0, T // G - 1) * G
+    """Tiles taken whole (data-parallel) before the stream-K part: every
+    full wave of G tiles."""
+    return (T // G) * G
 
 
 def streamk_schedule(T: int, nk: int, G: int) -> List[List[Tuple[int, int, int]]]:

@@ -143,14 +143,18 @@ def test_checkers_catch_planted_mistakes():
         sm.check_ws_execution(v2, o, r, cnt, T, 8, 4)
 
 
-def test_streamk_golden(golden):
-    rows = [tuple(map(int, r.split())) for r in golden("sk_T10_nk4_G4.txt")]
+@pytest.mark.parametrize("name,T,nk,G,partials", [
+    ("sk_T5_nk4_G3.txt", 5, 4, 3, {3: [(0, 0, 2), (1, 2, 4)], 4: [(1, 0, 1), (2, 1, 4)]}),
+    ("sk_T2_nk3_G4.txt", 2, 3, 4, {0: [(0, 0, 1), (1, 1, 3)], 1: [(2, 0, 1), (3, 1, 3)]}),
+])
+def test_streamk_golden(golden, name, T, nk, G, partials):
+    rows = [tuple(map(int, r.split())) for r in golden(name)]
     want = {}
     for p, v, kb, ke in rows:
         want.setdefault(p, []).append((v, kb, ke))
-    got = sm.streamk_schedule(10, 4, 4)
+    got = sm.streamk_schedule(T, nk, G)
     assert {p: s for p, s in enumerate(got)} == want
-    assert sm.streamk_partials(10, 4, 4) == {5: [(0, 0, 2), (1, 2, 4)], 8: [(2, 0, 2), (3, 2, 4)]}
+    assert sm.streamk_partials(T, nk, G) == partials
 
 
 @pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),
@@ -167,6 +171,11 @@ def test_streamk_cover_and_balance(T, nk, G):
     # stream-K part: per-program slab counts differ by at most one
     sk = [sum(ke - kb for v, kb, ke in segs if v >= dp) for segs in sched]
     assert max(sk) - min(sk) <= 1 and sum(sk) == (T - dp) * nk
+    # every full wave is data-parallel: fewer than G tiles are left to split,
+    # so no run is longer than one tile and none touches more than two tiles
+    assert dp % G == 0 and 0 <= T - dp < G
+    assert max(sk) <= nk
+    assert all(len([s for s in segs if s[0] >= dp]) <= 2 for segs in sched)
     # G divides T: nothing is split
     if T % G == 0:
         assert dp == T and not sm.streamk_partials(T, nk, G)
@@ -178,11 +187,16 @@ def test_streamk_cover_and_balance(T, nk, G):
 
 
 def test_streamk_checker_catches_planted_mistakes():
-    sched = [list(s) for s in sm.streamk_schedule(10, 4, 4)]
-    sched[1][1] = (5, 1, 4)                                 # slab 1 of tile 5 twice
+    sched = [list(s) for s in sm.streamk_schedule(5, 4, 3)]
+    sched[2][1] = (4, 0, 4)                                 # slab 0 of tile 4 twice
     with pytest.raises(AssertionError):
-        sm.check_streamk_cover(sched, 10, 4)
-    sched = [list(s) for s in sm.streamk_schedule(10, 4, 4)]
-    sched[3].pop()                                          # tile 9 dropped
+        sm.check_streamk_cover(sched, 5, 4)
+    sched = [list(s) for s in sm.streamk_schedule(5, 4, 3)]
+    sched[2].pop()                                          # slabs 1..3 of tile 4 dropped
     with pytest.raises(AssertionError):
-        sm.check_streamk_cover(sched, 10, 4)
+        sm.check_streamk_cover(sched, 5, 4)
+    # a run boundary off by one slab breaks the cover
+    sched = [list(s) for s in sm.streamk_schedule(5, 4, 3)]
+    sched[0][1] = (3, 0, 3)
+    with pytest.raises(AssertionError):
+        sm.check_streamk_cover(sched, 5, 4)
