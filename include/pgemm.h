@@ -74,10 +74,11 @@ typedef enum {
  *  BLOCKED_GROUPED  blocked ranges over the grouped order.
  *  STREAM_K         the comparator named by "Work Stealing Scheduler
  *                   Kernel" (tritonBLAS PR #65, benchmark harness), taken as
- *                   the data-parallel + stream-K hybrid: if G divides T all
- *                   tiles are data-parallel (stride-by-grid over the grouped
- *                   order); otherwise the first (T/G - 1)*G tiles are, and the
- *                   K-slabs of the rest are cut into G equal contiguous runs.
+ *                   a data-parallel + stream-K hybrid: every full wave,
+ *                   floor(T/G)*G tiles, is data-parallel (stride-by-grid over
+ *                   the grouped order), and the K-slabs of the remaining
+ *                   T mod G tiles are cut into G equal contiguous runs, each
+ *                   at most one tile long.
  *                   Tiles split between runs are summed (fp32, slab order)
  *                   by a fix-up kernel from per-program partial-sum slots in
  *                   a workspace the config allocates on first use (G x 2

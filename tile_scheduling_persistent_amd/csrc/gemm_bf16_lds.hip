@@ -510,13 +510,23 @@ KernelInfo info_one() {
   return ki;
 }
 
-// Stream-K fix-up: block v - dp sums tile v from the partial-sum slots of
-// the programs whose runs share it, in slab order, and stores it (rows past
-// M and columns past N dropped).  Tiles one program computed whole were
-// stored by that program.
+// Stream-K fix-up.  Each tile of the stream-K part is cut into
+// kFixBands bands of rows; block (v - dp) * kFixBands + band sums its band of
+// tile v from the partial-sum slots of the programs whose runs share the
+// tile, in slab order, and stores it (rows past M and columns past N
+// dropped).  Tiles one program computed whole were stored by that program.
+// Bands give the memory-bound pass many more blocks than tiles; each thread
+// keeps kFixVec independent 16-byte loads in flight per contributor.
+constexpr int kFixBands = 8;
+constexpr int kFixThreads = 256;
+
 template <int BM, int BN, bool OUT_BF16>
-__global__ void __launch_bounds__(256) sk_fixup_kernel(SkFixParams F) {
-  const int v = F.dp + blockIdx.x;
+__global__ void __launch_bounds__(kFixThreads) sk_fixup_kernel(SkFixParams F) {
+  constexpr int kBandElems = BM * BN / kFixBands;
+  constexpr int kFixVec = kBandElems / (kFixThreads * 4);
+  static_assert(kFixVec >= 1 && kBandElems % (kFixThreads * 4) == 0, "band shape");
+  const int v = F.dp + (int)(blockIdx.x / kFixBands);
+  const int band = (int)(blockIdx.x % kFixBands);
   if (v >= F.T) return;
   const long long j0 = (long long)(v - F.dp) * F.nk;
   const int q0 = pgs::sk_owner(j0, F.W, F.G), q1 = pgs::sk_owner(j0 + F.nk - 1, F.W, F.G);
@@ -524,22 +534,32 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(SkFixParams F) {
   int pm, pn;
   pgs::decode(pgs::kStreamK, v, F.num_pid_m, F.num_pid_n, F.gs, pm, pn);
   const int m0 = pm * BM, n0 = pn * BN;
-  for (int e = threadIdx.x * 4; e < BM * BN; e += 256 * 4) {
-    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int q = q0; q <= q1; ++q) {
-      if (pgs::sk_run_begin(q, F.W, F.G) == pgs::sk_run_begin(q + 1, F.W, F.G)) continue;
-      const int slot = pgs::sk_slot(q, v, F.dp, F.nk, F.W, F.G);
-      sum += *reinterpret_cast<const f32x4*>(F.ws + ((size_t)q * 2 + slot) * (size_t)(BM * BN) + e);
-    }
+  const int e0 = band * kBandElems + threadIdx.x * 4;
+  f32x4 sum[kFixVec];
+#pragma unroll
+  for (int i = 0; i < kFixVec; ++i) sum[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q = q0; q <= q1; ++q) {
+    if (pgs::sk_run_begin(q, F.W, F.G) == pgs::sk_run_begin(q + 1, F.W, F.G)) continue;
+    const int slot = pgs::sk_slot(q, v, F.dp, F.nk, F.W, F.G);
+    const f32x4* src = reinterpret_cast<const f32x4*>(F.ws + ((size_t)q * 2 + slot) * (size_t)(BM * BN) + e0);
+    f32x4 x[kFixVec];
+#pragma unroll
+    for (int i = 0; i < kFixVec; ++i) x[i] = __builtin_nontemporal_load(src + i * kFixThreads);
+#pragma unroll
+    for (int i = 0; i < kFixVec; ++i) sum[i] += x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kFixVec; ++i) {
+    const int e = e0 + i * kFixThreads * 4;
     const int r = m0 + e / BN, c = n0 + e % BN;
     if (r >= F.M || c >= F.N) continue;  // N % 8 == 0: the 4 columns are all in or all out
     if (OUT_BF16) {
       unsigned short* C = static_cast<unsigned short*>(F.C);
       *reinterpret_cast<u32x2*>(C + (size_t)r * F.N + c) =
-          u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+          u32x2{pack_bf16x2(sum[i][0], sum[i][1]), pack_bf16x2(sum[i][2], sum[i][3])};
     } else {
       float* C = static_cast<float*>(F.C);
-      *reinterpret_cast<f32x4*>(C + (size_t)r * F.N + c) = sum;
+      *reinterpret_cast<f32x4*>(C + (size_t)r * F.N + c) = sum[i];
     }
   }
 }
@@ -581,18 +601,18 @@ hipError_t launch_gemm_bf16_lds_sk(const GemmParams& p, int bm, int bn, bool out
 }
 
 hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, hipStream_t stream) {
-  const int blocks = f.T - f.dp;
-  if (blocks <= 0) return hipSuccess;
+  if (f.T - f.dp <= 0) return hipSuccess;
+  const dim3 blocks((unsigned)(f.T - f.dp) * kFixBands), threads(kFixThreads);
   if (bm == 256 && bn == 256) {
     if (out_bf16)
-      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, true>), dim3(blocks), dim3(256), 0, stream, f);
+      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, true>), blocks, threads, 0, stream, f);
     else
-      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, false>), dim3(blocks), dim3(256), 0, stream, f);
+      hipLaunchKernelGGL((sk_fixup_kernel<256, 256, false>), blocks, threads, 0, stream, f);
   } else if (bm == 128 && bn == 128) {
     if (out_bf16)
-      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, true>), dim3(blocks), dim3(256), 0, stream, f);
+      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, true>), blocks, threads, 0, stream, f);
     else
-      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, false>), dim3(blocks), dim3(256), 0, stream, f);
+      hipLaunchKernelGGL((sk_fixup_kernel<128, 128, false>), blocks, threads, 0, stream, f);
   } else {
     return hipErrorInvalidValue;
   }

@@ -98,17 +98,15 @@ PGS_FN int static_next(int kind, int v, int G, int end) {
   return n < end ? (int)n : end;
 }
 
-// Stream-K.  T tiles of nk K-slabs on G programs.  If G divides T every
-// tile is data-parallel; otherwise the first (T/G - 1)*G tiles (none when
-// T < G) are taken whole, stride-by-grid, and the W = (T - dp)*nk slabs of
-// the rest are cut into G contiguous runs: program p takes slab indices
-// [floor(p*W/G), floor((p+1)*W/G)) counted from tile dp.  A tile whose slabs
-// fall into several runs is finished from the runs' partial sums.
-PGS_FN int sk_dp_tiles(int T, int G) {
-  if (T % G == 0) return T;
-  const int w = T / G - 1;
-  return (w > 0 ? w : 0) * G;
-}
+// Stream-K.  T tiles of nk K-slabs on G programs.  Every full wave is
+// data-parallel: the first floor(T/G)*G tiles (all of them when G divides
+// T, none when T < G) are taken whole, stride-by-grid, and the
+// W = (T - dp)*nk slabs of the remaining T mod G tiles are cut into G
+// contiguous runs: program p takes slab indices [floor(p*W/G),
+// floor((p+1)*W/G)) counted from tile dp.  A run is never longer than one
+// tile, so it touches at most two tiles.  A tile whose slabs fall into
+// several runs is finished from the runs' partial sums.
+PGS_FN int sk_dp_tiles(int T, int G) { return (T / G) * G; }
 
 PGS_FN int64_t sk_run_begin(int p, int64_t W, int G) { return ((int64_t)p * W) / G; }
 
@@ -118,8 +116,8 @@ PGS_FN int sk_owner(int64_t j, int64_t W, int G) {
 }
 
 // Partial-sum slot of program q for tile v (v in the stream-K part, split):
-// 0 for the first tile of q's run, 1 for any later one (only its last can
-// be split).
+// 0 for the first tile of q's run, 1 for the second (a run touches at most
+// two tiles).
 PGS_FN int sk_slot(int q, int v, int dp, int nk, int64_t W, int G) {
   return (dp + (int)(sk_run_begin(q, W, G) / nk)) == v ? 0 : 1;
 }
