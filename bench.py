@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_CLOCK_GHZ = 2.4          # engine clock the dense peak is quoted at
 M = N = K = 8192
 SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
-          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8)]
+          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8), ("stream_k", 8)]
 HEADLINE = ("work_stealing", 8)
 CPU_ROWS = 4096
 
@@ -101,6 +101,8 @@ def measured_clock(pg, cfg, A, B, C, key):
     the timed steps; median over programs of shader cycles / wall time."""
     import torch
     sched, gs = key.rsplit("_g", 1) if "_g" in key else (key, "8")
+    if sched == "stream_k":
+        return None  # no witness on the stream-K path
     a = pg.make_args(tile=(256, 256, 64), group_size=int(gs), debug_flags=pg._abi.DEBUG_WITNESS)
     plan = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched, a)
     G, T = plan["grid"], plan["tiles"]
@@ -167,7 +169,7 @@ def main():
     only = set(s for s in args.only.split(",") if s)
     per = {}
     for sched, gs in SCHEDS:
-        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped") else "")
+        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped", "stream_k") else "")
         if only and sched not in only and key not in only:
             continue
         a = pg.make_args(tile=(256, 256, 64), group_size=gs)
@@ -188,13 +190,38 @@ def main():
             rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
             row = {}
-            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]:
+            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "stream_k"]:
                 a = pg.make_args(tile=(256, 256, 64))
                 fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
                 _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
                 row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
             ragged[f"{m}x{n}x{k}"] = row
             print(f"# ragged {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
+                  file=sys.stderr, flush=True)
+            del ra, rb, rc
+
+    # under-filled shapes (fewer 256x256 tiles than CUs, e.g. one GPU's share
+    # of an 8-way split of 8192^3): stream-K against the data-parallel
+    # schedulers, and against smaller tiles as the other way to fill the chip
+    skinny = {}
+    if not args.skip_extra:
+        from synthetic import bf16_bits_uniform
+        for (m, n, k) in [(8192, 1024, 8192), (1024, 8192, 8192), (2048, 2048, 8192)]:
+            ra = torch.from_numpy(bf16_bits_uniform((m, k), 1060 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            rb = torch.from_numpy(bf16_bits_uniform((k, n), 1061 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+            f = 2.0 * m * n * k
+            row = {}
+            for sched, tile in [("grouped", (256, 256, 64)), ("work_stealing", (256, 256, 64)),
+                                ("stream_k", (256, 256, 64)), ("grouped", (128, 128, 64)),
+                                ("work_stealing", (128, 128, 64)), ("stream_k", (128, 128, 64))]:
+                a = pg.make_args(tile=tile)
+                fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
+                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+                row[f"{sched}_{tile[0]}"] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2),
+                                             "event_ms_mean": round(ev_mean, 5)}
+            skinny[f"{m}x{n}x{k}"] = row
+            print(f"# skinny {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
                   file=sys.stderr, flush=True)
             del ra, rb, rc
 
@@ -268,9 +295,11 @@ def main():
                      "frac": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
                      "clock_ghz_measured": clock_ghz,
-                     "peak_at_measured_clock": round(PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ, 1),
-                     "frac_at_measured_clock": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12
-                                                     / (PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ), 4),
+                     "peak_at_measured_clock": (round(PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ, 1)
+                                                if clock_ghz else None),
+                     "frac_at_measured_clock": (round(flops / (h["event_ms_mean"] * 1e-3) / 1e12
+                                                      / (PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ), 4)
+                                                if clock_ghz else None),
                      "traffic_unit": "HBM bytes per launch (counter passes, copy-calibrated)",
                      "algorithmic_bytes": 2 * (M * K + K * N + M * N)},
         "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),
@@ -278,6 +307,7 @@ def main():
         "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                 for k, v in add.items()},
         "ragged": ragged,
+        "skinny": skinny,
         "fp8": fp8,
         "device": cfg.info,
     }
