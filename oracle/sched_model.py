@@ -26,6 +26,14 @@ Sources:
   silent: XCD x owns the contiguous range [floor(x*T/X), floor((x+1)*T/X))
   of the grouped order; a claim is fetch_add(counter, chunk) and a program
   stops at its first claim that starts at or beyond the range's length.
+* Work stealing across XCDs (reading taken where the pages stop: they keep
+  one counter per XCD and never cross XCDs).  Same ranges and counters; a
+  program's home counter is the XCD it runs on (any map of programs to
+  counters is allowed, so completion never depends on placement).  A
+  program claims from its home counter until a claim fails, then from the
+  next counter (x + 1 mod X), and so on; it stops after one failing claim
+  on every counter.  So each counter ends at chunk * (ceil(n_x / chunk) + G)
+  whatever the timing.
 * Stream-K (the comparator "Work Stealing Scheduler Kernel", tritonBLAS PR
   #65, benchmarks work stealing against; the page names it only).  Reading
   taken: a data-parallel + stream-K hybrid in the spirit of the published
@@ -48,6 +56,7 @@ GROUPED = "grouped"
 WORK_STEALING = "work_stealing"
 BLOCKED_GROUPED = "blocked_grouped"
 STREAM_K = "stream_k"
+WORK_STEALING_XCC = "work_stealing_xcc"
 STATIC_KINDS = (BLOCKED, INTERLEAVED, GROUPED, BLOCKED_GROUPED)
 
 
@@ -153,6 +162,90 @@ def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
         if speeds is not None:
             clock[p] += speeds[p] * (min(i + chunk, e - s) - i)
     return seqs, cnt
+
+
+def ws_owner(v: int, T: int, X: int) -> int:
+    """Counter (XCD range) that holds tile id v."""
+    for x, (s, e) in enumerate(ws_ranges(T, X)):
+        if s <= v < e:
+            return x
+    raise ValueError(f"tile {v} outside [0, {T})")
+
+
+def wsx_final_counters(T: int, G: int, X: int, chunk: int = 1) -> List[int]:
+    """Counter values after a complete launch of work stealing across XCDs:
+    every successful claim, and one failing claim per program on every
+    counter, added ``chunk``."""
+    return [chunk * (cdiv(e - s, chunk) + G) for s, e in ws_ranges(T, X)]
+
+
+def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence[int],
+                 gs: int = 8, chunk: int = 1, seed: int = 0, speeds: Sequence[float] = None):
+    """One possible execution of work stealing across XCDs.  ``homes[p]`` is
+    the counter program p starts on.  The interleaving is random, or with
+    ``speeds`` the program with the earliest clock (then the lowest id)
+    claims next; a failing claim takes no time.  Returns (per-program list
+    of (v, pid_m, pid_n), final counters)."""
+    T = num_pid_m * num_pid_n
+    ranges = ws_ranges(T, X)
+    cnt = [0] * X
+    seqs: List[List[Tuple[int, int, int]]] = [[] for _ in range(G)]
+    cur = [homes[p] % X for p in range(G)]
+    failed = [0] * G
+    active = list(range(G))
+    clock = [0.0] * G
+    r = random.Random(seed)
+    while active:
+        if speeds is None:
+            p = r.choice(active)
+        else:
+            p = min(active, key=lambda q: (clock[q], q))
+        x = cur[p]
+        s, e = ranges[x]
+        i = cnt[x]
+        cnt[x] += chunk
+        if i >= e - s:
+            failed[p] += 1
+            if failed[p] == X:
+                active.remove(p)
+            else:
+                cur[p] = (x + 1) % X
+            continue
+        for v in range(s + i, min(s + i + chunk, e)):
+            seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
+        if speeds is not None:
+            clock[p] += speeds[p] * (min(i + chunk, e - s) - i)
+    return seqs, cnt
+
+
+def check_wsx_execution(visits: Sequence[int], owner: Sequence[int], local_order: Sequence[int],
+                        counters: Sequence[int], homes: Sequence[int], T: int, G: int, X: int,
+                        chunk: int = 1) -> None:
+    """Invariants of every correct launch of work stealing across XCDs.
+    visits / owner / local_order are indexed by tile id; homes[p] is the
+    counter program p started on."""
+    for v in range(T):
+        if visits[v] != 1:
+            raise AssertionError(f"tile {v} visited {visits[v]} times")
+        if not (0 <= owner[v] < G):
+            raise AssertionError(f"tile {v} computed by program {owner[v]}")
+    by_prog: Dict[int, List[Tuple[int, int]]] = {}
+    for v in range(T):
+        by_prog.setdefault(owner[v], []).append((local_order[v], v))
+    for p, lst in by_prog.items():
+        lst.sort()
+        orders = [o for o, _ in lst]
+        if orders != list(range(len(lst))):
+            raise AssertionError(f"program {p}: local order {orders} not 0..n-1")
+        # counters are visited in the cyclic order from home, and the tiles
+        # taken from one counter rise
+        key = [((ws_owner(v, T, X) - homes[p]) % X, v) for _, v in lst]
+        if any(b <= a for a, b in zip(key, key[1:])):
+            raise AssertionError(f"program {p} (home {homes[p]}): tiles out of claim order "
+                                 f"{[v for _, v in lst]}")
+    want = wsx_final_counters(T, G, X, chunk)
+    if list(counters[:X]) != want:
+        raise AssertionError(f"final counters {list(counters[:X])} != {want}")
 
 
 def check_partition(seqs: Sequence[Sequence[Tuple[int, int, int]]],

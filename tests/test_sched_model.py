@@ -2,6 +2,7 @@
 property over many sizes, special cases that reduce to textbook orders, the
 work-stealing invariants under random interleavings, and planted mistakes."""
 import itertools
+import random
 
 import pytest
 
@@ -200,3 +201,78 @@ def test_streamk_checker_catches_planted_mistakes():
     sched[0][1] = (3, 0, 3)
     with pytest.raises(AssertionError):
         sm.check_streamk_cover(sched, 5, 4)
+
+
+# ---- work stealing across XCDs ----
+
+def test_wsx_golden(golden):
+    rows = [r.split() for r in golden("wsx_T6_X2_G3.txt")]
+    want = {}
+    for r in rows:
+        if r[0] == "counters":
+            counters = list(map(int, r[1:]))
+            continue
+        p, v, m, n = map(int, r)
+        want.setdefault(p, []).append((v, m, n))
+    seqs, cnt = sm.wsx_simulate(3, 2, 3, 2, homes=[0, 0, 1], speeds=[1, 1, 4])
+    assert {p: s for p, s in enumerate(seqs)} == want
+    assert cnt == counters == sm.wsx_final_counters(6, 3, 2)
+
+
+def _wsx_arrays(seqs, T):
+    visits, owner, order = [0] * T, [-1] * T, [-1] * T
+    for p, seq in enumerate(seqs):
+        for i, (v, _, _) in enumerate(seq):
+            visits[v] += 1
+            owner[v] = p
+            order[v] = i
+    return visits, owner, order
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(4, 4, 8, 4, 1), (5, 7, 3, 8, 1), (16, 16, 256, 8, 1),
+                                             (13, 23, 64, 8, 2), (1, 1, 8, 8, 1), (32, 4, 12, 8, 4)])
+def test_wsx_simulated_invariants(pm, pn, G, X, chunk):
+    T = pm * pn
+    rng = random.Random(G * 31 + X)
+    # homes: round-robin, all programs on one XCD, and random placements
+    for homes in ([p % X for p in range(G)], [0] * G, [rng.randrange(X) for _ in range(G)]):
+        for seed in range(3):
+            seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, chunk=chunk, seed=seed)
+            sm.check_partition(seqs, pm, pn)
+            visits, owner, order = _wsx_arrays(seqs, T)
+            sm.check_wsx_execution(visits, owner, order, cnt, homes, T, G, X, chunk)
+
+
+def test_wsx_steals_from_a_slow_xcd():
+    # programs on XCD 0 are ten times slower: the others take most of its range
+    G, X = 16, 4
+    homes = [p % X for p in range(G)]
+    speeds = [10.0 if homes[p] == 0 else 1.0 for p in range(G)]
+    seqs, _ = sm.wsx_simulate(16, 16, G, X, homes, speeds=speeds)
+    s0, e0 = sm.ws_ranges(256, X)[0]
+    stolen = sum(1 for p, seq in enumerate(seqs) if homes[p] != 0 for v, _, _ in seq if s0 <= v < e0)
+    assert stolen > (e0 - s0) // 2
+    # without stealing, XCD 0's programs compute all of it
+    seqs_ws, _ = sm.ws_simulate(16, 16, G, X, speeds=speeds)
+    assert all(p % X == 0 for p, seq in enumerate(seqs_ws) for v, _, _ in seq if s0 <= v < e0)
+
+
+def test_wsx_checker_catches_planted_mistakes():
+    pm, pn, G, X = 4, 4, 6, 4
+    T = pm * pn
+    homes = [0, 0, 1, 1, 2, 2]
+    seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, seed=5)
+    v, o, r = _wsx_arrays(seqs, T)
+    sm.check_wsx_execution(v, o, r, cnt, homes, T, G, X)
+    with pytest.raises(AssertionError):                    # a program that skipped its sweep
+        sm.check_wsx_execution(v, o, r, [c - 1 for c in cnt], homes, T, G, X)
+    with pytest.raises(AssertionError):                    # a tile computed twice
+        v2 = list(v)
+        v2[3] = 2
+        sm.check_wsx_execution(v2, o, r, cnt, homes, T, G, X)
+    # a program whose tiles are not in cyclic counter order from its home
+    p = max(range(G), key=lambda q: len({sm.ws_owner(t, T, X) for t, _, _ in seqs[q]}))
+    assert len({sm.ws_owner(t, T, X) for t, _, _ in seqs[p]}) > 1
+    with pytest.raises(AssertionError):
+        sm.check_wsx_execution(v, o, r, cnt, [(h + 1) % X if q == p else h
+                                              for q, h in enumerate(homes)], T, G, X)
