@@ -86,14 +86,27 @@ typedef enum {
  *                   operands, K and N multiples of 8), no witness; otherwise
  *                   PGEMM_ERR_UNSUPPORTED.  Results are deterministic but
  *                   not bitwise equal to the other schedulers on split
- *                   tiles (different summation order). */
+ *                   tiles (different summation order).
+ *  WORK_STEALING_XCC  work stealing across XCDs, the pages' per-XCD
+ *                   counters carried one step further: same counters and
+ *                   ranges, but a program's home counter is the hardware XCC
+ *                   it runs on (so its tiles stay in that XCD's L2 whatever
+ *                   the dispatch order), and once its home range is
+ *                   exhausted it claims from the next counters in cyclic
+ *                   order, stopping after one failing claim on each.  Every
+ *                   tile is still computed exactly once, completion does not
+ *                   depend on placement (any G >= 1), and each counter ends
+ *                   at n_x + G claims (n_x = tiles in its range; claims of
+ *                   several tiles for the add count once).  Costs up to X - 1 extra
+ *                   atomics per program at the end of its work. */
 typedef enum {
   PGEMM_SCHED_BLOCKED = 0,
   PGEMM_SCHED_INTERLEAVED = 1,
   PGEMM_SCHED_GROUPED = 2,
   PGEMM_SCHED_WORK_STEALING = 3,
   PGEMM_SCHED_BLOCKED_GROUPED = 4,
-  PGEMM_SCHED_STREAM_K = 5
+  PGEMM_SCHED_STREAM_K = 5,
+  PGEMM_SCHED_WORK_STEALING_XCC = 6
 } pgemm_sched;
 
 /* debug_flags (tests and measurement only). */
@@ -104,6 +117,9 @@ typedef enum {
 #define PGEMM_DEBUG_REGISTER_STAGED 0x8u /* bf16: use the register-staged kernel (the path taken
                                             for unaligned shapes) even where the direct-to-LDS
                                             kernel applies */
+#define PGEMM_DEBUG_STRAGGLER_XCC 0x10u /* every program on hardware XCC straggler_program waits
+                                           straggler_ns before each tile (not with
+                                           PGEMM_DEBUG_STRAGGLER: PGEMM_ERR_INVALID) */
 
 /* Optional per-call arguments; pass NULL for all defaults. */
 typedef struct {

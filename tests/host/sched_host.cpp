@@ -63,6 +63,58 @@ static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
   return 0;
 }
 
+// Work stealing across XCDs: G threads start on counter homes[p] and, once a
+// claim fails, move to the next counter in cyclic order, stopping after one
+// failing claim on each; the end of a claim is cut at the end of the range
+// that holds its first tile (pgs::ws_owner), as the kernels do.
+static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
+  const int T = pm * pn;
+  std::vector<int> homes(G);
+  unsigned lcg = 12345u;
+  for (int p = 0; p < G; ++p) {
+    lcg = lcg * 1103515245u + 12345u;
+    homes[p] = home_mode == 0 ? p % X : home_mode == 1 ? 0 : (int)((lcg >> 16) % (unsigned)X);
+  }
+  std::vector<std::atomic<int>> cnt(X);
+  for (auto& c : cnt) c.store(0);
+  std::vector<std::atomic<int>> visits(T);
+  for (auto& v : visits) v.store(0);
+  std::vector<int> owner(T, -1), order(T, -1);
+  std::vector<std::thread> th;
+  for (int p = 0; p < G; ++p) {
+    th.emplace_back([&, p] {
+      int x = homes[p], failed = 0, done = 0;
+      for (;;) {
+        const int begin = pgs::ws_range_begin(x, T, X);
+        const int n = pgs::ws_range_begin(x + 1, T, X) - begin;
+        const int i = cnt[x].fetch_add(chunk, std::memory_order_relaxed);
+        if (i >= n) {
+          if (++failed == X) break;
+          x = x + 1 == X ? 0 : x + 1;
+          continue;
+        }
+        const int v0 = begin + i;
+        const int range_end = pgs::ws_range_begin(pgs::ws_owner(v0, T, X) + 1, T, X);
+        const int e = v0 + chunk < range_end ? v0 + chunk : range_end;
+        for (int v = v0; v < e; ++v) {
+          visits[v].fetch_add(1);
+          owner[v] = p;
+          order[v] = done++;
+          std::this_thread::yield();
+        }
+      }
+    });
+  }
+  for (auto& t : th) t.join();
+  std::printf("homes:");
+  for (int p = 0; p < G; ++p) std::printf(" %d", homes[p]);
+  std::printf("\ncounters:");
+  for (int x = 0; x < X; ++x) std::printf(" %d", cnt[x].load());
+  std::printf("\n");
+  for (int v = 0; v < T; ++v) std::printf("%d %d %d %d\n", v, visits[v].load(), owner[v], order[v]);
+  return 0;
+}
+
 // Stream-K: every program's segments (tile, first slab, end slab, slot), then
 // for every split tile its contributors with the slots they wrote.
 static int sk_walk(int T, int nk, int G) {
@@ -98,6 +150,9 @@ int main(int argc, char** argv) {
   if (mode == "ws" && argc == 8)
     return ws_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                       std::atoi(argv[6]), std::atoi(argv[7]));
+  if (mode == "wsx" && argc == 8)
+    return wsx_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
+                       std::atoi(argv[6]), std::atoi(argv[7]));
   if (mode == "sk" && argc == 5)
     return sk_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   return 2;

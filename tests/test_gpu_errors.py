@@ -9,6 +9,7 @@ import torch
 
 import tile_scheduling_persistent_amd as pg
 from tile_scheduling_persistent_amd import _abi
+from oracle import sched_model as sm
 from synthetic import bf16_bits_uniform
 from tests.gpu_util import config, dev_bf16, note
 
@@ -127,6 +128,43 @@ def test_straggler_rebalanced_by_work_stealing():
     assert res["blocked"] == T // G
     peers = [p for p in range(G) if p % X == 0]
     assert res["work_stealing"] < T // G, res
+
+
+def test_slow_xcc_rebalanced_by_stealing_across_xccs():
+    """Every program on hardware XCC 0 waits 100 us before each tile.  Per-XCD
+    work stealing leaves XCC 0's range to XCC 0's programs; stealing across
+    XCDs lets the others take part of it, and still computes every tile
+    once with the exact final counters."""
+    cfg = config()
+    X = cfg.info["num_xcds"]
+    M = N = 4096
+    K = 256
+    tile = (128, 128, 64)
+    T = (M // 128) * (N // 128)
+    G = pg.plan_gemm(cfg, M, N, K, "bf16_out_f32", "work_stealing", pg.make_args(tile=tile))["grid"]
+    a, b = bf16_bits_uniform((M, K), 1), bf16_bits_uniform((K, N), 2)
+    A, B = dev_bf16(a), dev_bf16(b)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    cfg.witness_enable(T, G)
+    flags = _abi.DEBUG_WITNESS | _abi.DEBUG_STRAGGLER_XCC
+    s0, e0 = sm.ws_ranges(T, X)[0]
+    stolen = {}
+    for sched in ["work_stealing", "work_stealing_xcc"]:
+        note(f"slow XCC 0 under {sched}")
+        pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", sched,
+                     pg.make_args(tile=tile, debug_flags=flags, straggler_program=0,
+                                  straggler_ns=100_000))
+        w = cfg.witness_read(T, G)
+        assert np.all(w["visits"][:T] == 1)
+        xcc = (w["hw_id"][:G] >> 16) & 0xF
+        owner = w["owner"][:T]
+        stolen[sched] = int(sum(1 for v in range(s0, e0) if xcc[owner[v]] != 0))
+        if sched == "work_stealing_xcc":
+            homes = [int(h) % X for h in xcc]
+            sm.check_wsx_execution(w["visits"][:T].tolist(), owner.tolist(), w["order"][:T].tolist(),
+                                   w["counters"].tolist(), homes, T, G, X)
+    note(f"tiles of range 0 computed off XCC 0: {stolen}")
+    assert stolen["work_stealing_xcc"] > (e0 - s0) // 4, stolen
 
 
 def test_plan_matches_launch_shape():

@@ -14,7 +14,7 @@ from tests.gpu_util import (BF16_TOL, Guarded, assert_north_star, assert_within,
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]
+SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "work_stealing_xcc"]
 EDGE = [1, 2, 15, 63, 64, 65, 127, 128, 129, 255, 257]
 
 
@@ -156,6 +156,7 @@ def test_8192_all_schedulers():
     ref_bits = None
     for sched, gs, fl in [("blocked", 0, 0), ("interleaved", 0, 0), ("grouped", 8, 0), ("grouped", 16, 0),
                           ("work_stealing", 8, 0), ("work_stealing", 16, 0), ("blocked_grouped", 8, 0),
+                          ("work_stealing_xcc", 8, 0),
                           ("work_stealing", 8, pg._abi.DEBUG_REGISTER_STAGED)]:
         C = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, (256, 256, 64), group_size=gs,
                      debug_flags=fl)

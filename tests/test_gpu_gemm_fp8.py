@@ -12,7 +12,7 @@ from tests.gpu_util import FP8_TOL, Guarded, assert_north_star, assert_within, c
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]
+SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "work_stealing_xcc"]
 
 
 def make_inputs(M, N, K, seed):

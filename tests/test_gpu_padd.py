@@ -10,7 +10,7 @@ from tests.gpu_util import GUARD, SENTINEL_F32, config, dev_f32, note
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped"]
+SCHEDS = ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "work_stealing_xcc"]
 TILES = [(32, 16), (64, 64), (128, 128)]
 
 

@@ -1,7 +1,9 @@
 """GPU schedule witness: every tile computed exactly once under every scheduler;
 static schedules equal the oracle's model tile for tile; work-stealing runs
 satisfy the model's invariants (owner on the right XCD, increasing claims,
-final counters)."""
+final counters); work stealing across XCDs satisfies its own (each program
+starts on the counter of the hardware XCC it ran on, recorded by the
+witness)."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +16,7 @@ from tests.gpu_util import config, dev_bf16, dev_f32, note
 pytestmark = pytest.mark.gpu
 
 STATIC = ["blocked", "interleaved", "grouped", "blocked_grouped"]
+WS = ["work_stealing", "work_stealing_xcc"]
 
 
 def _check(w, kind, pm, pn, G, X, gs, chunk=1):
@@ -27,9 +30,13 @@ def _check(w, kind, pm, pn, G, X, gs, chunk=1):
             for i, (v, _, _) in enumerate(seq):
                 assert owner[v] == p and order[v] == i, (kind, v, owner[v], p, order[v], i)
             assert w["n_tiles"][p] == len(seq)
-    else:
+    elif kind == "work_stealing":
         sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(),
                               w["counters"].tolist(), T, G, X, chunk)
+    else:
+        homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
+        sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(),
+                               w["counters"].tolist(), homes, T, G, X, chunk)
 
 
 def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
@@ -55,7 +62,7 @@ def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
     return w, pm, pn, G, cfg.info["num_xcds"]
 
 
-@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("sched", STATIC + WS)
 @pytest.mark.parametrize("shape,tile", [
     ((512, 512, 512), (128, 128, 64)),
     ((5120, 5120, 256), (256, 256, 64)),
@@ -80,7 +87,7 @@ def test_gemm_witness_clock():
     assert np.all((ghz > 0.3) & (ghz < 3.0)), ghz
 
 
-@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("sched", STATIC + WS)
 @pytest.mark.parametrize("grid", [1, 7, 8, 13, 300])
 def test_gemm_schedule_grid_override(sched, grid):
     if sched == "work_stealing" and grid < config().info["num_xcds"]:
@@ -89,7 +96,7 @@ def test_gemm_schedule_grid_override(sched, grid):
     _check(w, sched, pm, pn, G, X, 3)
 
 
-@pytest.mark.parametrize("sched", STATIC + ["work_stealing"])
+@pytest.mark.parametrize("sched", STATIC + WS)
 @pytest.mark.parametrize("tile", [(32, 16), (128, 128)])
 def test_add_schedule_exactly_once(sched, tile):
     cfg = config()

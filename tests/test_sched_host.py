@@ -1,7 +1,8 @@
 """The library's scheduler header, built for the host with g++, against the
 oracle's schedule model: static walks tile for tile, and the work-stealing
-claim loop on real threads with std::atomic counters against the model's
-invariants."""
+claim loops (per-XCD, and across XCDs from arbitrary home counters) on real
+threads with std::atomic counters against the model's invariants, and the
+stream-K walker segment for segment."""
 import itertools
 import os
 import subprocess
@@ -54,6 +55,22 @@ def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     owner = [r[2] for r in rows]
     order = [r[3] for r in rows]
     sm.check_ws_execution(visits, owner, order, counters, T, G, X, chunk)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (19, 32, 256, 8, 1),
+                                             (33, 7, 64, 8, 4), (1, 1, 16, 8, 1), (3, 1, 5, 8, 1),
+                                             (13, 11, 3, 8, 2)])
+@pytest.mark.parametrize("home_mode", [0, 1, 2])
+def test_wsx_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk, home_mode):
+    out = subprocess.run([harness, "wsx", str(pm), str(pn), str(G), str(X), str(chunk), str(home_mode)],
+                         check=True, capture_output=True, text=True).stdout.strip().splitlines()
+    homes = list(map(int, out[0].split(":")[1].split()))
+    counters = list(map(int, out[1].split(":")[1].split()))
+    T = pm * pn
+    rows = [tuple(map(int, l.split())) for l in out[2:]]
+    assert len(rows) == T and len(homes) == G
+    sm.check_wsx_execution([r[1] for r in rows], [r[2] for r in rows], [r[3] for r in rows],
+                           counters, homes, T, G, X, chunk)
 
 
 @pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),

@@ -23,6 +23,7 @@ SCHEDULERS = {
     "work_stealing": _abi.SCHED_WORK_STEALING,
     "blocked_grouped": _abi.SCHED_BLOCKED_GROUPED,
     "stream_k": _abi.SCHED_STREAM_K,
+    "work_stealing_xcc": _abi.SCHED_WORK_STEALING_XCC,
 }
 DTYPES = {
     "bf16_out_f32": _abi.BF16_OUT_F32,

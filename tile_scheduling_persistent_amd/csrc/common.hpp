@@ -34,6 +34,7 @@ struct SchedParams {
   int chunk;          // tiles per work-stealing claim
   int straggler_program;  // -1: off
   int straggler_ns;
+  int straggler_xcc;      // straggler_program names a hardware XCC, not a program
   int wall_khz;       // wall-clock tick rate (straggler wait)
 };
 
@@ -132,6 +133,18 @@ __device__ __forceinline__ int hw_placement() {
   return (int)((hw & 0xffffu) | ((xcc & 0xfu) << 16));
 }
 
+// Hardware XCC (XCD) the calling wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfu);  // HW_REG_XCC_ID, 4 bits
+}
+
+// The straggler debug flag: true for the program it slows down (by program
+// id, or every program on one hardware XCC).
+__device__ __forceinline__ bool is_straggler(const SchedParams& s, int prog) {
+  if (s.straggler_program < 0) return false;
+  return s.straggler_xcc ? xcc_id() == s.straggler_program : prog == s.straggler_program;
+}
+
 // Bounded wait used by the straggler debug flag: returns after `ns`.
 __device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
   const long long t0 = wall_ticks();
@@ -139,46 +152,65 @@ __device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
   while (wall_ticks() - t0 < ticks) __builtin_amdgcn_s_sleep(2);
 }
 
-// Per-program view of the scheduler.  Static kinds walk arithmetically; the
-// work-stealing kind claims from counter p mod X.  first()/next() return a
-// tile id or -1 when the program is done.  For work stealing only one
-// thread of the workgroup may call them (each call is one claim).
+// Per-program view of the scheduler.  Static kinds walk arithmetically.
+// Work stealing claims from counter p mod X; work stealing across XCDs
+// starts on the counter of the XCD the program runs on and, once that range
+// is exhausted, claims from the next counters in cyclic order, stopping
+// after one failing claim on each (at most X atomics past its last tile).
+// first()/next() return a tile id or -1 when the program is done.  For the
+// work-stealing kinds only one thread of the workgroup may call them (each
+// call is at least one claim).
 struct Walker {
   SchedParams s;
   int p;
   int end;       // static: end of the walk
-  int x;         // work stealing: XCD / counter index
-  int begin, n;  // work stealing: the XCD's range [begin, begin + n)
+  int x;         // work stealing: current counter
+  int failed;    // work stealing across XCDs: counters found exhausted
+  int begin, n;  // work stealing: counter x's range [begin, begin + n)
+
+  __device__ __forceinline__ void set_counter(int c) {
+    const int X = s.X > 0 ? s.X : 1;
+    x = c;
+    begin = pgs::ws_range_begin(c, s.T, X);
+    n = pgs::ws_range_begin(c + 1, s.T, X) - begin;
+  }
 
   __device__ __forceinline__ Walker(const SchedParams& sp, int prog) : s(sp), p(prog) {
     end = 0;
-    x = prog % (sp.X > 0 ? sp.X : 1);
-    begin = pgs::ws_range_begin(x, sp.T, sp.X > 0 ? sp.X : 1);
-    n = pgs::ws_range_begin(x + 1, sp.T, sp.X > 0 ? sp.X : 1) - begin;
+    failed = 0;
+    const int X = sp.X > 0 ? sp.X : 1;
+    set_counter(sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X);
   }
 
-  // One claim of s.chunk tiles; returns the first claimed id or -1.
+  // Claims of s.chunk tiles; returns the first claimed id or -1.
   __device__ __forceinline__ int claim() {
-    const int i = __hip_atomic_fetch_add(s.counters + x, s.chunk, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return (i >= 0 && i < n) ? begin + i : -1;
+    for (;;) {
+      const int i = __hip_atomic_fetch_add(s.counters + x, s.chunk, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (i >= 0 && i < n) return begin + i;
+      if (s.kind != pgs::kWorkStealingXcc || ++failed >= s.X) return -1;
+      set_counter(x + 1 == s.X ? 0 : x + 1);
+    }
   }
 
-  // End (exclusive) of the chunk that starts at v (work stealing).
+  // End (exclusive) of the claim that starts at tile v: v + chunk, cut at the
+  // end of the counter range that holds v (any thread may call it).
   __device__ __forceinline__ int claim_end(int v) const {
+    const int X = s.X > 0 ? s.X : 1;
     const int e = v + s.chunk;
-    return e < begin + n ? e : begin + n;
+    const int range_end = pgs::ws_range_begin(pgs::ws_owner(v, s.T, X) + 1, s.T, X);
+    return e < range_end ? e : range_end;
   }
 
   __device__ __forceinline__ int first() {
-    if (s.kind == pgs::kWorkStealing) return claim();
+    if (pgs::work_stealing(s.kind)) return claim();
     int v;
     pgs::static_first(s.kind, p, s.T, s.G, v, end);
     return v < end ? v : -1;
   }
 
   __device__ __forceinline__ int next(int v) {
-    if (s.kind == pgs::kWorkStealing) return claim();
+    if (pgs::work_stealing(s.kind)) return claim();
     const int nv = pgs::static_next(s.kind, v, s.G, end);
     return nv < end ? nv : -1;
   }

@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
         P.w.owner[tile] = prog;
         P.w.order[tile] = it;
       }
-      if (P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
+      if (is_straggler(P.s, prog)) spin_ns(P.s.straggler_ns, P.s.wall_khz);
     }
 #pragma unroll
     for (int sn = 0; sn < S::SN; ++sn)

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   const int tid = threadIdx.x;
   const int prog = blockIdx.x;
   const int rows = P.rows, cols = P.cols;
-  const bool ws = P.s.kind == pgs::kWorkStealing;
+  const bool ws = pgs::work_stealing(P.s.kind);
   Walker walker(P.s, prog);
   long long t_start = 0, c_start = 0;
   if (WITNESS && tid == 0) {
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
           P.w.order[vt[u]] = done + u;
         }
     }
-    if (tid == 0 && P.s.straggler_program == prog) spin_ns(P.s.straggler_ns, P.s.wall_khz);
+    if (tid == 0 && is_straggler(P.s, prog)) spin_ns(P.s.straggler_ns, P.s.wall_khz);
 
     f32x4 xa[S::SLOTS], ya[S::SLOTS];
     long long off[S::SLOTS];

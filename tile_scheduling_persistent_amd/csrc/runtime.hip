@@ -92,7 +92,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
                         int num_pid_m, int num_pid_n, int default_grid, pgk::SchedParams& s) {
-  if ((int)sched < 0 || (int)sched > 5) return PGEMM_ERR_INVALID;
+  if ((int)sched < 0 || (int)sched > 6) return PGEMM_ERR_INVALID;
   const int64_t T = (int64_t)num_pid_m * num_pid_n;
   if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
   s.kind = (int)sched;
@@ -106,6 +106,7 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.chunk = 1;
   s.straggler_program = -1;
   s.straggler_ns = 0;
+  s.straggler_xcc = 0;
   s.wall_khz = cfg->wall_khz;
   if (s.G < 1 || s.gs < 1) return PGEMM_ERR_INVALID;
   if (s.kind == pgs::kWorkStealing && s.G < s.X) return PGEMM_ERR_INVALID;
@@ -114,6 +115,13 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
     if (args->straggler_ns < 0 || args->straggler_ns > 1000000000) return PGEMM_ERR_INVALID;
     s.straggler_program = args->straggler_program;
     s.straggler_ns = args->straggler_ns;
+  }
+  if (args && (args->debug_flags & PGEMM_DEBUG_STRAGGLER_XCC)) {
+    if (args->debug_flags & PGEMM_DEBUG_STRAGGLER) return PGEMM_ERR_INVALID;
+    if (args->straggler_ns < 0 || args->straggler_ns > 1000000000) return PGEMM_ERR_INVALID;
+    s.straggler_program = args->straggler_program;
+    s.straggler_ns = args->straggler_ns;
+    s.straggler_xcc = 1;
   }
   return PGEMM_OK;
 }
@@ -211,7 +219,7 @@ pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::
 
 pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
                             hipStream_t stream) {
-  if (s.kind != pgs::kWorkStealing) return PGEMM_OK;
+  if (!pgs::work_stealing(s.kind)) return PGEMM_OK;
   if (args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET)) return PGEMM_OK;
   // a fill kernel rather than a memset node, so that the call may be captured
   return pgk::launch_zero_i32(cfg->counters, cfg->capacity, stream) == hipSuccess

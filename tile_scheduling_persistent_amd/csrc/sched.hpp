@@ -11,7 +11,10 @@
 //    scheduler object with init / valid / next and a swizzle (group) size;
 //    its loop walks tile ids with a stride of the grid.
 //  - "Work Stealing Scheduler Kernel" (tritonBLAS PR #65): one counter per
-//    XCD, chosen by program id modulo the XCD count; stream-K is the
+//    XCD, chosen by program id modulo the XCD count (work stealing across
+//    XCDs extends it: the home counter is the XCD the program runs on, and a
+//    program whose home range is exhausted claims from the other counters in
+//    cyclic order); stream-K is the
 //    comparator its benchmark names (taken here as the data-parallel +
 //    stream-K hybrid of the published Stream-K method).
 #pragma once
@@ -34,12 +37,16 @@ enum Kind : int {
   kWorkStealing = 3,
   kBlockedGrouped = 4,
   kStreamK = 5,
+  kWorkStealingXcc = 6,
 };
+
+PGS_FN bool work_stealing(int kind) { return kind == kWorkStealing || kind == kWorkStealingXcc; }
 
 PGS_FN int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 PGS_FN bool grouped_order(int kind) {
-  return kind == kGrouped || kind == kWorkStealing || kind == kBlockedGrouped || kind == kStreamK;
+  return kind == kGrouped || kind == kWorkStealing || kind == kBlockedGrouped || kind == kStreamK ||
+         kind == kWorkStealingXcc;
 }
 
 // Tile id -> (pid_m, pid_n), dimension 0 (rows of tiles) fastest.
@@ -72,6 +79,12 @@ PGS_FN void decode(int kind, int v, int num_pid_m, int num_pid_n, int gs, int& p
 // Work stealing: XCD x owns tile ids [range_begin(x), range_begin(x + 1)).
 PGS_FN int ws_range_begin(int x, int T, int X) {
   return (int)(((int64_t)x * (int64_t)T) / (int64_t)X);
+}
+
+// Counter (XCD range) holding tile id v: the largest x with
+// ws_range_begin(x) <= v.
+PGS_FN int ws_owner(int v, int T, int X) {
+  return (int)((((int64_t)v + 1) * X + T - 1) / T) - 1;
 }
 
 // Static schedulers: first tile id of program p and the end of its walk.
