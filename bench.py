@@ -31,7 +31,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_CLOCK_GHZ = 2.4          # engine clock the dense peak is quoted at
 M = N = K = 8192
 SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
-          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8), ("stream_k", 8)]
+          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8), ("stream_k", 8),
+          ("work_stealing_xcc", 8)]
 HEADLINE = ("work_stealing", 8)
 CPU_ROWS = 4096
 
@@ -169,7 +170,7 @@ def main():
     only = set(s for s in args.only.split(",") if s)
     per = {}
     for sched, gs in SCHEDS:
-        key = f"{sched}" + (f"_g{gs}" if sched in ("grouped", "work_stealing", "blocked_grouped", "stream_k") else "")
+        key = f"{sched}" + (f"_g{gs}" if sched != "blocked" and sched != "interleaved" else "")
         if only and sched not in only and key not in only:
             continue
         a = pg.make_args(tile=(256, 256, 64), group_size=gs)
@@ -190,7 +191,8 @@ def main():
             rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
             row = {}
-            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "stream_k"]:
+            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "stream_k",
+                          "work_stealing_xcc"]:
                 a = pg.make_args(tile=(256, 256, 64))
                 fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
                 _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
@@ -224,6 +226,27 @@ def main():
             print(f"# skinny {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
                   file=sys.stderr, flush=True)
             del ra, rb, rc
+
+    # one slow XCD (every program on hardware XCC 0 waits 50 us before each
+    # tile, about one tile's time; a stand-in for an XCD shared with other
+    # work): per-XCD work stealing against stealing across XCDs, 8192x8192x2048
+    slow_xcc = {}
+    if not args.skip_extra and (not only or "work_stealing_xcc_g8" in only):
+        k2 = 2048
+        sa = torch.from_numpy(bf16_bits_normal((M, k2), 1070).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        sb = torch.from_numpy(bf16_bits_normal((k2, N), 1071).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        f = 2.0 * M * N * k2
+        for slow in (False, True):
+            for sched in ["grouped", "work_stealing", "work_stealing_xcc"]:
+                a = pg.make_args(tile=(256, 256, 64),
+                                 debug_flags=pg._abi.DEBUG_STRAGGLER_XCC if slow else 0,
+                                 straggler_program=0 if slow else -1, straggler_ns=50_000 if slow else 0)
+                fn = lambda: pg.pgemm_run(cfg, sa, sb, C, M, N, k2, "bf16_out_bf16", sched, a)  # noqa: E731
+                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+                slow_xcc[f"{sched}{'_slow' if slow else ''}"] = {
+                    "tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
+        print(f"# 8192x8192x2048, XCC 0 slowed by 50 us per tile: {slow_xcc}", file=sys.stderr, flush=True)
+        del sa, sb
 
     # block-scaled fp8 (workload 5): work stealing vs grouped
     fp8 = {}
@@ -308,6 +331,7 @@ def main():
                 for k, v in add.items()},
         "ragged": ragged,
         "skinny": skinny,
+        "slow_xcc": slow_xcc,
         "fp8": fp8,
         "device": cfg.info,
     }

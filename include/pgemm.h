@@ -92,13 +92,14 @@ typedef enum {
  *                   ranges, but a program's home counter is the hardware XCC
  *                   it runs on (so its tiles stay in that XCD's L2 whatever
  *                   the dispatch order), and once its home range is
- *                   exhausted it claims from the next counters in cyclic
- *                   order, stopping after one failing claim on each.  Every
- *                   tile is still computed exactly once, completion does not
- *                   depend on placement (any G >= 1), and each counter ends
- *                   at n_x + G claims (n_x = tiles in its range; claims of
- *                   several tiles for the add count once).  Costs up to X - 1 extra
- *                   atomics per program at the end of its work. */
+ *                   exhausted it reads the counters it has not passed (one
+ *                   round of loads), skips those past their range and claims
+ *                   from the next one in cyclic order that is not, stopping
+ *                   when none is left.  Every tile is still computed exactly
+ *                   once and completion does not depend on placement (any
+ *                   G >= 1); a program makes one failing claim on its home
+ *                   counter and at most one on each other.  Needs X <= 16
+ *                   (PGEMM_ERR_UNSUPPORTED otherwise). */
 typedef enum {
   PGEMM_SCHED_BLOCKED = 0,
   PGEMM_SCHED_INTERLEAVED = 1,

@@ -63,10 +63,11 @@ static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
   return 0;
 }
 
-// Work stealing across XCDs: G threads start on counter homes[p] and, once a
-// claim fails, move to the next counter in cyclic order, stopping after one
-// failing claim on each; the end of a claim is cut at the end of the range
-// that holds its first tile (pgs::ws_owner), as the kernels do.
+// Work stealing across XCDs: G threads start on counter homes[p]; after a
+// failing claim a thread reads the counters it has not passed (cyclic order),
+// skips those past their range and moves to the first that is not, or stops;
+// the end of a claim is cut at the end of the range that holds its first
+// tile (pgs::ws_owner), as the kernels do.
 static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
   const int T = pm * pn;
   std::vector<int> homes(G);
@@ -83,14 +84,22 @@ static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
   std::vector<std::thread> th;
   for (int p = 0; p < G; ++p) {
     th.emplace_back([&, p] {
-      int x = homes[p], failed = 0, done = 0;
+      int x = homes[p], passed = 0, done = 0;
+      auto range_n = [&](int c) { return pgs::ws_range_begin(c + 1, T, X) - pgs::ws_range_begin(c, T, X); };
       for (;;) {
         const int begin = pgs::ws_range_begin(x, T, X);
-        const int n = pgs::ws_range_begin(x + 1, T, X) - begin;
+        const int n = range_n(x);
         const int i = cnt[x].fetch_add(chunk, std::memory_order_relaxed);
         if (i >= n) {
-          if (++failed == X) break;
-          x = x + 1 == X ? 0 : x + 1;
+          if (++passed >= X) break;
+          const int left = X - passed;
+          std::vector<int> seen(left);
+          for (int j = 0; j < left; ++j) seen[j] = cnt[(x + 1 + j) % X].load(std::memory_order_relaxed);
+          int j = 0;
+          while (j < left && seen[j] >= range_n((x + 1 + j) % X)) ++j;
+          if (j == left) break;
+          passed += j;
+          x = (x + 1 + j) % X;
           continue;
         }
         const int v0 = begin + i;

@@ -216,7 +216,8 @@ def test_wsx_golden(golden):
         want.setdefault(p, []).append((v, m, n))
     seqs, cnt = sm.wsx_simulate(3, 2, 3, 2, homes=[0, 0, 1], speeds=[1, 1, 4])
     assert {p: s for p, s in enumerate(seqs)} == want
-    assert cnt == counters == sm.wsx_final_counters(6, 3, 2)
+    assert cnt == counters
+    assert sm.wsx_counter_bounds(6, 3, 2, [0, 0, 1]) == [(5, 6), (4, 6)]
 
 
 def _wsx_arrays(seqs, T):
@@ -264,8 +265,12 @@ def test_wsx_checker_catches_planted_mistakes():
     seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, seed=5)
     v, o, r = _wsx_arrays(seqs, T)
     sm.check_wsx_execution(v, o, r, cnt, homes, T, G, X)
-    with pytest.raises(AssertionError):                    # a program that skipped its sweep
-        sm.check_wsx_execution(v, o, r, [c - 1 for c in cnt], homes, T, G, X)
+    lo = [b[0] for b in sm.wsx_counter_bounds(T, G, X, homes)]
+    hi = [b[1] for b in sm.wsx_counter_bounds(T, G, X, homes)]
+    with pytest.raises(AssertionError):                    # a missing failing claim at home
+        sm.check_wsx_execution(v, o, r, [lo[0] - 1] + list(cnt[1:]), homes, T, G, X)
+    with pytest.raises(AssertionError):                    # two failing claims by one program
+        sm.check_wsx_execution(v, o, r, [hi[0] + 1] + list(cnt[1:]), homes, T, G, X)
     with pytest.raises(AssertionError):                    # a tile computed twice
         v2 = list(v)
         v2[3] = 2

@@ -22,6 +22,13 @@ struct Witness {
   int* n_tiles;       // [G] tiles the program computed
 };
 
+// Work-stealing counter x lives at counters[x * kCounterStride]: one 256-byte
+// block per counter, so claims on different counters never contend for one
+// cache line at the point where device-scope atomics are performed.
+constexpr int kCounterStride = 64;
+// Counters work stealing across XCDs can look at in one pass.
+constexpr int kMaxStealCounters = 16;
+
 struct SchedParams {
   int kind;           // pgs::Kind
   int T;              // tiles
@@ -30,7 +37,7 @@ struct SchedParams {
   int gs;             // group size of the grouped order
   int num_pid_m;      // tiles along dimension 0 (rows)
   int num_pid_n;      // tiles along dimension 1 (columns)
-  int* counters;      // work-stealing counters, zero at launch
+  int* counters;      // work-stealing counters (stride kCounterStride), zero at launch
   int chunk;          // tiles per work-stealing claim
   int straggler_program;  // -1: off
   int straggler_ns;
@@ -153,52 +160,75 @@ __device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
 }
 
 // Per-program view of the scheduler.  Static kinds walk arithmetically.
-// Work stealing claims from counter p mod X; work stealing across XCDs
-// starts on the counter of the XCD the program runs on and, once that range
-// is exhausted, claims from the next counters in cyclic order, stopping
-// after one failing claim on each (at most X atomics past its last tile).
-// first()/next() return a tile id or -1 when the program is done.  For the
-// work-stealing kinds only one thread of the workgroup may call them (each
-// call is at least one claim).
+// Work stealing claims from counter p mod X.  Work stealing across XCDs
+// starts on the counter of the XCD the program runs on; when a claim fails
+// it reads every counter it has not passed yet (one round of loads), skips
+// those already past their range, and moves to the first one that is not;
+// it stops when none is left, so it makes at most one failing claim per
+// counter.  first()/next() return a tile id or -1 when the program is done.
+// For the work-stealing kinds only one thread of the workgroup may call
+// them (each call is at least one claim).
 struct Walker {
   SchedParams s;
   int p;
   int end;       // static: end of the walk
   int x;         // work stealing: current counter
-  int failed;    // work stealing across XCDs: counters found exhausted
+  int passed;    // work stealing across XCDs: counters passed (home first)
   int begin, n;  // work stealing: counter x's range [begin, begin + n)
 
+  __device__ __forceinline__ int nx() const { return s.X > 0 ? s.X : 1; }
+  __device__ __forceinline__ int range_begin(int c) const { return pgs::ws_range_begin(c, s.T, nx()); }
+  __device__ __forceinline__ int* counter(int c) const { return s.counters + c * kCounterStride; }
+
   __device__ __forceinline__ void set_counter(int c) {
-    const int X = s.X > 0 ? s.X : 1;
     x = c;
-    begin = pgs::ws_range_begin(c, s.T, X);
-    n = pgs::ws_range_begin(c + 1, s.T, X) - begin;
+    begin = range_begin(c);
+    n = range_begin(c + 1) - begin;
   }
 
   __device__ __forceinline__ Walker(const SchedParams& sp, int prog) : s(sp), p(prog) {
     end = 0;
-    failed = 0;
-    const int X = sp.X > 0 ? sp.X : 1;
+    passed = 0;
+    const int X = nx();
     set_counter(sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X);
   }
 
   // Claims of s.chunk tiles; returns the first claimed id or -1.
   __device__ __forceinline__ int claim() {
+    const int X = nx();
     for (;;) {
-      const int i = __hip_atomic_fetch_add(s.counters + x, s.chunk, __ATOMIC_RELAXED,
+      const int i = __hip_atomic_fetch_add(counter(x), s.chunk, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       if (i >= 0 && i < n) return begin + i;
-      if (s.kind != pgs::kWorkStealingXcc || ++failed >= s.X) return -1;
-      set_counter(x + 1 == s.X ? 0 : x + 1);
+      if (s.kind != pgs::kWorkStealingXcc || ++passed >= X) return -1;
+      // the counters after x not passed yet: read them all, then take the first
+      // that still has tiles
+      const int left = X - passed;
+      int seen[kMaxStealCounters];
+#pragma unroll
+      for (int j = 0; j < kMaxStealCounters; ++j) {
+        int c = x + 1 + j;
+        c = c >= X ? c - X : c;
+        seen[j] = j < left ? __hip_atomic_load(counter(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      }
+      int j = 0;
+      for (; j < left; ++j) {
+        int c = x + 1 + j;
+        c = c >= X ? c - X : c;
+        if (seen[j] < range_begin(c + 1) - range_begin(c)) break;
+      }
+      if (j == left) return -1;
+      passed += j;
+      const int c = x + 1 + j;
+      set_counter(c >= X ? c - X : c);
     }
   }
 
   // End (exclusive) of the claim that starts at tile v: v + chunk, cut at the
   // end of the counter range that holds v (any thread may call it).
   __device__ __forceinline__ int claim_end(int v) const {
-    const int X = s.X > 0 ? s.X : 1;
     const int e = v + s.chunk;
-    const int range_end = pgs::ws_range_begin(pgs::ws_owner(v, s.T, X) + 1, s.T, X);
+    const int range_end = range_begin(pgs::ws_owner(v, s.T, nx()) + 1);
     return e < range_end ? e : range_end;
   }
 

@@ -26,7 +26,7 @@ struct pgemm_config {
   int clock_khz;
   int lds_per_cu;
   char arch[64];
-  int* counters;  // device, [capacity]
+  int* counters;  // device, [capacity * pgk::kCounterStride]; counter x at x * kCounterStride
   float* ws;          // stream-K partial-sum workspace (device), grown on demand
   size_t ws_bytes;
   // witness buffers (device)
@@ -110,6 +110,7 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.wall_khz = cfg->wall_khz;
   if (s.G < 1 || s.gs < 1) return PGEMM_ERR_INVALID;
   if (s.kind == pgs::kWorkStealing && s.G < s.X) return PGEMM_ERR_INVALID;
+  if (s.kind == pgs::kWorkStealingXcc && s.X > pgk::kMaxStealCounters) return PGEMM_ERR_UNSUPPORTED;
   if (s.X < 1 || s.X > cfg->capacity) return PGEMM_ERR_INVALID;
   if (args && (args->debug_flags & PGEMM_DEBUG_STRAGGLER)) {
     if (args->straggler_ns < 0 || args->straggler_ns > 1000000000) return PGEMM_ERR_INVALID;
@@ -222,7 +223,7 @@ pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk
   if (!pgs::work_stealing(s.kind)) return PGEMM_OK;
   if (args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET)) return PGEMM_OK;
   // a fill kernel rather than a memset node, so that the call may be captured
-  return pgk::launch_zero_i32(cfg->counters, cfg->capacity, stream) == hipSuccess
+  return pgk::launch_zero_i32(cfg->counters, cfg->capacity * pgk::kCounterStride, stream) == hipSuccess
              ? PGEMM_OK
              : PGEMM_ERR_LAUNCH;
 }
@@ -294,8 +295,9 @@ pgemm_status pgemm_config_create(int device, int max_xcds, pgemm_config** out) {
   c->clock_khz = prop.clockRate;
   c->lds_per_cu = (int)prop.maxSharedMemoryPerMultiProcessor;
   strncpy(c->arch, prop.gcnArchName, sizeof(c->arch) - 1);
-  hipError_t e = hipMalloc((void**)&c->counters, sizeof(int) * cap);
-  if (e == hipSuccess) e = hipMemset(c->counters, 0, sizeof(int) * cap);
+  const size_t cbytes = sizeof(int) * (size_t)cap * pgk::kCounterStride;
+  hipError_t e = hipMalloc((void**)&c->counters, cbytes);
+  if (e == hipSuccess) e = hipMemset(c->counters, 0, cbytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     if (c->counters) (void)hipFree(c->counters);
@@ -373,12 +375,18 @@ pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip
       {out->order, cfg->w_order, 4 * t},        {out->t_start, cfg->w_t_start, 8 * p},
       {out->t_end, cfg->w_t_end, 8 * p},        {out->hw_id, cfg->w_hw_id, 4 * p},
       {out->cycles, cfg->w_cycles, 8 * p},
-      {out->n_tiles, cfg->w_n_tiles, 4 * p},    {out->counters, cfg->counters, 4 * (size_t)cfg->capacity},
+      {out->n_tiles, cfg->w_n_tiles, 4 * p},
   };
   for (const Copy& c : cps) {
     if (!c.dst || c.bytes == 0) continue;
     if (hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyDeviceToHost) != hipSuccess)
       return PGEMM_ERR_DEVICE;
+  }
+  if (out->counters) {  // one counter per 256-byte block on the device, dense in the output
+    for (int x = 0; x < cfg->capacity; ++x)
+      if (hipMemcpy(out->counters + x, cfg->counters + (size_t)x * pgk::kCounterStride, sizeof(int),
+                    hipMemcpyDeviceToHost) != hipSuccess)
+        return PGEMM_ERR_DEVICE;
   }
   return PGEMM_OK;
 }
