@@ -30,10 +30,10 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_CLOCK_GHZ = 2.4          # engine clock the dense peak is quoted at
 M = N = K = 8192
-SCHEDS = [("blocked", 8), ("interleaved", 8), ("grouped", 8), ("grouped", 16),
-          ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8), ("stream_k", 8),
-          ("work_stealing_xcc", 8)]
-HEADLINE = ("work_stealing", 8)
+SCHEDS = [("blocked", 8, 0), ("interleaved", 8, 0), ("grouped", 8, 0), ("grouped", 16, 0),
+          ("work_stealing", 8, 0), ("work_stealing", 16, 0), ("blocked_grouped", 8, 0), ("stream_k", 8, 0),
+          ("work_stealing_xcc", 8, 0), ("work_stealing", 8, -1), ("work_stealing_xcc", 8, -1)]
+HEADLINE = ("work_stealing", 8)   # key work_stealing_g8: one tile per claim, as on the pages
 CPU_ROWS = 4096
 
 # HBM traffic of one 8192^3 launch of the bf16 GEMM kernel, from two
@@ -102,6 +102,7 @@ def measured_clock(pg, cfg, A, B, C, key):
     the timed steps; median over programs of shader cycles / wall time."""
     import torch
     sched, gs = key.rsplit("_g", 1) if "_g" in key else (key, "8")
+    gs = gs.split("_")[0]
     if sched == "stream_k":
         return None  # no witness on the stream-K path
     a = pg.make_args(tile=(256, 256, 64), group_size=int(gs), debug_flags=pg._abi.DEBUG_WITNESS)
@@ -169,11 +170,12 @@ def main():
 
     only = set(s for s in args.only.split(",") if s)
     per = {}
-    for sched, gs in SCHEDS:
-        key = f"{sched}" + (f"_g{gs}" if sched != "blocked" and sched != "interleaved" else "")
+    for sched, gs, chunk in SCHEDS:
+        key = f"{sched}" + (f"_g{gs}" if sched != "blocked" and sched != "interleaved" else "") + \
+            ("_pairs" if chunk < 0 else f"_c{chunk}" if chunk else "")
         if only and sched not in only and key not in only:
             continue
-        a = pg.make_args(tile=(256, 256, 64), group_size=gs)
+        a = pg.make_args(tile=(256, 256, 64), group_size=gs, claim_chunk=chunk)
         fn = lambda: pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)  # noqa: E731
         ms, ev_mean, ev_min = time_calls(fn, args.steps, args.warmup, stream)
         per[key] = {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "event_ms_mean": ev_mean,
@@ -191,12 +193,14 @@ def main():
             rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
             row = {}
-            for sched in ["blocked", "interleaved", "grouped", "work_stealing", "blocked_grouped", "stream_k",
-                          "work_stealing_xcc"]:
-                a = pg.make_args(tile=(256, 256, 64))
+            for sched, chunk in [("blocked", 0), ("interleaved", 0), ("grouped", 0), ("work_stealing", 0),
+                                 ("blocked_grouped", 0), ("stream_k", 0), ("work_stealing_xcc", 0),
+                                 ("work_stealing", -1), ("work_stealing_xcc", -1)]:
+                a = pg.make_args(tile=(256, 256, 64), claim_chunk=chunk)
                 fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
                 _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
-                row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
+                row[sched + ("_pairs" if chunk < 0 else "")] = {
+                    "tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
             ragged[f"{m}x{n}x{k}"] = row
             print(f"# ragged {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
                   file=sys.stderr, flush=True)

@@ -122,13 +122,23 @@ typedef enum {
                                            straggler_ns before each tile (not with
                                            PGEMM_DEBUG_STRAGGLER: PGEMM_ERR_INVALID) */
 
+/* claim_chunk value for paired claims (GEMM, both work-stealing kinds): the
+ * counter counts claims; with P = ceil(G / X) programs per counter, a range of
+ * n tiles hands out pairs of consecutive tiles over its first
+ * L = 2 * min(n / 2, P * (ceil(n / P) / 2)) tiles and single tiles after
+ * that, so a program computes neighbouring tiles back to back while, with
+ * equal speeds, none gets more tiles than under single claims. */
+#define PGEMM_CLAIM_PAIRS (-1)
+
 /* Optional per-call arguments; pass NULL for all defaults. */
 typedef struct {
   int tile_m, tile_n, tile_k; /* 0 => default: bf16 256x256x64, fp8 256x256x128 */
   int group_size;             /* grouped order rows per group; 0 => 8 */
   int grid;                   /* programs; 0 => number of CUs x workgroups of the selected
                                  kernel one CU holds at once (see pgemm_plan_gemm) */
-  int claim_chunk;            /* add only: tiles per work-stealing claim; 0 => default */
+  int claim_chunk;            /* tiles per work-stealing claim (consecutive in the counter's
+                                 range); GEMM 1..64 or PGEMM_CLAIM_PAIRS, 0 => 1; add 1..U
+                                 (tiles a program handles per step), 0 => U */
   const uint8_t* a_scale;     /* fp8: device, e8m0 [K/128][M] */
   const uint8_t* b_scale;     /* fp8: device, e8m0 [K/128][N] */
   unsigned debug_flags;       /* PGEMM_DEBUG_* */

@@ -35,6 +35,13 @@ Sources:
   skips those already past their range, and claims from the first that is
   not; it stops when none is left.  So it makes exactly one failing claim on
   its home counter and at most one on any other.
+* Paired claims (an option of both work-stealing kinds, not on the pages,
+  which claim one tile at a time).  The counter then counts claims, and
+  claim k of a range of n tiles takes tiles 2k, 2k+1 while k < L/2 and the
+  single tile L + (k - L/2) after that, with P = ceil(G / X) programs per
+  counter and L = 2 * min(floor(n / 2), P * floor(ceil(n / P) / 2)): pairs
+  for as many whole rounds of two as the range holds, so with equal speeds
+  no program computes more tiles than with single claims.
 * Stream-K (the comparator "Work Stealing Scheduler Kernel", tritonBLAS PR
   #65, benchmarks work stealing against; the page names it only).  Reading
   taken: a data-parallel + stream-K hybrid in the spirit of the published
@@ -120,22 +127,61 @@ def ws_programs_per_xcd(G: int, X: int) -> List[int]:
     return [sum(1 for p in range(G) if p % X == x) for x in range(X)]
 
 
-def ws_final_counters(T: int, G: int, X: int, chunk: int = 1) -> List[int]:
+def ws_final_counters(T: int, G: int, X: int, chunk=1) -> List[int]:
     """Counter values after a complete launch: every successful claim and
-    exactly one failing claim per program each added ``chunk``."""
+    exactly one failing claim per program each added ``chunk`` (under
+    PAIRS the counter counts claims)."""
     out = []
     for (s, e), w in zip(ws_ranges(T, X), ws_programs_per_xcd(G, X)):
         n = e - s
-        out.append(chunk * (cdiv(n, chunk) + w))
+        out.append(pair_claims(n, G, X) + w if chunk == PAIRS else chunk * (cdiv(n, chunk) + w))
     return out
 
 
+PAIRS = "pairs"
+
+
+def pair_span(n: int, G: int, X: int) -> int:
+    """Paired claims: the first L tiles of a range of n go out in pairs."""
+    P = cdiv(G, X)
+    return 2 * min(n // 2, P * (cdiv(n, P) // 2))
+
+
+def pair_claims(n: int, G: int, X: int) -> int:
+    """Paired claims: successful claims a range of n tiles hands out."""
+    L = pair_span(n, G, X)
+    return L // 2 + (n - L)
+
+
+def pair_claim(k: int, n: int, G: int, X: int):
+    """Paired claims: tiles [first, end) of claim k (counted from 0) of a
+    range of n tiles, relative to the range's start, or None past the end."""
+    L = pair_span(n, G, X)
+    if k < L // 2:
+        return 2 * k, 2 * k + 2
+    t = L + (k - L // 2)
+    return (t, t + 1) if t < n else None
+
+
+def _take(chunk, cnt, x, n, G, X):
+    """One claim on counter x: the tiles it gets, relative to the range's
+    start, as (first, end), or None when the range is exhausted."""
+    if chunk == PAIRS:
+        k = cnt[x]
+        cnt[x] += 1
+        return pair_claim(k, n, G, X)
+    i = cnt[x]
+    cnt[x] += chunk
+    return (i, min(i + chunk, n)) if i < n else None
+
+
 def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
-                chunk: int = 1, seed: int = 0, speeds: Sequence[float] = None):
+                chunk=1, seed: int = 0, speeds: Sequence[float] = None):
     """One possible work-stealing execution.
 
     Programs run concurrently; the interleaving is drawn at random (or, with
     ``speeds``, the program with the earliest finish time claims next).
+    ``chunk`` is the tiles per claim, or PAIRS.
     Returns (per-program list of (v, pid_m, pid_n), final counters)."""
     T = num_pid_m * num_pid_n
     if G < X:
@@ -153,15 +199,14 @@ def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
             p = min(active, key=lambda q: (clock[q], q))
         x = p % X
         s, e = ranges[x]
-        i = cnt[x]
-        cnt[x] += chunk
-        if i >= e - s:
+        got = _take(chunk, cnt, x, e - s, G, X)
+        if got is None:
             active.remove(p)
             continue
-        for v in range(s + i, min(s + i + chunk, e)):
+        for v in range(s + got[0], s + got[1]):
             seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
         if speeds is not None:
-            clock[p] += speeds[p] * (min(i + chunk, e - s) - i)
+            clock[p] += speeds[p] * (got[1] - got[0])
     return seqs, cnt
 
 
@@ -174,21 +219,26 @@ def ws_owner(v: int, T: int, X: int) -> int:
 
 
 def wsx_counter_bounds(T: int, G: int, X: int, homes: Sequence[int],
-                       chunk: int = 1) -> List[Tuple[int, int]]:
+                       chunk=1) -> List[Tuple[int, int]]:
     """Bounds on the counters after a complete launch of work stealing across
     XCDs: every successful claim and each program's failing claim on its
     home counter (lower), plus at most one failing claim per program on
-    every other counter (upper); each claim adds ``chunk``."""
+    every other counter (upper); each claim adds ``chunk`` (under PAIRS the
+    counter counts claims)."""
     out = []
     for x, (s, e) in enumerate(ws_ranges(T, X)):
-        claims = cdiv(e - s, chunk)
+        n = e - s
         at_home = sum(1 for h in homes if h % X == x)
-        out.append((chunk * (claims + at_home), chunk * (claims + G)))
+        if chunk == PAIRS:
+            out.append((pair_claims(n, G, X) + at_home, pair_claims(n, G, X) + G))
+        else:
+            claims = cdiv(n, chunk)
+            out.append((chunk * (claims + at_home), chunk * (claims + G)))
     return out
 
 
 def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence[int],
-                 gs: int = 8, chunk: int = 1, seed: int = 0, speeds: Sequence[float] = None):
+                 gs: int = 8, chunk=1, seed: int = 0, speeds: Sequence[float] = None):
     """One possible execution of work stealing across XCDs.  ``homes[p]`` is
     the counter program p starts on.  The interleaving is random, or with
     ``speeds`` the program with the earliest clock (then the lowest id)
@@ -210,15 +260,15 @@ def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence
             p = min(active, key=lambda q: (clock[q], q))
         x = cur[p]
         s, e = ranges[x]
-        i = cnt[x]
-        cnt[x] += chunk
-        if i >= e - s:
+        got = _take(chunk, cnt, x, e - s, G, X)
+        if got is None:
             passed[p] += 1
             nxt = None
             for j in range(X - passed[p]):          # counters not passed yet, in order
                 c = (x + 1 + j) % X
                 cs, ce = ranges[c]
-                if cnt[c] < ce - cs:
+                left = pair_claims(ce - cs, G, X) if chunk == PAIRS else ce - cs
+                if cnt[c] < left:
                     nxt = (j, c)
                     break
             if nxt is None:
@@ -227,16 +277,16 @@ def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence
                 passed[p] += nxt[0]
                 cur[p] = nxt[1]
             continue
-        for v in range(s + i, min(s + i + chunk, e)):
+        for v in range(s + got[0], s + got[1]):
             seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
         if speeds is not None:
-            clock[p] += speeds[p] * (min(i + chunk, e - s) - i)
+            clock[p] += speeds[p] * (got[1] - got[0])
     return seqs, cnt
 
 
 def check_wsx_execution(visits: Sequence[int], owner: Sequence[int], local_order: Sequence[int],
                         counters: Sequence[int], homes: Sequence[int], T: int, G: int, X: int,
-                        chunk: int = 1) -> None:
+                        chunk=1) -> None:
     """Invariants of every correct launch of work stealing across XCDs.
     visits / owner / local_order are indexed by tile id; homes[p] is the
     counter program p started on."""
@@ -288,7 +338,7 @@ def check_partition(seqs: Sequence[Sequence[Tuple[int, int, int]]],
 
 def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
                        local_order: Sequence[int], counters: Sequence[int],
-                       T: int, G: int, X: int, chunk: int = 1) -> None:
+                       T: int, G: int, X: int, chunk=1) -> None:
     """Invariants every correct work-stealing launch satisfies (the exact
     assignment depends on timing).  Arrays are indexed by tile id v:
     visits[v] = times computed, owner[v] = program, local_order[v] = its

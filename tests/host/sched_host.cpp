@@ -28,6 +28,20 @@ static int static_walk(int kind, int pm, int pn, int G, int gs) {
   return 0;
 }
 
+// One claim on `c` for a range of n tiles: [first, end) relative to the
+// range's start, or false when the range is exhausted.  chunk < 0: paired
+// claims (the counter counts claims, pgs::pair_claim maps them to tiles).
+static bool take(std::atomic<int>& c, int n, int chunk, int G, int X, int& first, int& end) {
+  if (chunk < 0) {
+    const int k = c.fetch_add(1, std::memory_order_relaxed);
+    return pgs::pair_claim(k, n, G, X, first, end);
+  }
+  const int i = c.fetch_add(chunk, std::memory_order_relaxed);
+  first = i;
+  end = i + chunk < n ? i + chunk : n;
+  return i < n;
+}
+
 // G threads claim from X atomic counters exactly as the kernels do.
 static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
   const int T = pm * pn;
@@ -44,9 +58,9 @@ static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
       const int n = pgs::ws_range_begin(x + 1, T, X) - begin;
       int done = 0;
       for (;;) {
-        const int i = cnt[x].fetch_add(chunk, std::memory_order_relaxed);
-        if (i >= n) break;
-        for (int v = begin + i; v < begin + (i + chunk < n ? i + chunk : n); ++v) {
+        int f, e;
+        if (!take(cnt[x], n, chunk, G, X, f, e)) break;
+        for (int v = begin + f; v < begin + e; ++v) {
           visits[v].fetch_add(1);
           owner[v] = p;
           order[v] = done++;
@@ -89,23 +103,25 @@ static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
       for (;;) {
         const int begin = pgs::ws_range_begin(x, T, X);
         const int n = range_n(x);
-        const int i = cnt[x].fetch_add(chunk, std::memory_order_relaxed);
-        if (i >= n) {
+        int f, e;
+        if (!take(cnt[x], n, chunk, G, X, f, e)) {
           if (++passed >= X) break;
           const int left = X - passed;
           std::vector<int> seen(left);
           for (int j = 0; j < left; ++j) seen[j] = cnt[(x + 1 + j) % X].load(std::memory_order_relaxed);
+          auto claims_of = [&](int m) { return chunk < 0 ? pgs::pair_claims(m, G, X) : m; };
           int j = 0;
-          while (j < left && seen[j] >= range_n((x + 1 + j) % X)) ++j;
+          while (j < left && seen[j] >= claims_of(range_n((x + 1 + j) % X))) ++j;
           if (j == left) break;
           passed += j;
           x = (x + 1 + j) % X;
           continue;
         }
-        const int v0 = begin + i;
+        // the end is cut at the end of the range holding the first tile
+        const int v0 = begin + f;
         const int range_end = pgs::ws_range_begin(pgs::ws_owner(v0, T, X) + 1, T, X);
-        const int e = v0 + chunk < range_end ? v0 + chunk : range_end;
-        for (int v = v0; v < e; ++v) {
+        const int ve = begin + e < range_end ? begin + e : range_end;
+        for (int v = v0; v < ve; ++v) {
           visits[v].fetch_add(1);
           owner[v] = p;
           order[v] = done++;
@@ -150,6 +166,22 @@ static int sk_walk(int T, int nk, int G) {
   return 0;
 }
 
+// Paired-claim map for ranges of 0..139 tiles: n, L, claims, then each
+// claim's first and end.
+static int pairs_map(int G, int X) {
+  for (int n = 0; n < 140; ++n) {
+    const int claims = pgs::pair_claims(n, G, X);
+    std::printf("%d %d %d", n, pgs::pair_span(n, G, X), claims);
+    for (int k = 0; k < claims; ++k) {
+      int f, e;
+      if (!pgs::pair_claim(k, n, G, X, f, e)) return 1;
+      std::printf(" %d %d", f, e);
+    }
+    std::printf("\n");
+  }
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc < 2) return 2;
   const std::string mode = argv[1];
@@ -162,6 +194,7 @@ int main(int argc, char** argv) {
   if (mode == "wsx" && argc == 8)
     return wsx_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                        std::atoi(argv[6]), std::atoi(argv[7]));
+  if (mode == "pairs" && argc == 4) return pairs_map(std::atoi(argv[2]), std::atoi(argv[3]));
   if (mode == "sk" && argc == 5)
     return sk_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   return 2;

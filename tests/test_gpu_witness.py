@@ -75,6 +75,32 @@ def test_gemm_schedule_exactly_once(sched, shape, tile):
     _check(w, sched, pm, pn, G, X, 8)
 
 
+@pytest.mark.parametrize("sched", WS)
+@pytest.mark.parametrize("chunk", [2, 3, pg._abi.CLAIM_PAIRS])
+@pytest.mark.parametrize("shape,tile", [((5120, 5120, 128), (256, 256, 64)),
+                                        ((4864, 8000, 64), (256, 256, 64)),
+                                        ((1100, 904, 64), (128, 128, 64))])
+def test_gemm_chunked_claims(sched, chunk, shape, tile):
+    """Claims of several consecutive tiles: every tile once, the claim order
+    and the final counters of the model with that chunk; same C as grouped."""
+    M, N, K = shape
+    cfg = config()
+    G = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched, pg.make_args(tile=tile))["grid"]
+    pm, pn = -(-M // tile[0]), -(-N // tile[1])
+    cfg.witness_enable(pm * pn, G)
+    A, B = dev_bf16(bf16_bits_uniform((M, K), 1)), dev_bf16(bf16_bits_uniform((K, N), 2))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    note(f"chunked claims {shape} tile={tile} {sched} chunk={chunk} grid={G}")
+    pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched,
+                 pg.make_args(tile=tile, claim_chunk=chunk, debug_flags=pg._abi.DEBUG_WITNESS))
+    w = cfg.witness_read(pm * pn, G)
+    _check(w, sched, pm, pn, G, cfg.info["num_xcds"], 8, sm.PAIRS if chunk < 0 else chunk)
+    Cg = torch.empty_like(C)
+    pg.pgemm_run(cfg, A, B, Cg, M, N, K, "bf16_out_bf16", "grouped", pg.make_args(tile=tile))
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), Cg.view(torch.int16))
+
+
 def test_gemm_witness_clock():
     """Per-program shader cycles over wall time give a plausible engine clock."""
     w, pm, pn, G, X = _gemm_witness(5120, 5120, 2048, (256, 256, 64), "work_stealing")

@@ -43,7 +43,8 @@ def test_static_walk_matches_model(harness, kind):
 
 @pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1),
                                              (19, 32, 256, 8, 1), (33, 7, 64, 8, 4),
-                                             (1, 1, 16, 8, 1)])
+                                             (1, 1, 16, 8, 1), (19, 32, 256, 8, -1),
+                                             (20, 20, 256, 8, -1), (5, 2, 4, 2, -1)])
 def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     out = subprocess.run([harness, "ws", str(pm), str(pn), str(G), str(X), "8", str(chunk)],
                          check=True, capture_output=True, text=True).stdout.strip().splitlines()
@@ -54,12 +55,12 @@ def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     visits = [r[1] for r in rows]
     owner = [r[2] for r in rows]
     order = [r[3] for r in rows]
-    sm.check_ws_execution(visits, owner, order, counters, T, G, X, chunk)
+    sm.check_ws_execution(visits, owner, order, counters, T, G, X, sm.PAIRS if chunk < 0 else chunk)
 
 
 @pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (19, 32, 256, 8, 1),
                                              (33, 7, 64, 8, 4), (1, 1, 16, 8, 1), (3, 1, 5, 8, 1),
-                                             (13, 11, 3, 8, 2)])
+                                             (13, 11, 3, 8, 2), (19, 32, 256, 8, -1), (13, 11, 3, 8, -1)])
 @pytest.mark.parametrize("home_mode", [0, 1, 2])
 def test_wsx_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk, home_mode):
     out = subprocess.run([harness, "wsx", str(pm), str(pn), str(G), str(X), str(chunk), str(home_mode)],
@@ -70,7 +71,7 @@ def test_wsx_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk, home
     rows = [tuple(map(int, l.split())) for l in out[2:]]
     assert len(rows) == T and len(homes) == G
     sm.check_wsx_execution([r[1] for r in rows], [r[2] for r in rows], [r[3] for r in rows],
-                           counters, homes, T, G, X, chunk)
+                           counters, homes, T, G, X, sm.PAIRS if chunk < 0 else chunk)
 
 
 @pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),
@@ -100,3 +101,13 @@ def test_streamk_walk_matches_model(harness, T, nk, G):
         head, _, rest = line.partition(":")
         split[int(head.split()[1])] = [tuple(map(int, t.split(","))) for t in rest.split()]
     assert split == want
+
+
+def test_pair_claim_map_matches_model(harness):
+    out = subprocess.run([harness, "pairs", "256", "8"], check=True, capture_output=True,
+                         text=True).stdout.strip().splitlines()
+    for line in out:
+        n, L, claims, *tiles = map(int, line.split())
+        assert L == sm.pair_span(n, 256, 8) and claims == sm.pair_claims(n, 256, 8), n
+        want = [t for k in range(claims) for t in sm.pair_claim(k, n, 256, 8)]
+        assert tiles == want, n

@@ -281,3 +281,85 @@ def test_wsx_checker_catches_planted_mistakes():
     with pytest.raises(AssertionError):
         sm.check_wsx_execution(v, o, r, cnt, [(h + 1) % X if q == p else h
                                               for q, h in enumerate(homes)], T, G, X)
+
+
+# ---- paired claims ----
+
+def test_ws_pairs_golden(golden):
+    rows = [r.split() for r in golden("ws_pairs_T10_X2_G4.txt")]
+    want = {}
+    for r in rows:
+        if r[0] == "counters":
+            counters = list(map(int, r[1:]))
+            continue
+        p, v, m, n = map(int, r)
+        want.setdefault(p, []).append((v, m, n))
+    seqs, cnt = sm.ws_simulate(5, 2, 4, 2, chunk=sm.PAIRS, speeds=[1, 1, 1, 1])
+    assert {p: s for p, s in enumerate(seqs)} == want
+    assert cnt == counters
+
+
+def test_pair_claim_map():
+    # P = ceil(256 / 8) = 32 programs per counter
+    assert sm.pair_span(128, 256, 8) == 128        # four rounds: all pairs
+    assert sm.pair_span(76, 256, 8) == 64          # three rounds: one round of pairs
+    assert sm.pair_span(50, 256, 8) == 50          # two rounds: all pairs
+    assert sm.pair_span(32, 256, 8) == 0           # one round: singles
+    assert sm.pair_span(33, 256, 8) == 32
+    assert sm.pair_claims(76, 256, 8) == 32 + 12
+    assert [sm.pair_claim(k, 76, 256, 8) for k in (0, 31, 32, 43, 44)] == \
+        [(0, 2), (62, 64), (64, 65), (75, 76), None]
+    # every tile of a range exactly once, in order
+    for n in range(0, 140):
+        tiles = [t for k in range(sm.pair_claims(n, 256, 8))
+                 for t in range(*sm.pair_claim(k, n, 256, 8))]
+        assert tiles == list(range(n))
+        assert sm.pair_claim(sm.pair_claims(n, 256, 8), n, 256, 8) is None
+
+
+@pytest.mark.parametrize("pm,pn,G,X", [(4, 4, 8, 4), (16, 16, 256, 8), (20, 20, 256, 8),
+                                       (19, 32, 256, 8), (12, 28, 256, 8), (5, 7, 9, 8)])
+def test_pairs_simulated_invariants(pm, pn, G, X):
+    T = pm * pn
+    for seed in range(3):
+        seqs, cnt = sm.ws_simulate(pm, pn, G, X, chunk=sm.PAIRS, seed=seed)
+        sm.check_partition(seqs, pm, pn)
+        v, o, r = _wsx_arrays(seqs, T)
+        sm.check_ws_execution(v, o, r, cnt, T, G, X, sm.PAIRS)
+        homes = [random.Random(seed).randrange(X) for _ in range(G)]
+        seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, chunk=sm.PAIRS, seed=seed)
+        sm.check_partition(seqs, pm, pn)
+        v, o, r = _wsx_arrays(seqs, T)
+        sm.check_wsx_execution(v, o, r, cnt, homes, T, G, X, sm.PAIRS)
+
+
+def test_pairs_keep_the_makespan_of_single_claims():
+    # equal speeds: no program computes more tiles than under single claims,
+    # and for 1.3-2.4 rounds per XCD most tiles come in consecutive pairs
+    for pm, pn in [(20, 20), (19, 32), (12, 28), (32, 32)]:
+        G, X = 256, 8
+        one, _ = sm.ws_simulate(pm, pn, G, X, chunk=1, speeds=[1] * G)
+        two, _ = sm.ws_simulate(pm, pn, G, X, chunk=sm.PAIRS, speeds=[1] * G)
+        assert max(map(len, two)) == max(map(len, one)), (pm, pn)
+        paired = sum(1 for s in two for a, b in zip(s, s[1:]) if b[0] == a[0] + 1)
+        assert paired >= (pm * pn) // 4, (pm, pn, paired)
+    # fixed pairs lose a round where a range is just over two rounds
+    fixed, _ = sm.ws_simulate(19, 32, 256, 8, chunk=2, speeds=[1] * 256)
+    one, _ = sm.ws_simulate(19, 32, 256, 8, chunk=1, speeds=[1] * 256)
+    assert max(map(len, fixed)) > max(map(len, one))
+
+
+def test_pairs_checker_catches_planted_mistakes():
+    pm, pn, G, X = 5, 2, 4, 2
+    T = pm * pn
+    seqs, cnt = sm.ws_simulate(pm, pn, G, X, chunk=sm.PAIRS, speeds=[1] * G)
+    v, o, r = _wsx_arrays(seqs, T)
+    sm.check_ws_execution(v, o, r, cnt, T, G, X, sm.PAIRS)
+    with pytest.raises(AssertionError):                     # one failing claim too many
+        sm.check_ws_execution(v, o, r, [cnt[0] + 1, cnt[1]], T, G, X, sm.PAIRS)
+    with pytest.raises(AssertionError):                     # a program's failing claim missing
+        sm.check_ws_execution(v, o, r, [cnt[0] - 1, cnt[1]], T, G, X, sm.PAIRS)
+    with pytest.raises(AssertionError):                     # a pair split across programs
+        o2 = list(o)
+        o2[1] = 2
+        sm.check_ws_execution(v, o2, r, cnt, T, G, X, sm.PAIRS)

@@ -175,6 +175,7 @@ struct Walker {
   int x;         // work stealing: current counter
   int passed;    // work stealing across XCDs: counters passed (home first)
   int begin, n;  // work stealing: counter x's range [begin, begin + n)
+  int cend;      // work stealing: end of the last claim (next() walks up to it)
 
   __device__ __forceinline__ int nx() const { return s.X > 0 ? s.X : 1; }
   __device__ __forceinline__ int range_begin(int c) const { return pgs::ws_range_begin(c, s.T, nx()); }
@@ -189,17 +190,34 @@ struct Walker {
   __device__ __forceinline__ Walker(const SchedParams& sp, int prog) : s(sp), p(prog) {
     end = 0;
     passed = 0;
+    cend = 0;
     const int X = nx();
     set_counter(sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X);
   }
 
-  // Claims of s.chunk tiles; returns the first claimed id or -1.
+  // Claims handed out by a range of m tiles (s.chunk < 0: paired claims).
+  __device__ __forceinline__ int claims_of(int m) const {
+    return s.chunk < 0 ? pgs::pair_claims(m, s.G, nx()) : m;
+  }
+
+  // One claim (s.chunk tiles, or a pair / single under paired claims);
+  // returns the first claimed id or -1, and sets cend to the claim's end.
   __device__ __forceinline__ int claim() {
     const int X = nx();
     for (;;) {
-      const int i = __hip_atomic_fetch_add(counter(x), s.chunk, __ATOMIC_RELAXED,
+      const int step = s.chunk < 0 ? 1 : s.chunk;
+      const int i = __hip_atomic_fetch_add(counter(x), step, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-      if (i >= 0 && i < n) return begin + i;
+      if (s.chunk < 0) {
+        int f, e;
+        if (i >= 0 && pgs::pair_claim(i, n, s.G, X, f, e)) {
+          cend = begin + e;
+          return begin + f;
+        }
+      } else if (i >= 0 && i < n) {
+        cend = claim_end(begin + i);
+        return begin + i;
+      }
       if (s.kind != pgs::kWorkStealingXcc || ++passed >= X) return -1;
       // the counters after x not passed yet: read them all, then take the first
       // that still has tiles
@@ -215,7 +233,7 @@ struct Walker {
       for (; j < left; ++j) {
         int c = x + 1 + j;
         c = c >= X ? c - X : c;
-        if (seen[j] < range_begin(c + 1) - range_begin(c)) break;
+        if (seen[j] < claims_of(range_begin(c + 1) - range_begin(c))) break;
       }
       if (j == left) return -1;
       passed += j;
@@ -239,8 +257,9 @@ struct Walker {
     return v < end ? v : -1;
   }
 
+  // The tile after v: the next one of the current claim, else a new claim.
   __device__ __forceinline__ int next(int v) {
-    if (pgs::work_stealing(s.kind)) return claim();
+    if (pgs::work_stealing(s.kind)) return v + 1 < cend ? v + 1 : claim();
     const int nv = pgs::static_next(s.kind, v, s.G, end);
     return nv < end ? nv : -1;
   }

@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kDefaultMaxXcds = 16;
 constexpr int kDefaultGroup = 8;
+constexpr int kMaxGemmChunk = 64;  // tiles per work-stealing claim, GEMM
 
 pgemm_status from_hip(hipError_t e) {
   if (e == hipSuccess) return PGEMM_OK;
@@ -104,6 +105,14 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.num_pid_n = num_pid_n;
   s.counters = cfg->counters;
   s.chunk = 1;
+  if (args && args->claim_chunk) {
+    if (args->claim_chunk == PGEMM_CLAIM_PAIRS)
+      s.chunk = -1;
+    else if (args->claim_chunk < 1 || args->claim_chunk > kMaxGemmChunk)
+      return PGEMM_ERR_INVALID;
+    else
+      s.chunk = args->claim_chunk;
+  }
   s.straggler_program = -1;
   s.straggler_ns = 0;
   s.straggler_xcc = 0;
@@ -516,6 +525,7 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
   if (st != PGEMM_OK) return st;
   const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
   p.s.chunk = step;
+  if (args && args->claim_chunk == PGEMM_CLAIM_PAIRS) return PGEMM_ERR_UNSUPPORTED;
   if (args && args->claim_chunk) {
     if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
     p.s.chunk = args->claim_chunk;

@@ -81,6 +81,37 @@ PGS_FN int ws_range_begin(int x, int T, int X) {
   return (int)(((int64_t)x * (int64_t)T) / (int64_t)X);
 }
 
+// Paired claims (work-stealing option): the counter counts claims, and claim
+// k of a range of n tiles takes tiles 2k, 2k+1 while k < L/2, then the single
+// tile L + (k - L/2), where P = ceil(G / X) programs share a counter and
+// L = 2 * min(n / 2, P * (ceil(n / P) / 2)): pairs for as many whole rounds of
+// two as the range holds, so with equal speeds no program gets more tiles
+// than with single claims.
+PGS_FN int pair_span(int n, int G, int X) {
+  const int P = cdiv(G, X);
+  const int a = n / 2, b = P * (cdiv(n, P) / 2);
+  return 2 * (a < b ? a : b);
+}
+
+PGS_FN int pair_claims(int n, int G, int X) {
+  const int L = pair_span(n, G, X);
+  return L / 2 + (n - L);
+}
+
+// Tiles [first, end) of claim k, relative to the range's start; false past
+// the end of the range.
+PGS_FN bool pair_claim(int k, int n, int G, int X, int& first, int& end) {
+  const int L = pair_span(n, G, X);
+  if (k < L / 2) {
+    first = 2 * k;
+    end = first + 2;
+    return true;
+  }
+  first = L + (k - L / 2);
+  end = first + 1;
+  return first < n;
+}
+
 // Counter (XCD range) holding tile id v: the largest x with
 // ws_range_begin(x) <= v.
 PGS_FN int ws_owner(int v, int T, int X) {
