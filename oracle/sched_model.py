@@ -35,6 +35,14 @@ Sources:
   skips those already past their range, and claims from the first that is
   not; it stops when none is left.  So it makes exactly one failing claim on
   its home counter and at most one on any other.
+* Several problems in one launch: "Implement persistent kernels" (Helion PR
+  #238), example output, PERSISTENT BLOCKED / INTERLEAVED WITH FOR EACH
+  PROGRAM ID (Multi-loop): the tiles of two problems share one virtual id
+  space, the first problem's ids first; an id past the first problem's tile
+  count is reduced by that count and decoded in the second.  Generalised
+  here to several problems by prefix sums of their tile counts; any
+  scheduler walks the shared space, and the id within a problem is decoded
+  as that scheduler decodes a single problem.
 * Paired claims (an option of both work-stealing kinds, not on the pages,
   which claim one tile at a time).  The counter then counts claims, and
   claim k of a range of n tiles takes tiles 2k, 2k+1 while k < L/2 and the
@@ -117,6 +125,56 @@ def static_schedule(kind: str, num_pid_m: int, num_pid_n: int, G: int,
             raise ValueError(kind)
         out.append([(v,) + decode(kind, v, num_pid_m, num_pid_n, gs) for v in vs])
     return out
+
+
+def multi_offsets(grids: Sequence[Tuple[int, int]]) -> List[int]:
+    """Prefix sums of the problems' tile counts: problem g owns virtual ids
+    [offsets[g], offsets[g + 1])."""
+    out = [0]
+    for pm, pn in grids:
+        out.append(out[-1] + pm * pn)
+    return out
+
+
+def multi_decode(kind: str, v: int, grids: Sequence[Tuple[int, int]], gs: int = 8) -> Tuple[int, int, int]:
+    """Virtual id v of the shared space -> (problem, pid_m, pid_n)."""
+    off = multi_offsets(grids)
+    g = 0
+    while v >= off[g + 1]:           # the ids of the problems before g are skipped
+        g += 1
+    pm, pn = grids[g]
+    return (g,) + decode(kind, v - off[g], pm, pn, gs)
+
+
+def multi_static_schedule(kind: str, grids: Sequence[Tuple[int, int]], G: int,
+                          gs: int = 8) -> List[List[Tuple[int, int, int, int]]]:
+    """Per program p, the ordered (v, problem, pid_m, pid_n) it computes."""
+    T = multi_offsets(grids)[-1]
+    out = []
+    for p in range(G):
+        if kind in (BLOCKED, BLOCKED_GROUPED):
+            vs = blocked_vpids(p, T, G)
+        elif kind in (INTERLEAVED, GROUPED):
+            vs = interleaved_vpids(p, T, G)
+        else:
+            raise ValueError(kind)
+        out.append([(v,) + multi_decode(kind, v, grids, gs) for v in vs])
+    return out
+
+
+def check_multi_partition(seqs, grids: Sequence[Tuple[int, int]]) -> None:
+    """Every tile of every problem computed exactly once."""
+    seen = {}
+    for p, seq in enumerate(seqs):
+        for v, g, pm, pn in seq:
+            if not (0 <= g < len(grids)) or not (0 <= pm < grids[g][0] and 0 <= pn < grids[g][1]):
+                raise AssertionError(f"program {p}: tile {(g, pm, pn)} outside its problem")
+            if (g, pm, pn) in seen:
+                raise AssertionError(f"tile {(g, pm, pn)} computed by {seen[(g, pm, pn)]} and {p}")
+            seen[(g, pm, pn)] = p
+    want = sum(pm * pn for pm, pn in grids)
+    if len(seen) != want:
+        raise AssertionError(f"{want - len(seen)} tiles never computed")
 
 
 def ws_ranges(T: int, X: int) -> List[Tuple[int, int]]:

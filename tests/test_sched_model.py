@@ -363,3 +363,43 @@ def test_pairs_checker_catches_planted_mistakes():
         o2 = list(o)
         o2[1] = 2
         sm.check_ws_execution(v, o2, r, cnt, T, G, X, sm.PAIRS)
+
+
+# ---- several problems in one launch ----
+
+def test_multi_blocked_golden(golden):
+    want = {}
+    for r in golden("multi_blocked_2problems_G4.txt"):
+        p, v, g, m, n = map(int, r.split())
+        want.setdefault(p, []).append((v, g, m, n))
+    got = sm.multi_static_schedule("blocked", [(3, 2), (2, 2)], 4)
+    assert {p: s for p, s in enumerate(got)} == want
+
+
+def test_multi_decode_reduces_to_single_problem():
+    # one problem: the shared space is the problem's own
+    for kind in sm.STATIC_KINDS:
+        for v in range(13 * 7):
+            assert sm.multi_decode(kind, v, [(13, 7)], 4) == (0,) + sm.decode(kind, v, 13, 7, 4)
+    # an empty problem takes no ids
+    assert sm.multi_offsets([(2, 3), (0, 5), (1, 1)]) == [0, 6, 6, 7]
+    assert sm.multi_decode("blocked", 6, [(2, 3), (0, 5), (1, 1)]) == (2, 0, 0)
+
+
+@pytest.mark.parametrize("kind", sm.STATIC_KINDS)
+@pytest.mark.parametrize("G", [1, 7, 256])
+def test_multi_partition(kind, G):
+    for grids in ([(3, 2), (2, 2)], [(1, 1)] * 5, [(17, 9), (0, 3), (4, 40), (33, 1)]):
+        sm.check_multi_partition(sm.multi_static_schedule(kind, grids, G, 3), grids)
+
+
+def test_multi_checker_catches_planted_mistakes():
+    grids = [(3, 2), (2, 2)]
+    seqs = [list(s) for s in sm.multi_static_schedule("interleaved", grids, 3)]
+    seqs[0][0] = (0, 1, 0, 0)                 # problem 0's first tile decoded in problem 1
+    with pytest.raises(AssertionError):
+        sm.check_multi_partition(seqs, grids)
+    seqs = [list(s) for s in sm.multi_static_schedule("interleaved", grids, 3)]
+    seqs[2].pop()                              # a tile dropped
+    with pytest.raises(AssertionError):
+        sm.check_multi_partition(seqs, grids)
