@@ -293,6 +293,31 @@ def main():
                 print(f"# add {tile} {sched}: {nbytes / (ev_mean * 1e-3) / 1e9:.0f} GB/s",
                       file=sys.stderr, flush=True)
 
+    # several adds in one persistent launch against one launch per add
+    multi_add = {}
+    if not args.skip_add:
+        shapes = [(4096, 4096), (2048, 8192), (8192, 1024), (1000, 3000), (513, 700)]
+        ops = []
+        for g, (r, c) in enumerate(shapes):
+            x = torch.from_numpy(f32_normal((r, c), 2100 + 2 * g)).to("cuda:0")
+            y = torch.from_numpy(f32_normal((r, c), 2101 + 2 * g)).to("cuda:0")
+            ops.append((x, y, torch.empty_like(x), r, c))
+        nbytes = sum(3 * r * c * 4 for r, c in shapes)
+        for tile in [(32, 16), (128, 128)]:
+            for sched in ["blocked", "work_stealing"]:
+                fn = lambda: pg.padd_run_multi(cfg, ops, tile[0], tile[1], sched)  # noqa: E731
+                _, ev_multi, _ = time_calls(fn, max(args.steps, 20), args.warmup, stream)
+
+                def separate():
+                    for o in ops:
+                        pg.padd_run(cfg, *o, tile[0], tile[1], sched)
+                _, ev_sep, _ = time_calls(separate, max(args.steps, 20), args.warmup, stream)
+                multi_add[f"{tile[0]}x{tile[1]}_{sched}"] = {
+                    "one_launch_gbs": round(nbytes / (ev_multi * 1e-3) / 1e9, 1),
+                    "one_launch_per_add_gbs": round(nbytes / (ev_sep * 1e-3) / 1e9, 1)}
+        print(f"# several adds ({len(shapes)} problems): {multi_add}", file=sys.stderr, flush=True)
+        del ops
+
     head_key = f"{HEADLINE[0]}_g{HEADLINE[1]}"
     if head_key not in per:
         head_key = next(iter(per))
@@ -334,6 +359,7 @@ def main():
         "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                 for k, v in add.items()},
         "ragged": ragged,
+        "multi_add": multi_add,
         "skinny": skinny,
         "slow_xcc": slow_xcc,
         "fp8": fp8,

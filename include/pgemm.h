@@ -98,7 +98,7 @@ typedef enum {
  *                   when none is left.  Every tile is still computed exactly
  *                   once and completion does not depend on placement (any
  *                   G >= 1); a program makes one failing claim on its home
- *                   counter and at most one on each other.  Needs X <= 16
+ *                   counter and at most one on each other.  Needs X <= 8
  *                   (PGEMM_ERR_UNSUPPORTED otherwise). */
 typedef enum {
   PGEMM_SCHED_BLOCKED = 0,
@@ -196,6 +196,31 @@ PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B
 PGEMM_API pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* C,
                       int64_t rows, int64_t cols, int tile_rows, int tile_cols,
                       pgemm_sched sched, const pgemm_args* args, void* hip_stream);
+
+/* Several adds in one persistent launch ("Implement persistent kernels",
+ * Helion PR #238, the multi-loop listings: two problems share one virtual
+ * program-id space, ids past the first problem's tile count are reduced by
+ * it and decoded in the second).  Here up to PADD_MAX_PROBLEMS problems:
+ * problem g owns the virtual tile ids from the sum of the earlier problems'
+ * tile counts on; the scheduler walks the shared space (work stealing: the
+ * XCD ranges split the shared space) and each id is decoded within its
+ * problem as padd_run decodes a single problem.  `problems` is a host array
+ * of `count` entries (1..PADD_MAX_PROBLEMS), read during the call.  rows or
+ * cols may be 0 (the problem has no tiles).  Each C may alias its own X or
+ * Y exactly; any other overlap of a C with a buffer of any problem is
+ * PGEMM_ERR_INVALID (the order of problems is not defined).  The witness
+ * indexes tiles by virtual id. */
+#define PADD_MAX_PROBLEMS 8
+typedef struct {
+  const float* X;  /* device, [rows][cols] */
+  const float* Y;  /* device, [rows][cols] */
+  float* C;        /* device, [rows][cols] */
+  int64_t rows, cols;
+} padd_problem;
+
+PGEMM_API pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int count,
+                            int tile_rows, int tile_cols, pgemm_sched sched,
+                            const pgemm_args* args, void* hip_stream);
 
 /* Witness buffers for PGEMM_DEBUG_WITNESS launches: per tile (up to
  * max_tiles) visit count, owner program and position in the owner's

@@ -31,8 +31,8 @@ DTYPES = {
     "fp8_b128_out_bf16": _abi.FP8E4M3_B128_OUT_BF16,
 }
 
-__all__ = ["Config", "pgemm_run", "padd_run", "plan_gemm", "plan_add", "SCHEDULERS", "DTYPES", "PgemmError", "status_str",
-           "make_args"]
+__all__ = ["Config", "pgemm_run", "padd_run", "padd_run_multi", "plan_gemm", "plan_add", "SCHEDULERS",
+           "DTYPES", "PgemmError", "status_str", "make_args"]
 
 
 def _check(where, code):
@@ -196,3 +196,21 @@ def padd_run(cfg: Config, X, Y, C, rows: int, cols: int, tile_rows: int, tile_co
                                int(rows), int(cols), int(tile_rows), int(tile_cols), _sched(sched),
                                ctypes.byref(args) if args is not None else None, _stream(stream))
     _check("padd_run", code)
+
+
+def padd_run_multi(cfg: Config, problems, tile_rows: int, tile_cols: int, sched, args=None,
+                   stream=None):
+    """Several adds C_g = X_g + Y_g (fp32) in one persistent launch; `problems`
+    is a sequence of (X, Y, C, rows, cols)."""
+    n = len(problems)
+    arr = (_abi.padd_problem * max(n, 1))()
+    for g, (X, Y, C, rows, cols) in enumerate(problems):
+        arr[g].X = _ptr(X, f"X[{g}]")
+        arr[g].Y = _ptr(Y, f"Y[{g}]")
+        arr[g].C = _ptr(C, f"C[{g}]")
+        arr[g].rows = int(rows)
+        arr[g].cols = int(cols)
+    code = _abi.lib().padd_run_multi(cfg.handle, arr, n, int(tile_rows), int(tile_cols), _sched(sched),
+                                     ctypes.byref(args) if args is not None else None, _stream(stream))
+    _check("padd_run_multi", code)
+

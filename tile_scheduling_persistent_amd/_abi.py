@@ -65,6 +65,14 @@ class pgemm_plan(ctypes.Structure):
     ]
 
 
+PADD_MAX_PROBLEMS = 8
+
+
+class padd_problem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
 _cfg_p = ctypes.c_void_p
 _lib = None
 
@@ -95,6 +103,10 @@ def lib() -> ctypes.CDLL:
                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                            ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.c_void_p]
     L.padd_run.restype = st
+    L.padd_run_multi.argtypes = [_cfg_p, ctypes.POINTER(padd_problem), ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, ctypes.POINTER(pgemm_args),
+                                 ctypes.c_void_p]
+    L.padd_run_multi.restype = st
     L.pgemm_witness_enable.argtypes = [_cfg_p, ctypes.c_int64, ctypes.c_int]
     L.pgemm_witness_enable.restype = st
     L.pgemm_witness_read.argtypes = [_cfg_p, ctypes.POINTER(pgemm_witness), ctypes.c_void_p]

@@ -26,8 +26,9 @@ struct Witness {
 // block per counter, so claims on different counters never contend for one
 // cache line at the point where device-scope atomics are performed.
 constexpr int kCounterStride = 64;
-// Counters work stealing across XCDs can look at in one pass.
-constexpr int kMaxStealCounters = 16;
+// Counters work stealing across XCDs can look at in one pass (the XCDs of
+// one MI355X).
+constexpr int kMaxStealCounters = 8;
 
 struct SchedParams {
   int kind;           // pgs::Kind
@@ -68,6 +69,18 @@ struct SkFixParams {
   int num_pid_m, num_pid_n, gs;
 };
 
+// Several adds in one launch: problem g owns the virtual tile ids
+// [tile0, tile0 + npm * npn) of the shared space the scheduler walks.
+constexpr int kMaxAddProblems = 8;
+struct AddProblem {
+  const float* X;
+  const float* Y;
+  float* C;
+  int rows, cols;
+  int tile0;     // first virtual tile id (prefix sum of the earlier problems' tiles)
+  int npm, npn;  // tiles along rows / columns
+};
+
 struct AddParams {
   const float* X;
   const float* Y;
@@ -75,6 +88,8 @@ struct AddParams {
   int rows, cols;
   SchedParams s;
   Witness w;
+  int nprob;     // several problems: 1..kMaxAddProblems entries of prob (0: X, Y, C above)
+  AddProblem prob[kMaxAddProblems];
 };
 
 // Launchers: return hipErrorInvalidValue when no kernel is built for the
@@ -85,6 +100,8 @@ hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec
                            bool witness, hipStream_t stream);
 hipError_t launch_padd(const AddParams& p, int tr, int tc, bool vec, bool witness,
                        hipStream_t stream);
+hipError_t launch_padd_multi(const AddParams& p, int tr, int tc, bool vec, bool witness,
+                             hipStream_t stream);
 hipError_t launch_zero_i32(int* ptr, int n, hipStream_t stream);
 hipError_t launch_fill_i32(int* ptr, int n, int value, hipStream_t stream);
 bool gemm_bf16_tile_supported(int bm, int bn, int bk);
@@ -252,9 +269,20 @@ struct Walker {
 
   __device__ __forceinline__ int first() {
     if (pgs::work_stealing(s.kind)) return claim();
+    return first_static();
+  }
+
+  // Static kinds only (no claim code): callers that walk many tiles per
+  // step keep the work-stealing path out of their unrolled loops.
+  __device__ __forceinline__ int first_static() {
     int v;
     pgs::static_first(s.kind, p, s.T, s.G, v, end);
     return v < end ? v : -1;
+  }
+
+  __device__ __forceinline__ int next_static(int v) {
+    const int nv = pgs::static_next(s.kind, v, s.G, end);
+    return nv < end ? nv : -1;
   }
 
   // The tile after v: the next one of the current claim, else a new claim.

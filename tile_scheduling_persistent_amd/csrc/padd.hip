@@ -15,6 +15,12 @@
 // scheduler gives the program (for work stealing: one claim of U tiles, and
 // the claim for the following step is issued before the current step's
 // loads so its latency is hidden).
+//
+// Several problems in one launch (the multi-loop listings of the same
+// page): the problems' tiles share one virtual id space, problem g's ids
+// starting at the sum of the earlier problems' tile counts; the scheduler
+// walks the shared space, and each id is located in its problem (an
+// unrolled comparison against the start ids) and decoded there.
 #include "common.hpp"
 
 namespace pgk {
@@ -39,7 +45,7 @@ struct AddShape {
   static_assert(TC % 4 == 0, "tile columns must be a multiple of 4");
 };
 
-template <int TR, int TC, bool VEC, bool WITNESS>
+template <int TR, int TC, bool VEC, bool WITNESS, bool MULTI>
 __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   using S = AddShape<TR, TC>;
   __shared__ int s_claim[2];
@@ -62,7 +68,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     __syncthreads();
     v0 = s_claim[0];
   } else {
-    v0 = walker.first();
+    v0 = walker.first_static();
   }
   int done = 0;  // tiles computed so far by this program
   int step = 0;
@@ -80,7 +86,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
 #pragma unroll
       for (int u = 0; u < S::U; ++u) {
         vt[u] = v;
-        if (v >= 0) v = walker.next(v);
+        if (v >= 0) v = walker.next_static(v);
       }
       next_v0 = v;
     }
@@ -98,6 +104,9 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     f32x4 xa[S::SLOTS], ya[S::SLOTS];
     long long off[S::SLOTS];
     int cnt[S::SLOTS];
+    const float* xb[S::SLOTS];  // several problems: the slot's problem's operands
+    const float* yb[S::SLOTS];
+    float* cb[S::SLOTS];
 #pragma unroll
     for (int j = 0; j < S::SLOTS; ++j) {
       const int idx = j * kThreads + tid;
@@ -105,14 +114,30 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
       const int e = idx % S::F4;
       cnt[j] = 0;
       off[j] = 0;
+      xb[j] = P.X;
+      yb[j] = P.Y;
+      cb[j] = P.C;
       if (u < S::U && vt[u] >= 0) {
-        int pm, pn;
-        walker.tile_coords(vt[u], pm, pn);
+        int pm, pn, rows_u = rows, cols_u = cols;
+        if (MULTI) {
+          AddProblem pr = P.prob[0];
+#pragma unroll
+          for (int q = 1; q < kMaxAddProblems; ++q)
+            if (q < P.nprob && vt[u] >= P.prob[q].tile0) pr = P.prob[q];
+          pgs::decode(P.s.kind, vt[u] - pr.tile0, pr.npm, pr.npn, P.s.gs, pm, pn);
+          rows_u = pr.rows;
+          cols_u = pr.cols;
+          xb[j] = pr.X;
+          yb[j] = pr.Y;
+          cb[j] = pr.C;
+        } else {
+          walker.tile_coords(vt[u], pm, pn);
+        }
         const int r = pm * TR + e / (TC / 4);
         const int c = pn * TC + (e % (TC / 4)) * 4;
-        if (r < rows && c < cols) {
-          off[j] = (long long)r * cols + c;
-          cnt[j] = cols - c < 4 ? cols - c : 4;
+        if (r < rows_u && c < cols_u) {
+          off[j] = (long long)r * cols_u + c;
+          cnt[j] = cols_u - c < 4 ? cols_u - c : 4;
         }
       }
     }
@@ -120,8 +145,8 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     for (int j = 0; j < S::SLOTS; ++j) {
       if (VEC) {
         if (cnt[j] > 0) {
-          const f32x4* px = reinterpret_cast<const f32x4*>(P.X + off[j]);
-          const f32x4* py = reinterpret_cast<const f32x4*>(P.Y + off[j]);
+          const f32x4* px = reinterpret_cast<const f32x4*>((MULTI ? xb[j] : P.X) + off[j]);
+          const f32x4* py = reinterpret_cast<const f32x4*>((MULTI ? yb[j] : P.Y) + off[j]);
           if (S::NT_LOAD) {
             xa[j] = __builtin_nontemporal_load(px);
             ya[j] = __builtin_nontemporal_load(py);
@@ -133,8 +158,8 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          xa[j][q] = q < cnt[j] ? P.X[off[j] + q] : 0.0f;
-          ya[j][q] = q < cnt[j] ? P.Y[off[j] + q] : 0.0f;
+          xa[j][q] = q < cnt[j] ? (MULTI ? xb[j] : P.X)[off[j] + q] : 0.0f;
+          ya[j][q] = q < cnt[j] ? (MULTI ? yb[j] : P.Y)[off[j] + q] : 0.0f;
         }
       }
     }
@@ -142,12 +167,13 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     for (int j = 0; j < S::SLOTS; ++j) {
       if (cnt[j] <= 0) continue;
       const f32x4 z = xa[j] + ya[j];
+      float* C = MULTI ? cb[j] : P.C;
       if (VEC) {
-        __builtin_nontemporal_store(z, reinterpret_cast<f32x4*>(P.C + off[j]));
+        __builtin_nontemporal_store(z, reinterpret_cast<f32x4*>(C + off[j]));
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (q < cnt[j]) P.C[off[j] + q] = z[q];
+          if (q < cnt[j]) C[off[j] + q] = z[q];
       }
     }
 #pragma unroll
@@ -171,18 +197,18 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   }
 }
 
-template <int TR, int TC>
+template <int TR, int TC, bool MULTI>
 hipError_t launch_tile(const AddParams& p, bool vec, bool witness, hipStream_t stream) {
   if (vec) {
     if (witness)
-      hipLaunchKernelGGL((padd_kernel<TR, TC, true, true>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((padd_kernel<TR, TC, true, true, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((padd_kernel<TR, TC, true, false>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((padd_kernel<TR, TC, true, false, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
   } else {
     if (witness)
-      hipLaunchKernelGGL((padd_kernel<TR, TC, false, true>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((padd_kernel<TR, TC, false, true, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((padd_kernel<TR, TC, false, false>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((padd_kernel<TR, TC, false, false, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -230,9 +256,18 @@ KernelInfo info_padd(int tr, int tc, bool vec) {
 
 hipError_t launch_padd(const AddParams& p, int tr, int tc, bool vec, bool witness,
                        hipStream_t stream) {
-  if (tr == 32 && tc == 16) return launch_tile<32, 16>(p, vec, witness, stream);
-  if (tr == 64 && tc == 64) return launch_tile<64, 64>(p, vec, witness, stream);
-  if (tr == 128 && tc == 128) return launch_tile<128, 128>(p, vec, witness, stream);
+  if (tr == 32 && tc == 16) return launch_tile<32, 16, false>(p, vec, witness, stream);
+  if (tr == 64 && tc == 64) return launch_tile<64, 64, false>(p, vec, witness, stream);
+  if (tr == 128 && tc == 128) return launch_tile<128, 128, false>(p, vec, witness, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_padd_multi(const AddParams& p, int tr, int tc, bool vec, bool witness,
+                             hipStream_t stream) {
+  if (p.nprob < 1 || p.nprob > kMaxAddProblems) return hipErrorInvalidValue;
+  if (tr == 32 && tc == 16) return launch_tile<32, 16, true>(p, vec, witness, stream);
+  if (tr == 64 && tc == 64) return launch_tile<64, 64, true>(p, vec, witness, stream);
+  if (tr == 128 && tc == 128) return launch_tile<128, 128, true>(p, vec, witness, stream);
   return hipErrorInvalidValue;
 }
 

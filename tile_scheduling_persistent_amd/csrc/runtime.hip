@@ -340,6 +340,84 @@ pgemm_status pgemm_config_destroy(pgemm_config* cfg) {
   return PGEMM_OK;
 }
 
+static bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  return an > 0 && bn > 0 && x < y + bn && y < x + an;
+}
+
+pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int count,
+                            int tile_rows, int tile_cols, pgemm_sched sched,
+                            const pgemm_args* args, void* hip_stream) {
+  if (!cfg || !problems || count < 1 || count > PADD_MAX_PROBLEMS) return PGEMM_ERR_INVALID;
+  if (tile_rows < 1 || tile_cols < 1) return PGEMM_ERR_INVALID;
+  if (!pgk::padd_tile_supported(tile_rows, tile_cols)) return PGEMM_ERR_UNSUPPORTED;
+  if (args && args->claim_chunk == PGEMM_CLAIM_PAIRS) return PGEMM_ERR_UNSUPPORTED;
+  const int dev = cfg->device;
+  pgk::AddParams p;
+  memset(&p, 0, sizeof(p));
+  p.nprob = count;
+  int64_t total = 0;
+  bool vec = true;
+  for (int g = 0; g < count; ++g) {
+    const padd_problem& q = problems[g];
+    if (!q.X || !q.Y || !q.C) return PGEMM_ERR_INVALID;
+    if (q.rows < 0 || q.cols < 0 || q.rows > 0x7fffffffLL || q.cols > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+    if (!is_device_ptr(q.X, dev) || !is_device_ptr(q.Y, dev) || !is_device_ptr(q.C, dev))
+      return PGEMM_ERR_INVALID;
+    const size_t bytes = (size_t)q.rows * (size_t)q.cols * 4;
+    // C against every buffer: its own X / Y may be the same buffer, nothing else may touch it
+    for (int h = 0; h < count; ++h) {
+      const padd_problem& o = problems[h];
+      const size_t ob = (size_t)o.rows * (size_t)o.cols * 4;
+      const void* bufs[3] = {o.X, o.Y, o.C};
+      for (int b = 0; b < 3; ++b) {
+        if (h == g && b == 2) continue;
+        const bool same = h == g && bufs[b] == (const void*)q.C;
+        if (!same && overlaps(q.C, bytes, bufs[b], ob)) return PGEMM_ERR_INVALID;
+      }
+    }
+    const int64_t npm = (q.rows + tile_rows - 1) / tile_rows, npn = (q.cols + tile_cols - 1) / tile_cols;
+    pgk::AddProblem& a = p.prob[g];
+    a.X = q.X;
+    a.Y = q.Y;
+    a.C = q.C;
+    a.rows = (int)q.rows;
+    a.cols = (int)q.cols;
+    a.tile0 = (int)total;
+    a.npm = (int)npm;
+    a.npn = (int)npn;
+    total += npm * npn;
+    if (total > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+    if (q.rows > 0 && q.cols > 0)
+      vec = vec && (q.cols % 4 == 0) && aligned(q.X, 16) && aligned(q.Y, 16) && aligned(q.C, 16);
+  }
+  if (total == 0) return PGEMM_OK;  // nothing to do
+  p.X = p.prob[0].X;
+  p.Y = p.prob[0].Y;
+  p.C = p.prob[0].C;
+  DeviceGuard gd(dev);
+  if (!gd.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
+  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, p.s);
+  if (st != PGEMM_OK) return st;
+  const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
+  p.s.chunk = step;
+  if (args && args->claim_chunk) {
+    if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
+    p.s.chunk = args->claim_chunk;
+  }
+  hipStream_t stream = (hipStream_t)hip_stream;
+  bool witness = false;
+  st = make_witness(cfg, args, p.s, p.w, witness, stream);
+  if (st != PGEMM_OK) return st;
+  st = reset_counters(cfg, args, p.s, stream);
+  if (st != PGEMM_OK) return st;
+  hipError_t e = pgk::launch_padd_multi(p, tile_rows, tile_cols, vec, witness, stream);
+  if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
 pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_programs) {
   if (!cfg || max_tiles < 1 || max_tiles > (1LL << 30) || max_programs < 1 ||
       max_programs > (1 << 20))
