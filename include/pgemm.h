@@ -197,6 +197,33 @@ PGEMM_API pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* 
                       int64_t rows, int64_t cols, int tile_rows, int tile_cols,
                       pgemm_sched sched, const pgemm_args* args, void* hip_stream);
 
+/* Several GEMMs in one persistent launch, the multi-problem loop of
+ * "Implement persistent kernels" (Helion PR #238, multi-loop listings)
+ * applied to the GEMM (a grouped GEMM): problem g's output tiles take the
+ * virtual tile ids from the sum of the earlier problems' tile counts on, the
+ * scheduler walks the shared space, and the persistent programs move from
+ * one problem's tile to another's without a new launch.  `problems` is a host
+ * array of `count` entries (1..PGEMM_MAX_PROBLEMS), read during the call.
+ * bf16 operands only (PGEMM_BF16_OUT_F32 / _OUT_BF16), one tile shape for
+ * all problems (args->tile_*), every problem on the direct-to-LDS kernel's
+ * terms (A, B, C 16-byte aligned, K and N multiples of 8; otherwise
+ * PGEMM_ERR_UNSUPPORTED); M or N may be 0, K >= 1.  Every scheduler but
+ * STREAM_K (PGEMM_ERR_UNSUPPORTED).  No C may overlap any operand or
+ * another C (PGEMM_ERR_INVALID).  Each problem's C is bit-identical to a
+ * pgemm_run of that problem with the same tile.  The witness indexes tiles
+ * by virtual id. */
+#define PGEMM_MAX_PROBLEMS 8
+typedef struct {
+  const void* A;   /* device, bf16 [M][K] */
+  const void* B;   /* device, bf16 [K][N] */
+  void* C;         /* device, [M][N] of the dtype's output type */
+  int64_t M, N, K;
+} pgemm_problem;
+
+PGEMM_API pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems, int count,
+                               pgemm_dtype dtype, pgemm_sched sched, const pgemm_args* args,
+                               void* hip_stream);
+
 /* Several adds in one persistent launch ("Implement persistent kernels",
  * Helion PR #238, the multi-loop listings: two problems share one virtual
  * program-id space, ids past the first problem's tile count are reduced by

@@ -31,7 +31,7 @@ DTYPES = {
     "fp8_b128_out_bf16": _abi.FP8E4M3_B128_OUT_BF16,
 }
 
-__all__ = ["Config", "pgemm_run", "padd_run", "padd_run_multi", "plan_gemm", "plan_add", "SCHEDULERS",
+__all__ = ["Config", "pgemm_run", "pgemm_run_grouped", "padd_run", "padd_run_multi", "plan_gemm", "plan_add", "SCHEDULERS",
            "DTYPES", "PgemmError", "status_str", "make_args"]
 
 
@@ -213,4 +213,20 @@ def padd_run_multi(cfg: Config, problems, tile_rows: int, tile_cols: int, sched,
     code = _abi.lib().padd_run_multi(cfg.handle, arr, n, int(tile_rows), int(tile_cols), _sched(sched),
                                      ctypes.byref(args) if args is not None else None, _stream(stream))
     _check("padd_run_multi", code)
+
+
+def pgemm_run_grouped(cfg: Config, problems, dtype, sched, args=None, stream=None):
+    """Several GEMMs C_g = A_g . B_g in one persistent launch; `problems` is a
+    sequence of (A, B, C, M, N, K)."""
+    n = len(problems)
+    arr = (_abi.pgemm_problem * max(n, 1))()
+    for g, (A, B, C, M, N, K) in enumerate(problems):
+        arr[g].A = _ptr(A, f"A[{g}]")
+        arr[g].B = _ptr(B, f"B[{g}]")
+        arr[g].C = _ptr(C, f"C[{g}]")
+        arr[g].M, arr[g].N, arr[g].K = int(M), int(N), int(K)
+    code = _abi.lib().pgemm_run_grouped(cfg.handle, arr, n, _dtype(dtype), _sched(sched),
+                                        ctypes.byref(args) if args is not None else None,
+                                        _stream(stream))
+    _check("pgemm_run_grouped", code)
 

@@ -73,6 +73,14 @@ class padd_problem(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
+PGEMM_MAX_PROBLEMS = 8
+
+
+class pgemm_problem(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 _cfg_p = ctypes.c_void_p
 _lib = None
 
@@ -107,6 +115,9 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int, ctypes.c_int, ctypes.POINTER(pgemm_args),
                                  ctypes.c_void_p]
     L.padd_run_multi.restype = st
+    L.pgemm_run_grouped.argtypes = [_cfg_p, ctypes.POINTER(pgemm_problem), ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.c_void_p]
+    L.pgemm_run_grouped.restype = st
     L.pgemm_witness_enable.argtypes = [_cfg_p, ctypes.c_int64, ctypes.c_int]
     L.pgemm_witness_enable.restype = st
     L.pgemm_witness_read.argtypes = [_cfg_p, ctypes.POINTER(pgemm_witness), ctypes.c_void_p]

@@ -46,6 +46,18 @@ struct SchedParams {
   int wall_khz;       // wall-clock tick rate (straggler wait)
 };
 
+// Several GEMMs in one launch: problem g owns the virtual tile ids
+// [tile0, tile0 + npm * npn) of the shared space the scheduler walks.
+constexpr int kMaxGemmProblems = 8;
+struct GemmProblem {
+  const void* A;   // [M][K]
+  const void* B;   // [K][N]
+  void* C;         // [M][N]
+  int M, N, K;
+  int tile0;       // first virtual tile id
+  int npm, npn;    // tiles along M / N
+};
+
 struct GemmParams {
   const void* A;      // [M][K]
   const void* B;      // [K][N]
@@ -56,6 +68,8 @@ struct GemmParams {
   int M, N, K;
   SchedParams s;
   Witness w;
+  int ngemm;          // several GEMMs: entries of gp in use (0: one problem, A..K above)
+  GemmProblem gp[kMaxGemmProblems];
 };
 
 // Stream-K fix-up: the tiles whose slabs several programs shared are summed
@@ -125,6 +139,9 @@ struct KernelInfo {
 hipError_t launch_gemm_bf16_lds_sk(const GemmParams& p, int bm, int bn, bool out_bf16,
                                    hipStream_t stream);
 hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, hipStream_t stream);
+hipError_t launch_gemm_bf16_lds_grouped(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
+                                        hipStream_t stream);
+KernelInfo info_gemm_bf16_lds_grouped(int bm, int bn, bool out_bf16);
 KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec);
 KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16);
 KernelInfo info_gemm_fp8(int bm, int bn);

@@ -105,7 +105,11 @@ __device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
 // of its own stream-K run instead of whole tiles; a segment that does not
 // cover its tile leaves fp32 partial sums in the program's workspace slot,
 // summed and stored by the fix-up kernel after this launch.
-template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS, bool SK>
+// GRP: several GEMMs in one launch.  Their tiles share one virtual id space
+// (problem g from P.gp[g].tile0 on); the loader and the matrix cores each
+// look up the problem of their tile (operands, sizes, slab count) when they
+// move on to it.
+template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS, bool SK, bool GRP>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   using S = Shape<BM, BN, BK, NST>;
   static_assert(NST == 2, "two LDS stages: the loads of slab g+1 run during slab g");
@@ -123,9 +127,13 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   const int wm = wave / S::WN;
   const int wn = wave % S::WN;
   const int prog = blockIdx.x;
-  const int M = P.M, N = P.N, K = P.K;
-  const unsigned short* __restrict__ A = static_cast<const unsigned short*>(P.A);
-  const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);
+  // The loader tile's problem and the matrix cores' tile's problem (one
+  // problem unless GRP).
+  int Ml = P.M, Nl = P.N, Kl = P.K;
+  const unsigned short* Al = static_cast<const unsigned short*>(P.A);
+  const unsigned short* Bl = static_cast<const unsigned short*>(P.B);
+  int Mc = P.M, Nc = P.N;
+  void* Cc = P.C;
 
   Walker walker(P.s, prog);
   long long t_start = 0, c_start = 0;
@@ -140,20 +148,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   // involution).  B likewise with swz_b.
   unsigned aoff[NA], boff[NB];
   int achk[NA], bchk[NB];
+  // row strides K (A) and N (B), in elements
+  auto lane_offsets = [&](int Kx, int Nx) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int q = wave * NA + i;
-    const int row = q * S::A_RPI + lane / S::A_CPR;
-    achk[i] = swz_a<BK>(row, lane % S::A_CPR);
-    aoff[i] = (unsigned)row * (unsigned)K * 2u + (unsigned)achk[i] * 16u;
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int q = wave * NA + i;
+      const int row = q * S::A_RPI + lane / S::A_CPR;
+      achk[i] = swz_a<BK>(row, lane % S::A_CPR);
+      aoff[i] = (unsigned)row * (unsigned)Kx * 2u + (unsigned)achk[i] * 16u;
+    }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int q = wave * NB + i;
-    const int row = q * S::B_RPI + lane / S::B_CPR;
-    bchk[i] = swz_b(row, lane % S::B_CPR);
-    boff[i] = (unsigned)row * (unsigned)N * 2u + (unsigned)bchk[i] * 16u;
-  }
+    for (int i = 0; i < NB; ++i) {
+      const int q = wave * NB + i;
+      const int row = q * S::B_RPI + lane / S::B_CPR;
+      bchk[i] = swz_b(row, lane % S::B_CPR);
+      boff[i] = (unsigned)row * (unsigned)Nx * 2u + (unsigned)bchk[i] * 16u;
+    }
+  };
+  lane_offsets(Kl, Nl);
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   // ---- LDS read offsets ----
@@ -176,14 +188,29 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     }
   }
 
+  // Problem of virtual tile v (GRP): the last one whose first id is <= v
+  // (empty problems own no ids), selected with constant indices.
+  auto problem_of = [&](int v) {
+    GemmProblem pr = P.gp[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGemmProblems; ++q)
+      if (q < P.ngemm && v >= P.gp[q].tile0) pr = P.gp[q];
+    return pr;
+  };
+
   auto coords = [&](int v, int& m0, int& n0) {
     int pm, pn;
-    walker.tile_coords(v, pm, pn);
+    if (GRP) {
+      const GemmProblem pr = problem_of(v);
+      pgs::decode(P.s.kind, v - pr.tile0, pr.npm, pr.npn, P.s.gs, pm, pn);
+    } else {
+      walker.tile_coords(v, pm, pn);
+    }
     m0 = pm * BM;
     n0 = pn * BN;
   };
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (P.K + BK - 1) / BK;
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
@@ -207,16 +234,28 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     cw.init(prog, P.s.T, P.s.G, nk);
   }
 
-  // The loader moves on to slabs [kb, ke) of tile t (t >= 0).
+  // The loader moves on to slabs [kb, ke) of tile t (t >= 0; ke < 0: to
+  // the end of the tile).
   auto begin_tile = [&](int t, int kb, int ke) {
     lt = t;
     lk = kb;
-    lke = ke;
+    if (GRP) {
+      const GemmProblem pr = problem_of(t);
+      Al = static_cast<const unsigned short*>(pr.A);
+      Bl = static_cast<const unsigned short*>(pr.B);
+      Ml = pr.M;
+      Nl = pr.N;
+      Kl = pr.K;
+      lane_offsets(Kl, Nl);
+      masked = true;  // ao / bo are rebuilt from the new offsets
+    }
+    lke = ke < 0 ? (Kl + BK - 1) / BK : ke;
     coords(t, lm0, ln0);
-    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
-    a_ptr = reinterpret_cast<unsigned long long>(A + (size_t)lm0 * K);
-    a_rec = (unsigned)(rows * K) * 2u;
-    b_ptr = reinterpret_cast<unsigned long long>(B + ln0);
+    int rows = (Ml - lm0) < BM ? (Ml - lm0) : BM;
+    rows = rows < 0 ? 0 : rows;  // never negative: an empty range reads zeros
+    a_ptr = reinterpret_cast<unsigned long long>(Al + (size_t)lm0 * Kl);
+    a_rec = (unsigned)(rows * Kl) * 2u;
+    b_ptr = reinterpret_cast<unsigned long long>(Bl + ln0);
   };
 
   // Pick the next slab for the loader (moving on to the next tile or
@@ -243,7 +282,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
             pend0 = t;
           else
             pend1 = t;
-          begin_tile(t, 0, nk);
+          begin_tile(t, 0, -1);
         }
       }
     }
@@ -251,24 +290,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     const bool load = lt >= 0;
     if (load) {
       ++lk;
-      if (!SK && lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+      if (!SK && lk == lke && tid == 0) s_next[claims & 1] = walker.next(lt);
     }
     // Slab k0 of the tile: A from column k0 (the range shrinks with it), B
     // from row k0 (the range ends with the slab's last row, so rows past K
     // read zero).
-    const int krows = (K - k0) < BK ? (K - k0) : BK;
+    const int krows = (Kl - k0) < BK ? (Kl - k0) : BK;
     const unsigned long long pa = a_ptr + (unsigned long long)k0 * 2u;
-    const unsigned long long pb = b_ptr + (unsigned long long)k0 * (unsigned long long)N * 2u;
+    const unsigned long long pb = b_ptr + (unsigned long long)k0 * (unsigned long long)Nl * 2u;
     rA = rsrc_words_u64(pa, load ? a_rec - (unsigned)k0 * 2u : 0u);
-    rB = rsrc_words_u64(pb, load ? (unsigned)(krows * N - ln0) * 2u : 0u);
+    rB = rsrc_words_u64(pb, load ? (unsigned)(krows * Nl - ln0) * 2u : 0u);
     // Per-lane offsets: the plain ones, except on a K-tail slab or an N-edge
     // tile (and the slab after one), where edge chunks are pushed out of range.
-    const bool edge = k0 + BK > K || ln0 + BN > N;
+    const bool edge = k0 + BK > Kl || ln0 + BN > Nl;
     if (edge || masked) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i) ao[i] = (k0 + achk[i] * 8 < K) ? aoff[i] : kOob;
+      for (int i = 0; i < NA; ++i) ao[i] = (k0 + achk[i] * 8 < Kl) ? aoff[i] : kOob;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 8 < N) ? boff[i] : kOob;
+      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 8 < Nl) ? boff[i] : kOob;
       masked = edge;
     }
   };
@@ -312,8 +351,10 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 
   auto epilogue = [&](int m0, int n0) {
     constexpr unsigned esz = OUT_BF16 ? 2u : 4u;
-    const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const auto rC = rsrc(static_cast<unsigned char*>(P.C) + ((size_t)m0 * N + n0) * esz,
+    const int N = Nc;
+    int rows = (Mc - m0) < BM ? (Mc - m0) : BM;
+    rows = rows < 0 ? 0 : rows;  // never negative: an empty range drops the stores
+    const auto rC = rsrc(static_cast<unsigned char*>(Cc) + ((size_t)m0 * N + n0) * esz,
                          (unsigned)((size_t)rows * N - n0) * esz);
     const int r0 = wm * S::TM + l32;
     const int c0 = wn * S::TN + 4 * (lane >> 5);
@@ -410,7 +451,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       lw.next(v, kb, ke, slot);
       begin_tile(v, kb, ke);
     } else {
-      begin_tile(ct, 0, nk);
+      begin_tile(ct, 0, -1);
     }
     prep();  // slab 0
 #pragma unroll
@@ -427,7 +468,19 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   int g = 0;   // slabs computed so far
   int it = 0;  // tiles finished
   int m0 = 0, n0 = 0;  // origin of tile ct (the loader may already be past it)
-  if (ct >= 0) coords(ct, m0, n0);
+  // The matrix cores move on to tile ct: its origin, and (GRP) its problem's
+  // output and slab count.
+  auto compute_tile = [&]() {
+    coords(ct, m0, n0);
+    if (GRP) {
+      const GemmProblem pr = problem_of(ct);
+      Mc = pr.M;
+      Nc = pr.N;
+      Cc = pr.C;
+      cnsl = (pr.K + BK - 1) / BK;
+    }
+  };
+  if (ct >= 0) compute_tile();
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -470,7 +523,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       pend0 = pend1;
       pend1 = -1;
     }
-    if (ct >= 0) coords(ct, m0, n0);
+    if (ct >= 0) compute_tile();
   }
 
   if (WITNESS && tid == 0) {
@@ -485,10 +538,10 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 constexpr int kBK = 64;   // slab depth
 constexpr int kNST = 2;   // LDS stages
 
-template <int BM, int BN, bool OUT_BF16, bool WITNESS, bool SK = false>
+template <int BM, int BN, bool OUT_BF16, bool WITNESS, bool SK = false, bool GRP = false>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   using S = Shape<BM, BN, kBK, kNST>;
-  auto kern = gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, WITNESS, SK>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, WITNESS, SK, GRP>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -500,12 +553,13 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, bool OUT_BF16>
+template <int BM, int BN, bool OUT_BF16, bool GRP = false>
 KernelInfo info_one() {
   using S = Shape<BM, BN, kBK, kNST>;
   static const KernelInfo ki = {
       kThreads, S::LDS_BYTES,
-      occupancy_of(reinterpret_cast<const void*>(gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, false, false>),
+      occupancy_of(reinterpret_cast<const void*>(
+                       gemm_bf16_lds_kernel<BM, BN, kBK, kNST, OUT_BF16, false, false, GRP>),
                    kThreads, S::LDS_BYTES)};
   return ki;
 }
@@ -617,6 +671,34 @@ hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, 
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_lds_grouped(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
+                                        hipStream_t stream) {
+  if (p.ngemm < 1 || p.ngemm > kMaxGemmProblems) return hipErrorInvalidValue;
+  if (bm == 256 && bn == 256) {
+    if (out_bf16)
+      return witness ? launch_one<256, 256, true, true, false, true>(p, stream)
+                     : launch_one<256, 256, true, false, false, true>(p, stream);
+    return witness ? launch_one<256, 256, false, true, false, true>(p, stream)
+                   : launch_one<256, 256, false, false, false, true>(p, stream);
+  }
+  if (bm == 128 && bn == 128) {
+    if (out_bf16)
+      return witness ? launch_one<128, 128, true, true, false, true>(p, stream)
+                     : launch_one<128, 128, true, false, false, true>(p, stream);
+    return witness ? launch_one<128, 128, false, true, false, true>(p, stream)
+                   : launch_one<128, 128, false, false, false, true>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+KernelInfo info_gemm_bf16_lds_grouped(int bm, int bn, bool out_bf16) {
+  if (bm == 256 && bn == 256)
+    return out_bf16 ? info_one<256, 256, true, true>() : info_one<256, 256, false, true>();
+  if (bm == 128 && bn == 128)
+    return out_bf16 ? info_one<128, 128, true, true>() : info_one<128, 128, false, true>();
+  return KernelInfo{0, 0, 0};
 }
 
 hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,

@@ -418,6 +418,82 @@ pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }
 
+pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems, int count,
+                               pgemm_dtype dtype, pgemm_sched sched, const pgemm_args* args,
+                               void* hip_stream) {
+  if (!cfg || !problems || count < 1 || count > PGEMM_MAX_PROBLEMS) return PGEMM_ERR_INVALID;
+  if (dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16) return PGEMM_ERR_UNSUPPORTED;
+  if ((int)sched == PGEMM_SCHED_STREAM_K) return PGEMM_ERR_UNSUPPORTED;
+  if (args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED)) return PGEMM_ERR_UNSUPPORTED;
+  int bm = 256, bn = 256, bk = 64;
+  if (args && (args->tile_m || args->tile_n || args->tile_k)) {
+    bm = args->tile_m;
+    bn = args->tile_n;
+    bk = args->tile_k;
+  }
+  if (bm < 1 || bn < 1 || bk < 1) return PGEMM_ERR_INVALID;
+  const int dev = cfg->device;
+  const size_t csz = dtype == PGEMM_BF16_OUT_F32 ? 4 : 2;
+  pgk::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.ngemm = count;
+  int64_t total = 0;
+  for (int g = 0; g < count; ++g) {
+    const pgemm_problem& q = problems[g];
+    if (!q.A || !q.B || !q.C) return PGEMM_ERR_INVALID;
+    if (q.M < 0 || q.N < 0 || q.K < 1 || q.M > 0x7fffffffLL || q.N > 0x7fffffffLL || q.K > 0x7fffffffLL)
+      return PGEMM_ERR_INVALID;
+    if (!is_device_ptr(q.A, dev) || !is_device_ptr(q.B, dev) || !is_device_ptr(q.C, dev))
+      return PGEMM_ERR_INVALID;
+    if (!aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.C, 16) ||
+        !pgk::gemm_bf16_lds_eligible(bm, bn, bk, q.N, q.K))
+      return PGEMM_ERR_UNSUPPORTED;
+    // each C overlaps no operand and no other output
+    const size_t cb = (size_t)q.M * q.N * csz;
+    for (int h = 0; h < count; ++h) {
+      const pgemm_problem& o = problems[h];
+      if (overlaps(q.C, cb, o.A, (size_t)o.M * o.K * 2) || overlaps(q.C, cb, o.B, (size_t)o.K * o.N * 2))
+        return PGEMM_ERR_INVALID;
+      if (h != g && overlaps(q.C, cb, o.C, (size_t)o.M * o.N * csz)) return PGEMM_ERR_INVALID;
+    }
+    const int64_t npm = (q.M + bm - 1) / bm, npn = (q.N + bn - 1) / bn;
+    pgk::GemmProblem& a = p.gp[g];
+    a.A = q.A;
+    a.B = q.B;
+    a.C = q.C;
+    a.M = (int)q.M;
+    a.N = (int)q.N;
+    a.K = (int)q.K;
+    a.tile0 = (int)total;
+    a.npm = (int)npm;
+    a.npn = (int)npn;
+    total += npm * npn;
+    if (total > 0x7fffffffLL) return PGEMM_ERR_INVALID;
+  }
+  if (total == 0) return PGEMM_OK;  // no tiles
+  p.A = p.gp[0].A;
+  p.B = p.gp[0].B;
+  p.C = p.gp[0].C;
+  p.M = p.gp[0].M;
+  p.N = p.gp[0].N;
+  p.K = p.gp[0].K;
+  DeviceGuard gd(dev);
+  if (!gd.ok) return PGEMM_ERR_DEVICE;
+  const pgk::KernelInfo ki = pgk::info_gemm_bf16_lds_grouped(bm, bn, csz == 2);
+  if (ki.threads == 0) return PGEMM_ERR_UNSUPPORTED;
+  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, p.s);
+  if (st != PGEMM_OK) return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  bool witness = false;
+  st = make_witness(cfg, args, p.s, p.w, witness, stream);
+  if (st != PGEMM_OK) return st;
+  st = reset_counters(cfg, args, p.s, stream);
+  if (st != PGEMM_OK) return st;
+  hipError_t e = pgk::launch_gemm_bf16_lds_grouped(p, bm, bn, csz == 2, witness, stream);
+  if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
+}
+
 pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_programs) {
   if (!cfg || max_tiles < 1 || max_tiles > (1LL << 30) || max_programs < 1 ||
       max_programs > (1 << 20))
