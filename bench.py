@@ -44,8 +44,8 @@ CPU_ROWS = 4096
 # the kernel sources it was measured on (hash below); otherwise reported as
 # null.
 TRAFFIC_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
-TRAFFIC_MEASURED = {"sources_sha256_16": "2ac7e287190487af",
-                    "fetch_bytes": 1807050817, "write_bytes": 144919334}
+TRAFFIC_MEASURED = {"sources_sha256_16": "c02db722e2116992",
+                    "fetch_bytes": 1715530864, "write_bytes": 143770156}
 
 
 def parse():
@@ -252,6 +252,36 @@ def main():
         print(f"# 8192x8192x2048, XCC 0 slowed by 50 us per tile: {slow_xcc}", file=sys.stderr, flush=True)
         del sa, sb
 
+    # several GEMMs in one persistent launch (experts of different sizes)
+    # against one launch per GEMM
+    grouped_gemm = {}
+    if not args.skip_extra:
+        from synthetic import bf16_bits_uniform
+        ms = [512, 1024, 256, 768, 2048, 128, 1536, 640]
+        gn, gk = 2048, 4096
+        probs = []
+        for g, m in enumerate(ms):
+            ga = torch.from_numpy(bf16_bits_uniform((m, gk), 1080 + g).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            gb = torch.from_numpy(bf16_bits_uniform((gk, gn), 1090 + g).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            probs.append((ga, gb, torch.empty((m, gn), dtype=torch.bfloat16, device="cuda:0"), m, gn, gk))
+        f = sum(2.0 * m * gn * gk for m in ms)
+        for sched in ["grouped", "work_stealing"]:
+            for tile in [(256, 256, 64), (128, 128, 64)]:
+                a = pg.make_args(tile=tile)
+                fn = lambda: pg.pgemm_run_grouped(cfg, probs, "bf16_out_bf16", sched, a)  # noqa: E731
+                _, ev_one, _ = time_calls(fn, args.steps, args.warmup, stream)
+
+                def separate():
+                    for pr in probs:
+                        pg.pgemm_run(cfg, *pr, "bf16_out_bf16", sched, a)
+                _, ev_sep, _ = time_calls(separate, args.steps, args.warmup, stream)
+                grouped_gemm[f"{sched}_{tile[0]}"] = {
+                    "one_launch_tflops": round(f / (ev_one * 1e-3) / 1e12, 2),
+                    "one_launch_per_gemm_tflops": round(f / (ev_sep * 1e-3) / 1e12, 2)}
+        print(f"# grouped GEMM ({len(ms)} problems, M = {ms}, N={gn}, K={gk}): {grouped_gemm}",
+              file=sys.stderr, flush=True)
+        del probs
+
     # block-scaled fp8 (workload 5): work stealing vs grouped
     fp8 = {}
     if not args.skip_extra:
@@ -360,6 +390,7 @@ def main():
                 for k, v in add.items()},
         "ragged": ragged,
         "multi_add": multi_add,
+        "grouped_gemm": grouped_gemm,
         "skinny": skinny,
         "slow_xcc": slow_xcc,
         "fp8": fp8,
