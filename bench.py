@@ -97,6 +97,31 @@ def time_calls(fn, steps, warmup, stream):
     return wall * 1e3 / steps, float(np.mean(durs)), float(np.min(durs))
 
 
+def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
+    """Scheduler balance from one witness launch (after the timed steps): per
+    program (one per CU at 256x256 tiles) the busy time from its start to its
+    end, against the span of the whole launch."""
+    import torch
+    a = pg.make_args(tile=(256, 256, 64), group_size=gs, claim_chunk=chunk,
+                     debug_flags=pg._abi.DEBUG_WITNESS)
+    plan = pg.plan_gemm(cfg, m, n, k, "bf16_out_bf16", sched, a)
+    G, T = plan["grid"], plan["tiles"]
+    cfg.witness_enable(T, G)
+    pg.pgemm_run(cfg, A, B, C, m, n, k, "bf16_out_bf16", sched, a)
+    torch.cuda.synchronize()
+    w = cfg.witness_read(T, G)
+    us = 1e3 / cfg.info["wall_clock_khz"]               # microseconds per wall tick
+    t0, t1 = w["t_start"][:G].astype(np.float64), w["t_end"][:G].astype(np.float64)
+    busy = (t1 - t0) * us
+    span = (t1.max() - t0.min()) * us
+    tiles = w["n_tiles"][:G]
+    return {"span_us": round(span, 1), "busy_mean_us": round(float(busy.mean()), 1),
+            "busy_min_us": round(float(busy.min()), 1), "busy_max_us": round(float(busy.max()), 1),
+            "idle_frac": round(1.0 - float(busy.sum()) / (G * span), 4),
+            "skew": round(float((busy.max() - busy.min()) / busy.mean()), 4),
+            "tiles_min": int(tiles.min()), "tiles_max": int(tiles.max())}
+
+
 def measured_clock(pg, cfg, A, B, C, key):
     """Engine clock (GHz) the headline launch runs at: one witness launch after
     the timed steps; median over programs of shader cycles / wall time."""
@@ -282,6 +307,27 @@ def main():
               file=sys.stderr, flush=True)
         del probs
 
+    # per-CU busy / idle skew of each scheduler (witness launches, untimed):
+    # 8192^3 and the ragged shapes
+    bal = {}
+    if not args.skip_extra:
+        from synthetic import bf16_bits_uniform
+        scheds = [("blocked", 8, 0), ("interleaved", 8, 0), ("grouped", 8, 0), ("blocked_grouped", 8, 0),
+                  ("work_stealing", 8, 0), ("work_stealing_xcc", 8, 0), ("work_stealing", 8, -1)]
+        shapes = [(M, N, K, A, B, C)]
+        for (m, n, k) in [(5120, 5120, 4096), (4864, 8000, 8192), (3000, 7000, 2048)]:
+            ra = torch.from_numpy(bf16_bits_uniform((m, k), 1040 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            rb = torch.from_numpy(bf16_bits_uniform((k, n), 1041 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            shapes.append((m, n, k, ra, rb, torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")))
+        for (m, n, k, ta, tb, tc) in shapes:
+            row = {}
+            for sched, gs, chunk in scheds:
+                row[sched + ("_pairs" if chunk < 0 else "")] = balance(pg, cfg, ta, tb, tc, m, n, k, sched, gs, chunk)
+            bal[f"{m}x{n}x{k}"] = row
+            print(f"# balance {m}x{n}x{k}: " + ", ".join(f"{s_}: idle {v['idle_frac']} skew {v['skew']}"
+                                                         for s_, v in row.items()), file=sys.stderr, flush=True)
+        del shapes
+
     # block-scaled fp8 (workload 5): work stealing vs grouped
     fp8 = {}
     if not args.skip_extra:
@@ -394,6 +440,7 @@ def main():
         "skinny": skinny,
         "slow_xcc": slow_xcc,
         "fp8": fp8,
+        "balance": bal,
         "device": cfg.info,
     }
     if not args.no_cpu_baseline:
