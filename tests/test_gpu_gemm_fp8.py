@@ -44,14 +44,14 @@ def test_closed_form_scales():
     want = np.zeros((M, N))
     for g in range(G):
         want += 128.0 * np.outer(2.0 ** (sa[g].astype(float) - 127), 2.0 ** (sb[g].astype(float) - 127))
-    for tile in [(128, 128, 128), (256, 256, 128)]:
+    for tile in [(128, 128, 128), (256, 256, 128), (128, 256, 128)]:
         for sched in SCHEDS:
             C = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile)
             assert C.guards_intact()
             assert np.array_equal(C.as_f64().reshape(M, N), want), (tile, sched)
 
 
-@pytest.mark.parametrize("tile", [(128, 128, 128), (256, 256, 128)])
+@pytest.mark.parametrize("tile", [(128, 128, 128), (256, 256, 128), (128, 256, 128)])
 def test_small_shapes(tile):
     shapes = [(1, 16, 128), (100, 112, 256), (129, 128, 384), (256, 272, 128), (300, 400, 256),
               (257, 16, 640), (64, 1024, 128)]
@@ -83,19 +83,23 @@ def _sampled(qa, sa, qb, sb, C, M, N, rows, what):
 
 
 def test_skinny_256x28672x8192():
-    """Workload 5a: M=256, N=28672, K=8192, 128x128x128 tiles, work stealing vs grouped."""
+    """Workload 5a: M=256, N=28672, K=8192, 128x128x128 tiles (and 128x256x128 on
+    the three-stage ring), work stealing vs grouped; every run bit-identical
+    (the tile shape never changes an element's K order)."""
     M, N, K = 256, 28672, 8192
     qa, sa, qb, sb = make_inputs(M, N, K, 1050)
     rows = np.array([0, 1, 31, 64, 127, 128, 200, 255])
     ref = None
-    for sched in ["work_stealing", "grouped", "blocked", "interleaved"]:
-        C = run_fp8(qa, sa, qb, sb, M, N, K, sched, (128, 128, 128))
+    for sched, tile in [("work_stealing", (128, 128, 128)), ("grouped", (128, 128, 128)),
+                        ("blocked", (128, 128, 128)), ("interleaved", (128, 128, 128)),
+                        ("work_stealing", (128, 256, 128)), ("grouped", (128, 256, 128))]:
+        C = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile)
         assert C.guards_intact()
         if ref is None:
             _sampled(qa, sa, qb, sb, C, M, N, rows, f"5a {sched}")
             ref = C.body_bits()
         else:
-            assert np.array_equal(C.body_bits(), ref), sched
+            assert np.array_equal(C.body_bits(), ref), (sched, tile)
 
 
 def test_square_8192():

@@ -56,6 +56,14 @@ __device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned lds_address,
                :: "s"(lds_address), "v"(voff), "s"(r) : "memory");
 }
 
+// buffer_load_ubyte ... lds: one byte per lane from byte offset voff,
+// written zero-extended to the LDS dword at M0 + 4 * lane (bytes past the
+// resource's range read as zero).
+__device__ __forceinline__ void load_lds_u8(rsrc_words_t r, unsigned lds_address, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
+               :: "s"(lds_address), "v"(voff), "s"(r) : "memory");
+}
+
 __device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned char* lds_dst, unsigned voff) {
   load_lds16(r, __builtin_amdgcn_readfirstlane(lds_addr(lds_dst)), voff);
 }

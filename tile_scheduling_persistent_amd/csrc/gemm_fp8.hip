@@ -14,11 +14,15 @@
 // lane passes its row's scale for the slab's group and the assignment of K
 // positions to MFMA blocks does not matter.
 //
-// Data movement and issue order as in gemm_bf16_lds.hip: two LDS stages of
-// 128-deep slabs filled by hand-issued buffer_load ... lds (gemm_device.hpp),
-// the next slab's loads spread over the MFMAs of the current one, the next
-// step's fragment reads after each MFMA, the loader's bookkeeping and the
-// next slab's scale bytes right after the barrier.  A ([m][k], 128-byte
+// Data movement and issue order as in gemm_bf16_lds.hip: a ring of NST LDS
+// stages of 128-deep slabs filled by hand-issued buffer_load ... lds
+// (gemm_device.hpp), the loads of slab g + NST - 1 spread over the MFMAs of
+// slab g, the next step's fragment reads after each MFMA, the loader's
+// bookkeeping right after the barrier.  The scale bytes of a slab travel
+// with it: byte-sized direct loads put each row's (column's) scale byte in
+// its own LDS dword of the stage, read back after the barrier.  Two stages
+// suit the MFMA-bound square tiles; a deeper ring keeps more bytes in
+// flight per CU where the kernel waits on HBM (few rows, long K).  A ([m][k], 128-byte
 // rows) and B ([k][n]) are chunk-swizzled against LDS bank conflicts
 // (swz_a, swz_b); A operands by ds_read_b128, B^T operands by
 // ds_read_b64_tr_b8 (within a 16-lane group, lane i points at row
@@ -43,15 +47,23 @@ constexpr int kThreads = 256;
 constexpr int BK = 128;          // bytes of K per slab = one scale group
 constexpr int kFmtE4M3 = 0;      // f8f6f4 operand format code of e4m3
 
-template <int BM, int BN>
+template <int BM, int BN, int NST_>
 struct Shape {
+  static constexpr int NST = NST_;
   static constexpr int WM = 2, WN = 2;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int SM = TM / 32, SN = TN / 32;
   static constexpr int A_BYTES = BM * BK;
   static constexpr int B_BYTES = BK * BN;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE + 16;  // + first tile, next tile [2]
+  // scale bytes: each wave loads those of its own TM rows / TN columns, 64
+  // per byte-sized direct load, one LDS dword each
+  static constexpr int SC_A = TM / 64, SC_B = TN / 64;
+  static constexpr int NSC = SC_A + SC_B;
+  static constexpr int SC_BYTES = 4 * NSC * 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  static constexpr int LDS_BYTES = NST * STAGE + 16;  // + first tile, next tile [2]
+  static_assert(TM % 64 == 0 && TN % 64 == 0, "whole byte-load groups per wave");
+  static_assert(NST >= 2 && NST <= 4, "LDS ring of two to four stages");
   static constexpr int A_INSTR = A_BYTES / 1024 / 4;
   static constexpr int B_INSTR = B_BYTES / 1024 / 4;
   static constexpr int B_ROWS_PER_INSTR = 1024 / BN;
@@ -77,20 +89,23 @@ __device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa
                                                          OPSEL_B, sb);
 }
 
-template <int BM, int BN, bool WITNESS>
+template <int BM, int BN, int NST, bool WITNESS>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
-  using S = Shape<BM, BN>;
-  constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NL = NA + NB;  // loads per wave per slab
+  using S = Shape<BM, BN, NST>;
+  constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NO = NA + NB;  // operand loads per wave per slab
+  constexpr int NL = NO + S::NSC;                                // all loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per 64-deep step
   constexpr int NRD = 4 * S::SN + 2 * S::SM;                     // LDS reads per step
-  // The next slab's loads are spread over the first SPREAD MFMAs of the
-  // slab (load d after MFMA d*SPREAD/NL), one at a time rather than a burst.
-  constexpr int SPREAD_W = 3 * NMF / 2 > NL ? 3 * NMF / 2 : NL;
+  // The operand loads of a slab are spread over the first SPREAD MFMAs of
+  // the slab (load d after MFMA d*SPREAD/NO), one at a time rather than a
+  // burst; its few scale-byte loads go out right after the loader's
+  // bookkeeping.
+  constexpr int SPREAD_W = 3 * NMF / 2 > NO ? 3 * NMF / 2 : NO;
   constexpr int SPREAD = SPREAD_W < 2 * NMF ? SPREAD_W : 2 * NMF;
-  static_assert(SPREAD >= NL, "one load per MFMA at most");
+  static_assert(SPREAD >= NO, "one operand load per MFMA at most");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  int* s_first = reinterpret_cast<int*>(smem + 2 * S::STAGE);
+  int* s_first = reinterpret_cast<int*>(smem + NST * S::STAGE);
   int* s_next = s_first + 1;  // [2]: the loader's next tile, double-buffered by claim parity
 
   const int tid = threadIdx.x;
@@ -167,7 +182,12 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
-  int pend = -1;            // tile the loader moved on to
+  // Tiles the loader moved on to that the matrix cores have not reached: the
+  // loader runs NST - 1 slabs ahead, so with one slab per tile that many can
+  // wait (oldest first).
+  int pend[NST - 1];
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) pend[i] = -1;
   int claims = 0;           // loader tile changes so far
   int lm0 = 0, ln0 = 0;     // loader tile origin
   rsrc_words_t rA, rB;      // resources of the slab being loaded
@@ -175,10 +195,9 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   unsigned a_rec = 0;                       // bytes of A from a_ptr to the tile's last row
   unsigned bo[NB];          // B offsets (column chunks past N pushed out of range)
   bool masked = true;       // bo holds masked offsets
-  unsigned soa[S::SM], sob[S::SN];  // scale byte offsets of the lane's rows / columns
-  // Scale bytes of the slab being loaded, one per sub-tile row of the lane
-  // (kept apart until the slab is consumed, so nothing waits for them early).
-  int sab[S::SM], sbb[S::SN];
+  // scale byte offsets of the wave's rows / columns (64 per load, lane = row)
+  unsigned soa[S::SC_A], sob[S::SC_B];
+  rsrc_words_t rSA, rSB;    // scale rows of the slab being loaded
 
   // Pick the next slab for the loader (moving on to the next tile once the
   // current one is issued), set up its resources and load its scales;
@@ -201,14 +220,14 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       masked = edge;
     }
 #pragma unroll
-    for (int s = 0; s < S::SM; ++s) {
-      const int m = lm0 + wm * S::TM + s * 32 + l32;
-      soa[s] = m < M ? (unsigned)m : kOob;
+    for (int i = 0; i < S::SC_A; ++i) {
+      const int m = lm0 + wm * S::TM + i * 64 + lane;
+      soa[i] = m < M ? (unsigned)m : kOob;
     }
 #pragma unroll
-    for (int s = 0; s < S::SN; ++s) {
-      const int n = ln0 + wn * S::TN + s * 32 + l32;
-      sob[s] = n < N ? (unsigned)n : kOob;
+    for (int i = 0; i < S::SC_B; ++i) {
+      const int n = ln0 + wn * S::TN + i * 64 + lane;
+      sob[i] = n < N ? (unsigned)n : kOob;
     }
   };
 
@@ -223,7 +242,13 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       ++claims;
       lt = -1;
       if (t >= 0) {
-        pend = t;
+        bool queued = false;  // into the first free entry (entries fill from 0)
+#pragma unroll
+        for (int i = 0; i < NST - 1; ++i)
+          if (!queued && pend[i] < 0) {
+            pend[i] = t;
+            queued = true;
+          }
         begin_tile(t);
       }
     }
@@ -237,21 +262,25 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     rB = rsrc_words_u64(b_ptr + (unsigned long long)k0 * (unsigned long long)N,
                         load ? (unsigned)(BK * N - ln0) : 0u);
     const int grp = k0 / BK;
-    const auto rSA = rsrc(P.sa + (size_t)grp * M, load ? (unsigned)M : 0u);
-    const auto rSB = rsrc(P.sb + (size_t)grp * N, load ? (unsigned)N : 0u);
-#pragma unroll
-    for (int s = 0; s < S::SM; ++s) sab[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSA, soa[s], 0, 0);
-#pragma unroll
-    for (int s = 0; s < S::SN; ++s) sbb[s] = (int)__builtin_amdgcn_raw_buffer_load_b8(rSB, sob[s], 0, 0);
+    rSA = rsrc_words_u64(reinterpret_cast<unsigned long long>(P.sa + (size_t)grp * M), load ? (unsigned)M : 0u);
+    rSB = rsrc_words_u64(reinterpret_cast<unsigned long long>(P.sb + (size_t)grp * N), load ? (unsigned)N : 0u);
   };
 
-  // Load d of the prepared slab into stage st.
+  // LDS dwords of this wave's scale bytes in a stage: A rows, then B columns.
+  const unsigned sc_off = (unsigned)(S::A_BYTES + S::B_BYTES + wave * S::NSC * 256);
+
+  // Load d of the prepared slab into stage st: operand chunks, then the
+  // wave's scale bytes.
   auto dma = [&](int st, int d) {
     const unsigned sb = lds0 + (unsigned)(st * S::STAGE);
     if (d < NA)
       load_lds16(rA, sb + (unsigned)((wave * NA + d) * 1024), aoff[d]);
-    else
+    else if (d < NO)
       load_lds16(rB, sb + (unsigned)(S::A_BYTES + (wave * NB + d - NA) * 1024), bo[d - NA]);
+    else if (d < NO + S::SC_A)
+      load_lds_u8(rSA, sb + sc_off + (unsigned)((d - NO) * 256), soa[d - NO]);
+    else
+      load_lds_u8(rSB, sb + sc_off + (unsigned)((d - NO) * 256), sob[d - NO - S::SC_A]);
   };
 
   f32x16 acc[S::SN][S::SM];
@@ -312,9 +341,15 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
   if (ct >= 0) {
     begin_tile(ct);
-    prep();
+    // slabs 0 .. NST-2 into stages 0 .. NST-2 (a barrier between preps: a
+    // claim thread 0 stores in one is read by every wave in the next)
 #pragma unroll
-    for (int d = 0; d < NL; ++d) dma(0, d);
+    for (int j = 0; j < NST - 1; ++j) {
+      if (j > 0) slab_barrier();
+      prep();
+#pragma unroll
+      for (int d = 0; d < NL; ++d) dma(j, d);
+    }
   }
 
   int g = 0;   // slabs computed so far
@@ -337,24 +372,32 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
     for (int ck = 0; ck < nk; ++ck) {
-      // Slab g (and its scale bytes) landed once this wave's loads are done
-      // and every wave has passed the barrier, which also frees the other
-      // stage for the loads of slab g+1.
-      wait_vm<0>();
+      // Slab g (operands and scale bytes) landed once this wave's loads of it
+      // are done (the loads of the NST - 2 slabs after it may still be in
+      // flight) and every wave has passed the barrier, which also frees the
+      // stage of slab g-1 for the loads of slab g + NST - 1.
+      wait_vm<(NST - 2) * NL>();
       slab_barrier();
-      const int st = g & 1;
+      const int st = g % NST;
+      const int st_dma = st == 0 ? NST - 1 : st - 1;
       {
+        const unsigned char* scb = smem + st * S::STAGE + sc_off;
         unsigned va = 0, vb = 0;
 #pragma unroll
-        for (int s = 0; s < S::SM; ++s) va |= (unsigned)sab[s] << (8 * s);
+        for (int s = 0; s < S::SM; ++s)
+          va |= (*reinterpret_cast<const unsigned*>(scb + (s * 32 + l32) * 4) & 0xffu) << (8 * s);
 #pragma unroll
-        for (int s = 0; s < S::SN; ++s) vb |= (unsigned)sbb[s] << (8 * s);
+        for (int s = 0; s < S::SN; ++s)
+          vb |= (*reinterpret_cast<const unsigned*>(scb + S::SC_A * 256 + (s * 32 + l32) * 4) & 0xffu)
+                << (8 * s);
         sa_reg = (int)va;
         sb_reg = (int)vb;
       }
 #pragma unroll
       for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
-      prep();  // overlaps the latency of the first reads
+      prep();  // slab g + NST - 1; overlaps the latency of the first reads
+#pragma unroll
+      for (int d = NO; d < NL; ++d) dma(st_dma, d);
       __builtin_amdgcn_sched_barrier(0);
       // Fixed issue order: MFMA, then its share of the next step's LDS reads,
       // then (first SPREAD MFMAs) a load of slab g+1.
@@ -369,8 +412,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
           }
           const int p = ks * NMF + j;
 #pragma unroll
-          for (int d = 0; d < NL; ++d)
-            if (d * SPREAD / NL == p) dma(st ^ 1, d);
+          for (int d = 0; d < NO; ++d)
+            if (d * SPREAD / NO == p) dma(st_dma, d);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -378,8 +421,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     }
     epilogue(m0, n0);
     ++it;
-    ct = pend;
-    pend = -1;
+    ct = pend[0];
+#pragma unroll
+    for (int i = 0; i + 1 < NST - 1; ++i) pend[i] = pend[i + 1];
+    pend[NST - 2] = -1;
     if (ct >= 0) coords(ct, m0, n0);
   }
 
@@ -392,10 +437,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   }
 }
 
-template <int BM, int BN, bool WITNESS>
+template <int BM, int BN, int NST, bool WITNESS>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
-  using S = Shape<BM, BN>;
-  auto kern = gemm_fp8_kernel<BM, BN, WITNESS>;
+  using S = Shape<BM, BN, NST>;
+  auto kern = gemm_fp8_kernel<BM, BN, NST, WITNESS>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -407,20 +452,23 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NST>
 KernelInfo info_one() {
-  using S = Shape<BM, BN>;
+  using S = Shape<BM, BN, NST>;
   static const KernelInfo ki = {
       kThreads, S::LDS_BYTES,
-      occupancy_of(reinterpret_cast<const void*>(gemm_fp8_kernel<BM, BN, false>), kThreads,
+      occupancy_of(reinterpret_cast<const void*>(gemm_fp8_kernel<BM, BN, NST, false>), kThreads,
                    S::LDS_BYTES)};
   return ki;
 }
 
 }  // namespace
 
+// Built tiles and their LDS rings: 256x256 and 128x128 (two stages), 128x256
+// (three stages: one program per CU with twice the B bytes of a 128x128
+// program in flight per slab, for shapes with few rows).
 bool gemm_fp8_tile_supported(int bm, int bn, int bk) {
-  return bk == 128 && ((bm == 256 && bn == 256) || (bm == 128 && bn == 128));
+  return bk == 128 && ((bm == 256 && bn == 256) || (bm == 128 && bn == 128) || (bm == 128 && bn == 256));
 }
 
 // Shapes the kernel handles: K a multiple of 128 (checked by the caller), N a
@@ -431,8 +479,9 @@ bool gemm_fp8_eligible(int bm, long long N, long long K) {
 }
 
 KernelInfo info_gemm_fp8(int bm, int bn) {
-  if (bm == 256 && bn == 256) return info_one<256, 256>();
-  if (bm == 128 && bn == 128) return info_one<128, 128>();
+  if (bm == 256 && bn == 256) return info_one<256, 256, 2>();
+  if (bm == 128 && bn == 128) return info_one<128, 128, 2>();
+  if (bm == 128 && bn == 256) return info_one<128, 256, 3>();
   return KernelInfo{0, 0, 0};
 }
 
@@ -440,9 +489,11 @@ hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec
                            hipStream_t stream) {
   if (!vec || bk != 128) return hipErrorInvalidValue;
   if (bm == 256 && bn == 256)
-    return witness ? launch_one<256, 256, true>(p, stream) : launch_one<256, 256, false>(p, stream);
+    return witness ? launch_one<256, 256, 2, true>(p, stream) : launch_one<256, 256, 2, false>(p, stream);
   if (bm == 128 && bn == 128)
-    return witness ? launch_one<128, 128, true>(p, stream) : launch_one<128, 128, false>(p, stream);
+    return witness ? launch_one<128, 128, 2, true>(p, stream) : launch_one<128, 128, 2, false>(p, stream);
+  if (bm == 128 && bn == 256)
+    return witness ? launch_one<128, 256, 3, true>(p, stream) : launch_one<128, 256, 3, false>(p, stream);
   return hipErrorInvalidValue;
 }
 
