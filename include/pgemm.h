@@ -204,20 +204,24 @@ PGEMM_API pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* 
  * scheduler walks the shared space, and the persistent programs move from
  * one problem's tile to another's without a new launch.  `problems` is a host
  * array of `count` entries (1..PGEMM_MAX_PROBLEMS), read during the call.
- * bf16 operands only (PGEMM_BF16_OUT_F32 / _OUT_BF16), one tile shape for
- * all problems (args->tile_*), every problem on the direct-to-LDS kernel's
- * terms (A, B, C 16-byte aligned, K and N multiples of 8; otherwise
- * PGEMM_ERR_UNSUPPORTED); M or N may be 0, K >= 1.  Every scheduler but
+ * bf16 (PGEMM_BF16_OUT_F32 / _OUT_BF16) on the direct-to-LDS kernel's terms
+ * (A, B, C 16-byte aligned, K and N multiples of 8), or block-scaled fp8
+ * (PGEMM_FP8E4M3_B128_OUT_BF16, each problem with its own a_scale / b_scale,
+ * K a multiple of 128, N of 16); otherwise PGEMM_ERR_UNSUPPORTED.  One tile
+ * shape for all problems (args->tile_*; args->a_scale / b_scale unused); M
+ * or N may be 0, K >= 1.  Every scheduler but
  * STREAM_K (PGEMM_ERR_UNSUPPORTED).  No C may overlap any operand or
  * another C (PGEMM_ERR_INVALID).  Each problem's C is bit-identical to a
  * pgemm_run of that problem with the same tile.  The witness indexes tiles
  * by virtual id. */
 #define PGEMM_MAX_PROBLEMS 8
 typedef struct {
-  const void* A;   /* device, bf16 [M][K] */
-  const void* B;   /* device, bf16 [K][N] */
+  const void* A;   /* device, bf16 or e4m3 [M][K] */
+  const void* B;   /* device, bf16 or e4m3 [K][N] */
   void* C;         /* device, [M][N] of the dtype's output type */
   int64_t M, N, K;
+  const uint8_t* a_scale;  /* fp8: device, e8m0 [K/128][M]; otherwise ignored */
+  const uint8_t* b_scale;  /* fp8: device, e8m0 [K/128][N]; otherwise ignored */
 } pgemm_problem;
 
 PGEMM_API pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems, int count,

@@ -10,8 +10,8 @@ import torch
 import tile_scheduling_persistent_amd as pg
 from oracle import gemm as og
 from oracle import sched_model as sm
-from synthetic import bf16_bits_uniform
-from tests.gpu_util import BF16_TOL, Guarded, assert_within, config, dev_bf16, note
+from synthetic import bf16_bits_uniform, fp8_blockscaled
+from tests.gpu_util import BF16_TOL, FP8_TOL, Guarded, assert_north_star, assert_within, config, dev_bf16, note
 
 pytestmark = pytest.mark.gpu
 
@@ -117,10 +117,57 @@ def test_grouped_errors():
         ([ok, (c, b, d, 256, 256, 128)], "bf16_out_bf16", "grouped", pg._abi.ERR_INVALID),   # reads c
         ([(a, b100, d, 256, 256, 100)], "bf16_out_bf16", "grouped", pg._abi.ERR_UNSUPPORTED),  # K % 8
         ([ok], "bf16_out_bf16", "stream_k", pg._abi.ERR_UNSUPPORTED),
-        ([ok], "fp8_b128_out_bf16", "grouped", pg._abi.ERR_UNSUPPORTED),
+        ([ok], "fp8_b128_out_bf16", "grouped", pg._abi.ERR_INVALID),                       # no scales
         ([(a, b, c, 256, 256, 0)], "bf16_out_bf16", "grouped", pg._abi.ERR_INVALID),          # K = 0
     ]
     for probs, dt, sched, code in cases:
         with pytest.raises(pg.PgemmError) as e:
             pg.pgemm_run_grouped(cfg, probs, dt, sched)
         assert e.value.code == code, (len(probs), dt, sched)
+
+
+# fp8: (M, N, K) per problem, K a multiple of 128, N of 16
+FP8_SETS = [
+    [(256, 1024, 512), (100, 272, 256), (0, 64, 128), (384, 128, 1024)],
+    [(96, 48, 128)] * 8,
+]
+
+
+@pytest.mark.parametrize("tile", [(128, 128, 128), (256, 256, 128), (128, 256, 128)])
+@pytest.mark.parametrize("si", range(len(FP8_SETS)))
+def test_grouped_fp8_parity(tile, si):
+    shapes = FP8_SETS[si]
+    cfg = config()
+    data, alone = [], []
+    for g, (M, N, K) in enumerate(shapes):
+        qa, sa = fp8_blockscaled(M, K, 4200 + 4 * g, 4202 + 4 * g, k_major=True)
+        qb, sb = fp8_blockscaled(N, K, 4201 + 4 * g, 4203 + 4 * g, k_major=False)
+        dev = [torch.from_numpy(x).to("cuda:0") if x.size else torch.empty(16, dtype=torch.uint8, device="cuda:0")
+               for x in (qa, qb, sa, sb)]
+        data.append((qa, sa, qb, sb, dev))
+        if M * N == 0:
+            alone.append(None)
+            continue
+        C = Guarded(M * N, "bf16")
+        pg.pgemm_run(cfg, dev[0], dev[1], C.view, M, N, K, "fp8_b128_out_bf16", "grouped",
+                     pg.make_args(tile=tile, a_scale=dev[2], b_scale=dev[3]))
+        torch.cuda.synchronize()
+        alone.append(C.body_bits())
+    for sched in SCHEDS:
+        probs, outs = [], []
+        for (M, N, K), (qa, sa, qb, sb, dev) in zip(shapes, data):
+            C = Guarded(M * N, "bf16")
+            probs.append((dev[0], dev[1], C.view if M * N else C.full, M, N, K, dev[2], dev[3]))
+            outs.append(C)
+        note(f"pgemm_run_grouped fp8 {shapes} sched={sched} tile={tile}")
+        pg.pgemm_run_grouped(cfg, probs, "fp8_b128_out_bf16", sched, pg.make_args(tile=tile))
+        torch.cuda.synchronize()
+        for g, ((M, N, K), (qa, sa, qb, sb, dev), C) in enumerate(zip(shapes, data, outs)):
+            assert C.guards_intact(), (shapes, sched, g)
+            if M * N == 0:
+                continue
+            assert np.array_equal(C.body_bits(), alone[g]), f"fp8 {shapes[g]} {sched}: differs from its own pgemm_run"
+            if sched == "grouped":
+                Cref, Abs = og.gemm_fp8_b128(qa, sa, qb, sb)
+                assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shapes[g]} {tile}")
+

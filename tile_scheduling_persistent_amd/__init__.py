@@ -217,14 +217,19 @@ def padd_run_multi(cfg: Config, problems, tile_rows: int, tile_cols: int, sched,
 
 def pgemm_run_grouped(cfg: Config, problems, dtype, sched, args=None, stream=None):
     """Several GEMMs C_g = A_g . B_g in one persistent launch; `problems` is a
-    sequence of (A, B, C, M, N, K)."""
+    sequence of (A, B, C, M, N, K), or (A, B, C, M, N, K, a_scale, b_scale)
+    for block-scaled fp8."""
     n = len(problems)
     arr = (_abi.pgemm_problem * max(n, 1))()
-    for g, (A, B, C, M, N, K) in enumerate(problems):
+    for g, pr in enumerate(problems):
+        A, B, C, M, N, K = pr[:6]
         arr[g].A = _ptr(A, f"A[{g}]")
         arr[g].B = _ptr(B, f"B[{g}]")
         arr[g].C = _ptr(C, f"C[{g}]")
         arr[g].M, arr[g].N, arr[g].K = int(M), int(N), int(K)
+        if len(pr) == 8:
+            arr[g].a_scale = _ptr(pr[6], f"a_scale[{g}]")
+            arr[g].b_scale = _ptr(pr[7], f"b_scale[{g}]")
     code = _abi.lib().pgemm_run_grouped(cfg.handle, arr, n, _dtype(dtype), _sched(sched),
                                         ctypes.byref(args) if args is not None else None,
                                         _stream(stream))

@@ -78,7 +78,8 @@ PGEMM_MAX_PROBLEMS = 8
 
 class pgemm_problem(ctypes.Structure):
     _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
-                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_scale", ctypes.c_void_p), ("b_scale", ctypes.c_void_p)]
 
 
 _cfg_p = ctypes.c_void_p

@@ -53,6 +53,8 @@ struct GemmProblem {
   const void* A;   // [M][K]
   const void* B;   // [K][N]
   void* C;         // [M][N]
+  const uint8_t* sa;  // fp8: e8m0 [K/128][M]
+  const uint8_t* sb;  // fp8: e8m0 [K/128][N]
   int M, N, K;
   int tile0;       // first virtual tile id
   int npm, npn;    // tiles along M / N
@@ -142,6 +144,8 @@ hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, 
 hipError_t launch_gemm_bf16_lds_grouped(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
                                         hipStream_t stream);
 KernelInfo info_gemm_bf16_lds_grouped(int bm, int bn, bool out_bf16);
+hipError_t launch_gemm_fp8_grouped(const GemmParams& p, int bm, int bn, bool witness, hipStream_t stream);
+KernelInfo info_gemm_fp8_grouped(int bm, int bn);
 KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec);
 KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16);
 KernelInfo info_gemm_fp8(int bm, int bn);

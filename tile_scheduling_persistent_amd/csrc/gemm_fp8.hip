@@ -89,7 +89,10 @@ __device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa
                                                          OPSEL_B, sb);
 }
 
-template <int BM, int BN, int NST, bool WITNESS>
+// GRP: several GEMMs in one launch (virtual tile ids shared by prefix sums,
+// P.gp[g] from tile0 on); the loader and the matrix cores each look up the
+// problem of their tile (operands, scales, sizes, slab count, output).
+template <int BM, int BN, int NST, bool WITNESS, bool GRP>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   using S = Shape<BM, BN, NST>;
   constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NO = NA + NB;  // operand loads per wave per slab
@@ -114,9 +117,15 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   const int wm = wave / S::WN;
   const int wn = wave % S::WN;
   const int prog = blockIdx.x;
-  const int M = P.M, N = P.N, K = P.K;
-  const unsigned char* __restrict__ A = static_cast<const unsigned char*>(P.A);
-  const unsigned char* __restrict__ B = static_cast<const unsigned char*>(P.B);
+  // The loader tile's problem and the matrix cores' tile's problem (one
+  // problem unless GRP).
+  int Ml = P.M, Nl = P.N, Kl = P.K;
+  const unsigned char* Al = static_cast<const unsigned char*>(P.A);
+  const unsigned char* Bl = static_cast<const unsigned char*>(P.B);
+  const uint8_t* SAl = P.sa;
+  const uint8_t* SBl = P.sb;
+  int Mc = P.M, Nc = P.N;
+  void* Cc = P.C;
 
   Walker walker(P.s, prog);
   long long t_start = 0, c_start = 0;
@@ -131,17 +140,21 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   // p%CPR, global chunk swz_b(row, p%CPR).
   unsigned aoff[NA], boff[NB];
   int bchk[NB];
+  // row strides K (A) and N (B), in bytes
+  auto lane_offsets = [&](int Kx, int Nx) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = (wave * NA + i) * 8 + (lane >> 3);
-    aoff[i] = (unsigned)row * (unsigned)K + (unsigned)swz_a(row, lane & 7) * 16u;
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int row = (wave * NA + i) * 8 + (lane >> 3);
+      aoff[i] = (unsigned)row * (unsigned)Kx + (unsigned)swz_a(row, lane & 7) * 16u;
+    }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int row = (wave * NB + i) * S::B_ROWS_PER_INSTR + lane / S::B_CPR;
-    bchk[i] = swz_b<BN>(row, lane % S::B_CPR);
-    boff[i] = (unsigned)row * (unsigned)N + (unsigned)bchk[i] * 16u;
-  }
+    for (int i = 0; i < NB; ++i) {
+      const int row = (wave * NB + i) * S::B_ROWS_PER_INSTR + lane / S::B_CPR;
+      bchk[i] = swz_b<BN>(row, lane % S::B_CPR);
+      boff[i] = (unsigned)row * (unsigned)Nx + (unsigned)bchk[i] * 16u;
+    }
+  };
+  lane_offsets(Kl, Nl);
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   // LDS read offsets.  A: lane l, sub-tile sm, step ks reads row
@@ -171,14 +184,29 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     }
   }
 
+  // Problem of virtual tile v (GRP): the last one whose first id is <= v,
+  // selected with constant indices.
+  auto problem_of = [&](int v) {
+    GemmProblem pr = P.gp[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGemmProblems; ++q)
+      if (q < P.ngemm && v >= P.gp[q].tile0) pr = P.gp[q];
+    return pr;
+  };
+
   auto coords = [&](int v, int& m0, int& n0) {
     int pm, pn;
-    walker.tile_coords(v, pm, pn);
+    if (GRP) {
+      const GemmProblem pr = problem_of(v);
+      pgs::decode(P.s.kind, v - pr.tile0, pr.npm, pr.npn, P.s.gs, pm, pn);
+    } else {
+      walker.tile_coords(v, pm, pn);
+    }
     m0 = pm * BM;
     n0 = pn * BN;
   };
 
-  const int nk = K / BK;
+  int nkl = Kl / BK;  // slabs of the loader's tile
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
@@ -208,26 +236,40 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   auto begin_tile = [&](int t) {
     lt = t;
     lk = 0;
+    if (GRP) {
+      const GemmProblem pr = problem_of(t);
+      Al = static_cast<const unsigned char*>(pr.A);
+      Bl = static_cast<const unsigned char*>(pr.B);
+      SAl = pr.sa;
+      SBl = pr.sb;
+      Ml = pr.M;
+      Nl = pr.N;
+      Kl = pr.K;
+      nkl = Kl / BK;
+      lane_offsets(Kl, Nl);
+      masked = true;  // bo is rebuilt from the new offsets
+    }
     coords(t, lm0, ln0);
-    const int rows = (M - lm0) < BM ? (M - lm0) : BM;
-    a_ptr = reinterpret_cast<unsigned long long>(A + (size_t)lm0 * K);
-    a_rec = (unsigned)(rows * K);
-    b_ptr = reinterpret_cast<unsigned long long>(B + ln0);
-    const bool edge = ln0 + BN > N;
+    int rows = (Ml - lm0) < BM ? (Ml - lm0) : BM;
+    rows = rows < 0 ? 0 : rows;  // never negative: an empty range reads zeros
+    a_ptr = reinterpret_cast<unsigned long long>(Al + (size_t)lm0 * Kl);
+    a_rec = (unsigned)(rows * Kl);
+    b_ptr = reinterpret_cast<unsigned long long>(Bl + ln0);
+    const bool edge = ln0 + BN > Nl;
     if (edge || masked) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 16 < N) ? boff[i] : kOob;
+      for (int i = 0; i < NB; ++i) bo[i] = (ln0 + bchk[i] * 16 < Nl) ? boff[i] : kOob;
       masked = edge;
     }
 #pragma unroll
     for (int i = 0; i < S::SC_A; ++i) {
       const int m = lm0 + wm * S::TM + i * 64 + lane;
-      soa[i] = m < M ? (unsigned)m : kOob;
+      soa[i] = m < Ml ? (unsigned)m : kOob;
     }
 #pragma unroll
     for (int i = 0; i < S::SC_B; ++i) {
       const int n = ln0 + wn * S::TN + i * 64 + lane;
-      sob[i] = n < N ? (unsigned)n : kOob;
+      sob[i] = n < Nl ? (unsigned)n : kOob;
     }
   };
 
@@ -237,7 +279,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     lt = __builtin_amdgcn_readfirstlane(lt);
     lk = __builtin_amdgcn_readfirstlane(lk);
     claims = __builtin_amdgcn_readfirstlane(claims);
-    if (lt >= 0 && lk == nk) {
+    if (lt >= 0 && lk == nkl) {
       const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
       ++claims;
       lt = -1;
@@ -256,14 +298,14 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     const bool load = lt >= 0;
     if (load) {
       ++lk;
-      if (lk == nk && tid == 0) s_next[claims & 1] = walker.next(lt);
+      if (lk == nkl && tid == 0) s_next[claims & 1] = walker.next(lt);
     }
     rA = rsrc_words_u64(a_ptr + (unsigned long long)k0, load ? a_rec - (unsigned)k0 : 0u);
-    rB = rsrc_words_u64(b_ptr + (unsigned long long)k0 * (unsigned long long)N,
-                        load ? (unsigned)(BK * N - ln0) : 0u);
+    rB = rsrc_words_u64(b_ptr + (unsigned long long)k0 * (unsigned long long)Nl,
+                        load ? (unsigned)(BK * Nl - ln0) : 0u);
     const int grp = k0 / BK;
-    rSA = rsrc_words_u64(reinterpret_cast<unsigned long long>(P.sa + (size_t)grp * M), load ? (unsigned)M : 0u);
-    rSB = rsrc_words_u64(reinterpret_cast<unsigned long long>(P.sb + (size_t)grp * N), load ? (unsigned)N : 0u);
+    rSA = rsrc_words_u64(reinterpret_cast<unsigned long long>(SAl + (size_t)grp * Ml), load ? (unsigned)Ml : 0u);
+    rSB = rsrc_words_u64(reinterpret_cast<unsigned long long>(SBl + (size_t)grp * Nl), load ? (unsigned)Nl : 0u);
   };
 
   // LDS dwords of this wave's scale bytes in a stage: A rows, then B columns.
@@ -322,8 +364,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   };
 
   auto epilogue = [&](int m0, int n0) {
-    const int rows = (M - m0) < BM ? (M - m0) : BM;
-    const auto rC = rsrc(static_cast<unsigned char*>(P.C) + ((size_t)m0 * N + n0) * 2,
+    const int N = Nc;
+    int rows = (Mc - m0) < BM ? (Mc - m0) : BM;
+    rows = rows < 0 ? 0 : rows;  // never negative: an empty range drops the stores
+    const auto rC = rsrc(static_cast<unsigned char*>(Cc) + ((size_t)m0 * N + n0) * 2,
                          (unsigned)((size_t)rows * N - n0) * 2u);
     const int r0 = wm * S::TM + l32;
     const unsigned eb = (unsigned)(r0 * N) * 2u;
@@ -355,7 +399,20 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   int g = 0;   // slabs computed so far
   int it = 0;  // tiles finished
   int m0 = 0, n0 = 0;  // origin of tile ct
-  if (ct >= 0) coords(ct, m0, n0);
+  int cnk = P.K / BK;  // slabs of tile ct
+  // The matrix cores move on to tile ct: its origin and (GRP) its problem's
+  // output and slab count.
+  auto compute_tile = [&]() {
+    coords(ct, m0, n0);
+    if (GRP) {
+      const GemmProblem pr = problem_of(ct);
+      Mc = pr.M;
+      Nc = pr.N;
+      Cc = pr.C;
+      cnk = pr.K / BK;
+    }
+  };
+  if (ct >= 0) compute_tile();
   while (ct >= 0) {
     if (tid == 0) {
       if (WITNESS) {
@@ -371,7 +428,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
-    for (int ck = 0; ck < nk; ++ck) {
+    for (int ck = 0; ck < cnk; ++ck) {
       // Slab g (operands and scale bytes) landed once this wave's loads of it
       // are done (the loads of the NST - 2 slabs after it may still be in
       // flight) and every wave has passed the barrier, which also frees the
@@ -425,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 #pragma unroll
     for (int i = 0; i + 1 < NST - 1; ++i) pend[i] = pend[i + 1];
     pend[NST - 2] = -1;
-    if (ct >= 0) coords(ct, m0, n0);
+    if (ct >= 0) compute_tile();
   }
 
   if (WITNESS && tid == 0) {
@@ -437,10 +494,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   }
 }
 
-template <int BM, int BN, int NST, bool WITNESS>
+template <int BM, int BN, int NST, bool WITNESS, bool GRP = false>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   using S = Shape<BM, BN, NST>;
-  auto kern = gemm_fp8_kernel<BM, BN, NST, WITNESS>;
+  auto kern = gemm_fp8_kernel<BM, BN, NST, WITNESS, GRP>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -452,12 +509,12 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NST>
+template <int BM, int BN, int NST, bool GRP = false>
 KernelInfo info_one() {
   using S = Shape<BM, BN, NST>;
   static const KernelInfo ki = {
       kThreads, S::LDS_BYTES,
-      occupancy_of(reinterpret_cast<const void*>(gemm_fp8_kernel<BM, BN, NST, false>), kThreads,
+      occupancy_of(reinterpret_cast<const void*>(gemm_fp8_kernel<BM, BN, NST, false, GRP>), kThreads,
                    S::LDS_BYTES)};
   return ki;
 }
@@ -494,6 +551,24 @@ hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec
     return witness ? launch_one<128, 128, 2, true>(p, stream) : launch_one<128, 128, 2, false>(p, stream);
   if (bm == 128 && bn == 256)
     return witness ? launch_one<128, 256, 3, true>(p, stream) : launch_one<128, 256, 3, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+KernelInfo info_gemm_fp8_grouped(int bm, int bn) {
+  if (bm == 256 && bn == 256) return info_one<256, 256, 2, true>();
+  if (bm == 128 && bn == 128) return info_one<128, 128, 2, true>();
+  if (bm == 128 && bn == 256) return info_one<128, 256, 3, true>();
+  return KernelInfo{0, 0, 0};
+}
+
+hipError_t launch_gemm_fp8_grouped(const GemmParams& p, int bm, int bn, bool witness, hipStream_t stream) {
+  if (p.ngemm < 1 || p.ngemm > kMaxGemmProblems) return hipErrorInvalidValue;
+  if (bm == 256 && bn == 256)
+    return witness ? launch_one<256, 256, 2, true, true>(p, stream) : launch_one<256, 256, 2, false, true>(p, stream);
+  if (bm == 128 && bn == 128)
+    return witness ? launch_one<128, 128, 2, true, true>(p, stream) : launch_one<128, 128, 2, false, true>(p, stream);
+  if (bm == 128 && bn == 256)
+    return witness ? launch_one<128, 256, 3, true, true>(p, stream) : launch_one<128, 256, 3, false, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -422,10 +422,11 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
                                pgemm_dtype dtype, pgemm_sched sched, const pgemm_args* args,
                                void* hip_stream) {
   if (!cfg || !problems || count < 1 || count > PGEMM_MAX_PROBLEMS) return PGEMM_ERR_INVALID;
-  if (dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16) return PGEMM_ERR_UNSUPPORTED;
+  const bool fp8 = dtype == PGEMM_FP8E4M3_B128_OUT_BF16;
+  if (!fp8 && dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16) return PGEMM_ERR_INVALID;
   if ((int)sched == PGEMM_SCHED_STREAM_K) return PGEMM_ERR_UNSUPPORTED;
   if (args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED)) return PGEMM_ERR_UNSUPPORTED;
-  int bm = 256, bn = 256, bk = 64;
+  int bm = 256, bn = 256, bk = fp8 ? 128 : 64;
   if (args && (args->tile_m || args->tile_n || args->tile_k)) {
     bm = args->tile_m;
     bn = args->tile_n;
@@ -445,14 +446,26 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
       return PGEMM_ERR_INVALID;
     if (!is_device_ptr(q.A, dev) || !is_device_ptr(q.B, dev) || !is_device_ptr(q.C, dev))
       return PGEMM_ERR_INVALID;
-    if (!aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.C, 16) ||
-        !pgk::gemm_bf16_lds_eligible(bm, bn, bk, q.N, q.K))
+    if (fp8) {
+      if (!q.a_scale || !q.b_scale || !is_device_ptr(q.a_scale, dev) || !is_device_ptr(q.b_scale, dev))
+        return PGEMM_ERR_INVALID;
+      if (q.K % 128 != 0) return PGEMM_ERR_INVALID;
+      if (!aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.C, 16) ||
+          !pgk::gemm_fp8_tile_supported(bm, bn, bk) || !pgk::gemm_fp8_eligible(bm, q.N, q.K))
+        return PGEMM_ERR_UNSUPPORTED;
+    } else if (!aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.C, 16) ||
+               !pgk::gemm_bf16_lds_eligible(bm, bn, bk, q.N, q.K)) {
       return PGEMM_ERR_UNSUPPORTED;
+    }
     // each C overlaps no operand and no other output
     const size_t cb = (size_t)q.M * q.N * csz;
+    const size_t esz = fp8 ? 1 : 2;
     for (int h = 0; h < count; ++h) {
       const pgemm_problem& o = problems[h];
-      if (overlaps(q.C, cb, o.A, (size_t)o.M * o.K * 2) || overlaps(q.C, cb, o.B, (size_t)o.K * o.N * 2))
+      if (overlaps(q.C, cb, o.A, (size_t)o.M * o.K * esz) || overlaps(q.C, cb, o.B, (size_t)o.K * o.N * esz))
+        return PGEMM_ERR_INVALID;
+      if (fp8 && (overlaps(q.C, cb, o.a_scale, (size_t)(o.K / 128) * o.M) ||
+                  overlaps(q.C, cb, o.b_scale, (size_t)(o.K / 128) * o.N)))
         return PGEMM_ERR_INVALID;
       if (h != g && overlaps(q.C, cb, o.C, (size_t)o.M * o.N * csz)) return PGEMM_ERR_INVALID;
     }
@@ -461,6 +474,8 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
     a.A = q.A;
     a.B = q.B;
     a.C = q.C;
+    a.sa = fp8 ? q.a_scale : nullptr;
+    a.sb = fp8 ? q.b_scale : nullptr;
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
@@ -474,12 +489,15 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   p.A = p.gp[0].A;
   p.B = p.gp[0].B;
   p.C = p.gp[0].C;
+  p.sa = p.gp[0].sa;
+  p.sb = p.gp[0].sb;
   p.M = p.gp[0].M;
   p.N = p.gp[0].N;
   p.K = p.gp[0].K;
   DeviceGuard gd(dev);
   if (!gd.ok) return PGEMM_ERR_DEVICE;
-  const pgk::KernelInfo ki = pgk::info_gemm_bf16_lds_grouped(bm, bn, csz == 2);
+  const pgk::KernelInfo ki =
+      fp8 ? pgk::info_gemm_fp8_grouped(bm, bn) : pgk::info_gemm_bf16_lds_grouped(bm, bn, csz == 2);
   if (ki.threads == 0) return PGEMM_ERR_UNSUPPORTED;
   pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, p.s);
   if (st != PGEMM_OK) return st;
@@ -489,7 +507,8 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   if (st != PGEMM_OK) return st;
   st = reset_counters(cfg, args, p.s, stream);
   if (st != PGEMM_OK) return st;
-  hipError_t e = pgk::launch_gemm_bf16_lds_grouped(p, bm, bn, csz == 2, witness, stream);
+  hipError_t e = fp8 ? pgk::launch_gemm_fp8_grouped(p, bm, bn, witness, stream)
+                     : pgk::launch_gemm_bf16_lds_grouped(p, bm, bn, csz == 2, witness, stream);
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }
