@@ -303,9 +303,30 @@ def main():
                 grouped_gemm[f"{sched}_{tile[0]}"] = {
                     "one_launch_tflops": round(f / (ev_one * 1e-3) / 1e12, 2),
                     "one_launch_per_gemm_tflops": round(f / (ev_sep * 1e-3) / 1e12, 2)}
+        # the same experts in block-scaled fp8 (256x256x128 tiles)
+        from synthetic import fp8_blockscaled
+        fprobs = []
+        for g, m in enumerate(ms):
+            qa, sa = fp8_blockscaled(m, gk, 1100 + g, 1120 + g, k_major=True)
+            qb, sb = fp8_blockscaled(gn, gk, 1110 + g, 1130 + g, k_major=False)
+            fprobs.append((torch.from_numpy(qa).to("cuda:0"), torch.from_numpy(qb).to("cuda:0"),
+                           torch.empty((m, gn), dtype=torch.bfloat16, device="cuda:0"), m, gn, gk,
+                           torch.from_numpy(sa).to("cuda:0"), torch.from_numpy(sb).to("cuda:0")))
+        for sched in ["grouped", "work_stealing"]:
+            fn = lambda: pg.pgemm_run_grouped(cfg, fprobs, "fp8_b128_out_bf16", sched)  # noqa: E731
+            _, ev_one, _ = time_calls(fn, args.steps, args.warmup, stream)
+
+            def separate_fp8():
+                for pr in fprobs:
+                    pg.pgemm_run(cfg, *pr[:6], "fp8_b128_out_bf16", sched,
+                                 pg.make_args(a_scale=pr[6], b_scale=pr[7]))
+            _, ev_sep, _ = time_calls(separate_fp8, args.steps, args.warmup, stream)
+            grouped_gemm[f"fp8_{sched}_256"] = {
+                "one_launch_tflops": round(f / (ev_one * 1e-3) / 1e12, 2),
+                "one_launch_per_gemm_tflops": round(f / (ev_sep * 1e-3) / 1e12, 2)}
         print(f"# grouped GEMM ({len(ms)} problems, M = {ms}, N={gn}, K={gk}): {grouped_gemm}",
               file=sys.stderr, flush=True)
-        del probs
+        del probs, fprobs
 
     # per-CU busy / idle skew of each scheduler (witness launches, untimed):
     # 8192^3 and the ragged shapes
