@@ -13,8 +13,10 @@ from tests.gpu_util import config, dev_bf16, dev_f32, note
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("sched", ["work_stealing", "grouped"])
+@pytest.mark.parametrize("sched", ["work_stealing", "grouped", "work_stealing_xcc", "stream_k"])
 def test_gemm_graph_replays(sched):
+    # stream-K: the eager call below sizes the workspace first, so the
+    # captured call allocates nothing
     cfg = config()
     M, N, K = 1536, 1280, 512
     A = dev_bf16(bf16_bits_uniform((M, K), 71))
@@ -63,3 +65,42 @@ def test_add_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {r}"
+
+
+def test_grouped_gemm_and_multi_add_graph_replays():
+    """Several GEMMs and several adds per launch, captured together."""
+    cfg = config()
+    shapes = [(512, 256, 128), (300, 512, 256), (64, 128, 64)]
+    probs, refs = [], []
+    for g, (M, N, K) in enumerate(shapes):
+        A = dev_bf16(bf16_bits_uniform((M, K), 80 + g))
+        B = dev_bf16(bf16_bits_uniform((K, N), 90 + g))
+        probs.append((A, B, torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0"), M, N, K))
+    adds = []
+    for g, (r, c) in enumerate([(700, 900), (64, 4096)]):
+        X, Y = dev_f32(f32_normal((r, c), 100 + g)), dev_f32(f32_normal((r, c), 110 + g))
+        adds.append((X, Y, torch.empty_like(X), r, c))
+    note("graph grouped GEMM + several adds")
+    pg.pgemm_run_grouped(cfg, probs, "bf16_out_bf16", "work_stealing")
+    pg.padd_run_multi(cfg, adds, 32, 16, "work_stealing")
+    torch.cuda.synchronize()
+    refs = [p[2].clone() for p in probs] + [a[2].clone() for a in adds]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pg.pgemm_run_grouped(cfg, probs, "bf16_out_bf16", "work_stealing")
+            pg.padd_run_multi(cfg, adds, 32, 16, "work_stealing")
+    torch.cuda.synchronize()
+    outs = [p[2] for p in probs] + [a[2] for a in adds]
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, ref) in enumerate(zip(outs, refs)):
+            assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o.view(torch.int32),
+                               ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), \
+                f"replay {r} output {i}"
+
