@@ -55,8 +55,10 @@ typedef enum {
   /* A, B OCP e4m3 bytes with one e8m0 scale byte per 128 consecutive K
    * elements per row of A (a_scale[K/128][M]) and per column of B
    * (b_scale[K/128][N]); value = e4m3(q) * 2^(scale - 127); fp32
-   * accumulate; C bf16.  K must be a multiple of 128, N a multiple of 16,
-   * and A, B, C 16-byte aligned (otherwise PGEMM_ERR_UNSUPPORTED). */
+   * accumulate; C bf16.  K must be a multiple of 128 (PGEMM_ERR_INVALID
+   * otherwise); N a multiple of 16, A, B, C 16-byte aligned, and one tile's
+   * panels within 32-bit byte offsets (tile_m*K, 128*N and tile_m*N*2 all
+   * below 2^31) (PGEMM_ERR_UNSUPPORTED otherwise). */
   PGEMM_FP8E4M3_B128_OUT_BF16 = 2
 } pgemm_dtype;
 
@@ -175,8 +177,11 @@ PGEMM_API pgemm_status pgemm_config_destroy(pgemm_config* cfg);
 
 /* C[M][N] = A[M][K] . B[K][N], all dense row-major on device `cfg`'s GPU.
  * A, B, C: device pointers owned by the caller; C must not alias A or B.
- * Elements of C outside [0, M) x [0, N) are never written.  With
- * PGEMM_SCHED_WORK_STEALING the counters are zeroed on `hip_stream` first.
+ * Elements of C outside [0, M) x [0, N) are never written.  With either
+ * work-stealing scheduler the counters are zeroed on `hip_stream` first.
+ * bf16 shapes the direct-to-LDS kernel cannot take (unaligned pointers, K
+ * or N not a multiple of 8, a tile's panels past 32-bit byte offsets) run
+ * on the register-staged kernel, which addresses with 64-bit offsets.
  * A config holds one counter array: calls with the same config on different
  * streams must not overlap.  Errors: NULL pointer, M, N or K < 1,
  * group_size < 1, grid < 1 (or < X for work stealing), fp8 without scales or
