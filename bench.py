@@ -60,7 +60,53 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only time a plain 256 MiB device-to-device copy (the reference kernel for "
                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--profile-only", choices=sorted(PROFILE_TARGETS), default=None,
+                   help="only time this one workload (for counter passes) and exit")
     return p.parse_args()
+
+
+# Single workloads for counter passes: name -> (kind, tile, scheduler).
+PROFILE_TARGETS = {
+    "add_8192sq_128x128_blocked": ("add", (128, 128), "blocked"),
+    "add_8192sq_128x128_work_stealing": ("add", (128, 128), "work_stealing"),
+    "add_8192sq_32x16_work_stealing": ("add", (32, 16), "work_stealing"),
+    "fp8_8192cube_work_stealing": ("fp8", (256, 256, 128), "work_stealing"),
+    "fp8_256x28672x8192_128x256_work_stealing": ("fp8_skinny", (128, 256, 128), "work_stealing"),
+}
+
+
+def profile_only(name, steps, warmup):
+    """Time one workload of the bench pass (same inputs) and print its event
+    time, so that a counter pass sees only that kernel (and the counter reset)."""
+    import torch
+    import tile_scheduling_persistent_amd as pg
+    from synthetic import f32_normal, fp8_blockscaled
+    kind, tile, sched = PROFILE_TARGETS[name]
+    cfg = pg.Config(0)
+    stream = torch.cuda.current_stream()
+    if kind == "add":
+        R = Cc = 8192
+        X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
+        Y = torch.from_numpy(f32_normal((R, Cc), 2002)).to("cuda:0")
+        Z = torch.empty_like(X)
+        nbytes, work = 3 * R * Cc * 4, None
+        fn = lambda: pg.padd_run(cfg, X, Y, Z, R, Cc, tile[0], tile[1], sched)  # noqa: E731
+    else:
+        m, n, k = (8192, 8192, 8192) if kind == "fp8" else (256, 28672, 8192)
+        qa, sa = fp8_blockscaled(m, k, 1050, 1052, k_major=True)
+        qb, sb = fp8_blockscaled(n, k, 1051, 1053, k_major=False)
+        dA, dB = torch.from_numpy(qa).to("cuda:0"), torch.from_numpy(qb).to("cuda:0")
+        dSA, dSB = torch.from_numpy(sa).to("cuda:0"), torch.from_numpy(sb).to("cuda:0")
+        dC = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
+        nbytes, work = m * k + k * n + (m + n) * (k // 128) + 2 * m * n, 2.0 * m * n * k
+        fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
+    _, ev_mean, _ = time_calls(fn, steps, warmup, stream)
+    out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5),
+           "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1)}
+    if work:
+        out["tflops"] = round(work / (ev_mean * 1e-3) / 1e12, 2)
+    print(json.dumps(out), flush=True)
 
 
 def copy_calibration(steps, warmup):
@@ -179,6 +225,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.steps, args.warmup)
+        return
+    if args.profile_only:
+        profile_only(args.profile_only, args.steps, args.warmup)
         return
     import torch
     import tile_scheduling_persistent_amd as pg
