@@ -99,6 +99,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   constexpr int NL = NO + S::NSC;                                // all loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per 64-deep step
   constexpr int NRD = 4 * S::SN + 2 * S::SM;                     // LDS reads per step
+  // B^T block sn of a slab's first step is first used by MFMA sn * SM; its
+  // reads go out after MFMA sn * SM - 3 (three 64-cycle MFMAs of slack), or
+  // with the slab's first reads if that is before MFMA 0.
+  constexpr auto early_b = [](int sn) { return sn * S::SM - 3; };
   // The operand loads of a slab are spread over the first SPREAD MFMAs of
   // the slab (load d after MFMA d*SPREAD/NO), one at a time rather than a
   // burst; its few scale-byte loads go out right after the loader's
@@ -437,33 +441,57 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       slab_barrier();
       const int st = g % NST;
       const int st_dma = st == 0 ? NST - 1 : st - 1;
+      // The slab's scale bytes gate every MFMA and the first step's B^T
+      // block 0 and A blocks gate the first ones, so those LDS reads go out
+      // first, all together; the loader's bookkeeping and the scale packing
+      // follow, and the other B^T blocks of the first step are read a few
+      // MFMAs before their first use (early_b).
+      unsigned sraw[S::SM + S::SN];
       {
         const unsigned char* scb = smem + st * S::STAGE + sc_off;
-        unsigned va = 0, vb = 0;
 #pragma unroll
         for (int s = 0; s < S::SM; ++s)
-          va |= (*reinterpret_cast<const unsigned*>(scb + (s * 32 + l32) * 4) & 0xffu) << (8 * s);
+          sraw[s] = *reinterpret_cast<const unsigned*>(scb + (s * 32 + l32) * 4);
 #pragma unroll
         for (int s = 0; s < S::SN; ++s)
-          vb |= (*reinterpret_cast<const unsigned*>(scb + S::SC_A * 256 + (s * 32 + l32) * 4) & 0xffu)
-                << (8 * s);
-        sa_reg = (int)va;
-        sb_reg = (int)vb;
+          sraw[S::SM + s] = *reinterpret_cast<const unsigned*>(scb + S::SC_A * 256 + (s * 32 + l32) * 4);
       }
 #pragma unroll
-      for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
+      for (int r = 0; r < 4 + 2 * S::SM; ++r) read(st, 0, 0, r);
+#pragma unroll
+      for (int sn = 1; sn < S::SN; ++sn)
+        if (early_b(sn) < 0)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) read(st, 0, 0, 4 * sn + q + 2 * S::SM);
+      __builtin_amdgcn_sched_barrier(0);
       prep();  // slab g + NST - 1; overlaps the latency of the first reads
 #pragma unroll
       for (int d = NO; d < NL; ++d) dma(st_dma, d);
       __builtin_amdgcn_sched_barrier(0);
-      // Fixed issue order: MFMA, then its share of the next step's LDS reads,
-      // then (first SPREAD MFMAs) a load of slab g+1.
+      {
+        unsigned va = 0, vb = 0;
+#pragma unroll
+        for (int s = 0; s < S::SM; ++s) va |= (sraw[s] & 0xffu) << (8 * s);
+#pragma unroll
+        for (int s = 0; s < S::SN; ++s) vb |= (sraw[S::SM + s] & 0xffu) << (8 * s);
+        sa_reg = (int)va;
+        sb_reg = (int)vb;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Fixed issue order: MFMA, then the first step's later B^T reads
+      // (first step only), its share of the next step's LDS reads, then
+      // (first SPREAD MFMAs) a load of slab g+1.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int j = 0; j < NMF; ++j) {
           mfma(ks, j);
           if (ks == 0) {
+#pragma unroll
+            for (int sn = 1; sn < S::SN; ++sn)
+              if (early_b(sn) == j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) read(st, 0, 0, 4 * sn + q + 2 * S::SM);
 #pragma unroll
             for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, 1, 1, r);
           }
