@@ -440,6 +440,22 @@ def main():
                 print(f"# add {tile} {sched}: {nbytes / (ev_mean * 1e-3) / 1e9:.0f} GB/s",
                       file=sys.stderr, flush=True)
 
+    # the same workloads through torch's own kernels on this machine (context,
+    # not a baseline): hipBLASLt for the 8192^3 bf16 GEMM, torch.add
+    vendor = {}
+    if not args.skip_extra:
+        Ct = torch.empty_like(C)
+        fn = lambda: torch.matmul(A, B, out=Ct)  # noqa: E731
+        _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+        vendor["torch_matmul_bf16_8192cube_tflops"] = round(flops / (ev_mean * 1e-3) / 1e12, 2)
+        del Ct
+    if not args.skip_add:
+        fn = lambda: torch.add(X, Y, out=Z)  # noqa: E731
+        _, ev_mean, _ = time_calls(fn, max(args.steps, 20), args.warmup, stream)
+        vendor["torch_add_8192sq_gbs"] = round(3 * 8192 * 8192 * 4 / (ev_mean * 1e-3) / 1e9, 1)
+    if vendor:
+        print(f"# torch on the same workloads: {vendor}", file=sys.stderr, flush=True)
+
     # several adds in one persistent launch against one launch per add
     multi_add = {}
     if not args.skip_add:
@@ -512,6 +528,7 @@ def main():
         "slow_xcc": slow_xcc,
         "fp8": fp8,
         "balance": bal,
+        "torch_same_box": vendor,
         "device": cfg.info,
     }
     if not args.no_cpu_baseline:
