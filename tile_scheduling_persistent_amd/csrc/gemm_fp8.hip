@@ -17,8 +17,10 @@
 // Data movement and issue order as in gemm_bf16_lds.hip: a ring of NST LDS
 // stages of 128-deep slabs filled by hand-issued buffer_load ... lds
 // (gemm_device.hpp), the loads of slab g + NST - 1 spread over the MFMAs of
-// slab g, the next step's fragment reads after each MFMA, the loader's
-// bookkeeping right after the barrier.  The scale bytes of a slab travel
+// slab g, the next step's fragment reads after each MFMA.  After the slab's
+// barrier the reads that gate the first MFMAs (scale bytes, first B^T
+// block, the A blocks) go out first and the loader's bookkeeping runs under
+// their latency.  The scale bytes of a slab travel
 // with it: byte-sized direct loads put each row's (column's) scale byte in
 // its own LDS dword of the stage, read back after the barrier.  Two stages
 // suit the MFMA-bound square tiles; a deeper ring keeps more bytes in
