@@ -403,7 +403,7 @@ def main():
     if not args.skip_extra:
         from synthetic import fp8_blockscaled
         for (m, n, k, tile) in [(256, 28672, 8192, (128, 128, 128)), (256, 28672, 8192, (128, 256, 128)),
-                                (8192, 8192, 8192, (256, 256, 128))]:
+                                (256, 28672, 8192, (256, 256, 128)), (8192, 8192, 8192, (256, 256, 128))]:
             qa, sa = fp8_blockscaled(m, k, 1050, 1052, k_major=True)
             qb, sb = fp8_blockscaled(n, k, 1051, 1053, k_major=False)
             dA, dB = torch.from_numpy(qa).to("cuda:0"), torch.from_numpy(qb).to("cuda:0")
@@ -412,7 +412,7 @@ def main():
             f = 2.0 * m * n * k
             nbytes = m * k + k * n + (m + n) * (k // 128) + 2 * m * n
             row = {}
-            for sched in ["grouped", "work_stealing"]:
+            for sched in ["grouped", "work_stealing", "stream_k"]:
                 a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
                 fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
                 _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
@@ -420,7 +420,7 @@ def main():
                               "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1),
                               "event_ms_mean": round(ev_mean, 5),
                               "grid": pg.plan_gemm(cfg, m, n, k, "fp8_b128_out_bf16", sched, a)["grid"]}
-            fp8[f"{m}x{n}x{k}" + ("" if tile[:2] in ((128, 128), (256, 256)) else f"_{tile[0]}x{tile[1]}")] = row
+            fp8[f"{m}x{n}x{k}_{tile[0]}x{tile[1]}"] = row
             print(f"# fp8 {m}x{n}x{k}: {row}", file=sys.stderr, flush=True)
             del dA, dB, dC, qa, qb
 

@@ -84,8 +84,9 @@ typedef enum {
  *                   Tiles split between runs are summed (fp32, slab order)
  *                   by a fix-up kernel from per-program partial-sum slots in
  *                   a workspace the config allocates on first use (G x 2
- *                   tiles of fp32).  bf16 direct-to-LDS kernel only (aligned
- *                   operands, K and N multiples of 8), no witness; otherwise
+ *                   tiles of fp32).  bf16 on the direct-to-LDS kernel
+ *                   (aligned operands, K and N multiples of 8) and block-
+ *                   scaled fp8, single problems, no witness; otherwise
  *                   PGEMM_ERR_UNSUPPORTED.  Results are deterministic but
  *                   not bitwise equal to the other schedulers on split
  *                   tiles (different summation order).

@@ -1,8 +1,9 @@
 """GPU parity of the stream-K scheduler (data-parallel full waves, slab runs
 for the rest, split tiles summed by the fix-up kernel) against the oracle,
-through the C ABI.  Tiles that no run splits are computed exactly as under
-the grouped scheduler (same tile, same slab order), so they must match it
-bit for bit; split tiles only within the tolerance."""
+through the C ABI, on the bf16 and the block-scaled fp8 kernels.  Tiles that
+no run splits are computed exactly as under the grouped scheduler (same
+tile, same slab order), so they must match it bit for bit; split tiles only
+within the tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -119,3 +120,60 @@ def test_streamk_unsupported_combinations():
     with pytest.raises(pg.PgemmError) as e:
         pg.pgemm_run(cfg, A2, B2, C, M, N, 100, "bf16_out_bf16", "stream_k")
     assert e.value.code == pg._abi.ERR_UNSUPPORTED
+
+
+# block-scaled fp8 under stream-K: N a multiple of 16, K of 128
+FP8_SHAPES = [(512, 512, 512), (1024, 1024, 128), (2048, 2048, 384), (1100, 912, 768),
+              (264, 8000, 256), (2304, 4352, 128)]
+FP8_TILES = [(128, 128, 128), (256, 256, 128), (128, 256, 128)]
+
+
+def _run_fp8(qa, sa, qb, sb, M, N, K, sched, tile):
+    from tests.gpu_util import dev_u8
+    cfg = config()
+    A, B, SA, SB = dev_u8(qa), dev_u8(qb), dev_u8(sa), dev_u8(sb)
+    C = Guarded(M * N, "bf16")
+    note(f"pgemm_run fp8 M={M} N={N} K={K} sched={sched} tile={tile}")
+    pg.pgemm_run(cfg, A, B, C.view, M, N, K, "fp8_b128_out_bf16", sched,
+                 pg.make_args(tile=tile, a_scale=SA, b_scale=SB))
+    torch.cuda.synchronize()
+    assert C.guards_intact(), (M, N, K, sched, tile)
+    return C
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES)
+def test_streamk_fp8_parity(shape):
+    from synthetic import fp8_blockscaled
+    from tests.gpu_util import FP8_TOL
+    M, N, K = shape
+    qa, sa = fp8_blockscaled(M, K, 3000 + M, 3002 + M, k_major=True)
+    qb, sb = fp8_blockscaled(N, K, 3001 + N, 3003 + N, k_major=False)
+    Cref, Abs = og.gemm_fp8_b128(qa, sa, qb, sb)
+    cfg = config()
+    for tile in FP8_TILES:
+        C = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
+        assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shape} {tile}")
+        Cg = _run_fp8(qa, sa, qb, sb, M, N, K, "grouped", tile)
+        G = pg.plan_gemm(cfg, M, N, K, "fp8_b128_out_bf16", "stream_k", pg.make_args(tile=tile))["grid"]
+        split = _split_mask(M, N, K, tile, G)
+        same = C.body_bits().reshape(M, N) == Cg.body_bits().reshape(M, N)
+        assert np.all(same | split), f"fp8 {shape} {tile}: unsplit tiles differ from grouped"
+
+
+def test_streamk_fp8_skinny_256x28672x8192():
+    """Workload 5a under stream-K: 112 tiles at 256x256 (all split over the
+    grid) and 224 at 128x256; sampled rows against the oracle, and two runs
+    bit-identical."""
+    from oracle.codecs import dequant_fp8_a, dequant_fp8_b
+    from synthetic import fp8_blockscaled
+    from tests.gpu_util import FP8_TOL
+    M, N, K = 256, 28672, 8192
+    qa, sa = fp8_blockscaled(M, K, 1050, 1052, k_major=True)
+    qb, sb = fp8_blockscaled(N, K, 1051, 1053, k_major=False)
+    rows = np.array([0, 1, 31, 64, 127, 128, 200, 255])
+    Cref, Abs = og.gemm_f64(dequant_fp8_a(qa[rows], sa[:, rows]), dequant_fp8_b(qb, sb))
+    for tile in [(256, 256, 128), (128, 256, 128)]:
+        C = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
+        assert_north_star(C.as_f64().reshape(M, N)[rows], Cref, Abs, FP8_TOL, f"5a stream_k {tile}")
+        C2 = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
+        assert np.array_equal(C.body_bits(), C2.body_bits()), f"5a stream_k {tile}: runs differ"

@@ -136,7 +136,7 @@ def test_fp8_a_beyond_4gib():
     Cref, Abs = og.gemm_f64(dequant_fp8_a(qa_base[rows % P_A], sa_base[:, rows % P_A]),
                             dequant_fp8_b(qb, sb))
     for sched, tile in [("work_stealing", (256, 256, 128)), ("grouped", (128, 128, 128)),
-                        ("interleaved", (128, 256, 128))]:
+                        ("interleaved", (128, 256, 128)), ("stream_k", (256, 256, 128))]:
         C = BigOut(M * N, wide=False)
         note(f"pgemm_run fp8 M={M} N={N} K={K} sched={sched} tile={tile}")
         pg.pgemm_run(cfg, A, B, C.body.view(torch.bfloat16), M, N, K, "fp8_b128_out_bf16", sched,

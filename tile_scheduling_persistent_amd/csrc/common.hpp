@@ -140,6 +140,7 @@ struct KernelInfo {
 };
 hipError_t launch_gemm_bf16_lds_sk(const GemmParams& p, int bm, int bn, bool out_bf16,
                                    hipStream_t stream);
+hipError_t launch_gemm_fp8_sk(const GemmParams& p, int bm, int bn, hipStream_t stream);
 hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, hipStream_t stream);
 hipError_t launch_gemm_bf16_lds_grouped(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
                                         hipStream_t stream);

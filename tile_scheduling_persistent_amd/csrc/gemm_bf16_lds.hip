@@ -667,6 +667,8 @@ hipError_t launch_sk_fixup(const SkFixParams& f, int bm, int bn, bool out_bf16, 
       hipLaunchKernelGGL((sk_fixup_kernel<128, 128, true>), blocks, threads, 0, stream, f);
     else
       hipLaunchKernelGGL((sk_fixup_kernel<128, 128, false>), blocks, threads, 0, stream, f);
+  } else if (bm == 128 && bn == 256 && out_bf16) {  // the fp8 kernel's 128x256 tile
+    hipLaunchKernelGGL((sk_fixup_kernel<128, 256, true>), blocks, threads, 0, stream, f);
   } else {
     return hipErrorInvalidValue;
   }

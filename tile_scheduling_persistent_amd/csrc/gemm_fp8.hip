@@ -41,6 +41,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
@@ -94,9 +95,14 @@ __device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa
 // GRP: several GEMMs in one launch (virtual tile ids shared by prefix sums,
 // P.gp[g] from tile0 on); the loader and the matrix cores each look up the
 // problem of their tile (operands, scales, sizes, slab count, output).
-template <int BM, int BN, int NST, bool WITNESS, bool GRP>
+// SK: stream-K.  The program walks the segments (tile, first slab, end slab)
+// of its stream-K run; a segment that does not cover its tile leaves fp32
+// partial sums in the program's workspace slot, summed and stored by the
+// fix-up kernel after this launch (the same one as the bf16 path's).
+template <int BM, int BN, int NST, bool WITNESS, bool GRP, bool SK = false>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   using S = Shape<BM, BN, NST>;
+  static_assert(!(SK && (GRP || WITNESS)), "stream-K runs one problem, without the witness");
   constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NO = NA + NB;  // operand loads per wave per slab
   constexpr int NL = NO + S::NSC;                                // all loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per 64-deep step
@@ -216,6 +222,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
 
   // ---- loader state ----
   int lt = -1, lk = 0;      // loader: tile, next slab
+  int lke = nkl;            // loader: end slab of its segment
   // Tiles the loader moved on to that the matrix cores have not reached: the
   // loader runs NST - 1 slabs ahead, so with one slab per tile that many can
   // wait (oldest first).
@@ -233,15 +240,24 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   unsigned soa[S::SC_A], sob[S::SC_B];
   rsrc_words_t rSA, rSB;    // scale rows of the slab being loaded
 
+  // Stream-K segment walkers of this program: one for the loader, one for
+  // the matrix cores (the same sequence, read at different times).
+  pgs::SkWalker lw, cw;
+  if (SK) {
+    lw.init(prog, P.s.T, P.s.G, P.K / BK);
+    cw.init(prog, P.s.T, P.s.G, P.K / BK);
+  }
+
   // Pick the next slab for the loader (moving on to the next tile once the
   // current one is issued), set up its resources and load its scales;
   // without one the resources are empty and the loads read zeros into a
   // stage no one reads.
-  // The loader moves on to tile t (t >= 0): per-tile bases, B offsets with
-  // column chunks past N pushed out of range, scale byte offsets.
-  auto begin_tile = [&](int t) {
+  // The loader moves on to slabs [kb, ke) of tile t (t >= 0; ke < 0: to the
+  // end of the tile): per-tile bases, B offsets with column chunks past N
+  // pushed out of range, scale byte offsets.
+  auto begin_tile = [&](int t, int kb, int ke) {
     lt = t;
-    lk = 0;
+    lk = kb;
     if (GRP) {
       const GemmProblem pr = problem_of(t);
       Al = static_cast<const unsigned char*>(pr.A);
@@ -255,6 +271,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       lane_offsets(Kl, Nl);
       masked = true;  // bo is rebuilt from the new offsets
     }
+    lke = ke < 0 ? nkl : ke;
     coords(t, lm0, ln0);
     int rows = (Ml - lm0) < BM ? (Ml - lm0) : BM;
     rows = rows < 0 ? 0 : rows;  // never negative: an empty range reads zeros
@@ -284,27 +301,33 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
     // branches scalar.
     lt = __builtin_amdgcn_readfirstlane(lt);
     lk = __builtin_amdgcn_readfirstlane(lk);
+    lke = __builtin_amdgcn_readfirstlane(lke);
     claims = __builtin_amdgcn_readfirstlane(claims);
-    if (lt >= 0 && lk == nkl) {
-      const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
-      ++claims;
+    if (lt >= 0 && lk == lke) {
       lt = -1;
-      if (t >= 0) {
-        bool queued = false;  // into the first free entry (entries fill from 0)
+      if (SK) {
+        int v, kb, ke, slot;
+        if (lw.next(v, kb, ke, slot)) begin_tile(v, kb, ke);
+      } else {
+        const int t = __builtin_amdgcn_readfirstlane(s_next[claims & 1]);
+        ++claims;
+        if (t >= 0) {
+          bool queued = false;  // into the first free entry (entries fill from 0)
 #pragma unroll
-        for (int i = 0; i < NST - 1; ++i)
-          if (!queued && pend[i] < 0) {
-            pend[i] = t;
-            queued = true;
-          }
-        begin_tile(t);
+          for (int i = 0; i < NST - 1; ++i)
+            if (!queued && pend[i] < 0) {
+              pend[i] = t;
+              queued = true;
+            }
+          begin_tile(t, 0, -1);
+        }
       }
     }
     const int k0 = lk * BK;
     const bool load = lt >= 0;
     if (load) {
       ++lk;
-      if (lk == nkl && tid == 0) s_next[claims & 1] = walker.next(lt);
+      if (!SK && lk == lke && tid == 0) s_next[claims & 1] = walker.next(lt);
     }
     rA = rsrc_words_u64(a_ptr + (unsigned long long)k0, load ? a_rec - (unsigned)k0 : 0u);
     rB = rsrc_words_u64(b_ptr + (unsigned long long)k0 * (unsigned long long)Nl,
@@ -386,11 +409,43 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
         store_block_bf16(acc[sn][sm], rC, eb + sm * rstep, wn * S::TN + sn * 32, ncols, hi);
   };
 
-  if (tid == 0) s_first[0] = walker.first();
-  __syncthreads();
-  int ct = __builtin_amdgcn_readfirstlane(s_first[0]);  // tile on the matrix cores
+  // Stream-K: the accumulators of a partial segment, fp32, into slot `slot`
+  // of this program's workspace ([BM][BN], tile-relative).
+  auto store_partial = [&](int slot) {
+    float* wsb = P.ws + ((size_t)prog * 2 + slot) * (size_t)(BM * BN);
+    const int r0 = wm * S::TM + l32;
+    const int c0 = wn * S::TN + 4 * hi;
+#pragma unroll
+    for (int sm = 0; sm < S::SM; ++sm)
+#pragma unroll
+      for (int sn = 0; sn < S::SN; ++sn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[sn][sm];
+          *reinterpret_cast<f32x4*>(wsb + (r0 + sm * 32) * BN + c0 + sn * 32 + 8 * q) =
+              f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+  };
+
+  int ct = -1;               // tile on the matrix cores
+  int cnk = P.K / BK;        // its slab count
+  int cslot = -1;            // its partial-sum slot (stream-K)
+  if (SK) {
+    int kb, ke;
+    if (cw.next(ct, kb, ke, cslot)) cnk = ke - kb;
+  } else {
+    if (tid == 0) s_first[0] = walker.first();
+    __syncthreads();
+    ct = __builtin_amdgcn_readfirstlane(s_first[0]);
+  }
   if (ct >= 0) {
-    begin_tile(ct);
+    if (SK) {
+      int v, kb, ke, slot;
+      lw.next(v, kb, ke, slot);
+      begin_tile(v, kb, ke);
+    } else {
+      begin_tile(ct, 0, -1);
+    }
     // slabs 0 .. NST-2 into stages 0 .. NST-2 (a barrier between preps: a
     // claim thread 0 stores in one is read by every wave in the next)
 #pragma unroll
@@ -405,7 +460,6 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   int g = 0;   // slabs computed so far
   int it = 0;  // tiles finished
   int m0 = 0, n0 = 0;  // origin of tile ct
-  int cnk = P.K / BK;  // slabs of tile ct
   // The matrix cores move on to tile ct: its origin and (GRP) its problem's
   // output and slab count.
   auto compute_tile = [&]() {
@@ -506,12 +560,21 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       }
       ++g;
     }
-    epilogue(m0, n0);
+    if (SK && cslot >= 0)
+      store_partial(cslot);
+    else
+      epilogue(m0, n0);
     ++it;
-    ct = pend[0];
+    if (SK) {
+      int kb, ke;
+      ct = -1;
+      if (cw.next(ct, kb, ke, cslot)) cnk = ke - kb;
+    } else {
+      ct = pend[0];
 #pragma unroll
-    for (int i = 0; i + 1 < NST - 1; ++i) pend[i] = pend[i + 1];
-    pend[NST - 2] = -1;
+      for (int i = 0; i + 1 < NST - 1; ++i) pend[i] = pend[i + 1];
+      pend[NST - 2] = -1;
+    }
     if (ct >= 0) compute_tile();
   }
 
@@ -524,10 +587,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   }
 }
 
-template <int BM, int BN, int NST, bool WITNESS, bool GRP = false>
+template <int BM, int BN, int NST, bool WITNESS, bool GRP = false, bool SK = false>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   using S = Shape<BM, BN, NST>;
-  auto kern = gemm_fp8_kernel<BM, BN, NST, WITNESS, GRP>;
+  auto kern = gemm_fp8_kernel<BM, BN, NST, WITNESS, GRP, SK>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -581,6 +644,13 @@ hipError_t launch_gemm_fp8(const GemmParams& p, int bm, int bn, int bk, bool vec
     return witness ? launch_one<128, 128, 2, true>(p, stream) : launch_one<128, 128, 2, false>(p, stream);
   if (bm == 128 && bn == 256)
     return witness ? launch_one<128, 256, 3, true>(p, stream) : launch_one<128, 256, 3, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_fp8_sk(const GemmParams& p, int bm, int bn, hipStream_t stream) {
+  if (bm == 256 && bn == 256) return launch_one<256, 256, 2, false, false, true>(p, stream);
+  if (bm == 128 && bn == 128) return launch_one<128, 128, 2, false, false, true>(p, stream);
+  if (bm == 128 && bn == 256) return launch_one<128, 256, 3, false, false, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

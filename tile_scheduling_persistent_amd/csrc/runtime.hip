@@ -620,8 +620,9 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   if (st != PGEMM_OK) return st;
   const bool sk = sched == PGEMM_SCHED_STREAM_K;
   if (sk) {
-    // stream-K runs on the direct-to-LDS bf16 kernel, without the witness
-    if (ch.kernel != PGEMM_KERNEL_BF16_LDS) return PGEMM_ERR_UNSUPPORTED;
+    // stream-K runs on the direct-to-LDS bf16 kernel and the fp8 kernel,
+    // without the witness
+    if (ch.kernel != PGEMM_KERNEL_BF16_LDS && ch.kernel != PGEMM_KERNEL_FP8) return PGEMM_ERR_UNSUPPORTED;
     if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
     st = ensure_workspace(cfg, (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float));
     if (st != PGEMM_OK) return st;
@@ -637,7 +638,8 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
 
   hipError_t e;
   if (fp8)
-    e = pgk::launch_gemm_fp8(p, ch.bm, ch.bn, ch.bk, true, witness, stream);
+    e = sk ? pgk::launch_gemm_fp8_sk(p, ch.bm, ch.bn, stream)
+           : pgk::launch_gemm_fp8(p, ch.bm, ch.bn, ch.bk, true, witness, stream);
   else if (sk)
     e = pgk::launch_gemm_bf16_lds_sk(p, ch.bm, ch.bn, ch.out_bf16, stream);
   else if (ch.kernel == PGEMM_KERNEL_BF16_LDS)
