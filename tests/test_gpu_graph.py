@@ -44,6 +44,38 @@ def test_gemm_graph_replays(sched):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
 
 
+@pytest.mark.parametrize("sched", ["work_stealing", "stream_k"])
+def test_fp8_gemm_graph_replays(sched):
+    """Block-scaled fp8 under work stealing and stream-K (1536x1280 at
+    256x256 tiles: 30 tiles on 256 programs, so stream-K splits every one)."""
+    from synthetic import fp8_blockscaled
+    from tests.gpu_util import dev_u8
+    cfg = config()
+    M, N, K = 1536, 1280, 512
+    qa, sa = fp8_blockscaled(M, K, 75, 77, k_major=True)
+    qb, sb = fp8_blockscaled(N, K, 76, 78, k_major=False)
+    A, B, SA, SB = dev_u8(qa), dev_u8(qb), dev_u8(sa), dev_u8(sb)
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty_like(ref)
+    args = pg.make_args(tile=(256, 256, 128), a_scale=SA, b_scale=SB)
+    note(f"graph fp8 gemm {M}x{N}x{K} {sched}")
+    pg.pgemm_run(cfg, A, B, ref, M, N, K, "fp8_b128_out_bf16", sched, args)  # eager; sizes the workspace
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pg.pgemm_run(cfg, A, B, out, M, N, K, "fp8_b128_out_bf16", sched, args)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        pg.pgemm_run(cfg, A, B, ref, M, N, K, "fp8_b128_out_bf16", sched, args)  # eager call in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+
+
 def test_add_graph_replays():
     cfg = config()
     rows, cols = 1000, 3000
