@@ -70,6 +70,9 @@ PROFILE_TARGETS = {
     "add_8192sq_128x128_blocked": ("add", (128, 128), "blocked"),
     "add_8192sq_128x128_work_stealing": ("add", (128, 128), "work_stealing"),
     "add_8192sq_32x16_work_stealing": ("add", (32, 16), "work_stealing"),
+    "add_8192sq_32x16_blocked": ("add", (32, 16), "blocked"),
+    "add_8192sq_32x16_interleaved": ("add", (32, 16), "interleaved"),
+    "add_8192sq_128x128_interleaved": ("add", (128, 128), "interleaved"),
     "fp8_8192cube_work_stealing": ("fp8", (256, 256, 128), "work_stealing"),
     "fp8_256x28672x8192_128x256_work_stealing": ("fp8_skinny", (128, 256, 128), "work_stealing"),
 }
