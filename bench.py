@@ -223,7 +223,7 @@ def cpu_baseline(a_bits, b_bits):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1 "
                                    "(the sharding plan is described, not run)"}))
         sys.exit(2)
     if args.copy_calibration:
@@ -443,7 +443,7 @@ def main():
                 print(f"# add {tile} {sched}: {nbytes / (ev_mean * 1e-3) / 1e9:.0f} GB/s",
                       file=sys.stderr, flush=True)
 
-    # the same workloads through torch's own kernels on this machine (context,
+    # the same workloads through torch's own kernels on this GPU (context,
     # not a baseline): hipBLASLt for the 8192^3 bf16 GEMM, torch.add
     vendor = {}
     if not args.skip_extra:

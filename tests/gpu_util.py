@@ -88,7 +88,7 @@ def assert_within(C: np.ndarray, Cref: np.ndarray, Abs: np.ndarray, tol: float,
         raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance, e.g. {rows}")
 
 
-def assert_north_star(C: np.ndarray, Cref: np.ndarray, Abs: np.ndarray, tol: float,
+def assert_abs_bound(C: np.ndarray, Cref: np.ndarray, Abs: np.ndarray, tol: float,
                       what: str = "") -> None:
     """The plain bound |C - Cref| <= tol * Abs, final rounding included."""
     err = np.abs(np.asarray(C, np.float64) - Cref)

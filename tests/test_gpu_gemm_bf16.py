@@ -9,7 +9,7 @@ import tile_scheduling_persistent_amd as pg
 from oracle import gemm as og
 from oracle.codecs import bf16_to_f64
 from synthetic import bf16_bits_normal, bf16_bits_uniform
-from tests.gpu_util import (BF16_TOL, Guarded, assert_north_star, assert_within, config,
+from tests.gpu_util import (BF16_TOL, Guarded, assert_abs_bound, assert_within, config,
                             dev_bf16, note)
 
 pytestmark = pytest.mark.gpu
@@ -104,7 +104,7 @@ def test_cfg1_512_fp32_out_full():
     Cref, Abs = og.gemm_bf16(a, b)
     C = run_gemm(a, b, M, N, K, "bf16_out_f32", "blocked", (128, 128, 64))
     assert C.guards_intact()
-    assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, "512^3")
+    assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, "512^3")
     for sched in SCHEDS[1:]:
         C2 = run_gemm(a, b, M, N, K, "bf16_out_f32", sched, (128, 128, 64))
         assert np.array_equal(C2.body_bits(), C.body_bits()), sched
@@ -115,7 +115,7 @@ def _sampled_check(a, b, C, M, N, rows, tol, what):
     B = bf16_to_f64(b)
     Cref, Abs = og.gemm_f64_sampled(A, B, rows, np.arange(N))
     got = C.as_f64().reshape(M, N)[rows, :]
-    assert_north_star(got, Cref, Abs, tol, what)
+    assert_abs_bound(got, Cref, Abs, tol, what)
 
 
 def _edge_rows(M, BM, rng, k=16):

@@ -11,7 +11,7 @@ import tile_scheduling_persistent_amd as pg
 from oracle import gemm as og
 from oracle import sched_model as sm
 from synthetic import bf16_bits_uniform, fp8_blockscaled
-from tests.gpu_util import BF16_TOL, FP8_TOL, Guarded, assert_north_star, assert_within, config, dev_bf16, note
+from tests.gpu_util import BF16_TOL, FP8_TOL, Guarded, assert_abs_bound, assert_within, config, dev_bf16, note
 
 pytestmark = pytest.mark.gpu
 
@@ -169,5 +169,5 @@ def test_grouped_fp8_parity(tile, si):
             assert np.array_equal(C.body_bits(), alone[g]), f"fp8 {shapes[g]} {sched}: differs from its own pgemm_run"
             if sched == "grouped":
                 Cref, Abs = og.gemm_fp8_b128(qa, sa, qb, sb)
-                assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shapes[g]} {tile}")
+                assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shapes[g]} {tile}")
 

@@ -13,7 +13,7 @@ from oracle import gemm as og
 from oracle import sched_model as sm
 from oracle.codecs import bf16_to_f64
 from synthetic import bf16_bits_normal, bf16_bits_uniform
-from tests.gpu_util import (BF16_TOL, Guarded, assert_north_star, assert_within, config,
+from tests.gpu_util import (BF16_TOL, Guarded, assert_abs_bound, assert_within, config,
                             dev_bf16, note)
 
 pytestmark = pytest.mark.gpu
@@ -99,7 +99,7 @@ def test_streamk_ragged_configs(shape):
     rows |= set(rng.integers(0, M, size=16).tolist())
     rows = np.array(sorted(rows))
     Cref, Abs = og.gemm_f64_sampled(bf16_to_f64(a), bf16_to_f64(b), rows, np.arange(N))
-    assert_north_star(C.as_f64().reshape(M, N)[rows, :], Cref, Abs, BF16_TOL, f"{shape} stream_k")
+    assert_abs_bound(C.as_f64().reshape(M, N)[rows, :], Cref, Abs, BF16_TOL, f"{shape} stream_k")
 
 
 def test_streamk_unsupported_combinations():
@@ -152,7 +152,7 @@ def test_streamk_fp8_parity(shape):
     cfg = config()
     for tile in FP8_TILES:
         C = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
-        assert_north_star(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shape} {tile}")
+        assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"fp8 {shape} {tile}")
         Cg = _run_fp8(qa, sa, qb, sb, M, N, K, "grouped", tile)
         G = pg.plan_gemm(cfg, M, N, K, "fp8_b128_out_bf16", "stream_k", pg.make_args(tile=tile))["grid"]
         split = _split_mask(M, N, K, tile, G)
@@ -174,6 +174,6 @@ def test_streamk_fp8_skinny_256x28672x8192():
     Cref, Abs = og.gemm_f64(dequant_fp8_a(qa[rows], sa[:, rows]), dequant_fp8_b(qb, sb))
     for tile in [(256, 256, 128), (128, 256, 128)]:
         C = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
-        assert_north_star(C.as_f64().reshape(M, N)[rows], Cref, Abs, FP8_TOL, f"5a stream_k {tile}")
+        assert_abs_bound(C.as_f64().reshape(M, N)[rows], Cref, Abs, FP8_TOL, f"5a stream_k {tile}")
         C2 = _run_fp8(qa, sa, qb, sb, M, N, K, "stream_k", tile)
         assert np.array_equal(C.body_bits(), C2.body_bits()), f"5a stream_k {tile}: runs differ"
