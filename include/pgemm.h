@@ -137,8 +137,13 @@ typedef enum {
 typedef struct {
   int tile_m, tile_n, tile_k; /* 0 => default: bf16 256x256x64, fp8 256x256x128 */
   int group_size;             /* grouped order rows per group; 0 => 8 */
-  int grid;                   /* programs; 0 => number of CUs x workgroups of the selected
-                                 kernel one CU holds at once (see pgemm_plan_gemm) */
+  int grid;                   /* programs; 0 => G0 = number of CUs x workgroups of the selected
+                                 kernel one CU holds at once; the GEMM's data-parallel
+                                 schedulers then take the balanced grid: the fewest
+                                 programs, a multiple of the XCD count X, that finish in
+                                 as many rounds of tiles as G0 (each XCD's ceil(T/X)
+                                 tiles over ceil(T/X) / rounds programs); stream-K and
+                                 the add keep G0 (see pgemm_plan_gemm) */
   int claim_chunk;            /* tiles per work-stealing claim (consecutive in the counter's
                                  range); GEMM 1..64 or PGEMM_CLAIM_PAIRS, 0 => 1; add 1..U
                                  (tiles a program handles per step), 0 => U */

@@ -185,6 +185,28 @@ def ws_programs_per_xcd(G: int, X: int) -> List[int]:
     return [sum(1 for p in range(G) if p % X == x) for x in range(X)]
 
 
+def ws_rounds(T: int, G: int, X: int) -> int:
+    """Rounds of tiles the busiest program of per-XCD work stealing takes at
+    equal tile times: the most, over the XCDs, of ceil(range length /
+    programs on that counter) (counter p mod X)."""
+    return max(cdiv(e - b, w) if w else (0 if e == b else 10**9)
+               for (b, e), w in zip(ws_ranges(T, X), ws_programs_per_xcd(G, X)))
+
+
+def balanced_grid(T: int, G: int, X: int) -> int:
+    """Default grid of the data-parallel GEMM schedulers, by its definition:
+    the smallest multiple of X, at most G, under which per-XCD work stealing
+    takes no more rounds than under G programs (searched one multiple at a
+    time).  G when T < 1, G < X or G is not a multiple of X."""
+    if T < 1 or G < X or G % X:
+        return G
+    want = ws_rounds(T, G, X)
+    for g in range(X, G + 1, X):
+        if ws_rounds(T, g, X) <= want:
+            return g
+    return G
+
+
 def ws_final_counters(T: int, G: int, X: int, chunk=1) -> List[int]:
     """Counter values after a complete launch: every successful claim and
     exactly one failing claim per program each added ``chunk`` (under

@@ -182,6 +182,12 @@ static int pairs_map(int G, int X) {
   return 0;
 }
 
+// Default GEMM grid for T = 0..Tmax tiles: T and the balanced grid.
+static int grid_map(int Tmax, int G, int X) {
+  for (int T = 0; T <= Tmax; ++T) std::printf("%d %d\n", T, pgs::balanced_grid(T, G, X));
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc < 2) return 2;
   const std::string mode = argv[1];
@@ -195,6 +201,7 @@ int main(int argc, char** argv) {
     return wsx_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                        std::atoi(argv[6]), std::atoi(argv[7]));
   if (mode == "pairs" && argc == 4) return pairs_map(std::atoi(argv[2]), std::atoi(argv[3]));
+  if (mode == "grid" && argc == 5) return grid_map(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   if (mode == "sk" && argc == 5)
     return sk_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   return 2;

@@ -168,19 +168,28 @@ def test_slow_xcc_rebalanced_by_stealing_across_xccs():
 
 
 def test_plan_matches_launch_shape():
-    """The default persistent grid is CUs x resident workgroups per CU of the
-    selected kernel: two for 128x128 GEMM tiles, one for 256x256."""
+    """The persistent grid starts from CUs x resident workgroups per CU of the
+    selected kernel (two for 128x128 GEMM tiles, one for 256x256); the GEMM's
+    data-parallel schedulers trim it to the balanced grid of the oracle's
+    schedule model, stream-K and the add keep all of it."""
     cfg = config()
-    cus = cfg.info["num_cus"]
+    cus, X = cfg.info["num_cus"], cfg.info["num_xcds"]
     big = pg.plan_gemm(cfg, 8192, 8192, 8192, "bf16_out_bf16", "work_stealing")
     small = pg.plan_gemm(cfg, 4096, 4096, 4096, "bf16_out_bf16", "work_stealing",
                          pg.make_args(tile=(128, 128, 64)))
     fp8 = pg.plan_gemm(cfg, 256, 28672, 8192, "fp8_b128_out_bf16", "grouped",
                        pg.make_args(tile=(128, 128, 128)))
+    ragged = pg.plan_gemm(cfg, 5120, 5120, 4096, "bf16_out_bf16", "interleaved")
+    ragged_sk = pg.plan_gemm(cfg, 5120, 5120, 4096, "bf16_out_bf16", "stream_k")
     add = pg.plan_add(cfg, 8192, 8192, 128, 128, "blocked")
-    note(f"plans {big} {small} {fp8} {add}")
-    for pl in (big, small, fp8, add):
-        assert pl["occupancy"] >= 1 and pl["grid"] == cus * pl["occupancy"]
+    note(f"plans {big} {small} {fp8} {ragged} {ragged_sk} {add}")
+    for pl in (big, small, fp8, ragged):
+        assert pl["occupancy"] >= 1
+        assert pl["grid"] == sm.balanced_grid(pl["tiles"], cus * pl["occupancy"], X)
+    for pl in (ragged_sk, add):
+        assert pl["grid"] == cus * pl["occupancy"]
+    if cus == 256 and X == 8:
+        assert (big["grid"], small["grid"], fp8["grid"], ragged["grid"]) == (256, 512, 448, 200)
     assert big["kernel"] == "bf16_lds" and big["tiles"] == 32 * 32 and big["occupancy"] == 1
     assert small["kernel"] == "bf16_lds" and small["occupancy"] == 2
     assert fp8["kernel"] == "fp8" and fp8["tiles"] == 2 * 224 and fp8["occupancy"] == 2

@@ -82,7 +82,9 @@ def test_grouped_schedule(sched):
     grids = [(-(-M // 128), -(-N // 128)) for M, N, K in shapes]
     T = sm.multi_offsets(grids)[-1]
     cfg = config()
-    G = pg.plan_gemm(cfg, 512, 512, 256, "bf16_out_bf16", sched, pg.make_args(tile=tile))["grid"]
+    # the launch's grid: the balanced grid of all problems' tiles together
+    occ = pg.plan_gemm(cfg, 512, 512, 256, "bf16_out_bf16", sched, pg.make_args(tile=tile))["occupancy"]
+    G = sm.balanced_grid(T, cfg.info["num_cus"] * occ, cfg.info["num_xcds"])
     cfg.witness_enable(T, G)
     _run(shapes, _data(shapes, 4100), "bf16_out_bf16", sched, tile, debug_flags=pg._abi.DEBUG_WITNESS)
     w = cfg.witness_read(T, G)

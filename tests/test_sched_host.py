@@ -111,3 +111,15 @@ def test_pair_claim_map_matches_model(harness):
         assert L == sm.pair_span(n, 256, 8) and claims == sm.pair_claims(n, 256, 8), n
         want = [t for k in range(claims) for t in sm.pair_claim(k, n, 256, 8)]
         assert tiles == want, n
+
+
+@pytest.mark.parametrize("G,X", [(256, 8), (512, 8), (64, 4), (13, 8), (8, 8), (7, 8), (32, 1)])
+def test_balanced_grid_matches_model(harness, G, X):
+    """The library's default GEMM grid equals the oracle's search over
+    multiples of X for every tile count up to 3000."""
+    out = subprocess.run([harness, "grid", "3000", str(G), str(X)], check=True, capture_output=True,
+                         text=True).stdout.strip().splitlines()
+    assert len(out) == 3001
+    for line in out:
+        T, g = map(int, line.split())
+        assert g == sm.balanced_grid(T, G, X), (T, G, X, g)

@@ -403,3 +403,49 @@ def test_multi_checker_catches_planted_mistakes():
     seqs[2].pop()                              # a tile dropped
     with pytest.raises(AssertionError):
         sm.check_multi_partition(seqs, grids)
+
+
+# Balanced default grid, values worked by hand from its definition (256 CUs,
+# 8 XCDs, one program per CU at 256x256 tiles, two at 128x128):
+#   T = 400: ranges of 50 tiles, 32 programs per XCD take 2 rounds; 25 per XCD
+#   also take 2 (50 / 25), 24 would take 3, so 200 programs.
+#   T = 608: ranges of 76, 3 rounds at 32; 26 per XCD take 3 (76 / 26 < 3),
+#   25 take 4, so 208.  T = 336: ranges of 42, 2 rounds; 21 per XCD, 168.
+#   T = 1024: ranges of 128, 4 rounds, 32 per XCD, 256 (unchanged).
+#   T = 16: ranges of 2, 1 round, 2 per XCD, 16.  T = 1: one range of 1
+#   tile (the others empty), 1 per XCD, 8.  T = 448 at 512 programs: ranges
+#   of 56, 1 round at 64 per XCD, 56 per XCD, 448.  T = 1025: ranges of 128
+#   or 129, 5 rounds at 32 per XCD; 26 per XCD also take 5 (129 / 26 < 5),
+#   25 take 6, so 208.  T = 257: ranges of 32 or 33, 2 rounds; 17 per XCD, 136.
+@pytest.mark.parametrize("T,G,want", [(400, 256, 200), (608, 256, 208), (336, 256, 168),
+                                      (1024, 256, 256), (16, 256, 16), (1, 256, 8),
+                                      (448, 512, 448), (0, 256, 256), (112, 256, 112),
+                                      (1025, 256, 208), (257, 256, 136)])
+def test_balanced_grid_hand_values(T, G, want):
+    assert sm.balanced_grid(T, G, 8) == want
+
+
+@pytest.mark.parametrize("G,X", [(256, 8), (512, 8), (64, 4), (24, 8)])
+def test_balanced_grid_properties(G, X):
+    """No scheduler takes more rounds under the balanced grid than work
+    stealing under G (static walks counted from the model's own schedules),
+    one multiple of X fewer would take more, and it never exceeds G."""
+    for T in list(range(1, 400)) + [400, 608, 336, 1024, 1500, 2048]:
+        g = sm.balanced_grid(T, G, X)
+        assert g % X == 0 and X <= g <= G, (T, g)
+        want = sm.ws_rounds(T, G, X)
+        assert sm.ws_rounds(T, g, X) <= want
+        if g > X:
+            assert sm.ws_rounds(T, g - X, X) > want, (T, g)
+        if T <= 400:
+            pm = T  # one row of tiles per column: the static walks over T tiles
+            for kind in ("blocked", "interleaved"):
+                seqs = sm.static_schedule(kind, pm, 1, g)
+                assert max(len(s) for s in seqs) <= want, (kind, T, g)
+
+
+def test_balanced_grid_planted_mistake():
+    """A grid one multiple of X too small (a plausible off-by-one in the
+    rounding) takes an extra round on a wave-quantised shape."""
+    T, G, X = 608, 256, 8
+    assert sm.ws_rounds(T, sm.balanced_grid(T, G, X) - X, X) == sm.ws_rounds(T, G, X) + 1

@@ -92,7 +92,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
-                        int num_pid_m, int num_pid_n, int default_grid, pgk::SchedParams& s) {
+                        int num_pid_m, int num_pid_n, int default_grid, bool balance,
+                        pgk::SchedParams& s) {
   if ((int)sched < 0 || (int)sched > 6) return PGEMM_ERR_INVALID;
   const int64_t T = (int64_t)num_pid_m * num_pid_n;
   if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
@@ -100,6 +101,10 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.T = (int)T;
   s.G = (args && args->grid) ? args->grid : default_grid;
   s.X = cfg->num_xcds;
+  // GEMM default: trimmed to the balanced grid (stream-K keeps every
+  // program: it splits the last round's tiles over all of them).
+  if (balance && !(args && args->grid) && sched != PGEMM_SCHED_STREAM_K)
+    s.G = pgs::balanced_grid(s.T, s.G, s.X);
   s.gs = (args && args->group_size) ? args->group_size : kDefaultGroup;
   s.num_pid_m = num_pid_m;
   s.num_pid_n = num_pid_n;
@@ -399,7 +404,7 @@ pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int
   DeviceGuard gd(dev);
   if (!gd.ok) return PGEMM_ERR_DEVICE;
   const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
-  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, p.s);
+  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, false, p.s);
   if (st != PGEMM_OK) return st;
   const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
   p.s.chunk = step;
@@ -499,7 +504,7 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   const pgk::KernelInfo ki =
       fp8 ? pgk::info_gemm_fp8_grouped(bm, bn) : pgk::info_gemm_bf16_lds_grouped(bm, bn, csz == 2);
   if (ki.threads == 0) return PGEMM_ERR_UNSUPPORTED;
-  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, p.s);
+  pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
@@ -616,7 +621,7 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   DeviceGuard g(dev);
   if (!g.ok) return PGEMM_ERR_DEVICE;
   const pgk::KernelInfo ki = gemm_info(ch);
-  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, p.s);
+  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
   const bool sk = sched == PGEMM_SCHED_STREAM_K;
   if (sk) {
@@ -696,7 +701,7 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
   DeviceGuard g(dev);
   if (!g.ok) return PGEMM_ERR_DEVICE;
   const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
-  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, p.s);
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, false, p.s);
   if (st != PGEMM_OK) return st;
   const int step = pgk::padd_tiles_per_step(tile_rows, tile_cols);
   p.s.chunk = step;
@@ -729,7 +734,7 @@ pgemm_status pgemm_plan_gemm(pgemm_config* cfg, const void* A, const void* B, co
   if (!g.ok) return PGEMM_ERR_DEVICE;
   const pgk::KernelInfo ki = gemm_info(ch);
   pgk::SchedParams s;
-  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, s);
+  st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, true, s);
   if (st != PGEMM_OK) return st;
   fill_plan(s, ki, ch.bm, ch.bn, ch.bk, ch.kernel, out);
   return PGEMM_OK;
@@ -750,7 +755,7 @@ pgemm_status pgemm_plan_add(pgemm_config* cfg, const float* X, const float* Y, c
   if (!g.ok) return PGEMM_ERR_DEVICE;
   const pgk::KernelInfo ki = pgk::info_padd(tile_rows, tile_cols, vec);
   pgk::SchedParams s;
-  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, s);
+  pgemm_status st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, false, s);
   if (st != PGEMM_OK) return st;
   fill_plan(s, ki, tile_rows, tile_cols, 0, PGEMM_KERNEL_ADD, out);
   return PGEMM_OK;

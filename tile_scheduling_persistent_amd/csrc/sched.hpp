@@ -81,6 +81,21 @@ PGS_FN int ws_range_begin(int x, int T, int X) {
   return (int)(((int64_t)x * (int64_t)T) / (int64_t)X);
 }
 
+// Default grid of the data-parallel GEMM schedulers: the fewest programs, a
+// multiple of X, that finish in as many rounds of tiles as G programs do.
+// The largest work-stealing range holds nx = ceil(T / X) tiles and its G / X
+// programs take r = ceil(nx / (G / X)) rounds; ceil(nx / r) programs per XCD
+// take the same r rounds, and so do the static walks (ceil(T / grid) <= r).
+// The programs left out would only have idled through the last round, and
+// with fewer CUs busy the busy ones run faster (measured on wave-quantised
+// shapes).  G itself when T < 1, G < X or G is not a multiple of X.
+PGS_FN int balanced_grid(int T, int G, int X) {
+  if (T < 1 || X < 1 || G < X || G % X != 0) return G;
+  const int nx = cdiv(T, X);
+  const int r = cdiv(nx, G / X);
+  return X * cdiv(nx, r);
+}
+
 // Paired claims (work-stealing option): the counter counts claims, and claim
 // k of a range of n tiles takes tiles 2k, 2k+1 while k < L/2, then the single
 // tile L + (k - L/2), where P = ceil(G / X) programs share a counter and
