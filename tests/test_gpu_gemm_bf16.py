@@ -167,3 +167,25 @@ def test_8192_all_schedulers():
             ref_bits = bits
         else:
             assert np.array_equal(bits, ref_bits), f"8192^3: {sched}/{gs} differs"
+
+
+@pytest.mark.parametrize("tile", [(128, 128, 64), (256, 256, 64)])
+def test_balanced_grid_same_bits_as_full_grid(tile):
+    """The default (balanced) grid changes which program computes a tile,
+    never the tile's K order: C is bit-identical to a launch on every
+    resident slot, for every data-parallel scheduler, on a ragged shape
+    whose tiles fill less than one round (the default grid is then the tile
+    count rounded up to the XCDs), and within the bound of the oracle."""
+    cfg = config()
+    M, N, K = 1300, 900, 256
+    a, b = bf16_bits_uniform((M, K), 4400), bf16_bits_uniform((K, N), 4401)
+    Cref, Abs = og.gemm_bf16(a, b)
+    for sched in SCHEDS:
+        plan = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched, pg.make_args(tile=tile))
+        full = cfg.info["num_cus"] * plan["occupancy"]
+        assert plan["grid"] <= full and plan["grid"] % cfg.info["num_xcds"] == 0
+        Cb = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, tile)
+        Cf = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, tile, grid=full)
+        assert Cb.guards_intact() and Cf.guards_intact(), sched
+        assert np.array_equal(Cb.body_bits(), Cf.body_bits()), f"{sched} {tile}: grid {plan['grid']} vs {full}"
+        assert_within(Cb.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, True, f"{sched} {tile} balanced grid")
