@@ -164,11 +164,21 @@ def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
     busy = (t1 - t0) * us
     span = (t1.max() - t0.min()) * us
     tiles = w["n_tiles"][:G]
+    X = cfg.info["num_xcds"]
+    xcc = (w["hw_id"][:G].astype(np.int64) >> 16) & 0xF    # hardware XCC of each program
+    vals, counts = np.unique(tiles, return_counts=True)
     return {"span_us": round(span, 1), "busy_mean_us": round(float(busy.mean()), 1),
             "busy_min_us": round(float(busy.min()), 1), "busy_max_us": round(float(busy.max()), 1),
             "idle_frac": round(1.0 - float(busy.sum()) / (G * span), 4),
+            "idle_frac_all_cus": round(1.0 - float(busy.sum()) / (cfg.info["num_cus"] * span), 4),
+            "imbalance": round(float(busy.max() / busy.mean()), 4),
             "skew": round(float((busy.max() - busy.min()) / busy.mean()), 4),
-            "tiles_min": int(tiles.min()), "tiles_max": int(tiles.max())}
+            "programs": int(G),
+            "tiles_min": int(tiles.min()), "tiles_max": int(tiles.max()),
+            "tiles_per_program_hist": {str(int(v)): int(c) for v, c in zip(vals, counts)},
+            "tiles_per_xcc": [int(tiles[xcc == x].sum()) for x in range(X)],
+            "programs_per_xcc": [int((xcc == x).sum()) for x in range(X)],
+            "xcc_is_p_mod_x": round(float(np.mean(xcc == (np.arange(G) % X))), 4)}
 
 
 def measured_clock(pg, cfg, A, B, C, key):
@@ -399,6 +409,10 @@ def main():
             bal[f"{m}x{n}x{k}"] = row
             print(f"# balance {m}x{n}x{k}: " + ", ".join(f"{s_}: idle {v['idle_frac']} skew {v['skew']}"
                                                          for s_, v in row.items()), file=sys.stderr, flush=True)
+            ws = row["work_stealing"]
+            print(f"#   {ws['programs']} programs, hardware XCC == p mod X for {ws['xcc_is_p_mod_x']:.0%}; "
+                  f"work stealing tiles per XCC {ws['tiles_per_xcc']}, per program {ws['tiles_per_program_hist']}",
+                  file=sys.stderr, flush=True)
         del shapes
 
     # block-scaled fp8 (workload 5): work stealing vs grouped
