@@ -75,6 +75,15 @@ PROFILE_TARGETS = {
     "add_8192sq_128x128_interleaved": ("add", (128, 128), "interleaved"),
     "fp8_8192cube_work_stealing": ("fp8", (256, 256, 128), "work_stealing"),
     "fp8_256x28672x8192_128x256_work_stealing": ("fp8_skinny", (128, 256, 128), "work_stealing"),
+    # ragged bf16 shapes (same inputs as the bench pass) at the default,
+    # balanced grid and, with "_grid256", on one program per CU
+    "bf16_5120x5120x4096_work_stealing": ("bf16:5120:5120:4096", (256, 256, 64), "work_stealing"),
+    "bf16_5120x5120x4096_work_stealing_grid256": ("bf16:5120:5120:4096:256", (256, 256, 64), "work_stealing"),
+    "bf16_5120x5120x4096_blocked_grouped": ("bf16:5120:5120:4096", (256, 256, 64), "blocked_grouped"),
+    "bf16_4864x8000x8192_work_stealing": ("bf16:4864:8000:8192", (256, 256, 64), "work_stealing"),
+    "bf16_4864x8000x8192_work_stealing_grid256": ("bf16:4864:8000:8192:256", (256, 256, 64), "work_stealing"),
+    "bf16_3000x7000x2048_work_stealing": ("bf16:3000:7000:2048", (256, 256, 64), "work_stealing"),
+    "bf16_3000x7000x2048_work_stealing_grid256": ("bf16:3000:7000:2048:256", (256, 256, 64), "work_stealing"),
 }
 
 
@@ -87,7 +96,18 @@ def profile_only(name, steps, warmup):
     kind, tile, sched = PROFILE_TARGETS[name]
     cfg = pg.Config(0)
     stream = torch.cuda.current_stream()
-    if kind == "add":
+    if kind.startswith("bf16:"):
+        from synthetic import bf16_bits_uniform
+        dims = [int(x) for x in kind.split(":")[1:]]
+        m, n, k = dims[:3]
+        grid = dims[3] if len(dims) > 3 else 0
+        ra = torch.from_numpy(bf16_bits_uniform((m, k), 1040 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        rb = torch.from_numpy(bf16_bits_uniform((k, n), 1041 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        a = pg.make_args(tile=tile, grid=grid)
+        nbytes, work = 2 * (m * k + k * n + m * n), 2.0 * m * n * k
+        fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
+    elif kind == "add":
         R = Cc = 8192
         X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
         Y = torch.from_numpy(f32_normal((R, Cc), 2002)).to("cuda:0")
@@ -106,6 +126,8 @@ def profile_only(name, steps, warmup):
         fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
     _, ev_mean, _ = time_calls(fn, steps, warmup, stream)
     out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5),
+           "grid": (pg.plan_gemm(cfg, m, n, k, "bf16_out_bf16", sched, a)["grid"]
+                    if kind.startswith("bf16:") else None),
            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1)}
     if work:
         out["tflops"] = round(work / (ev_mean * 1e-3) / 1e12, 2)
