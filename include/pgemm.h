@@ -124,6 +124,8 @@ typedef enum {
 #define PGEMM_DEBUG_STRAGGLER_XCC 0x10u /* every program on hardware XCC straggler_program waits
                                            straggler_ns before each tile (not with
                                            PGEMM_DEBUG_STRAGGLER: PGEMM_ERR_INVALID) */
+#define PGEMM_DEBUG_VALIDATE_ONLY 0x20u /* check every argument, buffer ranges included, and
+                                           return PGEMM_OK without enqueueing anything */
 
 /* claim_chunk value for paired claims (GEMM, both work-stealing kinds): the
  * counter counts claims; with P = ceil(G / X) programs per counter, a range of
@@ -168,7 +170,9 @@ typedef struct {
 
 /* Create a configuration for HIP device `device`: reads the CU count and the
  * XCD count, allocates and zeroes an int32 work-stealing counter array of
- * max_xcds entries (0 => 16).  Fails with PGEMM_ERR_INVALID if the device has more XCDs than max_xcds
+ * max_xcds entries (0 => 16), and allocates the stream-K workspace for the
+ * default grid of every stream-K tile (two fp32 tiles per program:
+ * CUs x 512 KiB at 256x256 tiles, 128 MiB on 256 CUs).  Fails with PGEMM_ERR_INVALID if the device has more XCDs than max_xcds
  * (the counter index p mod X would run past the array), with
  * PGEMM_ERR_UNSUPPORTED if the device is not gfx950.  *out receives the new
  * config, owned by the caller until pgemm_config_destroy. */
@@ -191,10 +195,15 @@ PGEMM_API pgemm_status pgemm_config_destroy(pgemm_config* cfg);
  * A config holds one counter array: calls with the same config on different
  * streams must not overlap.  Errors: NULL pointer, M, N or K < 1,
  * group_size < 1, grid < 1 (or < X for work stealing), fp8 without scales or
- * with K % 128 != 0 => PGEMM_ERR_INVALID; tile shape not built =>
- * PGEMM_ERR_UNSUPPORTED.  PGEMM_SCHED_STREAM_K may allocate (or grow, after
- * a device synchronisation) the config's workspace: PGEMM_ERR_OOM if that
- * fails. */
+ * with K % 128 != 0 => PGEMM_ERR_INVALID; a buffer whose byte range (A:
+ * M*K, B: K*N elements, C: M*N, scales: (K/128)*M and (K/128)*N bytes) does
+ * not lie inside one device allocation of the config's device =>
+ * PGEMM_ERR_INVALID (the kernels address by the sizes given, so a shorter
+ * buffer would be accessed past its end); tile shape not built =>
+ * PGEMM_ERR_UNSUPPORTED.  PGEMM_SCHED_STREAM_K uses the workspace the config
+ * allocated; only a grid larger than the default (args->grid) grows it,
+ * after a device synchronisation (PGEMM_ERR_OOM if that fails, and
+ * PGEMM_ERR_INVALID while the stream is being captured). */
 PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
                        int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
                        pgemm_sched sched, const pgemm_args* args, void* hip_stream);
@@ -202,7 +211,8 @@ PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B
 /* C[rows][cols] = X + Y (fp32, one IEEE add per element, round to nearest
  * even), persistent over tile_rows x tile_cols tiles with the same
  * schedulers (tile rows are dimension 0 of the decode).  Built tiles: 32x16,
- * 64x64, 128x128.  Same ownership, error and stream rules as pgemm_run.
+ * 64x64, 128x128.  Same ownership, error and stream rules as pgemm_run (X,
+ * Y and C must each span rows*cols floats inside one device allocation).
  * C may alias X or Y exactly (in place), not partially. */
 PGEMM_API pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* C,
                       int64_t rows, int64_t cols, int tile_rows, int tile_cols,

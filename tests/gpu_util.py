@@ -4,6 +4,7 @@ tests marked gpu."""
 from __future__ import annotations
 
 import sys
+import time
 
 import numpy as np
 import torch
@@ -16,12 +17,39 @@ GUARD = 4096        # elements of guard band on each side of an output
 SENTINEL_U16 = 0x7FC1
 SENTINEL_F32 = 0x7FC00001
 
+# Host-side deadline on every wait for GPU work in the tests: a launch that
+# never finishes fails its test with the name of the call instead of blocking
+# until an outer time limit kills the run.
+SYNC_DEADLINE_S = 90.0
+
 _CFG = None
+_LAST = "(no call noted yet)"
+
+
+class GpuDeadline(AssertionError):
+    """GPU work did not finish within the tests' deadline."""
 
 
 def note(msg: str) -> None:
+    global _LAST
+    _LAST = msg
     print(f"[gpu] {msg}", flush=True)
     sys.stdout.flush()
+
+
+def sync(what: str | None = None, timeout_s: float = SYNC_DEADLINE_S, stream=None) -> None:
+    """Wait for the work queued so far on `stream` (default: the current
+    stream), polling an event against a deadline; raise GpuDeadline naming
+    `what` (default: the last noted call) if it does not complete in time.
+    Then synchronise the device (every other stream)."""
+    ev = torch.cuda.Event()
+    ev.record(stream if stream is not None else torch.cuda.current_stream())
+    t0 = time.monotonic()
+    while not ev.query():
+        if time.monotonic() - t0 > timeout_s:
+            raise GpuDeadline(f"GPU work not finished after {timeout_s:.0f} s: {what or _LAST}")
+        time.sleep(0.0005)
+    torch.cuda.synchronize()
 
 
 def config() -> pg.Config:

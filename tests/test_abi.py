@@ -73,3 +73,47 @@ def test_config_create_without_gpu_reports_error():
     import tile_scheduling_persistent_amd as pg
     with pytest.raises(pg.PgemmError):
         pg.Config(0)
+
+
+def test_binding_checks_dtype_and_extent_before_any_device_call():
+    """The binding refuses a tensor of the wrong element type, or one too
+    short for the bytes the call would read or write, before the library is
+    called (a too-short output would otherwise be written past its end)."""
+    import torch
+    import tile_scheduling_persistent_amd as pg
+    M, N, K = 64, 48, 256
+    nb = pg.gemm_bytes(M, N, K, "bf16_out_bf16")
+    assert nb == {"A": M * K * 2, "B": K * N * 2, "C": M * N * 2}
+    assert pg.gemm_bytes(M, N, K, "bf16_out_f32")["C"] == M * N * 4
+    f8 = pg.gemm_bytes(M, N, K, "fp8_b128_out_bf16")
+    assert (f8["A"], f8["B"], f8["a_scale"], f8["b_scale"]) == (M * K, K * N, 2 * M, 2 * N)
+    ok = torch.empty(M * K, dtype=torch.bfloat16)
+    pg._check_tensor(ok, "A", ("bfloat16",), nb["A"])
+    with pytest.raises(ValueError, match="bytes"):
+        pg._check_tensor(torch.empty(M * K - 1, dtype=torch.bfloat16), "A", ("bfloat16",), nb["A"])
+    with pytest.raises(ValueError, match="dtype"):
+        pg._check_tensor(torch.empty(M * K, dtype=torch.float16), "A", ("bfloat16",), nb["A"])
+    with pytest.raises(ValueError, match="contiguous"):
+        pg._check_tensor(torch.empty(K, M, dtype=torch.bfloat16).t(), "A", ("bfloat16",), nb["A"])
+    # an fp32 C is twice a bf16 C: a bf16 buffer of M*N elements is too short for it
+    with pytest.raises(ValueError):
+        pg._check_tensor(torch.empty(M * N, dtype=torch.bfloat16), "C", ("float32",),
+                         pg.gemm_bytes(M, N, K, "bf16_out_f32")["C"])
+    # the whole GEMM argument set: a short C is caught before anything is launched
+    A = torch.empty(M * K, dtype=torch.bfloat16)
+    B = torch.empty(K * N, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="C"):
+        pg._gemm_ptrs(A, B, torch.empty(M * N - 8, dtype=torch.bfloat16), M, N, K, "bf16_out_bf16", None)
+    with pytest.raises(ValueError, match="dtype"):
+        pg._gemm_ptrs(A, B, torch.empty(M * N, dtype=torch.float32), M, N, K, "bf16_out_bf16", None)
+    # scales given to make_args are checked against M, N, K of the call
+    qa = torch.empty(M * K, dtype=torch.uint8)
+    qb = torch.empty(K * N, dtype=torch.uint8)
+    short = torch.empty((K // 128) * M - 1, dtype=torch.uint8)
+    args = pg._abi.pgemm_args()
+    args._scales = (short, torch.empty((K // 128) * N, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="a_scale"):
+        pg._gemm_ptrs(qa, qb, torch.empty(M * N, dtype=torch.bfloat16), M, N, K, "fp8_b128_out_bf16", args)
+    # host tensors that pass every other check are still refused
+    with pytest.raises(ValueError, match="GPU"):
+        pg._gemm_ptrs(A, B, torch.empty(M * N, dtype=torch.bfloat16), M, N, K, "bf16_out_bf16", None)

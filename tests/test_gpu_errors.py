@@ -11,7 +11,7 @@ import tile_scheduling_persistent_amd as pg
 from tile_scheduling_persistent_amd import _abi
 from oracle import sched_model as sm
 from synthetic import bf16_bits_uniform
-from tests.gpu_util import config, dev_bf16, note
+from tests.gpu_util import config, dev_bf16, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_invalid_arguments_enqueue_nothing():
     assert run(a, b, c, 64, 64, 64, 0, 3, ctypes.byref(args), s) == _abi.ERR_INVALID
     # fp8 without scales, or K not a multiple of 128
     assert run(a, b, c, 64, 64, 128, 2, 0, None, s) == _abi.ERR_INVALID
-    torch.cuda.synchronize()
+    sync()
     assert torch.all(C == 7.0)
     X = torch.zeros(100, dtype=torch.float32, device="cuda:0")
     assert L.padd_run(cfg.handle, X.data_ptr(), X.data_ptr(), X.data_ptr(), 10, 10, 7, 7, 0,
@@ -92,7 +92,7 @@ def test_stale_counters_are_detected():
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_f32", "work_stealing",
                  pg.make_args(debug_flags=flags | _abi.DEBUG_SKIP_RESET))
     w2 = cfg.witness_read(T, G)
-    torch.cuda.synchronize()
+    sync()
     assert np.all(w2["visits"] == 0)
     assert torch.all(C == -5.0)
     # the normal path resets and recovers
@@ -197,3 +197,56 @@ def test_plan_matches_launch_shape():
     assert pg.plan_gemm(cfg, 100, 100, 100, "bf16_out_bf16", "blocked", pg.make_args(grid=7))["grid"] == 7
     staged = pg.plan_gemm(cfg, 512, 512, 500, "bf16_out_bf16", "blocked")
     assert staged["kernel"] == "bf16_staged"
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    lib.hipFree.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def test_buffer_ranges_must_lie_in_one_allocation():
+    """The library checks each buffer's byte range against the device
+    allocation that holds it (the kernels address by the sizes given).  Probed
+    with PGEMM_DEBUG_VALIDATE_ONLY, so nothing is launched either way."""
+    cfg = config()
+    L = _abi.lib()
+    hip = _hip()
+    size = 4 << 20
+    p = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(p), size) == 0
+    try:
+        base, end = p.value, p.value + size
+        s = torch.cuda.current_stream().cuda_stream
+        chk = pg.make_args(debug_flags=_abi.DEBUG_VALIDATE_ONLY)
+        M, N, K = 256, 512, 1024
+        a, b = base, base + M * K * 2                       # A then B, 1.5 MiB
+        c_fit = end - M * N * 2                             # bf16 C ending at the allocation's end
+        run = lambda A, B, C, dt=1: L.pgemm_run(cfg.handle, A, B, C, M, N, K, dt, 3,  # noqa: E731
+                                               ctypes.byref(chk), s)
+        assert run(a, b, c_fit) == _abi.OK
+        assert run(a, b, c_fit + 256) == _abi.ERR_INVALID          # C runs 256 B past the end
+        assert run(a, b, c_fit, dt=0) == _abi.ERR_INVALID           # fp32 C is twice as long
+        c_mid = base + (3 << 19)                            # C at 1.5 MiB, clear of A and B below
+        assert run(a, b, c_mid) == _abi.OK
+        assert run(end - M * K * 2 + 16, b, c_mid) == _abi.ERR_INVALID   # A past the end
+        assert run(a, end - K * N * 2 + 2, c_mid) == _abi.ERR_INVALID    # B past the end
+        # the add: X, Y, C of rows * cols floats
+        r, cc = 64, 1024
+        x_fit = end - r * cc * 4
+        add = lambda X, Y, C: L.padd_run(cfg.handle, X, Y, C, r, cc, 32, 16, 0,  # noqa: E731
+                                        ctypes.byref(chk), s)
+        assert add(base, base + r * cc * 4, x_fit) == _abi.OK
+        assert add(base, base + r * cc * 4, x_fit + 4) == _abi.ERR_INVALID
+        assert add(x_fit + 4, base, base + r * cc * 4) == _abi.ERR_INVALID
+        # fp8 scales: [K/128][M] and [K/128][N] bytes
+        q = pg.make_args(a_scale=end - (K // 128) * M, b_scale=end - (K // 128) * N - 1,
+                         debug_flags=_abi.DEBUG_VALIDATE_ONLY)
+        fa, fb, fc = base, base + M * K, base + M * K + K * N
+        assert L.pgemm_run(cfg.handle, fa, fb, fc, M, N, K, 2, 3, ctypes.byref(q), s) == _abi.OK
+        q.a_scale = end - (K // 128) * M + 1
+        assert L.pgemm_run(cfg.handle, fa, fb, fc, M, N, K, 2, 3, ctypes.byref(q), s) == _abi.ERR_INVALID
+        sync("validate-only calls")
+    finally:
+        assert hip.hipFree(p) == 0

@@ -11,7 +11,7 @@ import tile_scheduling_persistent_amd as pg
 from oracle import gemm as og
 from oracle import sched_model as sm
 from synthetic import bf16_bits_uniform, fp8_blockscaled
-from tests.gpu_util import BF16_TOL, FP8_TOL, Guarded, assert_abs_bound, assert_within, config, dev_bf16, note
+from tests.gpu_util import BF16_TOL, FP8_TOL, Guarded, assert_abs_bound, assert_within, config, dev_bf16, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def _run(shapes, ab, out, sched, tile, **kw):
         outs.append(C)
     note(f"pgemm_run_grouped {shapes} {out} sched={sched} tile={tile} {kw}")
     pg.pgemm_run_grouped(cfg, probs, out, sched, pg.make_args(tile=tile, **kw))
-    torch.cuda.synchronize()
+    sync()
     return outs
 
 
@@ -60,7 +60,7 @@ def test_grouped_parity(tile, out, si):
             continue
         C = Guarded(M * N, "bf16" if out == "bf16_out_bf16" else "f32")
         pg.pgemm_run(cfg, dev_bf16(a), dev_bf16(b), C.view, M, N, K, out, "grouped", pg.make_args(tile=tile))
-        torch.cuda.synchronize()
+        sync()
         alone.append(C.body_bits())
     for sched in SCHEDS:
         outs = _run(shapes, ab, out, sched, tile)
@@ -153,7 +153,7 @@ def test_grouped_fp8_parity(tile, si):
         C = Guarded(M * N, "bf16")
         pg.pgemm_run(cfg, dev[0], dev[1], C.view, M, N, K, "fp8_b128_out_bf16", "grouped",
                      pg.make_args(tile=tile, a_scale=dev[2], b_scale=dev[3]))
-        torch.cuda.synchronize()
+        sync()
         alone.append(C.body_bits())
     for sched in SCHEDS:
         probs, outs = [], []
@@ -163,7 +163,7 @@ def test_grouped_fp8_parity(tile, si):
             outs.append(C)
         note(f"pgemm_run_grouped fp8 {shapes} sched={sched} tile={tile}")
         pg.pgemm_run_grouped(cfg, probs, "fp8_b128_out_bf16", sched, pg.make_args(tile=tile))
-        torch.cuda.synchronize()
+        sync()
         for g, ((M, N, K), (qa, sa, qb, sb, dev), C) in enumerate(zip(shapes, data, outs)):
             assert C.guards_intact(), (shapes, sched, g)
             if M * N == 0:

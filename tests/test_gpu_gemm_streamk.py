@@ -14,7 +14,7 @@ from oracle import sched_model as sm
 from oracle.codecs import bf16_to_f64
 from synthetic import bf16_bits_normal, bf16_bits_uniform
 from tests.gpu_util import (BF16_TOL, Guarded, assert_abs_bound, assert_within, config,
-                            dev_bf16, note)
+                            dev_bf16, note, sync)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def _run(A, B, M, N, K, out, sched, tile, **kw):
     args = pg.make_args(tile=tile, **kw)
     note(f"pgemm_run M={M} N={N} K={K} {out} sched={sched} tile={tile} {kw}")
     pg.pgemm_run(cfg, A, B, C.view, M, N, K, out, sched, args)
-    torch.cuda.synchronize()
+    sync()
     assert C.guards_intact(), (M, N, K, sched)
     return C
 
@@ -136,7 +136,7 @@ def _run_fp8(qa, sa, qb, sb, M, N, K, sched, tile):
     note(f"pgemm_run fp8 M={M} N={N} K={K} sched={sched} tile={tile}")
     pg.pgemm_run(cfg, A, B, C.view, M, N, K, "fp8_b128_out_bf16", sched,
                  pg.make_args(tile=tile, a_scale=SA, b_scale=SB))
-    torch.cuda.synchronize()
+    sync()
     assert C.guards_intact(), (M, N, K, sched, tile)
     return C
 

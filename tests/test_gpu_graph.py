@@ -8,7 +8,7 @@ import torch
 
 import tile_scheduling_persistent_amd as pg
 from synthetic import bf16_bits_uniform, f32_normal
-from tests.gpu_util import config, dev_bf16, dev_f32, note
+from tests.gpu_util import config, dev_bf16, dev_f32, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -26,21 +26,21 @@ def test_gemm_graph_replays(sched):
     args = pg.make_args(tile=(256, 256, 64))
     note(f"graph gemm {M}x{N}x{K} {sched}")
     pg.pgemm_run(cfg, A, B, ref, M, N, K, "bf16_out_bf16", sched, args)  # eager, also warms up
-    torch.cuda.synchronize()
+    sync()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
             pg.pgemm_run(cfg, A, B, out, M, N, K, "bf16_out_bf16", sched, args)
-    torch.cuda.synchronize()
+    sync()
     junk = torch.zeros(1 << 20, device="cuda:0")
     for r in range(4):
         out.fill_(float("nan"))
         junk.add_(1.0)                      # unrelated eager work between replays
         pg.pgemm_run(cfg, A, B, ref, M, N, K, "bf16_out_bf16", sched, args)  # eager call in between
-        torch.cuda.synchronize()
+        sync()
         g.replay()
-        torch.cuda.synchronize()
+        sync()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
 
 
@@ -60,19 +60,19 @@ def test_fp8_gemm_graph_replays(sched):
     args = pg.make_args(tile=(256, 256, 128), a_scale=SA, b_scale=SB)
     note(f"graph fp8 gemm {M}x{N}x{K} {sched}")
     pg.pgemm_run(cfg, A, B, ref, M, N, K, "fp8_b128_out_bf16", sched, args)  # eager; sizes the workspace
-    torch.cuda.synchronize()
+    sync()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
             pg.pgemm_run(cfg, A, B, out, M, N, K, "fp8_b128_out_bf16", sched, args)
-    torch.cuda.synchronize()
+    sync()
     for r in range(4):
         out.fill_(float("nan"))
         pg.pgemm_run(cfg, A, B, ref, M, N, K, "fp8_b128_out_bf16", sched, args)  # eager call in between
-        torch.cuda.synchronize()
+        sync()
         g.replay()
-        torch.cuda.synchronize()
+        sync()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
 
 
@@ -84,18 +84,18 @@ def test_add_graph_replays():
     out = torch.empty_like(X)
     note("graph add work stealing")
     pg.padd_run(cfg, X, Y, out, rows, cols, 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
             pg.padd_run(cfg, X, Y, out, rows, cols, 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     for r in range(4):
         out.fill_(float("nan"))
-        torch.cuda.synchronize()
+        sync()
         g.replay()
-        torch.cuda.synchronize()
+        sync()
         assert torch.equal(out, ref), f"replay {r}"
 
 
@@ -115,7 +115,7 @@ def test_grouped_gemm_and_multi_add_graph_replays():
     note("graph grouped GEMM + several adds")
     pg.pgemm_run_grouped(cfg, probs, "bf16_out_bf16", "work_stealing")
     pg.padd_run_multi(cfg, adds, 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     refs = [p[2].clone() for p in probs] + [a[2].clone() for a in adds]
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -123,14 +123,14 @@ def test_grouped_gemm_and_multi_add_graph_replays():
         with torch.cuda.graph(g, stream=side):
             pg.pgemm_run_grouped(cfg, probs, "bf16_out_bf16", "work_stealing")
             pg.padd_run_multi(cfg, adds, 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     outs = [p[2] for p in probs] + [a[2] for a in adds]
     for r in range(4):
         for o in outs:
             o.fill_(float("nan"))
-        torch.cuda.synchronize()
+        sync()
         g.replay()
-        torch.cuda.synchronize()
+        sync()
         for i, (o, ref) in enumerate(zip(outs, refs)):
             assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o.view(torch.int32),
                                ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), \

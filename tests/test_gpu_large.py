@@ -18,7 +18,7 @@ from oracle import gemm as og
 from oracle.add import add_f32
 from oracle.codecs import dequant_fp8_a, dequant_fp8_b
 from synthetic import bf16_bits_uniform, f32_normal, fp8_blockscaled, rng
-from tests.gpu_util import BF16_TOL, FP8_TOL, assert_abs_bound, assert_within, config, note
+from tests.gpu_util import BF16_TOL, FP8_TOL, assert_abs_bound, assert_within, config, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def test_bf16_a_beyond_4gib():
         note(f"pgemm_run bf16 M={M} N={N} K={K} sched={sched} tile={tile}")
         pg.pgemm_run(cfg, A, B, C.body.view(torch.bfloat16), M, N, K, "bf16_out_bf16", sched,
                      pg.make_args(tile=tile))
-        torch.cuda.synchronize()
+        sync()
         assert C.guards_intact(), sched
         got = C.rows(rows, N).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
         assert_abs_bound(got, Cref, Abs, BF16_TOL, f"A > 4 GiB {sched} {tile}")
@@ -111,7 +111,7 @@ def test_bf16_c_beyond_4gib(out):
         note(f"pgemm_run M={M} N={N} K={K} {out} sched={sched}")
         view = C.body.view(torch.float32) if wide else C.body.view(torch.bfloat16)
         pg.pgemm_run(cfg, A, B, view, M, N, K, out, sched, pg.make_args(tile=(256, 256, 64)))
-        torch.cuda.synchronize()
+        sync()
         assert C.guards_intact(), sched
         r = C.rows(rows, N)
         got = (r.view(torch.float32) if wide else r.view(torch.bfloat16).float()).cpu().numpy()
@@ -141,7 +141,7 @@ def test_fp8_a_beyond_4gib():
         note(f"pgemm_run fp8 M={M} N={N} K={K} sched={sched} tile={tile}")
         pg.pgemm_run(cfg, A, B, C.body.view(torch.bfloat16), M, N, K, "fp8_b128_out_bf16", sched,
                      pg.make_args(tile=tile, a_scale=SA, b_scale=SB))
-        torch.cuda.synchronize()
+        sync()
         assert C.guards_intact(), sched
         got = C.rows(rows, N).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
         assert_abs_bound(got, Cref, Abs, FP8_TOL, f"fp8 A > 4 GiB {sched} {tile}")
@@ -166,7 +166,7 @@ def test_add_beyond_4gib():
         C = BigOut(rows_n * cols, wide=True)
         note(f"padd_run {rows_n}x{cols} sched={sched} tile={tile}")
         pg.padd_run(cfg, X, Y, C.body.view(torch.float32), rows_n, cols, tile[0], tile[1], sched)
-        torch.cuda.synchronize()
+        sync()
         assert C.guards_intact(), sched
         got = C.rows(rows, cols).cpu().numpy().view(np.uint32)
         assert np.array_equal(got, want), (sched, tile)

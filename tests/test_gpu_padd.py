@@ -6,7 +6,7 @@ import torch
 import tile_scheduling_persistent_amd as pg
 from oracle.add import add_f32
 from synthetic import f32_normal
-from tests.gpu_util import GUARD, SENTINEL_F32, config, dev_f32, note
+from tests.gpu_util import GUARD, SENTINEL_F32, config, dev_f32, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ def run_add(x, y, tile, sched, **kw):
     C = full[GUARD:GUARD + rows * cols].view(torch.float32)
     note(f"padd_run {rows}x{cols} tile={tile} sched={sched} {kw}")
     pg.padd_run(cfg, X, Y, C, rows, cols, tile[0], tile[1], sched, pg.make_args(**kw))
-    torch.cuda.synchronize()
+    sync()
     h = full.cpu().numpy()
     assert np.all(h[:GUARD] == SENTINEL_F32) and np.all(h[GUARD + rows * cols:] == SENTINEL_F32)
     return h[GUARD:GUARD + rows * cols].view(np.float32).reshape(rows, cols)
@@ -71,5 +71,5 @@ def test_add_in_place():
     cfg = config()
     X, Y = dev_f32(x), dev_f32(y)
     pg.padd_run(cfg, X, Y, X, 300, 400, 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     assert np.array_equal(X.cpu().numpy().view(np.uint32), want)

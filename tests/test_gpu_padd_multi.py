@@ -10,7 +10,7 @@ import tile_scheduling_persistent_amd as pg
 from oracle import sched_model as sm
 from oracle.add import add_f32
 from synthetic import f32_normal
-from tests.gpu_util import Guarded, config, dev_f32, note
+from tests.gpu_util import Guarded, config, dev_f32, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def _run(shapes, xy, tile, sched, **kw):
         outs.append(C)
     note(f"padd_run_multi {shapes} tile={tile} sched={sched} {kw}")
     pg.padd_run_multi(cfg, devs, tile[0], tile[1], sched, pg.make_args(**kw))
-    torch.cuda.synchronize()
+    sync()
     return outs
 
 
@@ -97,7 +97,7 @@ def test_multi_add_one_problem_equals_single_call():
     C2 = torch.empty_like(X)
     pg.padd_run(cfg, X, Y, C1, 777, 1234, 32, 16, "grouped")
     pg.padd_run_multi(cfg, [(X, Y, C2, 777, 1234)], 32, 16, "grouped")
-    torch.cuda.synchronize()
+    sync()
     assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
 
 
@@ -108,7 +108,7 @@ def test_multi_add_in_place_and_errors():
     A, B, Cc, D = dev_f32(a), dev_f32(b), dev_f32(c), dev_f32(d)
     # in place within a problem is allowed
     pg.padd_run_multi(cfg, [(A, B, A, 300, 400), (Cc, D, Cc, 50, 60)], 32, 16, "work_stealing")
-    torch.cuda.synchronize()
+    sync()
     assert np.array_equal(A.cpu().numpy().view(np.uint32), add_f32(a, b).view(np.uint32))
     assert np.array_equal(Cc.cpu().numpy().view(np.uint32), add_f32(c, d).view(np.uint32))
     E = torch.empty_like(A)

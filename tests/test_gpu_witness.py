@@ -11,7 +11,7 @@ import torch
 import tile_scheduling_persistent_amd as pg
 from oracle import sched_model as sm
 from synthetic import bf16_bits_uniform, f32_normal
-from tests.gpu_util import config, dev_bf16, dev_f32, note
+from tests.gpu_util import config, dev_bf16, dev_f32, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
     C2 = torch.empty_like(C)
     pg.pgemm_run(cfg, A, B, C2, M, N, K, "bf16_out_bf16", sched,
                  pg.make_args(tile=tile, group_size=gs, grid=grid))
-    torch.cuda.synchronize()
+    sync()
     assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
     return w, pm, pn, G, cfg.info["num_xcds"]
 
@@ -97,7 +97,7 @@ def test_gemm_chunked_claims(sched, chunk, shape, tile):
     _check(w, sched, pm, pn, G, cfg.info["num_xcds"], 8, sm.PAIRS if chunk < 0 else chunk)
     Cg = torch.empty_like(C)
     pg.pgemm_run(cfg, A, B, Cg, M, N, K, "bf16_out_bf16", "grouped", pg.make_args(tile=tile))
-    torch.cuda.synchronize()
+    sync()
     assert torch.equal(C.view(torch.int16), Cg.view(torch.int16))
 
 

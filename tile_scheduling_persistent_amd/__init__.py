@@ -40,19 +40,61 @@ def _check(where, code):
         raise PgemmError(where, code)
 
 
-def _ptr(x, what, dtype=None):
-    """Device pointer of a torch tensor (contiguous, on a GPU) or a raw int pointer."""
+def _torch_dtypes(names):
+    import torch
+    return tuple(getattr(torch, n) for n in names if hasattr(torch, n))
+
+
+# Element types the calls accept: operands per pgemm_dtype, outputs, adds.
+_OPERAND = {_abi.BF16_OUT_F32: ("bfloat16",), _abi.BF16_OUT_BF16: ("bfloat16",),
+            _abi.FP8E4M3_B128_OUT_BF16: ("uint8", "float8_e4m3fn")}
+_OUTPUT = {_abi.BF16_OUT_F32: ("float32",), _abi.BF16_OUT_BF16: ("bfloat16",),
+           _abi.FP8E4M3_B128_OUT_BF16: ("bfloat16",)}
+_SCALE = ("uint8",)
+_F32 = ("float32",)
+
+
+def gemm_bytes(M: int, N: int, K: int, dtype) -> dict:
+    """Bytes each buffer of a GEMM call spans: A [M][K], B [K][N], C [M][N]
+    and (block-scaled fp8) the scales [K/128][M] and [K/128][N]."""
+    d = _dtype(dtype)
+    esz = 1 if d == _abi.FP8E4M3_B128_OUT_BF16 else 2
+    csz = 4 if d == _abi.BF16_OUT_F32 else 2
+    out = {"A": M * K * esz, "B": K * N * esz, "C": M * N * csz}
+    if d == _abi.FP8E4M3_B128_OUT_BF16:
+        out["a_scale"] = (K // 128) * M
+        out["b_scale"] = (K // 128) * N
+    return out
+
+
+def _check_tensor(x, what, dtypes=None, nbytes=None):
+    """Layout, element type and extent of a tensor argument (host-side checks,
+    before any device is involved).  Raw int pointers pass unchecked: the
+    library itself checks that every range lies inside one device allocation."""
     if isinstance(x, int):
-        return x
+        return
     import torch
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{what}: expected a torch tensor or an int device pointer")
-    if not x.is_cuda:
-        raise ValueError(f"{what}: tensor must live on the GPU")
     if not x.is_contiguous():
         raise ValueError(f"{what}: tensor must be contiguous (row-major)")
-    if dtype is not None and x.dtype not in dtype:
-        raise ValueError(f"{what}: dtype {x.dtype} not in {dtype}")
+    if dtypes is not None:
+        allowed = _torch_dtypes(dtypes)
+        if x.dtype not in allowed:
+            raise ValueError(f"{what}: dtype {x.dtype} not in {allowed}")
+    if nbytes is not None and x.numel() * x.element_size() < nbytes:
+        raise ValueError(f"{what}: tensor holds {x.numel() * x.element_size()} bytes, "
+                         f"the call reads or writes {nbytes}")
+
+
+def _ptr(x, what, dtypes=None, nbytes=None):
+    """Device pointer of a torch tensor (contiguous, on a GPU, of an allowed
+    dtype, at least nbytes long) or a raw int pointer."""
+    _check_tensor(x, what, dtypes, nbytes)
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError(f"{what}: tensor must live on the GPU")
     return x.data_ptr()
 
 
@@ -81,8 +123,9 @@ def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_sc
     a.group_size = group_size
     a.grid = grid
     a.claim_chunk = claim_chunk
-    a.a_scale = _ptr(a_scale, "a_scale") if a_scale is not None else None
-    a.b_scale = _ptr(b_scale, "b_scale") if b_scale is not None else None
+    a.a_scale = _ptr(a_scale, "a_scale", _SCALE) if a_scale is not None else None
+    a.b_scale = _ptr(b_scale, "b_scale", _SCALE) if b_scale is not None else None
+    a._scales = (a_scale, b_scale)  # checked against M, N, K when the call is made
     a.debug_flags = debug_flags
     a.straggler_program = straggler_program
     a.straggler_ns = straggler_ns
@@ -151,11 +194,25 @@ class Config:
 def pgemm_run(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=None,
               stream=None):
     """C[M][N] = A[M][K] . B[K][N] on the GPU (asynchronous on `stream`)."""
-    a = args if args is not None else None
-    code = _abi.lib().pgemm_run(cfg.handle, _ptr(A, "A"), _ptr(B, "B"), _ptr(C, "C"),
+    code = _abi.lib().pgemm_run(cfg.handle, *_gemm_ptrs(A, B, C, M, N, K, dtype, args),
                                 int(M), int(N), int(K), _dtype(dtype), _sched(sched),
-                                ctypes.byref(a) if a is not None else None, _stream(stream))
+                                ctypes.byref(args) if args is not None else None, _stream(stream))
     _check("pgemm_run", code)
+
+
+def _gemm_ptrs(A, B, C, M, N, K, dtype, args, where=""):
+    """Device pointers of a GEMM's A, B, C after every host-side check of
+    all its buffers (element types, extents, the scales passed in args)."""
+    d = _dtype(dtype)
+    nb = gemm_bytes(int(M), int(N), int(K), d) if d in _OPERAND else {}
+    if args is not None and "a_scale" in nb:
+        for name, t in zip(("a_scale", "b_scale"), getattr(args, "_scales", (None, None))):
+            if t is not None:
+                _check_tensor(t, name + where, _SCALE, nb[name])
+    checks = [(A, "A", _OPERAND.get(d)), (B, "B", _OPERAND.get(d)), (C, "C", _OUTPUT.get(d))]
+    for x, name, dts in checks:
+        _check_tensor(x, name + where, dts, nb.get(name))
+    return tuple(_ptr(x, name + where, dts, nb.get(name)) for x, name, dts in checks)
 
 
 def _plan_dict(pl) -> dict:
@@ -192,7 +249,9 @@ def plan_add(cfg: Config, rows: int, cols: int, tile_rows: int, tile_cols: int, 
 def padd_run(cfg: Config, X, Y, C, rows: int, cols: int, tile_rows: int, tile_cols: int, sched,
              args=None, stream=None):
     """C = X + Y (fp32) over tile_rows x tile_cols tiles (asynchronous on `stream`)."""
-    code = _abi.lib().padd_run(cfg.handle, _ptr(X, "X"), _ptr(Y, "Y"), _ptr(C, "C"),
+    nb = int(rows) * int(cols) * 4
+    code = _abi.lib().padd_run(cfg.handle, _ptr(X, "X", _F32, nb), _ptr(Y, "Y", _F32, nb),
+                               _ptr(C, "C", _F32, nb),
                                int(rows), int(cols), int(tile_rows), int(tile_cols), _sched(sched),
                                ctypes.byref(args) if args is not None else None, _stream(stream))
     _check("padd_run", code)
@@ -205,9 +264,10 @@ def padd_run_multi(cfg: Config, problems, tile_rows: int, tile_cols: int, sched,
     n = len(problems)
     arr = (_abi.padd_problem * max(n, 1))()
     for g, (X, Y, C, rows, cols) in enumerate(problems):
-        arr[g].X = _ptr(X, f"X[{g}]")
-        arr[g].Y = _ptr(Y, f"Y[{g}]")
-        arr[g].C = _ptr(C, f"C[{g}]")
+        nb = int(rows) * int(cols) * 4
+        arr[g].X = _ptr(X, f"X[{g}]", _F32, nb)
+        arr[g].Y = _ptr(Y, f"Y[{g}]", _F32, nb)
+        arr[g].C = _ptr(C, f"C[{g}]", _F32, nb)
         arr[g].rows = int(rows)
         arr[g].cols = int(cols)
     code = _abi.lib().padd_run_multi(cfg.handle, arr, n, int(tile_rows), int(tile_cols), _sched(sched),
@@ -223,13 +283,12 @@ def pgemm_run_grouped(cfg: Config, problems, dtype, sched, args=None, stream=Non
     arr = (_abi.pgemm_problem * max(n, 1))()
     for g, pr in enumerate(problems):
         A, B, C, M, N, K = pr[:6]
-        arr[g].A = _ptr(A, f"A[{g}]")
-        arr[g].B = _ptr(B, f"B[{g}]")
-        arr[g].C = _ptr(C, f"C[{g}]")
+        arr[g].A, arr[g].B, arr[g].C = _gemm_ptrs(A, B, C, M, N, K, dtype, None, f"[{g}]")
         arr[g].M, arr[g].N, arr[g].K = int(M), int(N), int(K)
         if len(pr) == 8:
-            arr[g].a_scale = _ptr(pr[6], f"a_scale[{g}]")
-            arr[g].b_scale = _ptr(pr[7], f"b_scale[{g}]")
+            nb = gemm_bytes(int(M), int(N), int(K), "fp8_b128_out_bf16")
+            arr[g].a_scale = _ptr(pr[6], f"a_scale[{g}]", _SCALE, nb["a_scale"])
+            arr[g].b_scale = _ptr(pr[7], f"b_scale[{g}]", _SCALE, nb["b_scale"])
     code = _abi.lib().pgemm_run_grouped(cfg.handle, arr, n, _dtype(dtype), _sched(sched),
                                         ctypes.byref(args) if args is not None else None,
                                         _stream(stream))

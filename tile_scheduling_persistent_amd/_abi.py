@@ -20,6 +20,7 @@ BF16_OUT_F32, BF16_OUT_BF16, FP8E4M3_B128_OUT_BF16 = range(3)
 # debug flags
 DEBUG_WITNESS, DEBUG_SKIP_RESET, DEBUG_STRAGGLER, DEBUG_REGISTER_STAGED = 0x1, 0x2, 0x4, 0x8
 DEBUG_STRAGGLER_XCC = 0x10
+DEBUG_VALIDATE_ONLY = 0x20
 # pgemm_args.claim_chunk value for paired claims
 CLAIM_PAIRS = -1
 # pgemm_kernel

@@ -51,9 +51,16 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // before each later LDS read, which serialises the slab pipeline.  The
 // kernels track completion themselves: s_waitcnt vmcnt on the issuing wave,
 // then a workgroup barrier, before any wave reads the slab.
+//
+// Both asm statements below write M0 and list it as clobbered, so the
+// compiler does not keep a value of its own in M0 across them.  M0 is a
+// reserved register to the AMDGPU backend, which warns about the clobber;
+// the warning is silenced for these two statements only.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned lds_address, unsigned voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_address), "v"(voff), "s"(r) : "memory");
+               :: "s"(lds_address), "v"(voff), "s"(r) : "memory", "m0");
 }
 
 // buffer_load_ubyte ... lds: one byte per lane from byte offset voff,
@@ -61,8 +68,9 @@ __device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned lds_address,
 // resource's range read as zero).
 __device__ __forceinline__ void load_lds_u8(rsrc_words_t r, unsigned lds_address, unsigned voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
-               :: "s"(lds_address), "v"(voff), "s"(r) : "memory");
+               :: "s"(lds_address), "v"(voff), "s"(r) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ void load_lds16(rsrc_words_t r, unsigned char* lds_dst, unsigned voff) {
   load_lds16(r, __builtin_amdgcn_readfirstlane(lds_addr(lds_dst)), voff);

@@ -66,6 +66,33 @@ bool is_device_ptr(const void* p, int dev) {
   return attr.device == dev;
 }
 
+// Does [p, p + bytes) lie inside one device allocation of device `dev`?  The
+// kernels take their address ranges from the sizes of the call, not from the
+// allocation, so a buffer shorter than the sizes say would be read or written
+// past its end.
+bool device_range(const void* p, size_t bytes, int dev) {
+  if (!is_device_ptr(p, dev)) return false;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const uintptr_t b = (uintptr_t)base, q = (uintptr_t)p;
+  return q >= b && q - b <= size && bytes <= size - (q - b);
+}
+
+// M * N * element size, or SIZE_MAX if it does not fit (then no allocation holds it).
+size_t span_bytes(int64_t rows, int64_t cols, size_t esz) {
+  if (rows <= 0 || cols <= 0) return 0;
+  const unsigned __int128 b = (unsigned __int128)rows * (unsigned __int128)cols * esz;
+  return b > (unsigned __int128)SIZE_MAX ? SIZE_MAX : (size_t)b;
+}
+
+bool validate_only(const pgemm_args* args) {
+  return args && (args->debug_flags & PGEMM_DEBUG_VALIDATE_ONLY);
+}
+
 struct DeviceGuard {
   int prev = -1;
   bool ok = false;
@@ -244,10 +271,16 @@ pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk
 
 
 // Stream-K workspace of at least `bytes`: two partial-sum slots per program.
-// Grown with hipFree / hipMalloc after synchronising the device, so no
-// launch still uses the old buffer.
-pgemm_status ensure_workspace(pgemm_config* cfg, size_t bytes) {
+// The config allocates it for the default grid of every stream-K tile when
+// it is created, so only a call with a larger grid (args->grid) lands here:
+// the workspace then grows with hipFree / hipMalloc after synchronising the
+// device, so no launch still uses the old buffer.  Under stream capture a
+// synchronisation is not allowed: PGEMM_ERR_INVALID, nothing enqueued.
+pgemm_status ensure_workspace(pgemm_config* cfg, size_t bytes, hipStream_t stream) {
   if (cfg->ws_bytes >= bytes) return PGEMM_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return PGEMM_ERR_DEVICE;
+  if (cap != hipStreamCaptureStatusNone) return PGEMM_ERR_INVALID;
   if (cfg->ws) {
     if (hipDeviceSynchronize() != hipSuccess) return PGEMM_ERR_DEVICE;
     (void)hipFree(cfg->ws);
@@ -310,11 +343,32 @@ pgemm_status pgemm_config_create(int device, int max_xcds, pgemm_config** out) {
   c->lds_per_cu = (int)prop.maxSharedMemoryPerMultiProcessor;
   strncpy(c->arch, prop.gcnArchName, sizeof(c->arch) - 1);
   const size_t cbytes = sizeof(int) * (size_t)cap * pgk::kCounterStride;
+  // Stream-K partial sums: two fp32 tile slots per program at the default
+  // grid (CUs x resident workgroups) of every tile the stream-K kernels take,
+  // allocated once here so that pgemm_run does not allocate.
+  size_t wsb = 0;
+  {
+    const int bf16_tiles[2][2] = {{256, 256}, {128, 128}};
+    const int fp8_tiles[3][2] = {{256, 256}, {128, 128}, {128, 256}};
+    for (const auto& t : bf16_tiles) {
+      const pgk::KernelInfo ki = pgk::info_gemm_bf16_lds(t[0], t[1], true);
+      const size_t b = (size_t)c->num_cus * (size_t)ki.occupancy * 2 * (size_t)t[0] * t[1] * sizeof(float);
+      wsb = b > wsb ? b : wsb;
+    }
+    for (const auto& t : fp8_tiles) {
+      const pgk::KernelInfo ki = pgk::info_gemm_fp8(t[0], t[1]);
+      const size_t b = (size_t)c->num_cus * (size_t)ki.occupancy * 2 * (size_t)t[0] * t[1] * sizeof(float);
+      wsb = b > wsb ? b : wsb;
+    }
+  }
   hipError_t e = hipMalloc((void**)&c->counters, cbytes);
   if (e == hipSuccess) e = hipMemset(c->counters, 0, cbytes);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->ws, wsb);
+  if (e == hipSuccess) c->ws_bytes = wsb;
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     if (c->counters) (void)hipFree(c->counters);
+    if (c->ws) (void)hipFree(c->ws);
     delete c;
     return from_hip(e);
   }
@@ -368,9 +422,9 @@ pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int
     const padd_problem& q = problems[g];
     if (!q.X || !q.Y || !q.C) return PGEMM_ERR_INVALID;
     if (q.rows < 0 || q.cols < 0 || q.rows > 0x7fffffffLL || q.cols > 0x7fffffffLL) return PGEMM_ERR_INVALID;
-    if (!is_device_ptr(q.X, dev) || !is_device_ptr(q.Y, dev) || !is_device_ptr(q.C, dev))
+    const size_t bytes = span_bytes(q.rows, q.cols, 4);
+    if (!device_range(q.X, bytes, dev) || !device_range(q.Y, bytes, dev) || !device_range(q.C, bytes, dev))
       return PGEMM_ERR_INVALID;
-    const size_t bytes = (size_t)q.rows * (size_t)q.cols * 4;
     // C against every buffer: its own X / Y may be the same buffer, nothing else may touch it
     for (int h = 0; h < count; ++h) {
       const padd_problem& o = problems[h];
@@ -412,6 +466,7 @@ pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int
     if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
     p.s.chunk = args->claim_chunk;
   }
+  if (validate_only(args)) return PGEMM_OK;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
@@ -449,10 +504,13 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
     if (!q.A || !q.B || !q.C) return PGEMM_ERR_INVALID;
     if (q.M < 0 || q.N < 0 || q.K < 1 || q.M > 0x7fffffffLL || q.N > 0x7fffffffLL || q.K > 0x7fffffffLL)
       return PGEMM_ERR_INVALID;
-    if (!is_device_ptr(q.A, dev) || !is_device_ptr(q.B, dev) || !is_device_ptr(q.C, dev))
+    const size_t qesz = fp8 ? 1 : 2;
+    if (!device_range(q.A, span_bytes(q.M, q.K, qesz), dev) || !device_range(q.B, span_bytes(q.K, q.N, qesz), dev) ||
+        !device_range(q.C, span_bytes(q.M, q.N, csz), dev))
       return PGEMM_ERR_INVALID;
     if (fp8) {
-      if (!q.a_scale || !q.b_scale || !is_device_ptr(q.a_scale, dev) || !is_device_ptr(q.b_scale, dev))
+      if (!q.a_scale || !q.b_scale || !device_range(q.a_scale, span_bytes(q.K / 128, q.M, 1), dev) ||
+          !device_range(q.b_scale, span_bytes(q.K / 128, q.N, 1), dev))
         return PGEMM_ERR_INVALID;
       if (q.K % 128 != 0) return PGEMM_ERR_INVALID;
       if (!aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.C, 16) ||
@@ -506,6 +564,7 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   if (ki.threads == 0) return PGEMM_ERR_UNSUPPORTED;
   pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
+  if (validate_only(args)) return PGEMM_OK;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
@@ -589,12 +648,14 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   if (fp8 && (!args || !args->a_scale || !args->b_scale)) return PGEMM_ERR_INVALID;
   const int bm = ch.bm, bn = ch.bn;
   const int dev = cfg->device;
-  if (!is_device_ptr(A, dev) || !is_device_ptr(B, dev) || !is_device_ptr(C, dev))
-    return PGEMM_ERR_INVALID;
-  if (fp8 && (!is_device_ptr(args->a_scale, dev) || !is_device_ptr(args->b_scale, dev)))
-    return PGEMM_ERR_INVALID;
   const size_t esz = fp8 ? 1 : 2;
   const size_t csz = dtype == PGEMM_BF16_OUT_F32 ? 4 : 2;
+  if (!device_range(A, span_bytes(M, K, esz), dev) || !device_range(B, span_bytes(K, N, esz), dev) ||
+      !device_range(C, span_bytes(M, N, csz), dev))
+    return PGEMM_ERR_INVALID;
+  if (fp8 && (!device_range(args->a_scale, span_bytes(K / 128, M, 1), dev) ||
+              !device_range(args->b_scale, span_bytes(K / 128, N, 1), dev)))
+    return PGEMM_ERR_INVALID;
   // C must not overlap A or B
   {
     const char* c0 = (const char*)C;
@@ -629,12 +690,14 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
     // without the witness
     if (ch.kernel != PGEMM_KERNEL_BF16_LDS && ch.kernel != PGEMM_KERNEL_FP8) return PGEMM_ERR_UNSUPPORTED;
     if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
-    st = ensure_workspace(cfg, (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float));
+  }
+  if (validate_only(args)) return PGEMM_OK;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (sk) {
+    st = ensure_workspace(cfg, (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float), stream);
     if (st != PGEMM_OK) return st;
     p.ws = cfg->ws;
   }
-
-  hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
@@ -679,9 +742,9 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
   if (tile_rows < 1 || tile_cols < 1) return PGEMM_ERR_INVALID;
   if (!pgk::padd_tile_supported(tile_rows, tile_cols)) return PGEMM_ERR_UNSUPPORTED;
   const int dev = cfg->device;
-  if (!is_device_ptr(X, dev) || !is_device_ptr(Y, dev) || !is_device_ptr(C, dev))
+  const size_t bytes = span_bytes(rows, cols, 4);
+  if (!device_range(X, bytes, dev) || !device_range(Y, bytes, dev) || !device_range(C, bytes, dev))
     return PGEMM_ERR_INVALID;
-  const size_t bytes = (size_t)rows * cols * 4;
   {
     const char* c0 = (const char*)C;
     const char* xs[2] = {(const char*)X, (const char*)Y};
@@ -710,6 +773,7 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
     if (args->claim_chunk < 1 || args->claim_chunk > step) return PGEMM_ERR_INVALID;
     p.s.chunk = args->claim_chunk;
   }
+  if (validate_only(args)) return PGEMM_OK;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
