@@ -1,6 +1,6 @@
 // Host build of the library's scheduler header (csrc/sched.hpp): prints the
-// schedule every program walks, and runs the work-stealing claim loop with
-// std::atomic counters on real threads.  Output is compared by
+// schedule every program walks, and runs the kernels' work-stealing claim
+// loop (pgs::ws_claim) with std::atomic counters on real threads.  Output is compared by
 // tests/test_sched_host.py against the oracle's schedule model.
 #include <atomic>
 #include <cstdio>
@@ -28,22 +28,22 @@ static int static_walk(int kind, int pm, int pn, int G, int gs) {
   return 0;
 }
 
-// One claim on `c` for a range of n tiles: [first, end) relative to the
-// range's start, or false when the range is exhausted.  chunk < 0: paired
-// claims (the counter counts claims, pgs::pair_claim maps them to tiles).
-static bool take(std::atomic<int>& c, int n, int chunk, int G, int X, int& first, int& end) {
-  if (chunk < 0) {
-    const int k = c.fetch_add(1, std::memory_order_relaxed);
-    return pgs::pair_claim(k, n, G, X, first, end);
-  }
-  const int i = c.fetch_add(chunk, std::memory_order_relaxed);
-  first = i;
-  end = i + chunk < n ? i + chunk : n;
-  return i < n;
-}
+// The counter operations the kernels perform with device atomics, on
+// std::atomic counters: the claim loop itself is the library's
+// (pgs::ws_claim), so these threads run the kernels' own claim and sweep code.
+struct HostOps {
+  std::atomic<int>* c;
+  int fetch_add(int x, int v) { return c[x].fetch_add(v, std::memory_order_relaxed); }
+  int load(int x) { return c[x].load(std::memory_order_relaxed); }
+};
 
-// G threads claim from X atomic counters exactly as the kernels do.
-static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
+// G threads walk the tiles as a kernel's programs do (Walker::first / next):
+// a claim, the tiles of that claim in order, then the next claim, until a
+// claim returns -1.  Thread p starts on counter homes[p]; `across` is work
+// stealing across XCDs.  Prints the homes, the final counters and, per tile,
+// visits, owner and the tile's position in its owner's sequence.
+static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
+                         const std::vector<int>& homes) {
   const int T = pm * pn;
   std::vector<std::atomic<int>> cnt(X);
   for (auto& c : cnt) c.store(0);
@@ -53,80 +53,18 @@ static int ws_threads(int pm, int pn, int G, int X, int gs, int chunk) {
   std::vector<std::thread> th;
   for (int p = 0; p < G; ++p) {
     th.emplace_back([&, p] {
-      const int x = p % X;
-      const int begin = pgs::ws_range_begin(x, T, X);
-      const int n = pgs::ws_range_begin(x + 1, T, X) - begin;
+      HostOps ops{cnt.data()};
+      pgs::WsWalk w;
+      pgs::ws_start(w, homes[p], T, X);
       int done = 0;
-      for (;;) {
-        int f, e;
-        if (!take(cnt[x], n, chunk, G, X, f, e)) break;
-        for (int v = begin + f; v < begin + e; ++v) {
-          visits[v].fetch_add(1);
-          owner[v] = p;
-          order[v] = done++;
-          std::this_thread::yield();
-        }
-      }
-    });
-  }
-  for (auto& t : th) t.join();
-  std::printf("counters:");
-  for (int x = 0; x < X; ++x) std::printf(" %d", cnt[x].load());
-  std::printf("\n");
-  for (int v = 0; v < T; ++v) std::printf("%d %d %d %d\n", v, visits[v].load(), owner[v], order[v]);
-  return 0;
-}
-
-// Work stealing across XCDs: G threads start on counter homes[p]; after a
-// failing claim a thread reads the counters it has not passed (cyclic order),
-// skips those past their range and moves to the first that is not, or stops;
-// the end of a claim is cut at the end of the range that holds its first
-// tile (pgs::ws_owner), as the kernels do.
-static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
-  const int T = pm * pn;
-  std::vector<int> homes(G);
-  unsigned lcg = 12345u;
-  for (int p = 0; p < G; ++p) {
-    lcg = lcg * 1103515245u + 12345u;
-    homes[p] = home_mode == 0 ? p % X : home_mode == 1 ? 0 : (int)((lcg >> 16) % (unsigned)X);
-  }
-  std::vector<std::atomic<int>> cnt(X);
-  for (auto& c : cnt) c.store(0);
-  std::vector<std::atomic<int>> visits(T);
-  for (auto& v : visits) v.store(0);
-  std::vector<int> owner(T, -1), order(T, -1);
-  std::vector<std::thread> th;
-  for (int p = 0; p < G; ++p) {
-    th.emplace_back([&, p] {
-      int x = homes[p], passed = 0, done = 0;
-      auto range_n = [&](int c) { return pgs::ws_range_begin(c + 1, T, X) - pgs::ws_range_begin(c, T, X); };
-      for (;;) {
-        const int begin = pgs::ws_range_begin(x, T, X);
-        const int n = range_n(x);
-        int f, e;
-        if (!take(cnt[x], n, chunk, G, X, f, e)) {
-          if (++passed >= X) break;
-          const int left = X - passed;
-          std::vector<int> seen(left);
-          for (int j = 0; j < left; ++j) seen[j] = cnt[(x + 1 + j) % X].load(std::memory_order_relaxed);
-          auto claims_of = [&](int m) { return chunk < 0 ? pgs::pair_claims(m, G, X) : m; };
-          int j = 0;
-          while (j < left && seen[j] >= claims_of(range_n((x + 1 + j) % X))) ++j;
-          if (j == left) break;
-          passed += j;
-          x = (x + 1 + j) % X;
-          continue;
-        }
-        // the end is cut at the end of the range holding the first tile
-        const int v0 = begin + f;
-        const int range_end = pgs::ws_range_begin(pgs::ws_owner(v0, T, X) + 1, T, X);
-        const int ve = begin + e < range_end ? begin + e : range_end;
-        for (int v = v0; v < ve; ++v) {
-          visits[v].fetch_add(1);
-          owner[v] = p;
-          order[v] = done++;
-          std::this_thread::yield();
-        }
+      int v = pgs::ws_claim(w, across, T, G, X, chunk, ops);
+      while (v >= 0) {
+        if (v >= T) std::abort();  // a claim past the tiles
+        visits[v].fetch_add(1);
+        owner[v] = p;
+        order[v] = done++;
+        std::this_thread::yield();
+        v = v + 1 < w.cend ? v + 1 : pgs::ws_claim(w, across, T, G, X, chunk, ops);
       }
     });
   }
@@ -138,6 +76,25 @@ static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
   std::printf("\n");
   for (int v = 0; v < T; ++v) std::printf("%d %d %d %d\n", v, visits[v].load(), owner[v], order[v]);
   return 0;
+}
+
+// Per-XCD work stealing: program p claims from counter p mod X.
+static int ws_threads(int pm, int pn, int G, int X, int chunk) {
+  std::vector<int> homes(G);
+  for (int p = 0; p < G; ++p) homes[p] = p % X;
+  return claim_threads(pm, pn, G, X, chunk, false, homes);
+}
+
+// Work stealing across XCDs from home counters p mod X (0), all 0 (1), or
+// pseudo-random (2).
+static int wsx_threads(int pm, int pn, int G, int X, int chunk, int home_mode) {
+  std::vector<int> homes(G);
+  unsigned lcg = 12345u;
+  for (int p = 0; p < G; ++p) {
+    lcg = lcg * 1103515245u + 12345u;
+    homes[p] = home_mode == 0 ? p % X : home_mode == 1 ? 0 : (int)((lcg >> 16) % (unsigned)X);
+  }
+  return claim_threads(pm, pn, G, X, chunk, true, homes);
 }
 
 // Stream-K: every program's segments (tile, first slab, end slab, slot), then
@@ -194,9 +151,9 @@ int main(int argc, char** argv) {
   if (mode == "static" && argc == 7)
     return static_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                        std::atoi(argv[6]));
-  if (mode == "ws" && argc == 8)
+  if (mode == "ws" && argc == 8)  // argv[6], the group size, does not enter the claims
     return ws_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
-                      std::atoi(argv[6]), std::atoi(argv[7]));
+                      std::atoi(argv[7]));
   if (mode == "wsx" && argc == 8)
     return wsx_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                        std::atoi(argv[6]), std::atoi(argv[7]));

@@ -119,13 +119,17 @@ def test_grouped_errors():
         ([ok, (c, b, d, 256, 256, 128)], "bf16_out_bf16", "grouped", pg._abi.ERR_INVALID),   # reads c
         ([(a, b100, d, 256, 256, 100)], "bf16_out_bf16", "grouped", pg._abi.ERR_UNSUPPORTED),  # K % 8
         ([ok], "bf16_out_bf16", "stream_k", pg._abi.ERR_UNSUPPORTED),
-        ([ok], "fp8_b128_out_bf16", "grouped", pg._abi.ERR_INVALID),                       # no scales
+        ([(a.data_ptr(), b.data_ptr(), c.data_ptr(), 256, 256, 128)], "fp8_b128_out_bf16", "grouped",
+         pg._abi.ERR_INVALID),                                                              # no scales
         ([(a, b, c, 256, 256, 0)], "bf16_out_bf16", "grouped", pg._abi.ERR_INVALID),          # K = 0
     ]
     for probs, dt, sched, code in cases:
         with pytest.raises(pg.PgemmError) as e:
             pg.pgemm_run_grouped(cfg, probs, dt, sched)
         assert e.value.code == code, (len(probs), dt, sched)
+    # bf16 tensors given as fp8 operands: refused by the binding before the call
+    with pytest.raises(ValueError, match="dtype"):
+        pg.pgemm_run_grouped(cfg, [ok], "fp8_b128_out_bf16", "grouped")
 
 
 # fp8: (M, N, K) per problem, K a multiple of 128, N of 16

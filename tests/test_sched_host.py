@@ -15,12 +15,39 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KINDS = {"blocked": 0, "interleaved": 1, "grouped": 2, "blocked_grouped": 4}
 
 
+SRC = os.path.join(ROOT, "tests", "host", "sched_host.cpp")
+# Sanitizer builds of the host harness (g++, CPU code only): ThreadSanitizer
+# for the claim loops on real threads, AddressSanitizer + UndefinedBehavior-
+# Sanitizer for every mode; any report aborts the run.
+SANITIZERS = {"thread": ["-fsanitize=thread"],
+              "address,undefined": ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]}
+SAN_ENV = {"TSAN_OPTIONS": "halt_on_error=1:exitcode=66", "ASAN_OPTIONS": "detect_leaks=1:exitcode=66",
+           "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
+
+
+def _build(tmp_path_factory, name, flags):
+    exe = str(tmp_path_factory.mktemp("sched") / name)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-Wall", "-Werror", "-pthread", *flags, SRC, "-o", exe],
+                   check=True)
+    return exe
+
+
 @pytest.fixture(scope="module")
 def harness(tmp_path_factory):
-    exe = str(tmp_path_factory.mktemp("sched") / "sched_host")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-pthread",
-                    os.path.join(ROOT, "tests", "host", "sched_host.cpp"), "-o", exe], check=True)
-    return exe
+    return _build(tmp_path_factory, "sched_host", [])
+
+
+@pytest.fixture(scope="module", params=sorted(SANITIZERS))
+def sanitized(request, tmp_path_factory):
+    return request.param, _build(tmp_path_factory, "sched_host_" + request.param.replace(",", "_"),
+                                 SANITIZERS[request.param])
+
+
+def _run_sanitized(exe, *args):
+    r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True,
+                       env={**os.environ, **SAN_ENV})
+    assert r.returncode == 0 and "Sanitizer" not in r.stderr, (args, r.returncode, r.stderr[-3000:])
+    return r.stdout.strip().splitlines()
 
 
 def _static(exe, kind, pm, pn, G, gs):
@@ -48,9 +75,15 @@ def test_static_walk_matches_model(harness, kind):
 def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     out = subprocess.run([harness, "ws", str(pm), str(pn), str(G), str(X), "8", str(chunk)],
                          check=True, capture_output=True, text=True).stdout.strip().splitlines()
-    counters = list(map(int, out[0].split(":")[1].split()))
+    _check_ws(out, pm, pn, G, X, chunk)
+
+
+def _check_ws(out, pm, pn, G, X, chunk):
+    homes = list(map(int, out[0].split(":")[1].split()))
+    assert homes == [p % X for p in range(G)]
+    counters = list(map(int, out[1].split(":")[1].split()))
     T = pm * pn
-    rows = [tuple(map(int, l.split())) for l in out[1:]]
+    rows = [tuple(map(int, l.split())) for l in out[2:]]
     assert len(rows) == T
     visits = [r[1] for r in rows]
     owner = [r[2] for r in rows]
@@ -65,6 +98,10 @@ def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
 def test_wsx_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk, home_mode):
     out = subprocess.run([harness, "wsx", str(pm), str(pn), str(G), str(X), str(chunk), str(home_mode)],
                          check=True, capture_output=True, text=True).stdout.strip().splitlines()
+    _check_wsx(out, pm, pn, G, X, chunk)
+
+
+def _check_wsx(out, pm, pn, G, X, chunk):
     homes = list(map(int, out[0].split(":")[1].split()))
     counters = list(map(int, out[1].split(":")[1].split()))
     T = pm * pn
@@ -123,3 +160,39 @@ def test_balanced_grid_matches_model(harness, G, X):
     for line in out:
         T, g = map(int, line.split())
         assert g == sm.balanced_grid(T, G, X), (T, G, X, g)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(32, 32, 256, 8, 1), (19, 32, 256, 8, -1), (33, 7, 64, 8, 4),
+                                             (13, 11, 3, 8, 2)])
+def test_claim_loops_under_sanitizers(sanitized, pm, pn, G, X, chunk):
+    """The kernels' claim and sweep code on real threads, built with
+    ThreadSanitizer and with AddressSanitizer + UndefinedBehaviorSanitizer:
+    no report, and the executions still satisfy the model's invariants."""
+    _, exe = sanitized
+    if G >= X:  # per-XCD work stealing needs a program on every counter
+        _check_ws(_run_sanitized(exe, "ws", pm, pn, G, X, 8, chunk), pm, pn, G, X, chunk)
+    for home_mode in (0, 1, 2):
+        _check_wsx(_run_sanitized(exe, "wsx", pm, pn, G, X, chunk, home_mode), pm, pn, G, X, chunk)
+
+
+def test_other_modes_under_sanitizers(sanitized):
+    name, exe = sanitized
+    if name == "thread":
+        pytest.skip("single-threaded modes: covered by the address / undefined build")
+    for kind in KINDS.values():
+        _run_sanitized(exe, "static", kind, 19, 32, 256, 8)
+    assert len(_run_sanitized(exe, "pairs", 256, 8)) == 140
+    assert len(_run_sanitized(exe, "grid", 3000, 256, 8)) == 3001
+    for T, nk, G in [(608, 128, 256), (3, 5, 256), (300, 2, 7)]:
+        _run_sanitized(exe, "sk", T, nk, G)
+
+
+def test_oracle_gemm_under_sanitizers(tmp_path):
+    """The oracle's C GEMM built with AddressSanitizer + UndefinedBehavior-
+    Sanitizer (and OpenMP), run on small and edge shapes against a plain loop."""
+    exe = str(tmp_path / "oracle_sanitize")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fopenmp", "-ffp-contract=off",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    os.path.join(ROOT, "tests", "host", "oracle_sanitize.c"), "-o", exe, "-lm"], check=True)
+    out = _run_sanitized(exe)
+    assert out == ["mismatches: 0"]

@@ -78,7 +78,7 @@ def _check_tensor(x, what, dtypes=None, nbytes=None):
         raise TypeError(f"{what}: expected a torch tensor or an int device pointer")
     if not x.is_contiguous():
         raise ValueError(f"{what}: tensor must be contiguous (row-major)")
-    if dtypes is not None:
+    if dtypes is not None and nbytes != 0:  # an empty buffer is never accessed
         allowed = _torch_dtypes(dtypes)
         if x.dtype not in allowed:
             raise ValueError(f"{what}: dtype {x.dtype} not in {allowed}")

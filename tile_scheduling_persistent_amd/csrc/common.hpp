@@ -26,9 +26,7 @@ struct Witness {
 // block per counter, so claims on different counters never contend for one
 // cache line at the point where device-scope atomics are performed.
 constexpr int kCounterStride = 64;
-// Counters work stealing across XCDs can look at in one pass (the XCDs of
-// one MI355X).
-constexpr int kMaxStealCounters = 8;
+using pgs::kMaxStealCounters;
 
 struct SchedParams {
   int kind;           // pgs::Kind
@@ -123,6 +121,7 @@ hipError_t launch_fill_i32(int* ptr, int n, int value, hipStream_t stream);
 bool gemm_bf16_tile_supported(int bm, int bn, int bk);
 bool gemm_bf16_vec_fits(int bm, int bk, long long N, long long K);
 bool gemm_bf16_lds_eligible(int bm, int bn, int bk, long long N, long long K);
+bool gemm_bf16_pp_eligible(int bm, int bn, int bk, long long N, long long K);
 hipError_t launch_gemm_bf16_lds(const GemmParams& p, int bm, int bn, bool out_bf16, bool witness,
                                 hipStream_t stream);
 bool gemm_fp8_tile_supported(int bm, int bn, int bk);
@@ -149,6 +148,8 @@ hipError_t launch_gemm_fp8_grouped(const GemmParams& p, int bm, int bn, bool wit
 KernelInfo info_gemm_fp8_grouped(int bm, int bn);
 KernelInfo info_gemm_bf16(int bm, int bn, int bk, bool out_bf16, bool vec);
 KernelInfo info_gemm_bf16_lds(int bm, int bn, bool out_bf16);
+KernelInfo info_gemm_bf16_pp(bool out_bf16);
+hipError_t launch_gemm_bf16_pp(const GemmParams& p, bool out_bf16, bool witness, hipStream_t stream);
 KernelInfo info_gemm_fp8(int bm, int bn);
 KernelInfo info_padd(int tr, int tc, bool vec);
 
@@ -198,96 +199,70 @@ __device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
   while (wall_ticks() - t0 < ticks) __builtin_amdgcn_s_sleep(2);
 }
 
+// Memory operations of the work-stealing claim (pgs::ws_claim) on the
+// counters, relaxed device-scope atomics.  ThreadOps: called by the one
+// thread that claims for its workgroup.  WaveOps: called by a whole wave with
+// every lane active; lane 0 performs the operation and the result is
+// broadcast, so the claim's state stays uniform (scalar registers).
+struct ThreadOps {
+  int* counters;
+  __device__ __forceinline__ int fetch_add(int c, int v) {
+    return __hip_atomic_fetch_add(counters + c * kCounterStride, v, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ int load(int c) {
+    return __hip_atomic_load(counters + c * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+struct WaveOps {
+  int* counters;
+  __device__ __forceinline__ int fetch_add(int c, int v) {
+    int r = 0;
+    if ((threadIdx.x & 63) == 0)
+      r = __hip_atomic_fetch_add(counters + c * kCounterStride, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(r);
+  }
+  __device__ __forceinline__ int load(int c) {
+    int r = 0;
+    if ((threadIdx.x & 63) == 0)
+      r = __hip_atomic_load(counters + c * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(r);
+  }
+};
+
 // Per-program view of the scheduler.  Static kinds walk arithmetically.
-// Work stealing claims from counter p mod X.  Work stealing across XCDs
-// starts on the counter of the XCD the program runs on; when a claim fails
-// it reads every counter it has not passed yet (one round of loads), skips
-// those already past their range, and moves to the first one that is not;
-// it stops when none is left, so it makes at most one failing claim per
-// counter.  first()/next() return a tile id or -1 when the program is done.
-// For the work-stealing kinds only one thread of the workgroup may call
-// them (each call is at least one claim).
+// Work stealing claims from counter p mod X; work stealing across XCDs starts
+// on the counter of the XCD the program runs on and moves on to the others
+// as pgs::ws_claim describes.  first()/next() return a tile id or -1 when the
+// program is done; for the work-stealing kinds each call may claim, so only
+// one thread of the workgroup may call them (or, with first_wave()/
+// next_wave(), one whole wave).
 struct Walker {
   SchedParams s;
   int p;
-  int end;       // static: end of the walk
-  int x;         // work stealing: current counter
-  int passed;    // work stealing across XCDs: counters passed (home first)
-  int begin, n;  // work stealing: counter x's range [begin, begin + n)
-  int cend;      // work stealing: end of the last claim (next() walks up to it)
+  int end;         // static: end of the walk
+  pgs::WsWalk ws;  // work stealing: the walk over the counters
 
   __device__ __forceinline__ int nx() const { return s.X > 0 ? s.X : 1; }
-  __device__ __forceinline__ int range_begin(int c) const { return pgs::ws_range_begin(c, s.T, nx()); }
-  __device__ __forceinline__ int* counter(int c) const { return s.counters + c * kCounterStride; }
-
-  __device__ __forceinline__ void set_counter(int c) {
-    x = c;
-    begin = range_begin(c);
-    n = range_begin(c + 1) - begin;
-  }
 
   __device__ __forceinline__ Walker(const SchedParams& sp, int prog) : s(sp), p(prog) {
     end = 0;
-    passed = 0;
-    cend = 0;
     const int X = nx();
-    set_counter(sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X);
+    pgs::ws_start(ws, sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X, sp.T, X);
   }
 
-  // Claims handed out by a range of m tiles (s.chunk < 0: paired claims).
-  __device__ __forceinline__ int claims_of(int m) const {
-    return s.chunk < 0 ? pgs::pair_claims(m, s.G, nx()) : m;
+  template <class Ops>
+  __device__ __forceinline__ int claim_with(Ops ops) {
+    return pgs::ws_claim(ws, s.kind == pgs::kWorkStealingXcc, s.T, s.G, nx(), s.chunk, ops);
   }
 
   // One claim (s.chunk tiles, or a pair / single under paired claims);
-  // returns the first claimed id or -1, and sets cend to the claim's end.
-  __device__ __forceinline__ int claim() {
-    const int X = nx();
-    for (;;) {
-      const int step = s.chunk < 0 ? 1 : s.chunk;
-      const int i = __hip_atomic_fetch_add(counter(x), step, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      if (s.chunk < 0) {
-        int f, e;
-        if (i >= 0 && pgs::pair_claim(i, n, s.G, X, f, e)) {
-          cend = begin + e;
-          return begin + f;
-        }
-      } else if (i >= 0 && i < n) {
-        cend = claim_end(begin + i);
-        return begin + i;
-      }
-      if (s.kind != pgs::kWorkStealingXcc || ++passed >= X) return -1;
-      // the counters after x not passed yet: read them all, then take the first
-      // that still has tiles
-      const int left = X - passed;
-      int seen[kMaxStealCounters];
-#pragma unroll
-      for (int j = 0; j < kMaxStealCounters; ++j) {
-        int c = x + 1 + j;
-        c = c >= X ? c - X : c;
-        seen[j] = j < left ? __hip_atomic_load(counter(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-      }
-      int j = 0;
-      for (; j < left; ++j) {
-        int c = x + 1 + j;
-        c = c >= X ? c - X : c;
-        if (seen[j] < claims_of(range_begin(c + 1) - range_begin(c))) break;
-      }
-      if (j == left) return -1;
-      passed += j;
-      const int c = x + 1 + j;
-      set_counter(c >= X ? c - X : c);
-    }
-  }
+  // returns the first claimed id or -1, and sets ws.cend to the claim's end.
+  __device__ __forceinline__ int claim() { return claim_with(ThreadOps{s.counters}); }
 
-  // End (exclusive) of the claim that starts at tile v: v + chunk, cut at the
-  // end of the counter range that holds v (any thread may call it).
-  __device__ __forceinline__ int claim_end(int v) const {
-    const int e = v + s.chunk;
-    const int range_end = range_begin(pgs::ws_owner(v, s.T, nx()) + 1);
-    return e < range_end ? e : range_end;
-  }
+  // End (exclusive) of the claim that starts at tile v (any thread may call it).
+  __device__ __forceinline__ int claim_end(int v) const { return pgs::ws_claim_end(v, s.chunk, s.T, nx()); }
 
   __device__ __forceinline__ int first() {
     if (pgs::work_stealing(s.kind)) return claim();
@@ -309,9 +284,19 @@ struct Walker {
 
   // The tile after v: the next one of the current claim, else a new claim.
   __device__ __forceinline__ int next(int v) {
-    if (pgs::work_stealing(s.kind)) return v + 1 < cend ? v + 1 : claim();
-    const int nv = pgs::static_next(s.kind, v, s.G, end);
-    return nv < end ? nv : -1;
+    if (pgs::work_stealing(s.kind)) return v + 1 < ws.cend ? v + 1 : claim();
+    return next_static(v);
+  }
+
+  // first() / next() called by every lane of one wave (the result and the
+  // walk's state are the same in every lane).
+  __device__ __forceinline__ int first_wave() {
+    if (pgs::work_stealing(s.kind)) return claim_with(WaveOps{s.counters});
+    return first_static();
+  }
+  __device__ __forceinline__ int next_wave(int v) {
+    if (pgs::work_stealing(s.kind)) return v + 1 < ws.cend ? v + 1 : claim_with(WaveOps{s.counters});
+    return next_static(v);
   }
 
   __device__ __forceinline__ void tile_coords(int v, int& pid_m, int& pid_n) const {

@@ -29,7 +29,7 @@
 //    loader's bookkeeping (tile switch, claim, buffer resources) is scalar
 //    pointer arithmetic except on edge slabs.
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
-//    so that the ds_read_b128 operand reads hit distinct banks (see swz_a).
+//    so that the ds_read_b128 operand reads hit distinct banks (see bf16_swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
 //    c ^ 4*(k & 3)); the k-contiguous operand the MFMA needs is produced by
 //    ds_read_b64_tr_b16: within each 16-lane group, lane i points at row
@@ -82,25 +82,6 @@ struct Shape {
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && 1024 % B_ROW == 0, "slab splits into 1 KiB loads");
 };
 
-// LDS banks: 64 x 4 bytes.  A ds_read_b128 is served 16 lanes at a time and
-// a ds_read_b64 (also the transposing form) 32 lanes at a time, so a read is
-// conflict-free when those lanes hit distinct 16- (8-) byte slots of a
-// 256-byte window.
-//
-// Physical chunk of logical chunk c in row `row` of A: the MFMA operand read
-// touches 16 consecutive rows at one logical chunk; the XOR spreads them
-// over the 16 slots (128-byte rows: 2 rows per window x 8 chunks; 64-byte
-// rows: 4 rows x 4 chunks).
-template <int BK>
-__device__ __forceinline__ int swz_a(int row, int c) {
-  return BK == 64 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
-}
-
-// Physical chunk of logical chunk c in row k of B: a transposing read of 32
-// lanes touches 4 consecutive rows x 4 consecutive chunks; XOR-ing chunk
-// bits 2-3 with the row moves the 4 rows to different quarter windows.
-__device__ __forceinline__ int swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
-
 // SK: stream-K.  The program walks segments (tile, first slab, end slab)
 // of its own stream-K run instead of whole tiles; a segment that does not
 // cover its tile leaves fp32 partial sums in the program's workspace slot,
@@ -144,8 +125,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 
   // ---- global -> LDS load offsets (per lane, relative to the slab bases) ----
   // A: instruction q covers rows RPI*q ..; lane p -> row RPI*q + p/CPR, LDS
-  // chunk p%CPR, global chunk swz_a(row, p%CPR) (the swizzle is an
-  // involution).  B likewise with swz_b.
+  // chunk p%CPR, global chunk bf16_swz_a(row, p%CPR) (the swizzle is an
+  // involution).  B likewise with bf16_swz_b.
   unsigned aoff[NA], boff[NB];
   int achk[NA], bchk[NB];
   // row strides K (A) and N (B), in elements
@@ -154,14 +135,14 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     for (int i = 0; i < NA; ++i) {
       const int q = wave * NA + i;
       const int row = q * S::A_RPI + lane / S::A_CPR;
-      achk[i] = swz_a<BK>(row, lane % S::A_CPR);
+      achk[i] = bf16_swz_a<BK>(row, lane % S::A_CPR);
       aoff[i] = (unsigned)row * (unsigned)Kx * 2u + (unsigned)achk[i] * 16u;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int q = wave * NB + i;
       const int row = q * S::B_RPI + lane / S::B_CPR;
-      bchk[i] = swz_b(row, lane % S::B_CPR);
+      bchk[i] = bf16_swz_b(row, lane % S::B_CPR);
       boff[i] = (unsigned)row * (unsigned)Nx * 2u + (unsigned)bchk[i] * 16u;
     }
   };
@@ -174,7 +155,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
   for (int kk = 0; kk < S::KK; ++kk) {
     const int row = wm * S::TM + l32;
-    rd_a[kk] = (unsigned)(row * S::A_ROW + swz_a<BK>(row, kk * 2 + (lane >> 5)) * 16);
+    rd_a[kk] = (unsigned)(row * S::A_ROW + bf16_swz_a<BK>(row, kk * 2 + (lane >> 5)) * 16);
   }
   unsigned rd_b[S::SN];
   {
@@ -183,7 +164,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
     for (int sn = 0; sn < S::SN; ++sn) {
       const int n = wn * S::TN + sn * 32 + (g & 1) * 16 + 4 * a;
-      const int c = swz_b(krow, n >> 3);
+      const int c = bf16_swz_b(krow, n >> 3);
       rd_b[sn] = (unsigned)(S::A_BYTES + krow * S::B_ROW + c * 16 + 8 * (a & 1));
     }
   }

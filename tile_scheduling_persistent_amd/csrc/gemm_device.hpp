@@ -109,6 +109,26 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// LDS layout of the bf16 kernels' operand slabs.
+// LDS banks: 64 x 4 bytes.  A ds_read_b128 is served 16 lanes at a time and
+// a ds_read_b64 (also the transposing form) 32 lanes at a time, so a read is
+// conflict-free when those lanes hit distinct 16- (8-) byte slots of a
+// 256-byte window.
+//
+// Physical chunk of logical chunk c in row `row` of A: the MFMA operand read
+// touches 16 consecutive rows at one logical chunk; the XOR spreads them
+// over the 16 slots (128-byte rows: 2 rows per window x 8 chunks; 64-byte
+// rows: 4 rows x 4 chunks).
+template <int BK>
+__device__ __forceinline__ int bf16_swz_a(int row, int c) {
+  return BK == 64 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
+}
+
+// Physical chunk of logical chunk c in row k of B: a transposing read of 32
+// lanes touches 4 consecutive rows x 4 consecutive chunks; XOR-ing chunk
+// bits 2-3 with the row moves the 4 rows to different quarter windows.
+__device__ __forceinline__ int bf16_swz_b(int k, int c) { return c ^ (4 * (k & 3)); }
+
 // Store one 32x32 block of fp32 accumulators as bf16.  Layout of
 // v_mfma_f32_32x32 with B^T as the first operand: lane l holds row l % 32,
 // columns 8g + 4*(l/32) .. +3 in registers 4g .. 4g+3 (g = 0..3).  Swapping
@@ -118,15 +138,19 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 // those of g = 2q+1, stored as one 16-byte chunk.  row_off: byte offset of
 // the lane's row at column 0 of the block's tile; col0: the block's first
 // column; chunks at or past ncols are dropped (ncols a multiple of 8).
-template <typename Acc>
+// AGPR_READS: read each accumulator with an explicit v_accvgpr_read (for
+// kernels whose accumulators must stay in AGPRs); otherwise the compiler
+// places them.
+template <bool AGPR_READS = true, typename Acc>
 __device__ __forceinline__ void store_block_bf16(const Acc& a, __amdgpu_buffer_rsrc_t rC,
                                                  unsigned row_off, int col0, int ncols, int hi) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  auto rd = [&](int i) { return AGPR_READS ? acc_read(a[i]) : a[i]; };
   unsigned pk[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    pk[g][0] = pack_bf16x2(acc_read(a[4 * g]), acc_read(a[4 * g + 1]));
-    pk[g][1] = pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]));
+    pk[g][0] = pack_bf16x2(rd(4 * g), rd(4 * g + 1));
+    pk[g][1] = pack_bf16x2(rd(4 * g + 2), rd(4 * g + 3));
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {

@@ -1,6 +1,7 @@
 // Tile schedulers of the persistent kernels: integer functions shared by host
-// and device code.  No memory access happens here; the work-stealing claim
-// itself (one atomic on the XCD's counter) lives in the kernels.
+// and device code.  No memory access happens here: the work-stealing claim
+// loop (ws_claim) takes its counter operations from the caller (device
+// atomics in the kernels, std::atomic in the host harness).
 //
 // Sources (page title, section):
 //  - "Implement persistent kernels" (Helion PR #238), example output: blocked
@@ -131,6 +132,93 @@ PGS_FN bool pair_claim(int k, int n, int G, int X, int& first, int& end) {
 // ws_range_begin(x) <= v.
 PGS_FN int ws_owner(int v, int T, int X) {
   return (int)((((int64_t)v + 1) * X + T - 1) / T) - 1;
+}
+
+// Counters work stealing across XCDs can look at in one pass (the XCDs of
+// one MI355X).
+constexpr int kMaxStealCounters = 8;
+
+// Claims a range of m tiles hands out (chunk < 0: paired claims).
+PGS_FN int ws_claims_of(int m, int chunk, int G, int X) {
+  return chunk < 0 ? pair_claims(m, G, X) : m;
+}
+
+// End (exclusive) of the claim of `chunk` tiles that starts at tile v, cut at
+// the end of the counter range that holds v.
+PGS_FN int ws_claim_end(int v, int chunk, int T, int X) {
+  const int e = v + chunk;
+  const int range_end = ws_range_begin(ws_owner(v, T, X) + 1, T, X);
+  return e < range_end ? e : range_end;
+}
+
+// One program's position in the work-stealing walk.
+struct WsWalk {
+  int x;        // counter it claims from
+  int passed;   // counters passed so far, the home counter first (across XCDs)
+  int begin, n; // counter x's range [begin, begin + n)
+  int cend;     // end (exclusive) of the last claim
+};
+
+PGS_FN void ws_set_counter(WsWalk& w, int c, int T, int X) {
+  w.x = c;
+  w.begin = ws_range_begin(c, T, X);
+  w.n = ws_range_begin(c + 1, T, X) - w.begin;
+}
+
+PGS_FN void ws_start(WsWalk& w, int home, int T, int X) {
+  w.passed = 0;
+  w.cend = 0;
+  ws_set_counter(w, home, T, X);
+}
+
+// One claim from counter w.x: `chunk` consecutive tiles, or under paired
+// claims (chunk < 0) claim k's pair or single tile (pair_claim).  Work
+// stealing across XCDs (across = true) goes on after a failing claim: it
+// reads every counter it has not passed yet (one round of loads, cyclic order
+// from w.x), skips those whose range is exhausted and claims from the first
+// that is not; it stops when none is left, so it makes at most one failing
+// claim per counter.  Returns the first claimed tile id and sets w.cend, or
+// -1 when the program is done.  `ops` performs the memory operations on
+// counter c: fetch_add(c, v) returns the old value, load(c) reads it (the
+// kernels: device atomics, by one thread or by one lane for a whole wave;
+// the host harness: std::atomic).  Needs X <= kMaxStealCounters when across.
+template <class Ops>
+PGS_FN int ws_claim(WsWalk& w, bool across, int T, int G, int X, int chunk, Ops& ops) {
+  for (;;) {
+    const int step = chunk < 0 ? 1 : chunk;
+    const int i = ops.fetch_add(w.x, step);
+    if (chunk < 0) {
+      int f, e;
+      if (i >= 0 && pair_claim(i, w.n, G, X, f, e)) {
+        w.cend = w.begin + e;
+        return w.begin + f;
+      }
+    } else if (i >= 0 && i < w.n) {
+      w.cend = ws_claim_end(w.begin + i, chunk, T, X);
+      return w.begin + i;
+    }
+    if (!across || ++w.passed >= X) return -1;
+    const int left = X - w.passed;
+    int seen[kMaxStealCounters];
+#if defined(__HIPCC__)
+#pragma unroll
+#endif
+    for (int j = 0; j < kMaxStealCounters; ++j) {
+      int c = w.x + 1 + j;
+      c = c >= X ? c - X : c;
+      seen[j] = j < left ? ops.load(c) : 0;
+    }
+    int j = 0;
+    for (; j < left; ++j) {
+      int c = w.x + 1 + j;
+      c = c >= X ? c - X : c;
+      if (seen[j] < ws_claims_of(ws_range_begin(c + 1, T, X) - ws_range_begin(c, T, X), chunk, G, X)) break;
+    }
+    if (j == left) return -1;
+    w.passed += j;
+    const int c = w.x + 1 + j;
+    ws_set_counter(w, c >= X ? c - X : c, T, X);
+  }
 }
 
 // Static schedulers: first tile id of program p and the end of its walk.
