@@ -208,6 +208,26 @@ PGEMM_API pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B
                        int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
                        pgemm_sched sched, const pgemm_args* args, void* hip_stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bit for bit), errors and stream rules as pgemm_run,
+ * but the work-stealing counters and the stream-K partial sums live in a
+ * static device array of PGEMM_NOALLOC_SCRATCH_BYTES on each device (held
+ * from the first pgemm_config_create on that device until the process ends)
+ * instead of the config's buffers, so the call allocates nothing at any
+ * grid.  Limits: stream-K's partial sums, grid x 2 x tile_m x tile_n x 4
+ * bytes, must fit in 64 MiB (the default grid fits at 128x128 and 128x256
+ * tiles; at 256x256 tiles pass args->grid <= 128), otherwise
+ * PGEMM_ERR_INVALID with nothing enqueued; at most 16 XCDs; no witness
+ * (PGEMM_ERR_UNSUPPORTED).  Every call on a GPU uses that GPU's one array,
+ * which keeps the last call's contents (the counters are cleared on the
+ * stream before each work-stealing launch): calls that overlap in time on
+ * one GPU, from any stream or config, race and must not be made. */
+#define PGEMM_NOALLOC_SCRATCH_BYTES ((64u << 20) + 4096u)
+PGEMM_API pgemm_status pgemm_run_noalloc(pgemm_config* cfg, const void* A, const void* B, void* C,
+                               int64_t M, int64_t N, int64_t K, pgemm_dtype dtype,
+                               pgemm_sched sched, const pgemm_args* args, void* hip_stream);
+
 /* C[rows][cols] = X + Y (fp32, one IEEE add per element, round to nearest
  * even), persistent over tile_rows x tile_cols tiles with the same
  * schedulers (tile rows are dimension 0 of the decode).  Built tiles: 32x16,

@@ -31,7 +31,7 @@ DTYPES = {
     "fp8_b128_out_bf16": _abi.FP8E4M3_B128_OUT_BF16,
 }
 
-__all__ = ["Config", "pgemm_run", "pgemm_run_grouped", "padd_run", "padd_run_multi", "plan_gemm", "plan_add", "SCHEDULERS",
+__all__ = ["Config", "pgemm_run", "pgemm_run_noalloc", "pgemm_run_grouped", "padd_run", "padd_run_multi", "plan_gemm", "plan_add", "SCHEDULERS",
            "DTYPES", "PgemmError", "status_str", "make_args"]
 
 
@@ -198,6 +198,18 @@ def pgemm_run(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=N
                                 int(M), int(N), int(K), _dtype(dtype), _sched(sched),
                                 ctypes.byref(args) if args is not None else None, _stream(stream))
     _check("pgemm_run", code)
+
+
+def pgemm_run_noalloc(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=None,
+                      stream=None):
+    """pgemm_run without any device allocation: the work-stealing counters and
+    the stream-K partial sums come from the library's static per-device
+    scratch (calls on one GPU must not overlap)."""
+    code = _abi.lib().pgemm_run_noalloc(cfg.handle, *_gemm_ptrs(A, B, C, M, N, K, dtype, args),
+                                        int(M), int(N), int(K), _dtype(dtype), _sched(sched),
+                                        ctypes.byref(args) if args is not None else None,
+                                        _stream(stream))
+    _check("pgemm_run_noalloc", code)
 
 
 def _gemm_ptrs(A, B, C, M, N, K, dtype, args, where=""):

@@ -75,6 +75,8 @@ class padd_problem(ctypes.Structure):
 
 
 PGEMM_MAX_PROBLEMS = 8
+# bytes of the static device scratch pgemm_run_noalloc uses on each device
+NOALLOC_SCRATCH_BYTES = (64 << 20) + 4096
 
 
 class pgemm_problem(ctypes.Structure):
@@ -109,6 +111,8 @@ def lib() -> ctypes.CDLL:
                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                             ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.c_void_p]
     L.pgemm_run.restype = st
+    L.pgemm_run_noalloc.argtypes = L.pgemm_run.argtypes
+    L.pgemm_run_noalloc.restype = st
     L.padd_run.argtypes = [_cfg_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                            ctypes.c_int, ctypes.POINTER(pgemm_args), ctypes.c_void_p]

@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/pgemm.h"
@@ -29,6 +30,7 @@ struct pgemm_config {
   int* counters;  // device, [capacity * pgk::kCounterStride]; counter x at x * kCounterStride
   float* ws;          // stream-K partial-sum workspace (device), grown on demand
   size_t ws_bytes;
+  unsigned char* scratch;  // this device's address of the static `scratch` array
   // witness buffers (device)
   int64_t w_tiles;
   int w_programs;
@@ -263,8 +265,10 @@ pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk
                             hipStream_t stream) {
   if (!pgs::work_stealing(s.kind)) return PGEMM_OK;
   if (args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET)) return PGEMM_OK;
-  // a fill kernel rather than a memset node, so that the call may be captured
-  return pgk::launch_zero_i32(cfg->counters, cfg->capacity * pgk::kCounterStride, stream) == hipSuccess
+  // a fill kernel rather than a memset node, so that the call may be captured;
+  // s.counters is the config's array or the static scratch's
+  const int n = s.counters == cfg->counters ? cfg->capacity : s.X;
+  return pgk::launch_zero_i32(s.counters, n * pgk::kCounterStride, stream) == hipSuccess
              ? PGEMM_OK
              : PGEMM_ERR_LAUNCH;
 }
@@ -294,6 +298,57 @@ pgemm_status ensure_workspace(pgemm_config* cfg, size_t bytes, hipStream_t strea
   cfg->ws_bytes = bytes;
   return PGEMM_OK;
 }
+
+// Device memory of the allocation-free entry point (pgemm_run_noalloc): one
+// static array per device, `scratch`, holding the work-stealing counters
+// (kScratchCounters blocks of 256 bytes) followed by the stream-K partial-sum
+// slots.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol): pgemm_config_create looks up the
+// device address with hipGetSymbolAddress, once per device with that device
+// current, and every use goes through that address.  Every call on a GPU
+// shares its array; calls that overlap on one GPU race.
+constexpr int kScratchCounters = 16;
+constexpr size_t kScratchCounterBytes = (size_t)kScratchCounters * pgk::kCounterStride * sizeof(int);
+constexpr size_t kScratchWsBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = kScratchCounterBytes + kScratchWsBytes;
+static_assert(kScratchCounterBytes % 256 == 0, "partial sums start 256-byte aligned");
+static_assert(PGEMM_NOALLOC_SCRATCH_BYTES == kScratchBytes, "header states the scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices];  // per device: address of `scratch` there, or null
+
+// Address of `scratch` on `device` (the caller has made it current).
+pgemm_status scratch_address(int device, unsigned char** out) {
+  if (device < 0 || device >= kMaxDevices) return PGEMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return PGEMM_ERR_DEVICE;
+    }
+    g_scratch[device] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch[device];
+  return PGEMM_OK;
+}
+
+// Device scratch of one GEMM call: the work-stealing counters and the
+// stream-K partial sums, either the config's allocations (which may grow for
+// a larger grid) or the static scratch (which never does).
+struct CallBuffers {
+  int* counters;
+  int n_counters;
+  float* ws;
+  size_t ws_bytes;
+  bool growable;
+};
+
+pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                       int64_t K, pgemm_dtype dtype, pgemm_sched sched, const pgemm_args* args,
+                       void* hip_stream, CallBuffers buf);
 
 }  // namespace
 
@@ -360,6 +415,10 @@ pgemm_status pgemm_config_create(int device, int max_xcds, pgemm_config** out) {
       const size_t b = (size_t)c->num_cus * (size_t)ki.occupancy * 2 * (size_t)t[0] * t[1] * sizeof(float);
       wsb = b > wsb ? b : wsb;
     }
+  }
+  if (scratch_address(device, &c->scratch) != PGEMM_OK) {
+    delete c;
+    return PGEMM_ERR_DEVICE;
   }
   hipError_t e = hipMalloc((void**)&c->counters, cbytes);
   if (e == hipSuccess) e = hipMemset(c->counters, 0, cbytes);
@@ -640,7 +699,30 @@ pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip
 pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M,
                        int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
                        const pgemm_args* args, void* hip_stream) {
-  if (!cfg || !A || !B || !C) return PGEMM_ERR_INVALID;
+  if (!cfg) return PGEMM_ERR_INVALID;
+  return gemm_call(cfg, A, B, C, M, N, K, dtype, sched, args, hip_stream,
+                   CallBuffers{cfg->counters, cfg->capacity, cfg->ws, cfg->ws_bytes, true});
+}
+
+pgemm_status pgemm_run_noalloc(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M,
+                               int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
+                               const pgemm_args* args, void* hip_stream) {
+  if (!cfg || !cfg->scratch) return PGEMM_ERR_INVALID;
+  if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
+  return gemm_call(cfg, A, B, C, M, N, K, dtype, sched, args, hip_stream,
+                   CallBuffers{reinterpret_cast<int*>(cfg->scratch), kScratchCounters,
+                               reinterpret_cast<float*>(cfg->scratch + kScratchCounterBytes),
+                               kScratchWsBytes, false});
+}
+
+}  // extern "C"
+
+namespace {
+
+pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                       int64_t K, pgemm_dtype dtype, pgemm_sched sched, const pgemm_args* args,
+                       void* hip_stream, CallBuffers buf) {
+  if (!A || !B || !C) return PGEMM_ERR_INVALID;
   GemmChoice ch;
   pgemm_status st = choose_gemm(M, N, K, dtype, args, A, B, C, ch);
   if (st != PGEMM_OK) return st;
@@ -684,19 +766,27 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   const pgk::KernelInfo ki = gemm_info(ch);
   st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
+  if (p.s.X > buf.n_counters) return PGEMM_ERR_INVALID;
+  p.s.counters = buf.counters;
   const bool sk = sched == PGEMM_SCHED_STREAM_K;
+  const size_t ws_need = sk ? (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float) : 0;
   if (sk) {
     // stream-K runs on the direct-to-LDS bf16 kernel and the fp8 kernel,
     // without the witness
     if (ch.kernel != PGEMM_KERNEL_BF16_LDS && ch.kernel != PGEMM_KERNEL_FP8) return PGEMM_ERR_UNSUPPORTED;
     if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
+    // the static scratch never grows: a grid whose partial sums do not fit is refused
+    if (ws_need > buf.ws_bytes && !buf.growable) return PGEMM_ERR_INVALID;
   }
   if (validate_only(args)) return PGEMM_OK;
   hipStream_t stream = (hipStream_t)hip_stream;
   if (sk) {
-    st = ensure_workspace(cfg, (size_t)p.s.G * 2 * (size_t)ch.bm * ch.bn * sizeof(float), stream);
-    if (st != PGEMM_OK) return st;
-    p.ws = cfg->ws;
+    if (ws_need > buf.ws_bytes) {
+      st = ensure_workspace(cfg, ws_need, stream);
+      if (st != PGEMM_OK) return st;
+      buf.ws = cfg->ws;
+    }
+    p.ws = buf.ws;
   }
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
@@ -716,7 +806,7 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
     e = pgk::launch_gemm_bf16(p, ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec, witness, stream);
   if (e == hipSuccess && sk) {
     pgk::SkFixParams f;
-    f.ws = cfg->ws;
+    f.ws = buf.ws;
     f.C = C;
     f.M = (int)M;
     f.N = (int)N;
@@ -733,6 +823,10 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
 
 pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* C, int64_t rows,
                       int64_t cols, int tile_rows, int tile_cols, pgemm_sched sched,
