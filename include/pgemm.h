@@ -154,7 +154,24 @@ typedef struct {
   unsigned debug_flags;       /* PGEMM_DEBUG_* */
   int straggler_program;      /* with PGEMM_DEBUG_STRAGGLER */
   int straggler_ns;           /* with PGEMM_DEBUG_STRAGGLER */
+  int pipeline;               /* bf16 256x256x64 tiles on the direct-to-LDS terms: PGEMM_PIPELINE_*;
+                                 0 => PGEMM_PIPELINE_DEFAULT */
 } pgemm_args;
+
+/* pgemm_args.pipeline: how the bf16 256x256x64 kernel feeds its matrix cores.
+ *  FOUR_WAVE  four waves, one per SIMD, each owning a 128x128 sub-tile; loads,
+ *             LDS reads and MFMAs interleaved in each wave's own stream.
+ *  PINGPONG   eight waves, two per SIMD, in two groups that alternate between
+ *             matrix work and memory work every two k-steps (one group's LDS
+ *             reads, loads and epilogue run under the other group's MFMAs);
+ *             the AMD form of the warp-role pipeline of "[Feature] Introduce
+ *             tile scheduler" (TileLang PR #2441, MXFP8 example).  Single
+ *             problems under every scheduler but STREAM_K (which, like
+ *             pgemm_run_grouped, keeps the four-wave kernel).
+ * Both give bit-identical C: the per-tile K order is the same. */
+#define PGEMM_PIPELINE_DEFAULT 0
+#define PGEMM_PIPELINE_FOUR_WAVE 1
+#define PGEMM_PIPELINE_PINGPONG 2
 
 typedef struct pgemm_config pgemm_config; /* opaque */
 
@@ -325,7 +342,8 @@ typedef enum {
   PGEMM_KERNEL_BF16_LDS = 0,     /* bf16, direct-to-LDS loads (16-byte aligned, K and N % 8 == 0) */
   PGEMM_KERNEL_BF16_STAGED = 1,  /* bf16, register-staged (any shape and alignment) */
   PGEMM_KERNEL_FP8 = 2,          /* block-scaled fp8 */
-  PGEMM_KERNEL_ADD = 3           /* persistent add */
+  PGEMM_KERNEL_ADD = 3,          /* persistent add */
+  PGEMM_KERNEL_BF16_PINGPONG = 4 /* bf16, eight waves in ping-pong (PGEMM_PIPELINE_PINGPONG) */
 } pgemm_kernel;
 
 /* Launch a call would make.  A persistent launch runs one program per

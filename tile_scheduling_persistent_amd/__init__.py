@@ -115,8 +115,12 @@ def _dtype(d):
     return DTYPES[d] if isinstance(d, str) else int(d)
 
 
+PIPELINES = {"default": _abi.PIPELINE_DEFAULT, "four_wave": _abi.PIPELINE_FOUR_WAVE,
+             "pingpong": _abi.PIPELINE_PINGPONG}
+
+
 def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_scale=None,
-              debug_flags=0, straggler_program=-1, straggler_ns=0):
+              debug_flags=0, straggler_program=-1, straggler_ns=0, pipeline="default"):
     a = _abi.pgemm_args()
     if tile is not None:
         a.tile_m, a.tile_n, a.tile_k = (tuple(tile) + (0,))[:3]
@@ -129,6 +133,7 @@ def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_sc
     a.debug_flags = debug_flags
     a.straggler_program = straggler_program
     a.straggler_ns = straggler_ns
+    a.pipeline = PIPELINES[pipeline] if isinstance(pipeline, str) else int(pipeline)
     return a
 
 

@@ -24,9 +24,11 @@ DEBUG_VALIDATE_ONLY = 0x20
 # pgemm_args.claim_chunk value for paired claims
 CLAIM_PAIRS = -1
 # pgemm_kernel
-KERNEL_BF16_LDS, KERNEL_BF16_STAGED, KERNEL_FP8, KERNEL_ADD = range(4)
+KERNEL_BF16_LDS, KERNEL_BF16_STAGED, KERNEL_FP8, KERNEL_ADD, KERNEL_BF16_PINGPONG = range(5)
 KERNEL_NAMES = {KERNEL_BF16_LDS: "bf16_lds", KERNEL_BF16_STAGED: "bf16_staged", KERNEL_FP8: "fp8",
-                KERNEL_ADD: "add"}
+                KERNEL_ADD: "add", KERNEL_BF16_PINGPONG: "bf16_pingpong"}
+# pgemm_args.pipeline
+PIPELINE_DEFAULT, PIPELINE_FOUR_WAVE, PIPELINE_PINGPONG = 0, 1, 2
 
 
 class pgemm_args(ctypes.Structure):
@@ -36,6 +38,7 @@ class pgemm_args(ctypes.Structure):
         ("a_scale", ctypes.c_void_p), ("b_scale", ctypes.c_void_p),
         ("debug_flags", ctypes.c_uint),
         ("straggler_program", ctypes.c_int), ("straggler_ns", ctypes.c_int),
+        ("pipeline", ctypes.c_int),
     ]
 
 

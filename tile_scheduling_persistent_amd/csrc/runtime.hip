@@ -49,6 +49,8 @@ namespace {
 constexpr int kDefaultMaxXcds = 16;
 constexpr int kDefaultGroup = 8;
 constexpr int kMaxGemmChunk = 64;  // tiles per work-stealing claim, GEMM
+// PGEMM_PIPELINE_DEFAULT takes the ping-pong kernel where it applies.
+constexpr bool kPingPongDefault = false;
 
 pgemm_status from_hip(hipError_t e) {
   if (e == hipSuccess) return PGEMM_OK;
@@ -179,8 +181,8 @@ struct GemmChoice {
   bool vec;  // register-staged kernel: 16-byte vector path
 };
 
-pgemm_status choose_gemm(int64_t M, int64_t N, int64_t K, pgemm_dtype dtype, const pgemm_args* args,
-                         const void* A, const void* B, const void* C, GemmChoice& ch) {
+pgemm_status choose_gemm(int64_t M, int64_t N, int64_t K, pgemm_dtype dtype, pgemm_sched sched,
+                         const pgemm_args* args, const void* A, const void* B, const void* C, GemmChoice& ch) {
   if (M < 1 || N < 1 || K < 1 || M > 0x7fffffffLL || N > 0x7fffffffLL || K > 0x7fffffffLL)
     return PGEMM_ERR_INVALID;
   const bool fp8 = dtype == PGEMM_FP8E4M3_B128_OUT_BF16;
@@ -208,8 +210,17 @@ pgemm_status choose_gemm(int64_t M, int64_t N, int64_t K, pgemm_dtype dtype, con
   }
   if (!pgk::gemm_bf16_tile_supported(ch.bm, ch.bn, ch.bk)) return PGEMM_ERR_UNSUPPORTED;
   const bool staged = args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED);
+  const int pipe = args ? args->pipeline : PGEMM_PIPELINE_DEFAULT;
+  if (pipe < PGEMM_PIPELINE_DEFAULT || pipe > PGEMM_PIPELINE_PINGPONG) return PGEMM_ERR_INVALID;
   if (!staged && al && pgk::gemm_bf16_lds_eligible(ch.bm, ch.bn, ch.bk, N, K)) {
     ch.kernel = PGEMM_KERNEL_BF16_LDS;
+    // the ping-pong kernel: 256x256x64 tiles, one problem, not stream-K
+    const bool pp = sched != PGEMM_SCHED_STREAM_K && pgk::gemm_bf16_pp_eligible(ch.bm, ch.bn, ch.bk, N, K);
+    if (pipe == PGEMM_PIPELINE_PINGPONG && !pp) return PGEMM_ERR_UNSUPPORTED;
+    if (pipe == PGEMM_PIPELINE_PINGPONG || (pipe == PGEMM_PIPELINE_DEFAULT && pp && kPingPongDefault))
+      ch.kernel = PGEMM_KERNEL_BF16_PINGPONG;
+  } else if (pipe == PGEMM_PIPELINE_PINGPONG) {
+    return PGEMM_ERR_UNSUPPORTED;
   } else {
     ch.kernel = PGEMM_KERNEL_BF16_STAGED;
     ch.vec = (K % 8 == 0) && (N % 8 == 0) && al && pgk::gemm_bf16_vec_fits(ch.bm, ch.bk, N, K);
@@ -221,6 +232,7 @@ pgk::KernelInfo gemm_info(const GemmChoice& ch) {
   switch (ch.kernel) {
     case PGEMM_KERNEL_FP8: return pgk::info_gemm_fp8(ch.bm, ch.bn);
     case PGEMM_KERNEL_BF16_LDS: return pgk::info_gemm_bf16_lds(ch.bm, ch.bn, ch.out_bf16);
+    case PGEMM_KERNEL_BF16_PINGPONG: return pgk::info_gemm_bf16_pp(ch.out_bf16);
     default: return pgk::info_gemm_bf16(ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec);
   }
 }
@@ -545,6 +557,9 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   if (!fp8 && dtype != PGEMM_BF16_OUT_F32 && dtype != PGEMM_BF16_OUT_BF16) return PGEMM_ERR_INVALID;
   if ((int)sched == PGEMM_SCHED_STREAM_K) return PGEMM_ERR_UNSUPPORTED;
   if (args && (args->debug_flags & PGEMM_DEBUG_REGISTER_STAGED)) return PGEMM_ERR_UNSUPPORTED;
+  if (args && args->pipeline == PGEMM_PIPELINE_PINGPONG) return PGEMM_ERR_UNSUPPORTED;  // four-wave kernel only
+  if (args && (args->pipeline < PGEMM_PIPELINE_DEFAULT || args->pipeline > PGEMM_PIPELINE_PINGPONG))
+    return PGEMM_ERR_INVALID;
   int bm = 256, bn = 256, bk = fp8 ? 128 : 64;
   if (args && (args->tile_m || args->tile_n || args->tile_k)) {
     bm = args->tile_m;
@@ -724,7 +739,7 @@ pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C,
                        void* hip_stream, CallBuffers buf) {
   if (!A || !B || !C) return PGEMM_ERR_INVALID;
   GemmChoice ch;
-  pgemm_status st = choose_gemm(M, N, K, dtype, args, A, B, C, ch);
+  pgemm_status st = choose_gemm(M, N, K, dtype, sched, args, A, B, C, ch);
   if (st != PGEMM_OK) return st;
   const bool fp8 = ch.kernel == PGEMM_KERNEL_FP8;
   if (fp8 && (!args || !args->a_scale || !args->b_scale)) return PGEMM_ERR_INVALID;
@@ -802,6 +817,8 @@ pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C,
     e = pgk::launch_gemm_bf16_lds_sk(p, ch.bm, ch.bn, ch.out_bf16, stream);
   else if (ch.kernel == PGEMM_KERNEL_BF16_LDS)
     e = pgk::launch_gemm_bf16_lds(p, ch.bm, ch.bn, ch.out_bf16, witness, stream);
+  else if (ch.kernel == PGEMM_KERNEL_BF16_PINGPONG)
+    e = pgk::launch_gemm_bf16_pp(p, ch.out_bf16, witness, stream);
   else
     e = pgk::launch_gemm_bf16(p, ch.bm, ch.bn, ch.bk, ch.out_bf16, ch.vec, witness, stream);
   if (e == hipSuccess && sk) {
@@ -884,7 +901,7 @@ pgemm_status pgemm_plan_gemm(pgemm_config* cfg, const void* A, const void* B, co
                              const pgemm_args* args, pgemm_plan* out) {
   if (!cfg || !out) return PGEMM_ERR_INVALID;
   GemmChoice ch;
-  pgemm_status st = choose_gemm(M, N, K, dtype, args, A, B, C, ch);
+  pgemm_status st = choose_gemm(M, N, K, dtype, sched, args, A, B, C, ch);
   if (st != PGEMM_OK) return st;
   const int64_t npm = (M + ch.bm - 1) / ch.bm, npn = (N + ch.bn - 1) / ch.bn;
   if (npm > 0x7fffffffLL || npn > 0x7fffffffLL) return PGEMM_ERR_INVALID;
