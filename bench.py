@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_CLOCK_GHZ = 2.4          # engine clock the dense peak is quoted at
 M = N = K = 8192
@@ -35,6 +36,8 @@ SCHEDS = [("blocked", 8, 0), ("interleaved", 8, 0), ("grouped", 8, 0), ("grouped
           ("work_stealing_xcc", 8, 0), ("work_stealing", 8, -1), ("work_stealing_xcc", 8, -1)]
 HEADLINE = ("work_stealing", 8)   # key work_stealing_g8: one tile per claim, as on the pages
 CPU_ROWS = 4096
+SETTLE_S = 2.0        # untimed repeats of the headline call before the timed steps (engine clock settles)
+RAGGED_ROUNDS = 3     # interleaved rounds over the schedulers on the ragged shapes
 
 # HBM traffic of one 8192^3 launch of the bf16 GEMM kernel, from two
 # rocprofv3 counter passes over `bench.py --only work_stealing_g8` (FETCH_SIZE,
@@ -65,8 +68,13 @@ def parse():
     return p.parse_args()
 
 
-# Single workloads for counter passes: name -> (kind, tile, scheduler).
+# Single workloads for counter passes: name -> (kind, tile, scheduler[, pipeline]).
 PROFILE_TARGETS = {
+    # the headline workload (A, B normal(0,1) from seeds 1030 / 1031)
+    "bf16_8192cube_work_stealing": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing"),
+    "bf16_8192cube_work_stealing_pingpong": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing", "pingpong"),
+    "bf16_8192cube_work_stealing_four_wave": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing", "four_wave"),
+    "bf16_512cube_fp32_blocked": ("bf16f:512:512:512", (128, 128, 64), "blocked"),
     "add_8192sq_128x128_blocked": ("add", (128, 128), "blocked"),
     "add_8192sq_128x128_work_stealing": ("add", (128, 128), "work_stealing"),
     "add_8192sq_32x16_work_stealing": ("add", (32, 16), "work_stealing"),
@@ -93,20 +101,29 @@ def profile_only(name, steps, warmup):
     import torch
     import tile_scheduling_persistent_amd as pg
     from synthetic import f32_normal, fp8_blockscaled
-    kind, tile, sched = PROFILE_TARGETS[name]
+    kind, tile, sched = PROFILE_TARGETS[name][:3]
+    pipeline = PROFILE_TARGETS[name][3] if len(PROFILE_TARGETS[name]) > 3 else "default"
     cfg = pg.Config(0)
     stream = torch.cuda.current_stream()
-    if kind.startswith("bf16:"):
-        from synthetic import bf16_bits_uniform
+    if kind.split(":")[0] in ("bf16", "bf16n", "bf16f"):
+        from synthetic import bf16_bits_normal, bf16_bits_uniform
         dims = [int(x) for x in kind.split(":")[1:]]
         m, n, k = dims[:3]
         grid = dims[3] if len(dims) > 3 else 0
-        ra = torch.from_numpy(bf16_bits_uniform((m, k), 1040 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
-        rb = torch.from_numpy(bf16_bits_uniform((k, n), 1041 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
-        rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
-        a = pg.make_args(tile=tile, grid=grid)
-        nbytes, work = 2 * (m * k + k * n + m * n), 2.0 * m * n * k
-        fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
+        if kind.startswith("bf16n:"):
+            ab = bf16_bits_normal((m, k), 1030), bf16_bits_normal((k, n), 1031)
+        elif kind.startswith("bf16f:"):
+            ab = bf16_bits_uniform((m, k), 1010), bf16_bits_uniform((k, n), 1011)
+        else:
+            ab = bf16_bits_uniform((m, k), 1040 + m), bf16_bits_uniform((k, n), 1041 + n)
+        ra = torch.from_numpy(ab[0].view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        rb = torch.from_numpy(ab[1].view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        out = "bf16_out_f32" if kind.startswith("bf16f:") else "bf16_out_bf16"
+        rc = torch.empty((m, n), dtype=torch.float32 if out == "bf16_out_f32" else torch.bfloat16, device="cuda:0")
+        a = pg.make_args(tile=tile, grid=grid, pipeline=pipeline)
+        nbytes, work = 2 * (m * k + k * n) + rc.element_size() * m * n, 2.0 * m * n * k
+        fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, out, sched, a)  # noqa: E731
+        settle(fn, SETTLE_S)
     elif kind == "add":
         R = Cc = 8192
         X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
@@ -124,10 +141,11 @@ def profile_only(name, steps, warmup):
         a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
         nbytes, work = m * k + k * n + (m + n) * (k // 128) + 2 * m * n, 2.0 * m * n * k
         fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
-    _, ev_mean, _ = time_calls(fn, steps, warmup, stream)
-    out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5),
-           "grid": (pg.plan_gemm(cfg, m, n, k, "bf16_out_bf16", sched, a)["grid"]
-                    if kind.startswith("bf16:") else None),
+    d = event_means(fn, steps, warmup, stream)
+    ev_mean = float(np.mean(d))
+    out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5), "event_ms_median": round(float(np.median(d)), 5),
+           "plan": (pg.plan_gemm(cfg, m, n, k, "bf16_out_f32" if kind.startswith("bf16f:") else "bf16_out_bf16",
+                                 sched, a) if kind.split(":")[0] in ("bf16", "bf16n", "bf16f") else None),
            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1)}
     if work:
         out["tflops"] = round(work / (ev_mean * 1e-3) / 1e12, 2)
@@ -147,6 +165,40 @@ def copy_calibration(steps, warmup):
     print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
                                            "event_ms_mean": round(ev_mean, 5),
                                            "gbs": round(8 * n / (ev_mean * 1e-3) / 1e9, 1)}}), flush=True)
+
+
+def settle(fn, seconds):
+    """Repeat `fn` (untimed) for `seconds`: the engine clock under a sustained
+    load is lower than at the first launches, and the timed steps should see
+    the sustained clock."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
+def event_means(fn, steps, warmup, stream):
+    """Per-call HIP-event durations (ms) of `steps` calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def rounds_summary(work, means_ms, unit_scale=1e12):
+    """Median / min / max rate over rounds (work per call / mean call time)."""
+    rates = sorted(work / (m * 1e-3) / unit_scale for m in means_ms)
+    return {"median": round(float(np.median(rates)), 2), "min": round(rates[0], 2),
+            "max": round(rates[-1], 2), "rounds": len(rates)}
 
 
 def time_calls(fn, steps, warmup, stream):
@@ -235,6 +287,42 @@ def measured_traffic():
     return TRAFFIC_MEASURED["fetch_bytes"] + TRAFFIC_MEASURED["write_bytes"]
 
 
+def rooflines(flops, head, fp8, add, cfg1, traffic):
+    """One roofline record per measured kernel: achieved algorithmic work per
+    launch / mean HIP-event launch time, against the peak of its bound."""
+    out = [{"kernel": "gemm_bf16", "workload": f"bf16 8192^3, bf16 C, 256x256x64, {HEADLINE[0]} g{HEADLINE[1]}",
+            "bound": "mfma", "achieved": round(flops / (head["event_ms_mean"] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": traffic}]
+    for key, sched, bound in [("8192x8192x8192_256x256", "work_stealing", "mfma"),
+                              ("256x28672x8192_128x256", "work_stealing", "hbm"),
+                              ("256x28672x8192_128x256", "grouped", "hbm"),
+                              ("256x28672x8192_128x128", "work_stealing", "hbm")]:
+        r = fp8.get(key, {}).get(sched)
+        if not r:
+            continue
+        shape, tile = key.split("_")
+        if bound == "mfma":
+            out.append({"kernel": "gemm_fp8", "workload": f"fp8 e4m3 {shape}, block scales, {tile}x128, {sched}",
+                        "bound": "mfma", "achieved": r["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "traffic": None})
+        else:
+            out.append({"kernel": "gemm_fp8", "workload": f"fp8 e4m3 {shape}, block scales, {tile}x128, {sched}",
+                        "bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "traffic": None})
+    for key in ("128x128_blocked", "128x128_work_stealing", "32x16_blocked", "32x16_work_stealing"):
+        if key in add:
+            out.append({"kernel": "padd", "workload": f"fp32 add 8192x8192, {key.replace('_', ' tiles, ', 1)}",
+                        "bound": "hbm", "achieved": round(add[key]["gbs"], 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "traffic": None})
+    if cfg1:
+        out.append({"kernel": "gemm_bf16", "workload": cfg1["workload"], "bound": "launch",
+                    "achieved": cfg1["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": None,
+                    "note": "16 tiles on 16 of 256 CUs: the matrix-core peak is not reachable"})
+    for r in out:
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+    return out
+
+
 def cpu_baseline(a_bits, b_bits):
     """The oracle on a bounded sample: CPU_ROWS full rows of C (K = 8192)."""
     from oracle import gemm as og
@@ -278,6 +366,8 @@ def main():
     flops = 2.0 * M * N * K
 
     only = set(s for s in args.only.split(",") if s)
+    settle(lambda: pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", HEADLINE[0],
+                                pg.make_args(tile=(256, 256, 64), group_size=HEADLINE[1])), SETTLE_S)
     per = {}
     for sched, gs, chunk in SCHEDS:
         key = f"{sched}" + (f"_g{gs}" if sched != "blocked" and sched != "interleaved" else "") + \
@@ -292,27 +382,85 @@ def main():
                     "frac_peak": flops / (ev_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         print(f"# {key}: {ms:.4f} ms/step, {per[key]['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    # ragged, wave-quantised shapes (workload 4): every scheduler
+    # the two bf16 pipelines on the same workload (the default one is timed above)
+    per_pipeline = {}
+    if not args.skip_extra and not only:
+        for pipe in ("four_wave", "pingpong"):
+            row = {}
+            for sched, gs, chunk in [("work_stealing", 8, 0), ("grouped", 8, 0), ("interleaved", 8, 0),
+                                     ("blocked_grouped", 8, 0), ("work_stealing", 8, -1)]:
+                a = pg.make_args(tile=(256, 256, 64), group_size=gs, claim_chunk=chunk, pipeline=pipe)
+                fn = lambda: pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, a)  # noqa: E731
+                d = event_means(fn, args.steps, args.warmup, stream)
+                row[sched + ("_pairs" if chunk < 0 else "")] = round(flops / (np.mean(d) * 1e-3) / 1e12, 2)
+            per_pipeline[pipe] = row
+            print(f"# 8192^3 {pipe}: {row}", file=sys.stderr, flush=True)
+
+    # workload 1: 512^3 bf16, fp32 C, 128x128x64 tiles, blocked (16 tiles:
+    # bound by launch and latency, not by the matrix cores)
+    cfg1 = {}
+    if not args.skip_extra:
+        from synthetic import bf16_bits_uniform
+        a1 = torch.from_numpy(bf16_bits_uniform((512, 512), 1010).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        b1 = torch.from_numpy(bf16_bits_uniform((512, 512), 1011).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        c1 = torch.empty((512, 512), dtype=torch.float32, device="cuda:0")
+        args1 = pg.make_args(tile=(128, 128, 64))
+        fn = lambda: pg.pgemm_run(cfg, a1, b1, c1, 512, 512, 512, "bf16_out_f32", "blocked", args1)  # noqa: E731
+        d = event_means(fn, max(args.steps, 50), args.warmup, stream)
+        f1 = 2.0 * 512 ** 3
+        cfg1 = {"workload": "bf16 512^3, fp32 C, 128x128x64 tiles, blocked (16 tiles)",
+                "event_ms_mean": round(float(np.mean(d)), 5), "event_ms_median": round(float(np.median(d)), 5),
+                "tflops": round(f1 / (np.mean(d) * 1e-3) / 1e12, 2),
+                "programs": pg.plan_gemm(cfg, 512, 512, 512, "bf16_out_f32", "blocked", args1)["grid"]}
+        print(f"# cfg 1 (512^3): {cfg1}", file=sys.stderr, flush=True)
+
+    # ragged, wave-quantised shapes (workload 4): every scheduler, in
+    # RAGGED_ROUNDS interleaved rounds (each round times every scheduler once,
+    # so clock drift spreads over all of them), at the default balanced grid
+    # and at one program per CU (the pages' grid)
     ragged = {}
     if not args.skip_extra:
         from synthetic import bf16_bits_uniform
+        ragged_scheds = [("blocked", 0), ("interleaved", 0), ("grouped", 0), ("blocked_grouped", 0),
+                         ("work_stealing", 0), ("work_stealing_xcc", 0), ("work_stealing", -1),
+                         ("work_stealing_xcc", -1), ("stream_k", 0)]
+        static_keys = ["blocked", "interleaved", "grouped", "blocked_grouped"]
+        ws_keys = ["work_stealing", "work_stealing_xcc", "work_stealing_pairs", "work_stealing_xcc_pairs"]
         for (m, n, k) in [(5120, 5120, 4096), (4864, 8000, 8192), (3000, 7000, 2048)]:
             ra = torch.from_numpy(bf16_bits_uniform((m, k), 1040 + m).view(np.int16)).to("cuda:0").view(torch.bfloat16)
             rb = torch.from_numpy(bf16_bits_uniform((k, n), 1041 + n).view(np.int16)).to("cuda:0").view(torch.bfloat16)
             rc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
-            row = {}
-            for sched, chunk in [("blocked", 0), ("interleaved", 0), ("grouped", 0), ("work_stealing", 0),
-                                 ("blocked_grouped", 0), ("stream_k", 0), ("work_stealing_xcc", 0),
-                                 ("work_stealing", -1), ("work_stealing_xcc", -1)]:
-                a = pg.make_args(tile=(256, 256, 64), claim_chunk=chunk)
-                fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a)  # noqa: E731
-                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
-                row[sched + ("_pairs" if chunk < 0 else "")] = {
-                    "tflops": round(f / (ev_mean * 1e-3) / 1e12, 2), "event_ms_mean": round(ev_mean, 5)}
-            ragged[f"{m}x{n}x{k}"] = row
-            print(f"# ragged {m}x{n}x{k}: " + ", ".join(f"{s_}={v['tflops']}" for s_, v in row.items()),
-                  file=sys.stderr, flush=True)
+            shape_rec = {}
+            for grid_name, grid in [("balanced_grid", 0), ("grid_per_cu", cfg.info["num_cus"])]:
+                calls = {}
+                for sched, chunk in ragged_scheds:
+                    if sched == "stream_k" and grid:
+                        continue
+                    a = pg.make_args(tile=(256, 256, 64), claim_chunk=chunk, grid=grid)
+                    calls[sched + ("_pairs" if chunk < 0 else "")] = (
+                        lambda a=a, sched=sched: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, "bf16_out_bf16", sched, a))
+                settle(next(iter(calls.values())), 0.5)
+                means = {key: [] for key in calls}
+                for _ in range(RAGGED_ROUNDS):
+                    for key, fn in calls.items():
+                        means[key].append(float(np.mean(event_means(fn, args.steps, 3, stream))))
+                rec = {key: rounds_summary(f, v) for key, v in means.items()}
+                best_static = max(static_keys, key=lambda x: rec[x]["median"])
+                best_ws = max(ws_keys, key=lambda x: rec[x]["median"])
+                rec["_summary"] = {
+                    "programs": pg.plan_gemm(cfg, m, n, k, "bf16_out_bf16", "work_stealing",
+                                             pg.make_args(tile=(256, 256, 64), grid=grid))["grid"],
+                    "best_static": best_static, "best_work_stealing": best_ws,
+                    "work_stealing_over_best_static": round(rec["work_stealing"]["median"]
+                                                            / rec[best_static]["median"], 4),
+                    "best_work_stealing_over_best_static": round(rec[best_ws]["median"]
+                                                                 / rec[best_static]["median"], 4)}
+                shape_rec[grid_name] = rec
+                print(f"# ragged {m}x{n}x{k} {grid_name}: " +
+                      ", ".join(f"{s_}={v['median']}" for s_, v in rec.items() if not s_.startswith("_")) +
+                      f"; {rec['_summary']}", file=sys.stderr, flush=True)
+            ragged[f"{m}x{n}x{k}"] = shape_rec
             del ra, rb, rc
 
     # under-filled shapes (fewer 256x256 tiles than CUs, e.g. one GPU's share
@@ -556,8 +704,12 @@ def main():
                                                 if clock_ghz else None),
                      "traffic_unit": "HBM bytes per launch (counter passes, copy-calibrated)",
                      "algorithmic_bytes": 2 * (M * K + K * N + M * N)},
+        "rooflines": rooflines(flops, h, fp8, add, cfg1, measured_traffic()),
         "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),
                               "event_ms_mean": round(v["event_ms_mean"], 5)} for k, v in per.items()},
+        "per_pipeline": per_pipeline,
+        "default_pipeline": head_plan["kernel"],
+        "cfg1_512cube": cfg1,
         "add": {k: {"gbs": round(v["gbs"], 1), "frac_hbm": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                 for k, v in add.items()},
         "ragged": ragged,

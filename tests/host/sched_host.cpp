@@ -35,6 +35,7 @@ struct HostOps {
   std::atomic<int>* c;
   int fetch_add(int x, int v) { return c[x].fetch_add(v, std::memory_order_relaxed); }
   int load(int x) { return c[x].load(std::memory_order_relaxed); }
+  void store(int x, int v) { c[x].store(v, std::memory_order_relaxed); }
 };
 
 // G threads walk the tiles as a kernel's programs do (Walker::first / next):
@@ -43,7 +44,7 @@ struct HostOps {
 // stealing across XCDs.  Prints the homes, the final counters and, per tile,
 // visits, owner and the tile's position in its owner's sequence.
 static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
-                         const std::vector<int>& homes) {
+                         const std::vector<int>& homes, bool self_reset = false) {
   const int T = pm * pn;
   std::vector<std::atomic<int>> cnt(X);
   for (auto& c : cnt) c.store(0);
@@ -56,15 +57,16 @@ static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
       HostOps ops{cnt.data()};
       pgs::WsWalk w;
       pgs::ws_start(w, homes[p], T, X);
+      const int reset_at = self_reset ? pgs::ws_last_claim_value(w.n, chunk, G, X, w.x) : -1;
       int done = 0;
-      int v = pgs::ws_claim(w, across, T, G, X, chunk, ops);
+      int v = pgs::ws_claim(w, across, T, G, X, chunk, ops, reset_at);
       while (v >= 0) {
         if (v >= T) std::abort();  // a claim past the tiles
         visits[v].fetch_add(1);
         owner[v] = p;
         order[v] = done++;
         std::this_thread::yield();
-        v = v + 1 < w.cend ? v + 1 : pgs::ws_claim(w, across, T, G, X, chunk, ops);
+        v = v + 1 < w.cend ? v + 1 : pgs::ws_claim(w, across, T, G, X, chunk, ops, reset_at);
       }
     });
   }
@@ -83,6 +85,22 @@ static int ws_threads(int pm, int pn, int G, int X, int chunk) {
   std::vector<int> homes(G);
   for (int p = 0; p < G; ++p) homes[p] = p % X;
   return claim_threads(pm, pn, G, X, chunk, false, homes);
+}
+
+// Per-XCD work stealing whose last failing claim on each counter zeroes it:
+// prints each counter's reset value, then as ws_threads (the final counters
+// should all be zero).
+static int wsr_threads(int pm, int pn, int G, int X, int chunk) {
+  const int T = pm * pn;
+  std::printf("reset_at:");
+  for (int x = 0; x < X; ++x) {
+    const int n = pgs::ws_range_begin(x + 1, T, X) - pgs::ws_range_begin(x, T, X);
+    std::printf(" %d", pgs::ws_last_claim_value(n, chunk, G, X, x));
+  }
+  std::printf("\n");
+  std::vector<int> homes(G);
+  for (int p = 0; p < G; ++p) homes[p] = p % X;
+  return claim_threads(pm, pn, G, X, chunk, false, homes, true);
 }
 
 // Work stealing across XCDs from home counters p mod X (0), all 0 (1), or
@@ -154,6 +172,9 @@ int main(int argc, char** argv) {
   if (mode == "ws" && argc == 8)  // argv[6], the group size, does not enter the claims
     return ws_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                       std::atoi(argv[7]));
+  if (mode == "wsr" && argc == 7)
+    return wsr_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
+                       std::atoi(argv[6]));
   if (mode == "wsx" && argc == 8)
     return wsx_threads(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]),
                        std::atoi(argv[6]), std::atoi(argv[7]));

@@ -250,3 +250,85 @@ def test_buffer_ranges_must_lie_in_one_allocation():
         sync("validate-only calls")
     finally:
         assert hip.hipFree(p) == 0
+
+
+def test_counters_zeroed_by_their_last_claim():
+    """Per-XCD work stealing zeroes each counter with the last failing claim
+    of the launch, so back-to-back launches need no fill kernel: every launch
+    of a sequence (bf16 on both pipelines, block-scaled fp8, the add, single
+    and paired claims, interleaved with stealing across XCDs, witness and
+    skipped-reset launches, which leave the counters dirty and make the next
+    call refill them) computes the same bits, and after every launch that
+    resets itself the counters read zero."""
+    cfg = config()
+    X = cfg.info["num_xcds"]
+    M, N, K = 1536, 1280, 256
+    a, b = bf16_bits_uniform((M, K), 21), bf16_bits_uniform((K, N), 22)
+    A, B = dev_bf16(a), dev_bf16(b)
+    cfg.witness_enable(64, 1024)
+
+    def counters():
+        return cfg.witness_read(0, 0)["counters"][:X]
+
+    def gemm(sched, **kw):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        note(f"self-reset sequence: {sched} {kw}")
+        pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, pg.make_args(tile=(256, 256, 64), **kw))
+        sync()
+        return C.view(torch.int16).cpu().numpy()
+
+    ref = gemm("grouped")
+    seq = [("work_stealing", {}, True), ("work_stealing", {}, True),
+           ("work_stealing", {"claim_chunk": _abi.CLAIM_PAIRS}, True),
+           ("work_stealing", {"claim_chunk": 3}, True),
+           ("work_stealing", {"pipeline": "pingpong"}, True),
+           ("work_stealing_xcc", {}, False), ("work_stealing", {}, True),
+           ("work_stealing", {"debug_flags": _abi.DEBUG_WITNESS}, False), ("work_stealing", {}, True),
+           ("work_stealing", {"tile": (128, 128, 64)}, True), ("work_stealing", {}, True)]
+    for sched, kw, resets in seq:
+        kw = dict(kw)
+        tile = kw.pop("tile", None)
+        if tile:
+            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+            pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched, pg.make_args(tile=tile, **kw))
+            sync()
+            got = C.view(torch.int16).cpu().numpy()
+        else:
+            got = gemm(sched, **kw)
+        assert np.array_equal(got, ref), (sched, kw)
+        c = counters()
+        if resets:
+            assert np.all(c == 0), (sched, kw, c)
+        else:
+            assert np.any(c != 0), (sched, kw, c)
+    # a skipped reset after a self-resetting launch finds zeroed counters and
+    # computes everything; the launch after it refills (the flag marks them dirty)
+    gemm("work_stealing")
+    assert np.array_equal(gemm("work_stealing", debug_flags=_abi.DEBUG_SKIP_RESET), ref)
+    assert np.array_equal(gemm("work_stealing"), ref)
+    assert np.all(counters() == 0)
+    # the add and block-scaled fp8 on the same counters
+    xs = torch.randn(3000, 2000, device="cuda:0")
+    ys = torch.randn(3000, 2000, device="cuda:0")
+    want = (xs + ys).cpu().numpy().view(np.uint32)
+    for _ in range(3):
+        z = torch.empty_like(xs)
+        pg.padd_run(cfg, xs, ys, z, 3000, 2000, 128, 128, "work_stealing")
+        sync()
+        assert np.array_equal(z.cpu().numpy().view(np.uint32), want)
+        assert np.all(counters() == 0)
+    from synthetic import fp8_blockscaled
+    qa, sa = fp8_blockscaled(512, 1024, 31, 32, k_major=True)
+    qb, sb = fp8_blockscaled(768, 1024, 33, 34, k_major=False)
+    fa, fb = torch.from_numpy(qa).cuda(), torch.from_numpy(qb).cuda()
+    fsa, fsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    outs = []
+    for sched in ("grouped", "work_stealing", "work_stealing"):
+        C = torch.empty((512, 768), dtype=torch.bfloat16, device="cuda:0")
+        pg.pgemm_run(cfg, fa, fb, C, 512, 768, 1024, "fp8_b128_out_bf16", sched,
+                     pg.make_args(tile=(128, 128, 128), a_scale=fsa, b_scale=fsb))
+        sync()
+        outs.append(C.view(torch.int16).cpu().numpy())
+        if sched == "work_stealing":
+            assert np.all(counters() == 0)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

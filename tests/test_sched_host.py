@@ -196,3 +196,36 @@ def test_oracle_gemm_under_sanitizers(tmp_path):
                     os.path.join(ROOT, "tests", "host", "oracle_sanitize.c"), "-o", exe, "-lm"], check=True)
     out = _run_sanitized(exe)
     assert out == ["mismatches: 0"]
+
+
+def _check_wsr(out, pm, pn, G, X, chunk):
+    """Self-resetting per-XCD work stealing: the reset value of each counter is
+    the oracle's final counter value minus one step, every counter ends at
+    zero, and the execution satisfies the model's invariants."""
+    T = pm * pn
+    c = sm.PAIRS if chunk < 0 else chunk
+    step = 1 if chunk < 0 else chunk
+    reset_at = list(map(int, out[0].split(":")[1].split()))
+    final = sm.ws_final_counters(T, G, X, c)
+    assert reset_at == [f - step for f in final], (reset_at, final)
+    counters = list(map(int, out[2].split(":")[1].split()))
+    assert counters == [0] * X
+    rows = [tuple(map(int, l.split())) for l in out[3:]]
+    sm.check_ws_execution([r[1] for r in rows], [r[2] for r in rows], [r[3] for r in rows],
+                          final, T, G, X, c)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (19, 32, 256, 8, 1),
+                                             (33, 7, 64, 8, 4), (1, 1, 16, 8, 1), (19, 32, 256, 8, -1),
+                                             (20, 20, 256, 8, -1), (5, 2, 4, 2, -1), (20, 20, 200, 8, 1),
+                                             (7, 9, 13, 8, 1), (16, 25, 200, 8, 3)])
+def test_ws_self_reset_leaves_counters_zero(harness, pm, pn, G, X, chunk):
+    out = subprocess.run([harness, "wsr", str(pm), str(pn), str(G), str(X), str(chunk)],
+                         check=True, capture_output=True, text=True).stdout.strip().splitlines()
+    _check_wsr(out, pm, pn, G, X, chunk)
+
+
+def test_ws_self_reset_under_sanitizers(sanitized):
+    _, exe = sanitized
+    for pm, pn, G, X, chunk in [(32, 32, 256, 8, 1), (19, 32, 256, 8, -1), (7, 9, 13, 8, 1)]:
+        _check_wsr(_run_sanitized(exe, "wsr", pm, pn, G, X, chunk), pm, pn, G, X, chunk)

@@ -37,6 +37,7 @@ struct SchedParams {
   int num_pid_m;      // tiles along dimension 0 (rows)
   int num_pid_n;      // tiles along dimension 1 (columns)
   int* counters;      // work-stealing counters (stride kCounterStride), zero at launch
+  int self_reset;     // per-XCD work stealing: the last failing claim on a counter zeroes it
   int chunk;          // tiles per work-stealing claim
   int straggler_program;  // -1: off
   int straggler_ns;
@@ -213,6 +214,9 @@ struct ThreadOps {
   __device__ __forceinline__ int load(int c) {
     return __hip_atomic_load(counters + c * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __device__ __forceinline__ void store(int c, int v) {
+    __hip_atomic_store(counters + c * kCounterStride, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 };
 
 struct WaveOps {
@@ -229,6 +233,10 @@ struct WaveOps {
       r = __hip_atomic_load(counters + c * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return __builtin_amdgcn_readfirstlane(r);
   }
+  __device__ __forceinline__ void store(int c, int v) {
+    if ((threadIdx.x & 63) == 0)
+      __hip_atomic_store(counters + c * kCounterStride, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 };
 
 // Per-program view of the scheduler.  Static kinds walk arithmetically.
@@ -243,6 +251,7 @@ struct Walker {
   int p;
   int end;         // static: end of the walk
   pgs::WsWalk ws;  // work stealing: the walk over the counters
+  int reset_at;    // per-XCD work stealing with self_reset: see pgs::ws_claim
 
   __device__ __forceinline__ int nx() const { return s.X > 0 ? s.X : 1; }
 
@@ -250,11 +259,14 @@ struct Walker {
     end = 0;
     const int X = nx();
     pgs::ws_start(ws, sp.kind == pgs::kWorkStealingXcc ? xcc_id() % X : prog % X, sp.T, X);
+    reset_at = (sp.self_reset && sp.kind == pgs::kWorkStealing)
+                   ? pgs::ws_last_claim_value(ws.n, sp.chunk, sp.G, X, ws.x)
+                   : -1;
   }
 
   template <class Ops>
   __device__ __forceinline__ int claim_with(Ops ops) {
-    return pgs::ws_claim(ws, s.kind == pgs::kWorkStealingXcc, s.T, s.G, nx(), s.chunk, ops);
+    return pgs::ws_claim(ws, s.kind == pgs::kWorkStealingXcc, s.T, s.G, nx(), s.chunk, ops, reset_at);
   }
 
   // One claim (s.chunk tiles, or a pair / single under paired claims);

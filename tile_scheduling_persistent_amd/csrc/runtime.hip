@@ -28,6 +28,7 @@ struct pgemm_config {
   int lds_per_cu;
   char arch[64];
   int* counters;  // device, [capacity * pgk::kCounterStride]; counter x at x * kCounterStride
+  bool counters_dirty;  // the counters may hold a launch's values (see reset_counters)
   float* ws;          // stream-K partial-sum workspace (device), grown on demand
   size_t ws_bytes;
   unsigned char* scratch;  // this device's address of the static `scratch` array
@@ -140,6 +141,7 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.num_pid_m = num_pid_m;
   s.num_pid_n = num_pid_n;
   s.counters = cfg->counters;
+  s.self_reset = 0;
   s.chunk = 1;
   if (args && args->claim_chunk) {
     if (args->claim_chunk == PGEMM_CLAIM_PAIRS)
@@ -273,16 +275,28 @@ pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::
   return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH;
 }
 
-pgemm_status reset_counters(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
-                            hipStream_t stream) {
+// Work-stealing counters before a launch.  Per-XCD work stealing leaves its
+// counters zeroed at the end of the launch (the last failing claim on each
+// zeroes it, pgs::ws_claim), so the stream-ordered fill kernel the pages'
+// reset-before-every-launch calls for runs only when the counters may hold
+// values of an earlier launch: after a witness launch (its final counters are
+// read back), after stealing across XCDs (whose failing claims per counter
+// vary), after a launch that skipped the reset, and on first use.  `dirty`
+// tracks that for one counter array of n_counters entries.
+pgemm_status reset_counters(const pgemm_args* args, pgk::SchedParams& s, int n_counters, bool* dirty,
+                            bool witness, hipStream_t stream) {
+  s.self_reset = 0;
   if (!pgs::work_stealing(s.kind)) return PGEMM_OK;
-  if (args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET)) return PGEMM_OK;
-  // a fill kernel rather than a memset node, so that the call may be captured;
-  // s.counters is the config's array or the static scratch's
-  const int n = s.counters == cfg->counters ? cfg->capacity : s.X;
-  return pgk::launch_zero_i32(s.counters, n * pgk::kCounterStride, stream) == hipSuccess
-             ? PGEMM_OK
-             : PGEMM_ERR_LAUNCH;
+  const bool skip = args && (args->debug_flags & PGEMM_DEBUG_SKIP_RESET);
+  const bool self = s.kind == pgs::kWorkStealing && !witness && !skip;
+  if (!skip && (*dirty || !self)) {
+    // a fill kernel rather than a memset node, so that the call may be captured
+    if (pgk::launch_zero_i32(s.counters, n_counters * pgk::kCounterStride, stream) != hipSuccess)
+      return PGEMM_ERR_LAUNCH;
+  }
+  s.self_reset = self ? 1 : 0;
+  *dirty = !self;
+  return PGEMM_OK;
 }
 
 
@@ -330,6 +344,14 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 unsigned char* g_scratch[kMaxDevices];  // per device: address of `scratch` there, or null
+bool g_scratch_dirty[kMaxDevices] = {true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true,
+                                     true, true, true, true, true, true, true, true};  // first use fills
 
 // Address of `scratch` on `device` (the caller has made it current).
 pgemm_status scratch_address(int device, unsigned char** out) {
@@ -353,6 +375,7 @@ pgemm_status scratch_address(int device, unsigned char** out) {
 struct CallBuffers {
   int* counters;
   int n_counters;
+  bool* dirty;  // the counters may hold a launch's values
   float* ws;
   size_t ws_bytes;
   bool growable;
@@ -542,7 +565,7 @@ pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* problems, int
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
-  st = reset_counters(cfg, args, p.s, stream);
+  st = reset_counters(args, p.s, cfg->capacity, &cfg->counters_dirty, witness, stream);
   if (st != PGEMM_OK) return st;
   hipError_t e = pgk::launch_padd_multi(p, tile_rows, tile_cols, vec, witness, stream);
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;
@@ -643,7 +666,7 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
-  st = reset_counters(cfg, args, p.s, stream);
+  st = reset_counters(args, p.s, cfg->capacity, &cfg->counters_dirty, witness, stream);
   if (st != PGEMM_OK) return st;
   hipError_t e = fp8 ? pgk::launch_gemm_fp8_grouped(p, bm, bn, witness, stream)
                      : pgk::launch_gemm_bf16_lds_grouped(p, bm, bn, csz == 2, witness, stream);
@@ -716,7 +739,7 @@ pgemm_status pgemm_run(pgemm_config* cfg, const void* A, const void* B, void* C,
                        const pgemm_args* args, void* hip_stream) {
   if (!cfg) return PGEMM_ERR_INVALID;
   return gemm_call(cfg, A, B, C, M, N, K, dtype, sched, args, hip_stream,
-                   CallBuffers{cfg->counters, cfg->capacity, cfg->ws, cfg->ws_bytes, true});
+                   CallBuffers{cfg->counters, cfg->capacity, &cfg->counters_dirty, cfg->ws, cfg->ws_bytes, true});
 }
 
 pgemm_status pgemm_run_noalloc(pgemm_config* cfg, const void* A, const void* B, void* C, int64_t M,
@@ -725,7 +748,7 @@ pgemm_status pgemm_run_noalloc(pgemm_config* cfg, const void* A, const void* B, 
   if (!cfg || !cfg->scratch) return PGEMM_ERR_INVALID;
   if (args && (args->debug_flags & PGEMM_DEBUG_WITNESS)) return PGEMM_ERR_UNSUPPORTED;
   return gemm_call(cfg, A, B, C, M, N, K, dtype, sched, args, hip_stream,
-                   CallBuffers{reinterpret_cast<int*>(cfg->scratch), kScratchCounters,
+                   CallBuffers{reinterpret_cast<int*>(cfg->scratch), kScratchCounters, &g_scratch_dirty[cfg->device],
                                reinterpret_cast<float*>(cfg->scratch + kScratchCounterBytes),
                                kScratchWsBytes, false});
 }
@@ -806,7 +829,7 @@ pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C,
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
-  st = reset_counters(cfg, args, p.s, stream);
+  st = reset_counters(args, p.s, buf.n_counters, buf.dirty, witness, stream);
   if (st != PGEMM_OK) return st;
 
   hipError_t e;
@@ -889,7 +912,7 @@ pgemm_status padd_run(pgemm_config* cfg, const float* X, const float* Y, float* 
   bool witness = false;
   st = make_witness(cfg, args, p.s, p.w, witness, stream);
   if (st != PGEMM_OK) return st;
-  st = reset_counters(cfg, args, p.s, stream);
+  st = reset_counters(args, p.s, cfg->capacity, &cfg->counters_dirty, witness, stream);
   if (st != PGEMM_OK) return st;
   hipError_t e = pgk::launch_padd(p, tile_rows, tile_cols, vec, witness, stream);
   if (e == hipErrorInvalidValue) return PGEMM_ERR_UNSUPPORTED;

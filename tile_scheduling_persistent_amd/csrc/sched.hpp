@@ -151,6 +151,21 @@ PGS_FN int ws_claim_end(int v, int chunk, int T, int X) {
   return e < range_end ? e : range_end;
 }
 
+// Programs whose home counter is x under per-XCD work stealing (p mod X).
+PGS_FN int ws_programs_on(int x, int G, int X) { return G / X + (x < G % X ? 1 : 0); }
+
+// Per-XCD work stealing: the value the last claim on counter x of one launch
+// reads.  The counter's n tiles are handed out by a fixed number of
+// successful claims, and each of the counter's programs then makes exactly
+// one failing claim, so the launch's final counter value is known in advance
+// and the claim that reads that value minus one step is the last operation on
+// the counter in the launch.
+PGS_FN int ws_last_claim_value(int n, int chunk, int G, int X, int x) {
+  const int step = chunk < 0 ? 1 : chunk;
+  const int claims = chunk < 0 ? pair_claims(n, G, X) : cdiv(n, chunk);
+  return step * (claims + ws_programs_on(x, G, X) - 1);
+}
+
 // One program's position in the work-stealing walk.
 struct WsWalk {
   int x;        // counter it claims from
@@ -179,11 +194,15 @@ PGS_FN void ws_start(WsWalk& w, int home, int T, int X) {
 // that is not; it stops when none is left, so it makes at most one failing
 // claim per counter.  Returns the first claimed tile id and sets w.cend, or
 // -1 when the program is done.  `ops` performs the memory operations on
-// counter c: fetch_add(c, v) returns the old value, load(c) reads it (the
-// kernels: device atomics, by one thread or by one lane for a whole wave;
-// the host harness: std::atomic).  Needs X <= kMaxStealCounters when across.
+// counter c: fetch_add(c, v) returns the old value, load(c) reads it, store(c,
+// v) writes it (the kernels: device atomics, by one thread or by one lane for
+// a whole wave; the host harness: std::atomic).  Needs X <= kMaxStealCounters
+// when across.  reset_at >= 0 (per-XCD work stealing only): the failing claim
+// that reads reset_at (ws_last_claim_value) stores zero into the counter, so
+// the counters leave the launch as they entered it and the next launch needs
+// no reset of its own.
 template <class Ops>
-PGS_FN int ws_claim(WsWalk& w, bool across, int T, int G, int X, int chunk, Ops& ops) {
+PGS_FN int ws_claim(WsWalk& w, bool across, int T, int G, int X, int chunk, Ops& ops, int reset_at = -1) {
   for (;;) {
     const int step = chunk < 0 ? 1 : chunk;
     const int i = ops.fetch_add(w.x, step);
@@ -197,7 +216,11 @@ PGS_FN int ws_claim(WsWalk& w, bool across, int T, int G, int X, int chunk, Ops&
       w.cend = ws_claim_end(w.begin + i, chunk, T, X);
       return w.begin + i;
     }
-    if (!across || ++w.passed >= X) return -1;
+    if (!across) {
+      if (i == reset_at) ops.store(w.x, 0);
+      return -1;
+    }
+    if (++w.passed >= X) return -1;
     const int left = X - w.passed;
     int seen[kMaxStealCounters];
 #if defined(__HIPCC__)
