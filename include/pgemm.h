@@ -156,7 +156,33 @@ typedef struct {
   int straggler_ns;           /* with PGEMM_DEBUG_STRAGGLER */
   int pipeline;               /* bf16 256x256x64 tiles on the direct-to-LDS terms: PGEMM_PIPELINE_*;
                                  0 => PGEMM_PIPELINE_DEFAULT */
+  int program_order;          /* GEMM static walks: PGEMM_ORDER_*; 0 => DEFAULT */
 } pgemm_args;
+
+/* pgemm_args.program_order: which workgroup plays which program of a GEMM's
+ * static walk (BLOCKED, INTERLEAVED, GROUPED, BLOCKED_GROUPED).  The hardware
+ * hands workgroup i of a launch to XCD i mod X.
+ *  XCD_MAJOR  when X > 1 divides G, workgroup i plays program
+ *             (i mod X) * (G / X) + i / X: the programs of one XCD have
+ *             consecutive ids, so in the grouped order the tiles they take in
+ *             one round form a compact block whose operand panels meet in
+ *             that XCD's L2, as a work-stealing range does; otherwise as
+ *             DISPATCH.
+ *  DISPATCH   workgroup i plays program i.
+ *  DEFAULT    XCD_MAJOR where it makes the programs' first tiles touch fewer
+ *             operand panels per XCD (rows of tiles weighted by tile_m plus
+ *             columns weighted by tile_n, summed over the XCDs) than
+ *             DISPATCH, else DISPATCH (for the plain decode with many rows of
+ *             tiles, consecutive ids form a column and the round robin is the
+ *             compact assignment); pgemm_plan.xcd_major reports the choice.
+ * The set of tiles each program takes, and so C, is the same under all; the
+ * witness records programs by this number (owner, per-program arrays).  The
+ * work-stealing kinds and stream-K always number programs by workgroup (a
+ * work-stealing program's home counter is the XCD it runs on), and so does
+ * the add. */
+#define PGEMM_ORDER_DEFAULT 0
+#define PGEMM_ORDER_DISPATCH 1
+#define PGEMM_ORDER_XCD_MAJOR 2
 
 /* pgemm_args.pipeline: how the bf16 256x256x64 kernel feeds its matrix cores.
  *  FOUR_WAVE  four waves, one per SIMD, each owning a 128x128 sub-tile; loads,
@@ -358,6 +384,7 @@ typedef struct {
   int threads;       /* per workgroup */
   int lds_bytes;     /* dynamic LDS per workgroup */
   pgemm_kernel kernel;
+  int xcd_major;     /* 1: programs numbered XCD-major (see pgemm_args.program_order) */
 } pgemm_plan;
 
 /* The launch pgemm_run would make with the same arguments (no pointer is

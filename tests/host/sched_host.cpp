@@ -163,6 +163,13 @@ static int grid_map(int Tmax, int G, int X) {
   return 0;
 }
 
+// Program numbering of the static walks: each workgroup id and the program
+// it plays.
+static int order_map(int G, int X, int xcd_major) {
+  for (int hw = 0; hw < G; ++hw) std::printf("%d %d\n", hw, pgs::program_of(hw, G, X, xcd_major));
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc < 2) return 2;
   const std::string mode = argv[1];
@@ -180,6 +187,7 @@ int main(int argc, char** argv) {
                        std::atoi(argv[6]), std::atoi(argv[7]));
   if (mode == "pairs" && argc == 4) return pairs_map(std::atoi(argv[2]), std::atoi(argv[3]));
   if (mode == "grid" && argc == 5) return grid_map(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
+  if (mode == "order" && argc == 5) return order_map(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   if (mode == "sk" && argc == 5)
     return sk_walk(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]));
   return 2;

@@ -39,26 +39,28 @@ def _check(w, kind, pm, pn, G, X, gs, chunk=1):
                                w["counters"].tolist(), homes, T, G, X, chunk)
 
 
-def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0):
+def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0, order="default"):
     cfg = config()
     G = pg.plan_gemm(cfg, M, N, K, "bf16_out_bf16", sched,
-                     pg.make_args(tile=tile, group_size=gs, grid=grid))["grid"]
+                     pg.make_args(tile=tile, group_size=gs, grid=grid, program_order=order))["grid"]
     pm, pn = -(-M // tile[0]), -(-N // tile[1])
     cfg.witness_enable(pm * pn, G)
     a = bf16_bits_uniform((M, K), 1)
     b = bf16_bits_uniform((K, N), 2)
     A, B = dev_bf16(a), dev_bf16(b)
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
-    note(f"witness gemm {M}x{N}x{K} tile={tile} {sched} gs={gs} grid={G}")
+    note(f"witness gemm {M}x{N}x{K} tile={tile} {sched} gs={gs} grid={G} order={order}")
     pg.pgemm_run(cfg, A, B, C, M, N, K, "bf16_out_bf16", sched,
-                 pg.make_args(tile=tile, group_size=gs, grid=grid, debug_flags=pg._abi.DEBUG_WITNESS))
+                 pg.make_args(tile=tile, group_size=gs, grid=grid, debug_flags=pg._abi.DEBUG_WITNESS,
+                              program_order=order))
     w = cfg.witness_read(pm * pn, G)
     # the witness build computes the same bits as the timed build
     C2 = torch.empty_like(C)
     pg.pgemm_run(cfg, A, B, C2, M, N, K, "bf16_out_bf16", sched,
-                 pg.make_args(tile=tile, group_size=gs, grid=grid))
+                 pg.make_args(tile=tile, group_size=gs, grid=grid, program_order=order))
     sync()
     assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    w["C"] = C
     return w, pm, pn, G, cfg.info["num_xcds"]
 
 
@@ -99,6 +101,56 @@ def test_gemm_chunked_claims(sched, chunk, shape, tile):
     pg.pgemm_run(cfg, A, B, Cg, M, N, K, "bf16_out_bf16", "grouped", pg.make_args(tile=tile))
     sync()
     assert torch.equal(C.view(torch.int16), Cg.view(torch.int16))
+
+
+@pytest.mark.parametrize("sched", STATIC)
+def test_gemm_program_order(sched):
+    """Static walks under both program numberings: the schedule of the model
+    for the programs as numbered, the same C, and (hardware placement being
+    round robin) the programs of XCD x are [x*G/X, (x+1)*G/X) under
+    XCD-major numbering and {x, x+X, ...} under dispatch order."""
+    M, N, K, tile = 5120, 5120, 256, (256, 256, 64)
+    res = {}
+    for order in ("xcd_major", "dispatch"):
+        plan = pg.plan_gemm(config(), M, N, K, "bf16_out_bf16", sched,
+                            pg.make_args(tile=tile, program_order=order))
+        w, pm, pn, G, X = _gemm_witness(M, N, K, tile, sched, order=order)
+        assert G % X == 0 and plan["xcd_major"] == (order == "xcd_major")
+        _check(w, sched, pm, pn, G, X, 8)
+        xcc = (w["hw_id"][:G].astype(np.int64) >> 16) & 0xF
+        q = np.arange(G)
+        want = q // (G // X) if order == "xcd_major" else q % X
+        frac = float(np.mean(xcc == want))
+        note(f"{sched} order={order}: fraction of programs on the expected XCD {frac:.3f}")
+        assert frac >= 0.9, (sched, order, frac)
+        res[order] = w["C"]
+    assert torch.equal(res["xcd_major"].view(torch.int16), res["dispatch"].view(torch.int16))
+
+
+@pytest.mark.parametrize("shape,dtype,tile,sched,want", [
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "grouped", True),
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "blocked", True),
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "interleaved", False),
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "blocked_grouped", False),
+    ((256, 28672, 8192), "fp8_b128_out_bf16", (128, 256, 128), "interleaved", True),
+    ((4864, 8000, 8192), "bf16_out_bf16", (256, 256, 64), "grouped", True),
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "work_stealing", False),
+    ((8192, 8192, 8192), "bf16_out_bf16", (256, 256, 64), "stream_k", False),
+    ((1100, 900, 64), "bf16_out_bf16", (128, 128, 64), "grouped", False),  # grid 7: not a multiple of X
+])
+def test_default_program_order(shape, dtype, tile, sched, want):
+    """The default numbering is the one whose programs' first tiles touch fewer
+    operand panels per XCD (rows of tiles x tile_m + columns x tile_n over the
+    XCDs; the counts for these launches worked out from the oracle's static
+    schedules: grouped 8192^3 96 vs 264 panels of 256, interleaved 264 vs 96,
+    blocked-grouped 144 vs 96, fp8 256x28672 interleaved 30720 vs 58368),
+    never XCD-major for work stealing or stream-K; the same decision twice in
+    a row (the cached one)."""
+    M, N, K = shape
+    grid = 7 if shape == (1100, 900, 64) else 0
+    for _ in range(2):
+        plan = pg.plan_gemm(config(), M, N, K, dtype, sched, pg.make_args(tile=tile, grid=grid))
+        assert plan["xcd_major"] == want, plan
 
 
 def test_gemm_witness_clock():

@@ -162,6 +162,26 @@ def test_balanced_grid_matches_model(harness, G, X):
         assert g == sm.balanced_grid(T, G, X), (T, G, X, g)
 
 
+@pytest.mark.parametrize("G,X", [(256, 8), (224, 8), (8, 8), (64, 4), (250, 8), (7, 8), (96, 1), (1, 1)])
+def test_program_order(harness, G, X):
+    """XCD-major program numbering: a bijection of the grid; with X > 1
+    dividing G, the workgroups the hardware places on XCD x (ids = x mod X,
+    round robin) play exactly programs [x*G/X, (x+1)*G/X), in workgroup
+    order; otherwise, and with the option off, workgroup i plays program i."""
+    for xm in (0, 1):
+        out = subprocess.run([harness, "order", str(G), str(X), str(xm)], check=True, capture_output=True,
+                             text=True).stdout.strip().splitlines()
+        prog = [int(line.split()[1]) for line in out]
+        assert [int(line.split()[0]) for line in out] == list(range(G))
+        assert sorted(prog) == list(range(G))
+        if xm and X > 1 and G % X == 0:
+            per = G // X
+            for x in range(X):
+                assert [prog[hw] for hw in range(x, G, X)] == list(range(x * per, (x + 1) * per)), (G, X, x)
+        else:
+            assert prog == list(range(G))
+
+
 @pytest.mark.parametrize("pm,pn,G,X,chunk", [(32, 32, 256, 8, 1), (19, 32, 256, 8, -1), (33, 7, 64, 8, 4),
                                              (13, 11, 3, 8, 2)])
 def test_claim_loops_under_sanitizers(sanitized, pm, pn, G, X, chunk):
@@ -183,6 +203,7 @@ def test_other_modes_under_sanitizers(sanitized):
         _run_sanitized(exe, "static", kind, 19, 32, 256, 8)
     assert len(_run_sanitized(exe, "pairs", 256, 8)) == 140
     assert len(_run_sanitized(exe, "grid", 3000, 256, 8)) == 3001
+    assert len(_run_sanitized(exe, "order", 224, 8, 1)) == 224
     for T, nk, G in [(608, 128, 256), (3, 5, 256), (300, 2, 7)]:
         _run_sanitized(exe, "sk", T, nk, G)
 

@@ -115,12 +115,14 @@ def _dtype(d):
     return DTYPES[d] if isinstance(d, str) else int(d)
 
 
+ORDERS = {"default": _abi.ORDER_DEFAULT, "dispatch": _abi.ORDER_DISPATCH, "xcd_major": _abi.ORDER_XCD_MAJOR}
 PIPELINES = {"default": _abi.PIPELINE_DEFAULT, "four_wave": _abi.PIPELINE_FOUR_WAVE,
              "pingpong": _abi.PIPELINE_PINGPONG}
 
 
 def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_scale=None,
-              debug_flags=0, straggler_program=-1, straggler_ns=0, pipeline="default"):
+              debug_flags=0, straggler_program=-1, straggler_ns=0, pipeline="default",
+              program_order="default"):
     a = _abi.pgemm_args()
     if tile is not None:
         a.tile_m, a.tile_n, a.tile_k = (tuple(tile) + (0,))[:3]
@@ -134,6 +136,7 @@ def make_args(tile=None, group_size=0, grid=0, claim_chunk=0, a_scale=None, b_sc
     a.straggler_program = straggler_program
     a.straggler_ns = straggler_ns
     a.pipeline = PIPELINES[pipeline] if isinstance(pipeline, str) else int(pipeline)
+    a.program_order = ORDERS[program_order] if isinstance(program_order, str) else int(program_order)
     return a
 
 
@@ -235,7 +238,8 @@ def _gemm_ptrs(A, B, C, M, N, K, dtype, args, where=""):
 def _plan_dict(pl) -> dict:
     return {"grid": pl.grid, "occupancy": pl.occupancy, "tiles": pl.tiles,
             "tile": (pl.tile_m, pl.tile_n, pl.tile_k), "threads": pl.threads,
-            "lds_bytes": pl.lds_bytes, "kernel": _abi.KERNEL_NAMES.get(pl.kernel, str(pl.kernel))}
+            "lds_bytes": pl.lds_bytes, "kernel": _abi.KERNEL_NAMES.get(pl.kernel, str(pl.kernel)),
+            "xcd_major": bool(pl.xcd_major)}
 
 
 def plan_gemm(cfg: Config, M: int, N: int, K: int, dtype, sched, args=None, A=None, B=None,

@@ -29,6 +29,8 @@ KERNEL_NAMES = {KERNEL_BF16_LDS: "bf16_lds", KERNEL_BF16_STAGED: "bf16_staged", 
                 KERNEL_ADD: "add", KERNEL_BF16_PINGPONG: "bf16_pingpong"}
 # pgemm_args.pipeline
 PIPELINE_DEFAULT, PIPELINE_FOUR_WAVE, PIPELINE_PINGPONG = 0, 1, 2
+# pgemm_args.program_order
+ORDER_DEFAULT, ORDER_DISPATCH, ORDER_XCD_MAJOR = 0, 1, 2
 
 
 class pgemm_args(ctypes.Structure):
@@ -38,7 +40,7 @@ class pgemm_args(ctypes.Structure):
         ("a_scale", ctypes.c_void_p), ("b_scale", ctypes.c_void_p),
         ("debug_flags", ctypes.c_uint),
         ("straggler_program", ctypes.c_int), ("straggler_ns", ctypes.c_int),
-        ("pipeline", ctypes.c_int),
+        ("pipeline", ctypes.c_int), ("program_order", ctypes.c_int),
     ]
 
 
@@ -66,6 +68,7 @@ class pgemm_plan(ctypes.Structure):
         ("grid", ctypes.c_int), ("occupancy", ctypes.c_int), ("tiles", ctypes.c_int64),
         ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
         ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("kernel", ctypes.c_int),
+        ("xcd_major", ctypes.c_int),
     ]
 
 

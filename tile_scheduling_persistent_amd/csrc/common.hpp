@@ -38,6 +38,7 @@ struct SchedParams {
   int num_pid_n;      // tiles along dimension 1 (columns)
   int* counters;      // work-stealing counters (stride kCounterStride), zero at launch
   int self_reset;     // per-XCD work stealing: the last failing claim on a counter zeroes it
+  int xcd_major;      // static walks: programs numbered XCD-major (pgs::program_of)
   int chunk;          // tiles per work-stealing claim
   int straggler_program;  // -1: off
   int straggler_ns;

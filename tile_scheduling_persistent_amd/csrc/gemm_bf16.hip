@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
   const int wave = tid >> 6;
   const int wm = wave / S::WN;
   const int wn = wave % S::WN;
-  const int prog = blockIdx.x;
+  const int prog = pgs::program_of(blockIdx.x, P.s.G, P.s.X, P.s.xcd_major);
   const int M = P.M, N = P.N, K = P.K;
   const unsigned short* __restrict__ A = static_cast<const unsigned short*>(P.A);
   const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);

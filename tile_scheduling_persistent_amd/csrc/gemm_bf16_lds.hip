@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN;
   const int wn = wave % S::WN;
-  const int prog = blockIdx.x;
+  const int prog = pgs::program_of(blockIdx.x, P.s.G, P.s.X, P.s.xcd_major);
   // The loader tile's problem and the matrix cores' tile's problem (one
   // problem unless GRP).
   int Ml = P.M, Nl = P.N, Kl = P.K;
@@ -490,6 +490,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       kstep(st ^ 1, 0, (S::KK - 1) & 1, st, 0);
       ++g;
     }
+    mfma_results_ready();  // the epilogue reads the accumulators with acc_read
     if (SK && cslot >= 0)
       store_partial(cslot);
     else

@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(pp::kThreads) gemm_bf16_pp_kernel(GemmParams P
   const int q = wave & 3;
   const int wm = q >> 1;            // rows wm*128 ..
   const int wn = grp * 2 + (q & 1); // columns wn*64 ..
-  const int prog = blockIdx.x;
+  const int prog = pgs::program_of(blockIdx.x, P.s.G, P.s.X, P.s.xcd_major);
   const int M = P.M, N = P.N, K = P.K;
   const unsigned short* Ag = static_cast<const unsigned short*>(P.A);
   const unsigned short* Bg = static_cast<const unsigned short*>(P.B);

@@ -101,6 +101,19 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
+// Wait for the results of the MFMAs issued so far before acc_read touches
+// them.  The hazard logic of the compiler does not look into the inline asm
+// of acc_read, so it neither keeps those reads after the MFMAs that write the
+// accumulators nor pads them with the wait states an MFMA result needs
+// (16-pass XDL write, then VALU read: 18).  Call it after the tile's last
+// MFMA: 24 wait states cover that MFMA, and every earlier one finished
+// before it.  The sched_barriers keep MFMAs and reads on their own side.
+__device__ __forceinline__ void mfma_results_ready() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Two floats rounded to bf16 (nearest even) and packed, the first in the
 // low half.
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {

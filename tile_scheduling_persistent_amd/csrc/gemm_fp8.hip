@@ -14,13 +14,13 @@
 // lane passes its row's scale for the slab's group and the assignment of K
 // positions to MFMA blocks does not matter.
 //
-// Data movement and issue order as in gemm_bf16_lds.hip: a ring of NST LDS
-// stages of 128-deep slabs filled by hand-issued buffer_load ... lds
-// (gemm_device.hpp), the loads of slab g + NST - 1 spread over the MFMAs of
-// slab g, the next step's fragment reads after each MFMA.  After the slab's
-// barrier the reads that gate the first MFMAs (scale bytes, first B^T
-// block, the A blocks) go out first and the loader's bookkeeping runs under
-// their latency.  The scale bytes of a slab travel
+// Data movement as in gemm_bf16_lds.hip: a ring of NST LDS stages of
+// 128-deep slabs filled by hand-issued buffer_load ... lds (gemm_device.hpp),
+// the loads of slab g + NST - 1 spread over the MFMAs of one slab period,
+// the next step's fragment reads after each MFMA.  The slab barrier sits
+// between the two 64-deep steps of a slab: after it, the previous slab's
+// second step (fragments already in registers) covers the latency of the
+// new slab's first reads.  The scale bytes of a slab travel
 // with it: byte-sized direct loads put each row's (column's) scale byte in
 // its own LDS dword of the stage, read back after the barrier.  Two stages
 // suit the MFMA-bound square tiles; a deeper ring keeps more bytes in
@@ -107,14 +107,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   constexpr int NL = NO + S::NSC;                                // all loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per 64-deep step
   constexpr int NRD = 4 * S::SN + 2 * S::SM;                     // LDS reads per step
-  // B^T block sn of a slab's first step is first used by MFMA sn * SM; its
-  // reads go out after MFMA sn * SM - 3 (three 64-cycle MFMAs of slack), or
-  // with the slab's first reads if that is before MFMA 0.
-  constexpr auto early_b = [](int sn) { return sn * S::SM - 3; };
-  // The operand loads of a slab are spread over the first SPREAD MFMAs of
-  // the slab (load d after MFMA d*SPREAD/NO), one at a time rather than a
-  // burst; its few scale-byte loads go out right after the loader's
-  // bookkeeping.
+  // The operand loads of a slab are spread over the first SPREAD MFMA
+  // positions of its period (load d after position d*SPREAD/NO), one at a
+  // time rather than a burst; its few scale-byte loads go out right after the
+  // loader's bookkeeping.
   constexpr int SPREAD_W = 3 * NMF / 2 > NO ? 3 * NMF / 2 : NO;
   constexpr int SPREAD = SPREAD_W < 2 * NMF ? SPREAD_W : 2 * NMF;
   static_assert(SPREAD >= NO, "one operand load per MFMA at most");
@@ -128,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN;
   const int wn = wave % S::WN;
-  const int prog = blockIdx.x;
+  const int prog = pgs::program_of(blockIdx.x, P.s.G, P.s.X, P.s.xcd_major);
   // The loader tile's problem and the matrix cores' tile's problem (one
   // problem unless GRP).
   int Ml = P.M, Nl = P.N, Kl = P.K;
@@ -488,78 +484,118 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
-    for (int ck = 0; ck < cnk; ++ck) {
-      // Slab g (operands and scale bytes) landed once this wave's loads of it
-      // are done (the loads of the NST - 2 slabs after it may still be in
-      // flight) and every wave has passed the barrier, which also frees the
-      // stage of slab g-1 for the loads of slab g + NST - 1.
+    // One period per slab g: barrier, then step 1 of slab g-1 (fragments in
+    // slot 1, scales of g-1) while step 0 of slab g is read into slot 0, then
+    // step 0 of slab g while its step 1 is read into slot 1.  The barrier thus
+    // sits between the two steps of a slab, and the first MFMAs after it use
+    // fragments already in registers: the latency of the new slab's first
+    // reads hides under the old slab's second step instead of stalling the
+    // matrix cores.  The tile's first slab (peeled off the loop) has no
+    // previous step to overlap; its last slab's step 1 runs after the loop.
+    //
+    // Slab g (operands and scale bytes) landed once this wave's loads of it
+    // are done (the loads of the NST - 2 slabs after it may still be in
+    // flight) and every wave has passed the barrier.  Every wave has also
+    // finished its LDS reads of slab g-1 (lgkmcnt(0) before the barrier; its
+    // step 1 is in registers), which frees that stage for the loads of slab
+    // g + NST - 1.
+    auto slab_start = [&](unsigned (&sraw)[S::SM + S::SN]) {
       wait_vm<(NST - 2) * NL>();
       slab_barrier();
-      const int st = g % NST;
-      const int st_dma = st == 0 ? NST - 1 : st - 1;
-      // The slab's scale bytes gate every MFMA and the first step's B^T
-      // block 0 and A blocks gate the first ones, so those LDS reads go out
-      // first, all together; the loader's bookkeeping and the scale packing
-      // follow, and the other B^T blocks of the first step are read a few
-      // MFMAs before their first use (early_b).
-      unsigned sraw[S::SM + S::SN];
-      {
-        const unsigned char* scb = smem + st * S::STAGE + sc_off;
+      const unsigned char* scb = smem + (g % NST) * S::STAGE + sc_off;
 #pragma unroll
-        for (int s = 0; s < S::SM; ++s)
-          sraw[s] = *reinterpret_cast<const unsigned*>(scb + (s * 32 + l32) * 4);
+      for (int s = 0; s < S::SM; ++s)
+        sraw[s] = *reinterpret_cast<const unsigned*>(scb + (s * 32 + l32) * 4);
 #pragma unroll
-        for (int s = 0; s < S::SN; ++s)
-          sraw[S::SM + s] = *reinterpret_cast<const unsigned*>(scb + S::SC_A * 256 + (s * 32 + l32) * 4);
-      }
-#pragma unroll
-      for (int r = 0; r < 4 + 2 * S::SM; ++r) read(st, 0, 0, r);
-#pragma unroll
-      for (int sn = 1; sn < S::SN; ++sn)
-        if (early_b(sn) < 0)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) read(st, 0, 0, 4 * sn + q + 2 * S::SM);
+      for (int s = 0; s < S::SN; ++s)
+        sraw[S::SM + s] = *reinterpret_cast<const unsigned*>(scb + S::SC_A * 256 + (s * 32 + l32) * 4);
       __builtin_amdgcn_sched_barrier(0);
-      prep();  // slab g + NST - 1; overlaps the latency of the first reads
+    };
+    // A slab's scale bytes packed for opsel: byte s of the A word is the
+    // scale of sub-tile sm = s, likewise for B.
+    auto pack_scales = [&](const unsigned (&sraw)[S::SM + S::SN], int& va_out, int& vb_out) {
+      unsigned va = 0, vb = 0;
 #pragma unroll
-      for (int d = NO; d < NL; ++d) dma(st_dma, d);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        unsigned va = 0, vb = 0;
+      for (int s = 0; s < S::SM; ++s) va |= (sraw[s] & 0xffu) << (8 * s);
 #pragma unroll
-        for (int s = 0; s < S::SM; ++s) va |= (sraw[s] & 0xffu) << (8 * s);
+      for (int s = 0; s < S::SN; ++s) vb |= (sraw[S::SM + s] & 0xffu) << (8 * s);
+      va_out = (int)va;
+      vb_out = (int)vb;
+    };
+    // Step 0 of slab g with its step-1 reads and the rest of the loads.
+    auto step0_period = [&](int st, int st_dma) {
 #pragma unroll
-        for (int s = 0; s < S::SN; ++s) vb |= (sraw[S::SM + s] & 0xffu) << (8 * s);
-        sa_reg = (int)va;
-        sb_reg = (int)vb;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Fixed issue order: MFMA, then the first step's later B^T reads
-      // (first step only), its share of the next step's LDS reads, then
-      // (first SPREAD MFMAs) a load of slab g+1.
+      for (int j = 0; j < NMF; ++j) {
+        mfma(0, j);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+        for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, 1, 1, r);
 #pragma unroll
-        for (int j = 0; j < NMF; ++j) {
-          mfma(ks, j);
-          if (ks == 0) {
-#pragma unroll
-            for (int sn = 1; sn < S::SN; ++sn)
-              if (early_b(sn) == j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) read(st, 0, 0, 4 * sn + q + 2 * S::SM);
-#pragma unroll
-            for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, 1, 1, r);
-          }
-          const int p = ks * NMF + j;
-#pragma unroll
-          for (int d = 0; d < NO; ++d)
-            if (d * SPREAD / NO == p) dma(st_dma, d);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int d = 0; d < NO; ++d)
+          if (d * SPREAD / NO == NMF + j) dma(st_dma, d);
+        __builtin_amdgcn_sched_barrier(0);
       }
       ++g;
+    };
+    {
+      // first slab of the tile: its step-0 reads, the loader's bookkeeping
+      // under their latency, then the loads of the first MFMA positions
+      unsigned sraw[S::SM + S::SN];
+      slab_start(sraw);
+      const int st = g % NST;
+      const int st_dma = st == 0 ? NST - 1 : st - 1;
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) read(st, 0, 0, r);
+      __builtin_amdgcn_sched_barrier(0);
+      prep();  // slab g + NST - 1
+#pragma unroll
+      for (int d = NO; d < NL; ++d) dma(st_dma, d);
+#pragma unroll
+      for (int d = 0; d < NO; ++d)
+        if (d * SPREAD / NO < NMF) dma(st_dma, d);
+      pack_scales(sraw, sa_reg, sb_reg);
+      __builtin_amdgcn_sched_barrier(0);
+      step0_period(st, st_dma);
     }
+    for (int ck = 1; ck < cnk; ++ck) {
+      unsigned sraw[S::SM + S::SN];
+      slab_start(sraw);
+      const int st = g % NST;
+      const int st_dma = st == 0 ? NST - 1 : st - 1;
+      // step 1 of slab g-1 while step 0 of slab g is read; the loader's
+      // bookkeeping after its first MFMA
+      mfma(1, 0);
+#pragma unroll
+      for (int r = 0; r < NRD / NMF; ++r) read(st, 0, 0, r);
+      __builtin_amdgcn_sched_barrier(0);
+      prep();  // slab g + NST - 1
+#pragma unroll
+      for (int d = NO; d < NL; ++d) dma(st_dma, d);
+#pragma unroll
+      for (int d = 0; d < NO; ++d)
+        if (d * SPREAD / NO == 0) dma(st_dma, d);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 1; j < NMF; ++j) {
+        mfma(1, j);
+#pragma unroll
+        for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st, 0, 0, r);
+#pragma unroll
+        for (int d = 0; d < NO; ++d)
+          if (d * SPREAD / NO == j) dma(st_dma, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pack_scales(sraw, sa_reg, sb_reg);
+      __builtin_amdgcn_sched_barrier(0);
+      step0_period(st, st_dma);
+    }
+    // step 1 of the tile's last slab, then the wait for its results (the
+    // epilogue reads the accumulators with acc_read)
+#pragma unroll
+    for (int j = 0; j < NMF; ++j) {
+      mfma(1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_results_ready();
     if (SK && cslot >= 0)
       store_partial(cslot);
     else

@@ -12,11 +12,21 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/pgemm.h"
 #include "common.hpp"
+
+// The program numbering choose_order last made for a single GEMM, by its
+// scheduler parameters and tile.
+struct OrderChoice {
+  bool valid = false;
+  int key[10];
+  int xcd_major;
+};
 
 struct pgemm_config {
   int device;
@@ -32,6 +42,7 @@ struct pgemm_config {
   float* ws;          // stream-K partial-sum workspace (device), grown on demand
   size_t ws_bytes;
   unsigned char* scratch;  // this device's address of the static `scratch` array
+  OrderChoice order_choice;  // the last single-GEMM numbering decision (choose_order)
   // witness buffers (device)
   int64_t w_tiles;
   int w_programs;
@@ -123,6 +134,9 @@ void free_witness(pgemm_config* c) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
+// balance: GEMM (balanced default grid); the add keeps the full grid.  The
+// program numbering starts as the workgroup order; GEMM paths then call
+// choose_order.
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
                         int num_pid_m, int num_pid_n, int default_grid, bool balance,
                         pgk::SchedParams& s) {
@@ -156,6 +170,10 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   s.straggler_xcc = 0;
   s.wall_khz = cfg->wall_khz;
   if (s.G < 1 || s.gs < 1) return PGEMM_ERR_INVALID;
+  const int order = args ? args->program_order : PGEMM_ORDER_DEFAULT;
+  if (order != PGEMM_ORDER_DEFAULT && order != PGEMM_ORDER_DISPATCH && order != PGEMM_ORDER_XCD_MAJOR)
+    return PGEMM_ERR_INVALID;
+  s.xcd_major = 0;
   if (s.kind == pgs::kWorkStealing && s.G < s.X) return PGEMM_ERR_INVALID;
   if (s.kind == pgs::kWorkStealingXcc && s.X > pgk::kMaxStealCounters) return PGEMM_ERR_UNSUPPORTED;
   if (s.X < 1 || s.X > cfg->capacity) return PGEMM_ERR_INVALID;
@@ -172,6 +190,75 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
     s.straggler_xcc = 1;
   }
   return PGEMM_OK;
+}
+
+// Operand panels the first tiles of a static walk's programs touch, summed
+// over the XCDs (workgroup i runs on XCD i mod X): distinct rows of tiles
+// weighted by the tile's rows (bm) plus distinct columns of tiles weighted by
+// its columns (bn), per problem.  Proportional to the bytes each XCD's L2
+// has to fetch for its programs' first round.  gp / ngemm: the problems of a
+// grouped launch (virtual tile ids), or none for one GEMM.
+int64_t first_round_panels(const pgk::SchedParams& s, int xcd_major, int bm, int bn,
+                           const pgk::GemmProblem* gp, int ngemm) {
+  std::vector<std::vector<int64_t>> rows(s.X), cols(s.X);
+  for (int hw = 0; hw < s.G; ++hw) {
+    const int q = pgs::program_of(hw, s.G, s.X, xcd_major);
+    int v, end;
+    pgs::static_first(s.kind, q, s.T, s.G, v, end);
+    if (v >= end) continue;
+    int g = 0, local = v, npm = s.num_pid_m, npn = s.num_pid_n;
+    for (int i = 1; i < ngemm; ++i)
+      if (v >= gp[i].tile0) g = i;
+    if (ngemm > 0) {
+      local = v - gp[g].tile0;
+      npm = gp[g].npm;
+      npn = gp[g].npn;
+    }
+    int pm, pn;
+    pgs::decode(s.kind, local, npm, npn, s.gs, pm, pn);
+    rows[hw % s.X].push_back(((int64_t)g << 32) | (uint32_t)pm);
+    cols[hw % s.X].push_back(((int64_t)g << 32) | (uint32_t)pn);
+  }
+  int64_t total = 0;
+  for (int x = 0; x < s.X; ++x) {
+    for (auto* k : {&rows[x], &cols[x]}) {
+      std::sort(k->begin(), k->end());
+      const int64_t n = std::unique(k->begin(), k->end()) - k->begin();
+      total += n * (k == &rows[x] ? bm : bn);
+    }
+  }
+  return total;
+}
+
+// Program numbering of a GEMM's static walk (pgemm_args.program_order).
+// DEFAULT takes XCD-major numbering where it makes the first round touch
+// fewer operand panels per XCD than the workgroup order, which depends on
+// the decode: for the grouped order, an XCD's consecutive ids form a compact
+// block of tiles; for the plain decode with many rows of tiles, they form a
+// column, and the round robin of the workgroup order is the compact one.
+void choose_order(pgemm_config* cfg, const pgemm_args* args, pgk::SchedParams& s, int bm, int bn,
+                  const pgk::GemmProblem* gp, int ngemm) {
+  s.xcd_major = 0;
+  const int order = args ? args->program_order : PGEMM_ORDER_DEFAULT;
+  if (order == PGEMM_ORDER_DISPATCH || pgs::work_stealing(s.kind) || s.kind == pgs::kStreamK ||
+      s.X < 2 || s.G % s.X != 0)
+    return;
+  if (order == PGEMM_ORDER_XCD_MAJOR) {
+    s.xcd_major = 1;
+    return;
+  }
+  OrderChoice& c = cfg->order_choice;
+  const int key[10] = {s.kind, s.T, s.G, s.X, s.gs, s.num_pid_m, s.num_pid_n, bm, bn, ngemm};
+  if (ngemm == 0 && c.valid && memcmp(c.key, key, sizeof(key)) == 0) {
+    s.xcd_major = c.xcd_major;
+    return;
+  }
+  s.xcd_major = first_round_panels(s, 1, bm, bn, gp, ngemm) < first_round_panels(s, 0, bm, bn, gp, ngemm);
+  if (ngemm == 0) {
+    memcpy(c.key, key, sizeof(key));
+    c.xcd_major = s.xcd_major;
+    c.valid = true;
+  }
 }
 
 // Kernel a GEMM call takes, from shapes, formats, tile and pointer alignment
@@ -250,6 +337,7 @@ void fill_plan(const pgk::SchedParams& s, const pgk::KernelInfo& ki, int bm, int
   out->threads = ki.threads;
   out->lds_bytes = ki.lds_bytes;
   out->kernel = kernel;
+  out->xcd_major = s.xcd_major;
 }
 
 pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::SchedParams& s,
@@ -661,6 +749,7 @@ pgemm_status pgemm_run_grouped(pgemm_config* cfg, const pgemm_problem* problems,
   if (ki.threads == 0) return PGEMM_ERR_UNSUPPORTED;
   pgemm_status st = make_sched(cfg, sched, args, (int)total, 1, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
+  choose_order(cfg, args, p.s, bm, bn, p.gp, p.ngemm);
   if (validate_only(args)) return PGEMM_OK;
   hipStream_t stream = (hipStream_t)hip_stream;
   bool witness = false;
@@ -804,6 +893,7 @@ pgemm_status gemm_call(pgemm_config* cfg, const void* A, const void* B, void* C,
   const pgk::KernelInfo ki = gemm_info(ch);
   st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, true, p.s);
   if (st != PGEMM_OK) return st;
+  choose_order(cfg, args, p.s, ch.bm, ch.bn, nullptr, 0);
   if (p.s.X > buf.n_counters) return PGEMM_ERR_INVALID;
   p.s.counters = buf.counters;
   const bool sk = sched == PGEMM_SCHED_STREAM_K;
@@ -934,6 +1024,7 @@ pgemm_status pgemm_plan_gemm(pgemm_config* cfg, const void* A, const void* B, co
   pgk::SchedParams s;
   st = make_sched(cfg, sched, args, (int)npm, (int)npn, cfg->num_cus * ki.occupancy, true, s);
   if (st != PGEMM_OK) return st;
+  choose_order(cfg, args, s, ch.bm, ch.bn, nullptr, 0);
   fill_plan(s, ki, ch.bm, ch.bn, ch.bk, ch.kernel, out);
   return PGEMM_OK;
 }

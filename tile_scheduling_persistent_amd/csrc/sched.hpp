@@ -77,6 +77,19 @@ PGS_FN void decode(int kind, int v, int num_pid_m, int num_pid_n, int gs, int& p
     decode_plain(v, num_pid_m, pid_m, pid_n);
 }
 
+// Program numbering of the static walks.  The hardware hands workgroup i of
+// a launch to XCD i mod X (round robin), so workgroups with consecutive ids
+// run on different XCDs and share no L2.  XCD-major numbering gives the
+// programs of one XCD consecutive ids: workgroup i plays program
+// (i mod X) * (G / X) + i / X, and the neighbouring tiles of a static walk's
+// round (which share operand panels) meet in one L2, as a work-stealing range
+// does.  A bijection of [0, G); the identity unless xcd_major is set and
+// X > 1 divides G.
+PGS_FN int program_of(int hw, int G, int X, int xcd_major) {
+  if (!xcd_major || X < 2 || G % X != 0) return hw;
+  return (hw % X) * (G / X) + hw / X;
+}
+
 // Work stealing: XCD x owns tile ids [range_begin(x), range_begin(x + 1)).
 PGS_FN int ws_range_begin(int x, int T, int X) {
   return (int)(((int64_t)x * (int64_t)T) / (int64_t)X);
