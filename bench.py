@@ -39,16 +39,29 @@ CPU_ROWS = 4096
 SETTLE_S = 2.0        # untimed repeats of the headline call before the timed steps (engine clock settles)
 RAGGED_ROUNDS = 3     # interleaved rounds over the schedulers on the ragged shapes
 
-# HBM traffic of one 8192^3 launch of the bf16 GEMM kernel, from two
-# rocprofv3 counter passes over `bench.py --only work_stealing_g8` (FETCH_SIZE,
-# WRITE_SIZE; KiB per dispatch, mean of 5 dispatches), each scaled by what
-# the same counter reads for a plain 256 MiB device copy (`bench.py
-# --copy-calibration`: FETCH_SIZE x2.000, WRITE_SIZE x1.000).  Valid only for
-# the kernel sources it was measured on (hash below); otherwise reported as
-# null.
-TRAFFIC_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
-TRAFFIC_MEASURED = {"sources_sha256_16": "a59ec5089df66011",
-                    "fetch_bytes": 1891481600, "write_bytes": 142954496}
+# Memory traffic of one launch: what the L2s send to the memory controllers,
+# from rocprofv3 counter passes over `bench.py --profile-only <target>`:
+# TCC_EA0_RDREQ_DRAM_32B_sum and TCC_EA0_WRREQ_WRITE_DRAM_32B_sum (32-byte
+# units of read and write requests bound for the memory controllers, a
+# 128-byte request counting 4; median of the last 4 dispatches) x 32 bytes.
+# On a plain 256 MiB device copy (`bench.py --copy-calibration`) they read
+# exactly 256 MiB each way, so no calibration factor applies.  Hits in the
+# Infinity Cache, which sits on the memory side, are included: no counter
+# here separates them from DRAM.  A record holds only for the kernel sources
+# it was measured on (hash); otherwise the traffic is reported as null.
+BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
+FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
+ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp"]
+TRAFFIC = {
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "c112c82ac892bbb9",
+                                    "read_bytes": 1879208160, "write_bytes": 145080880},
+    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "ca0d82f607ea2149",
+                                   "read_bytes": 811890752, "write_bytes": 145407008},
+    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "ca0d82f607ea2149",
+                                                 "read_bytes": 253829632, "write_bytes": 14680320},
+    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "a60d92e4b7b705c1",
+                                   "read_bytes": 536937472, "write_bytes": 268585280},
+}
 
 
 def parse():
@@ -64,7 +77,9 @@ def parse():
                    help="only time a plain 256 MiB device-to-device copy (the reference kernel for "
                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--profile-only", choices=sorted(PROFILE_TARGETS), default=None,
-                   help="only time this one workload (for counter passes) and exit")
+                   help="only time this one workload (for traces and counter passes) and exit")
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="with --profile-only: seconds of untimed calls first (0 for counter passes)")
     return p.parse_args()
 
 
@@ -83,6 +98,7 @@ PROFILE_TARGETS = {
     "add_8192sq_128x128_interleaved": ("add", (128, 128), "interleaved"),
     "fp8_8192cube_work_stealing": ("fp8", (256, 256, 128), "work_stealing"),
     "fp8_256x28672x8192_128x256_work_stealing": ("fp8_skinny", (128, 256, 128), "work_stealing"),
+    "fp8_256x28672x8192_128x256_grouped": ("fp8_skinny", (128, 256, 128), "grouped"),
     # ragged bf16 shapes (same inputs as the bench pass) at the default,
     # balanced grid and, with "_grid256", on one program per CU
     "bf16_5120x5120x4096_work_stealing": ("bf16:5120:5120:4096", (256, 256, 64), "work_stealing"),
@@ -95,9 +111,11 @@ PROFILE_TARGETS = {
 }
 
 
-def profile_only(name, steps, warmup):
+def profile_only(name, steps, warmup, settle_s):
     """Time one workload of the bench pass (same inputs) and print its event
-    time, so that a counter pass sees only that kernel (and the counter reset)."""
+    time, so that a trace or counter pass sees only that kernel: settle_s
+    seconds of untimed calls (the engine clock settles, as in the bench
+    pass), then warmup and steps calls."""
     import torch
     import tile_scheduling_persistent_amd as pg
     from synthetic import f32_normal, fp8_blockscaled
@@ -123,7 +141,6 @@ def profile_only(name, steps, warmup):
         a = pg.make_args(tile=tile, grid=grid, pipeline=pipeline)
         nbytes, work = 2 * (m * k + k * n) + rc.element_size() * m * n, 2.0 * m * n * k
         fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, out, sched, a)  # noqa: E731
-        settle(fn, SETTLE_S)
     elif kind == "add":
         R = Cc = 8192
         X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
@@ -141,9 +158,12 @@ def profile_only(name, steps, warmup):
         a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
         nbytes, work = m * k + k * n + (m + n) * (k // 128) + 2 * m * n, 2.0 * m * n * k
         fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
+    settle(fn, settle_s)
     d = event_means(fn, steps, warmup, stream)
+    batch = event_batch_ms(fn, steps, 2, stream)
     ev_mean = float(np.mean(d))
     out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5), "event_ms_median": round(float(np.median(d)), 5),
+           "batch_ms_per_call": round(batch, 5),
            "plan": (pg.plan_gemm(cfg, m, n, k, "bf16_out_f32" if kind.startswith("bf16f:") else "bf16_out_bf16",
                                  sched, a) if kind.split(":")[0] in ("bf16", "bf16n", "bf16f") else None),
            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1)}
@@ -194,6 +214,52 @@ def event_means(fn, steps, warmup, stream):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
+def event_batch_ms(fn, steps, warmup, stream):
+    """Mean time per call (ms) of `steps` calls enqueued back to back between
+    one pair of HIP events on `stream`.  The warm-up calls go right before the
+    first event, so the GPU is busy while the host enqueues the timed calls;
+    for kernels longer than the host's cost per call the GPU then runs them
+    back to back, and the mean is the kernel time plus the gap between
+    consecutive launches (per-call event pairs add their own commands to that
+    gap)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def graph_ms_per_call(fn, calls, replays, stream):
+    """Mean time per call (ms) of `calls` calls captured in one HIP graph,
+    median over `replays` replays: the launch rate the device sustains when
+    the host's cost per call is out of the way (for kernels shorter than that
+    cost).  Only for calls that record no memset into the graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    fn()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / calls)
+    del g
+    return float(np.median(out))
+
+
 def rounds_summary(work, means_ms, unit_scale=1e12):
     """Median / min / max rate over rounds (work per call / mean call time)."""
     rates = sorted(work / (m * 1e-3) / unit_scale for m in means_ms)
@@ -240,6 +306,11 @@ def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
     tiles = w["n_tiles"][:G]
     X = cfg.info["num_xcds"]
     xcc = (w["hw_id"][:G].astype(np.int64) >> 16) & 0xF    # hardware XCC of each program
+    q = np.arange(G)
+    # the XCD each program should run on: workgroup i goes to XCD i mod X, and
+    # program q is workgroup q, or workgroup (q mod (G/X)) * X + q / (G/X)
+    # under XCD-major numbering
+    home = q // (G // X) if plan["xcd_major"] else q % X
     vals, counts = np.unique(tiles, return_counts=True)
     return {"span_us": round(span, 1), "busy_mean_us": round(float(busy.mean()), 1),
             "busy_min_us": round(float(busy.min()), 1), "busy_max_us": round(float(busy.max()), 1),
@@ -252,7 +323,8 @@ def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
             "tiles_per_program_hist": {str(int(v)): int(c) for v, c in zip(vals, counts)},
             "tiles_per_xcc": [int(tiles[xcc == x].sum()) for x in range(X)],
             "programs_per_xcc": [int((xcc == x).sum()) for x in range(X)],
-            "xcc_is_p_mod_x": round(float(np.mean(xcc == (np.arange(G) % X))), 4)}
+            "xcd_major": bool(plan["xcd_major"]),
+            "xcc_as_numbered": round(float(np.mean(xcc == home)), 4)}
 
 
 def measured_clock(pg, cfg, A, B, C, key):
@@ -275,24 +347,32 @@ def measured_clock(pg, cfg, A, B, C, key):
     return round(float(np.median(w["cycles"][ok] / dt[ok])) / 1e9, 3)
 
 
-def measured_traffic():
-    """Counter-derived HBM bytes per launch, or None if the kernel changed since."""
+def measured_traffic(target):
+    """Counter-derived memory bytes per launch of a profile target, or None if
+    its kernel sources changed since the counters were taken."""
     import hashlib
+    rec = TRAFFIC.get(target)
+    if rec is None:
+        return None
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in rec["sources"]:
         with open(os.path.join(ROOT, "tile_scheduling_persistent_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest()[:16] != TRAFFIC_MEASURED["sources_sha256_16"]:
+    if h.hexdigest()[:16] != rec["sha256_16"]:
         return None
-    return TRAFFIC_MEASURED["fetch_bytes"] + TRAFFIC_MEASURED["write_bytes"]
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
-def rooflines(flops, head, fp8, add, cfg1, traffic):
+def rooflines(flops, head, fp8, add, cfg1):
     """One roofline record per measured kernel: achieved algorithmic work per
-    launch / mean HIP-event launch time, against the peak of its bound."""
+    launch / mean HIP-event launch time, against the peak of its bound, with
+    the counter-derived memory traffic per launch where it was measured."""
     out = [{"kernel": "gemm_bf16", "workload": f"bf16 8192^3, bf16 C, 256x256x64, {HEADLINE[0]} g{HEADLINE[1]}",
             "bound": "mfma", "achieved": round(flops / (head["event_ms_mean"] * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": traffic}]
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "traffic": measured_traffic("bf16_8192cube_work_stealing")}]
+    fp8_traffic = {("8192x8192x8192_256x256", "work_stealing"): "fp8_8192cube_work_stealing",
+                   ("256x28672x8192_128x256", "work_stealing"): "fp8_256x28672x8192_128x256_work_stealing"}
     for key, sched, bound in [("8192x8192x8192_256x256", "work_stealing", "mfma"),
                               ("256x28672x8192_128x256", "work_stealing", "hbm"),
                               ("256x28672x8192_128x256", "grouped", "hbm"),
@@ -304,16 +384,16 @@ def rooflines(flops, head, fp8, add, cfg1, traffic):
         if bound == "mfma":
             out.append({"kernel": "gemm_fp8", "workload": f"fp8 e4m3 {shape}, block scales, {tile}x128, {sched}",
                         "bound": "mfma", "achieved": r["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                        "traffic": None})
+                        "traffic": measured_traffic(fp8_traffic.get((key, sched)))})
         else:
             out.append({"kernel": "gemm_fp8", "workload": f"fp8 e4m3 {shape}, block scales, {tile}x128, {sched}",
                         "bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "traffic": None})
+                        "traffic": measured_traffic(fp8_traffic.get((key, sched)))})
     for key in ("128x128_blocked", "128x128_work_stealing", "32x16_blocked", "32x16_work_stealing"):
         if key in add:
             out.append({"kernel": "padd", "workload": f"fp32 add 8192x8192, {key.replace('_', ' tiles, ', 1)}",
                         "bound": "hbm", "achieved": round(add[key]["gbs"], 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "traffic": None})
+                        "unit": "GB/s", "traffic": measured_traffic(f"add_8192sq_{key}")})
     if cfg1:
         out.append({"kernel": "gemm_bf16", "workload": cfg1["workload"], "bound": "launch",
                     "achieved": cfg1["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": None,
@@ -350,7 +430,7 @@ def main():
         copy_calibration(args.steps, args.warmup)
         return
     if args.profile_only:
-        profile_only(args.profile_only, args.steps, args.warmup)
+        profile_only(args.profile_only, args.steps, args.warmup, args.settle)
         return
     import torch
     import tile_scheduling_persistent_amd as pg
@@ -407,10 +487,13 @@ def main():
         args1 = pg.make_args(tile=(128, 128, 64))
         fn = lambda: pg.pgemm_run(cfg, a1, b1, c1, 512, 512, 512, "bf16_out_f32", "blocked", args1)  # noqa: E731
         d = event_means(fn, max(args.steps, 50), args.warmup, stream)
+        gms = graph_ms_per_call(fn, 100, 5, stream)
         f1 = 2.0 * 512 ** 3
         cfg1 = {"workload": "bf16 512^3, fp32 C, 128x128x64 tiles, blocked (16 tiles)",
                 "event_ms_mean": round(float(np.mean(d)), 5), "event_ms_median": round(float(np.median(d)), 5),
-                "tflops": round(f1 / (np.mean(d) * 1e-3) / 1e12, 2),
+                "event_tflops": round(f1 / (np.mean(d) * 1e-3) / 1e12, 2),
+                "graph_ms_per_call": round(gms, 5),
+                "tflops": round(f1 / (gms * 1e-3) / 1e12, 2),
                 "programs": pg.plan_gemm(cfg, 512, 512, 512, "bf16_out_f32", "blocked", args1)["grid"]}
         print(f"# cfg 1 (512^3): {cfg1}", file=sys.stderr, flush=True)
 
@@ -580,7 +663,7 @@ def main():
             print(f"# balance {m}x{n}x{k}: " + ", ".join(f"{s_}: idle {v['idle_frac']} skew {v['skew']}"
                                                          for s_, v in row.items()), file=sys.stderr, flush=True)
             ws = row["work_stealing"]
-            print(f"#   {ws['programs']} programs, hardware XCC == p mod X for {ws['xcc_is_p_mod_x']:.0%}; "
+            print(f"#   {ws['programs']} programs, hardware XCC == p mod X for {ws['xcc_as_numbered']:.0%}; "
                   f"work stealing tiles per XCC {ws['tiles_per_xcc']}, per program {ws['tiles_per_program_hist']}",
                   file=sys.stderr, flush=True)
         del shapes
@@ -598,15 +681,26 @@ def main():
             dC = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
             nbytes = m * k + k * n + (m + n) * (k // 128) + 2 * m * n
-            row = {}
+            # settle the clock, then interleaved rounds of the schedulers
+            calls = {}
             for sched in ["grouped", "work_stealing", "stream_k"]:
                 a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
-                fn = lambda: pg.pgemm_run(cfg, dA, dB, dC, m, n, k, "fp8_b128_out_bf16", sched, a)  # noqa: E731
-                _, ev_mean, _ = time_calls(fn, args.steps, args.warmup, stream)
+                calls[sched] = (a, lambda a=a, sched=sched: pg.pgemm_run(cfg, dA, dB, dC, m, n, k,
+                                                                         "fp8_b128_out_bf16", sched, a))
+            settle(calls["grouped"][1], 0.5)
+            means = {s_: [] for s_ in calls}
+            for _ in range(RAGGED_ROUNDS):
+                for s_, (_, fn) in calls.items():
+                    means[s_].append(event_batch_ms(fn, args.steps, 3, stream))
+            row = {}
+            for sched, (a, _) in calls.items():
+                ev_mean = float(np.median(means[sched]))
+                plan = pg.plan_gemm(cfg, m, n, k, "fp8_b128_out_bf16", sched, a)
                 row[sched] = {"tflops": round(f / (ev_mean * 1e-3) / 1e12, 2),
                               "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1),
-                              "event_ms_mean": round(ev_mean, 5),
-                              "grid": pg.plan_gemm(cfg, m, n, k, "fp8_b128_out_bf16", sched, a)["grid"]}
+                              "batch_ms_per_call": round(ev_mean, 5),
+                              "rounds_gbs": rounds_summary(nbytes, means[sched], 1e9),
+                              "grid": plan["grid"], "xcd_major": plan["xcd_major"]}
             fp8[f"{m}x{n}x{k}_{tile[0]}x{tile[1]}"] = row
             print(f"# fp8 {m}x{n}x{k}: {row}", file=sys.stderr, flush=True)
             del dA, dB, dC, qa, qb
@@ -621,9 +715,11 @@ def main():
         for tile in [(32, 16), (128, 128)]:
             for sched in ["blocked", "interleaved", "grouped", "work_stealing"]:
                 fn = lambda: pg.padd_run(cfg, X, Y, Z, R, Cc, tile[0], tile[1], sched)  # noqa: E731
-                ms, ev_mean, _ = time_calls(fn, max(args.steps, 20), args.warmup, stream)
+                settle(fn, 0.3)
+                ev_mean = float(np.median([event_batch_ms(fn, max(args.steps, 20), 2, stream)
+                                           for _ in range(RAGGED_ROUNDS)]))
                 add[f"{tile[0]}x{tile[1]}_{sched}"] = {"gbs": nbytes / (ev_mean * 1e-3) / 1e9,
-                                                       "event_ms_mean": ev_mean}
+                                                       "batch_ms_per_call": ev_mean}
                 print(f"# add {tile} {sched}: {nbytes / (ev_mean * 1e-3) / 1e9:.0f} GB/s",
                       file=sys.stderr, flush=True)
 
@@ -695,16 +791,16 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (h["event_ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic("bf16_8192cube_work_stealing"),
                      "clock_ghz_measured": clock_ghz,
                      "peak_at_measured_clock": (round(PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ, 1)
                                                 if clock_ghz else None),
                      "frac_at_measured_clock": (round(flops / (h["event_ms_mean"] * 1e-3) / 1e12
                                                       / (PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ), 4)
                                                 if clock_ghz else None),
-                     "traffic_unit": "HBM bytes per launch (counter passes, copy-calibrated)",
+                     "traffic_unit": "bytes per launch the L2s send to the memory controllers (Infinity Cache hits included)",
                      "algorithmic_bytes": 2 * (M * K + K * N + M * N)},
-        "rooflines": rooflines(flops, h, fp8, add, cfg1, measured_traffic()),
+        "rooflines": rooflines(flops, h, fp8, add, cfg1),
         "per_scheduler": {k: {"tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4),
                               "event_ms_mean": round(v["event_ms_mean"], 5)} for k, v in per.items()},
         "per_pipeline": per_pipeline,
