@@ -40,9 +40,15 @@ def _check(where, code):
         raise PgemmError(where, code)
 
 
+_DTYPES_OF = {}
+
+
 def _torch_dtypes(names):
-    import torch
-    return tuple(getattr(torch, n) for n in names if hasattr(torch, n))
+    t = _DTYPES_OF.get(names)
+    if t is None:
+        import torch
+        t = _DTYPES_OF[names] = tuple(getattr(torch, n) for n in names if hasattr(torch, n))
+    return t
 
 
 # Element types the calls accept: operands per pgemm_dtype, outputs, adds.
@@ -87,10 +93,8 @@ def _check_tensor(x, what, dtypes=None, nbytes=None):
                          f"the call reads or writes {nbytes}")
 
 
-def _ptr(x, what, dtypes=None, nbytes=None):
-    """Device pointer of a torch tensor (contiguous, on a GPU, of an allowed
-    dtype, at least nbytes long) or a raw int pointer."""
-    _check_tensor(x, what, dtypes, nbytes)
+def _dev(x, what):
+    """Device pointer of a checked tensor argument (or a raw int pointer)."""
     if isinstance(x, int):
         return x
     if not x.is_cuda:
@@ -98,9 +102,20 @@ def _ptr(x, what, dtypes=None, nbytes=None):
     return x.data_ptr()
 
 
-def _stream(stream):
+def _ptr(x, what, dtypes=None, nbytes=None):
+    """Device pointer of a torch tensor (contiguous, on a GPU, of an allowed
+    dtype, at least nbytes long) or a raw int pointer."""
+    _check_tensor(x, what, dtypes, nbytes)
+    return _dev(x, what)
+
+
+def _stream(stream, device=None):
+    """Raw HIP stream handle: `stream` itself (an int or a torch stream), else
+    torch's current stream on `device` (the config's device)."""
     if stream is None:
         import torch
+        if device is not None:
+            return torch._C._cuda_getCurrentRawStream(device)
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
@@ -195,7 +210,7 @@ class Config:
         w.tiles = tiles
         w.programs = programs
         _check("pgemm_witness_read",
-               _abi.lib().pgemm_witness_read(self.handle, ctypes.byref(w), _stream(stream)))
+               _abi.lib().pgemm_witness_read(self.handle, ctypes.byref(w), _stream(stream, self.device)))
         return out
 
 
@@ -204,7 +219,7 @@ def pgemm_run(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched, args=N
     """C[M][N] = A[M][K] . B[K][N] on the GPU (asynchronous on `stream`)."""
     code = _abi.lib().pgemm_run(cfg.handle, *_gemm_ptrs(A, B, C, M, N, K, dtype, args),
                                 int(M), int(N), int(K), _dtype(dtype), _sched(sched),
-                                ctypes.byref(args) if args is not None else None, _stream(stream))
+                                ctypes.byref(args) if args is not None else None, _stream(stream, cfg.device))
     _check("pgemm_run", code)
 
 
@@ -216,7 +231,7 @@ def pgemm_run_noalloc(cfg: Config, A, B, C, M: int, N: int, K: int, dtype, sched
     code = _abi.lib().pgemm_run_noalloc(cfg.handle, *_gemm_ptrs(A, B, C, M, N, K, dtype, args),
                                         int(M), int(N), int(K), _dtype(dtype), _sched(sched),
                                         ctypes.byref(args) if args is not None else None,
-                                        _stream(stream))
+                                        _stream(stream, cfg.device))
     _check("pgemm_run_noalloc", code)
 
 
@@ -229,10 +244,11 @@ def _gemm_ptrs(A, B, C, M, N, K, dtype, args, where=""):
         for name, t in zip(("a_scale", "b_scale"), getattr(args, "_scales", (None, None))):
             if t is not None:
                 _check_tensor(t, name + where, _SCALE, nb[name])
-    checks = [(A, "A", _OPERAND.get(d)), (B, "B", _OPERAND.get(d)), (C, "C", _OUTPUT.get(d))]
-    for x, name, dts in checks:
-        _check_tensor(x, name + where, dts, nb.get(name))
-    return tuple(_ptr(x, name + where, dts, nb.get(name)) for x, name, dts in checks)
+    ops, outs = _OPERAND.get(d), _OUTPUT.get(d)
+    _check_tensor(A, "A" + where, ops, nb.get("A"))
+    _check_tensor(B, "B" + where, ops, nb.get("B"))
+    _check_tensor(C, "C" + where, outs, nb.get("C"))
+    return _dev(A, "A" + where), _dev(B, "B" + where), _dev(C, "C" + where)
 
 
 def _plan_dict(pl) -> dict:
@@ -274,7 +290,7 @@ def padd_run(cfg: Config, X, Y, C, rows: int, cols: int, tile_rows: int, tile_co
     code = _abi.lib().padd_run(cfg.handle, _ptr(X, "X", _F32, nb), _ptr(Y, "Y", _F32, nb),
                                _ptr(C, "C", _F32, nb),
                                int(rows), int(cols), int(tile_rows), int(tile_cols), _sched(sched),
-                               ctypes.byref(args) if args is not None else None, _stream(stream))
+                               ctypes.byref(args) if args is not None else None, _stream(stream, cfg.device))
     _check("padd_run", code)
 
 
@@ -292,7 +308,7 @@ def padd_run_multi(cfg: Config, problems, tile_rows: int, tile_cols: int, sched,
         arr[g].rows = int(rows)
         arr[g].cols = int(cols)
     code = _abi.lib().padd_run_multi(cfg.handle, arr, n, int(tile_rows), int(tile_cols), _sched(sched),
-                                     ctypes.byref(args) if args is not None else None, _stream(stream))
+                                     ctypes.byref(args) if args is not None else None, _stream(stream, cfg.device))
     _check("padd_run_multi", code)
 
 
@@ -312,6 +328,6 @@ def pgemm_run_grouped(cfg: Config, problems, dtype, sched, args=None, stream=Non
             arr[g].b_scale = _ptr(pr[7], f"b_scale[{g}]", _SCALE, nb["b_scale"])
     code = _abi.lib().pgemm_run_grouped(cfg.handle, arr, n, _dtype(dtype), _sched(sched),
                                         ctypes.byref(args) if args is not None else None,
-                                        _stream(stream))
+                                        _stream(stream, cfg.device))
     _check("pgemm_run_grouped", code)
 
