@@ -307,10 +307,12 @@ def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
     X = cfg.info["num_xcds"]
     xcc = (w["hw_id"][:G].astype(np.int64) >> 16) & 0xF    # hardware XCC of each program
     q = np.arange(G)
-    # the XCD each program should run on: workgroup i goes to XCD i mod X, and
-    # program q is workgroup q, or workgroup (q mod (G/X)) * X + q / (G/X)
-    # under XCD-major numbering
-    home = q // (G // X) if plan["xcd_major"] else q % X
+    # programs that should share an XCD: workgroups go round robin over the
+    # XCDs (from whichever XCD the hardware starts at), and program q is
+    # workgroup q, or workgroup (q mod (G/X)) * X + q / (G/X) under XCD-major
+    # numbering; share of programs on their group's most common XCD
+    groups = q // (G // X) if plan["xcd_major"] else q % X
+    together = sum(int(np.unique(xcc[groups == g], return_counts=True)[1].max()) for g in np.unique(groups))
     vals, counts = np.unique(tiles, return_counts=True)
     return {"span_us": round(span, 1), "busy_mean_us": round(float(busy.mean()), 1),
             "busy_min_us": round(float(busy.min()), 1), "busy_max_us": round(float(busy.max()), 1),
@@ -324,7 +326,7 @@ def balance(pg, cfg, A, B, C, m, n, k, sched, gs=8, chunk=0):
             "tiles_per_xcc": [int(tiles[xcc == x].sum()) for x in range(X)],
             "programs_per_xcc": [int((xcc == x).sum()) for x in range(X)],
             "xcd_major": bool(plan["xcd_major"]),
-            "xcc_as_numbered": round(float(np.mean(xcc == home)), 4)}
+            "xcc_as_numbered": round(together / G, 4)}
 
 
 def measured_clock(pg, cfg, A, B, C, key):
@@ -663,7 +665,7 @@ def main():
             print(f"# balance {m}x{n}x{k}: " + ", ".join(f"{s_}: idle {v['idle_frac']} skew {v['skew']}"
                                                          for s_, v in row.items()), file=sys.stderr, flush=True)
             ws = row["work_stealing"]
-            print(f"#   {ws['programs']} programs, hardware XCC == p mod X for {ws['xcc_as_numbered']:.0%}; "
+            print(f"#   {ws['programs']} programs, on the XCC of their p mod X class: {ws['xcc_as_numbered']:.0%}; "
                   f"work stealing tiles per XCC {ws['tiles_per_xcc']}, per program {ws['tiles_per_program_hist']}",
                   file=sys.stderr, flush=True)
         del shapes

@@ -161,10 +161,12 @@ typedef struct {
 
 /* pgemm_args.program_order: which workgroup plays which program of a GEMM's
  * static walk (BLOCKED, INTERLEAVED, GROUPED, BLOCKED_GROUPED).  The hardware
- * hands workgroup i of a launch to XCD i mod X.
+ * hands the workgroups of a launch to the XCDs round robin (workgroup i to
+ * XCD (i + o) mod X, o depending on earlier launches), so the workgroups of
+ * one XCD are those of one residue of i mod X.
  *  XCD_MAJOR  when X > 1 divides G, workgroup i plays program
  *             (i mod X) * (G / X) + i / X: the programs of one XCD have
- *             consecutive ids, so in the grouped order the tiles they take in
+ *             consecutive ids (whatever o is), so in the grouped order the tiles they take in
  *             one round form a compact block whose operand panels meet in
  *             that XCD's L2, as a work-stealing range does; otherwise as
  *             DISPATCH.

@@ -193,7 +193,8 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
 }
 
 // Operand panels the first tiles of a static walk's programs touch, summed
-// over the XCDs (workgroup i runs on XCD i mod X): distinct rows of tiles
+// over the XCDs (the workgroups of one XCD are one residue class of i mod X):
+// distinct rows of tiles
 // weighted by the tile's rows (bm) plus distinct columns of tiles weighted by
 // its columns (bn), per problem.  Proportional to the bytes each XCD's L2
 // has to fetch for its programs' first round.  gp / ngemm: the problems of a

@@ -77,9 +77,11 @@ PGS_FN void decode(int kind, int v, int num_pid_m, int num_pid_n, int gs, int& p
     decode_plain(v, num_pid_m, pid_m, pid_n);
 }
 
-// Program numbering of the static walks.  The hardware hands workgroup i of
-// a launch to XCD i mod X (round robin), so workgroups with consecutive ids
-// run on different XCDs and share no L2.  XCD-major numbering gives the
+// Program numbering of the static walks.  The hardware hands the workgroups
+// of a launch to the XCDs round robin (workgroup i to XCD (i + o) mod X, the
+// start o depending on earlier launches), so workgroups with consecutive ids
+// run on different XCDs and share no L2, and one XCD's workgroups are one
+// residue class of i mod X.  XCD-major numbering gives the
 // programs of one XCD consecutive ids: workgroup i plays program
 // (i mod X) * (G / X) + i / X, and the neighbouring tiles of a static walk's
 // round (which share operand panels) meet in one L2, as a work-stealing range
