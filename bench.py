@@ -38,6 +38,7 @@ HEADLINE = ("work_stealing", 8)   # key work_stealing_g8: one tile per claim, as
 CPU_ROWS = 4096
 SETTLE_S = 2.0        # untimed repeats of the headline call before the timed steps (engine clock settles)
 RAGGED_ROUNDS = 3     # interleaved rounds over the schedulers on the ragged shapes
+ROOFLINE_SETTLE_S = 0.4  # untimed repeats of a short kernel before each of its timed batches
 
 # Memory traffic of one launch: what the L2s send to the memory controllers,
 # from rocprofv3 counter passes over `bench.py --profile-only <target>`:
@@ -53,14 +54,22 @@ BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp
 FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp"]
 ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp"]
 TRAFFIC = {
-    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "c112c82ac892bbb9",
-                                    "read_bytes": 1879208160, "write_bytes": 145080880},
-    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "ca0d82f607ea2149",
-                                   "read_bytes": 811890752, "write_bytes": 145407008},
-    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "ca0d82f607ea2149",
-                                                 "read_bytes": 253829632, "write_bytes": 14680320},
-    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "a60d92e4b7b705c1",
-                                   "read_bytes": 536937472, "write_bytes": 268585280},
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "0541bcf0f07b9eff",
+        "read_bytes": 1715144832, "write_bytes": 145547872},
+    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "90b5b579266ee177",
+        "read_bytes": 811824128, "write_bytes": 146922720},
+    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "90b5b579266ee177",
+        "read_bytes": 253828608, "write_bytes": 14680320},
+    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "90b5b579266ee177",
+        "read_bytes": 253792256, "write_bytes": 14680064},
+    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "5509aa2f68eea253",
+        "read_bytes": 536936448, "write_bytes": 268578560},
+    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "5509aa2f68eea253",
+        "read_bytes": 536964608, "write_bytes": 268608768},
+    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "5509aa2f68eea253",
+        "read_bytes": 1073833984, "write_bytes": 268435456},
+    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "5509aa2f68eea253",
+        "read_bytes": 537009152, "write_bytes": 353951488},
 }
 
 
@@ -99,6 +108,7 @@ PROFILE_TARGETS = {
     "fp8_8192cube_work_stealing": ("fp8", (256, 256, 128), "work_stealing"),
     "fp8_256x28672x8192_128x256_work_stealing": ("fp8_skinny", (128, 256, 128), "work_stealing"),
     "fp8_256x28672x8192_128x256_grouped": ("fp8_skinny", (128, 256, 128), "grouped"),
+    "fp8_256x28672x8192_128x256_stream_k": ("fp8_skinny", (128, 256, 128), "stream_k"),
     # ragged bf16 shapes (same inputs as the bench pass) at the default,
     # balanced grid and, with "_grid256", on one program per CU
     "bf16_5120x5120x4096_work_stealing": ("bf16:5120:5120:4096", (256, 256, 64), "work_stealing"),
@@ -108,6 +118,15 @@ PROFILE_TARGETS = {
     "bf16_4864x8000x8192_work_stealing_grid256": ("bf16:4864:8000:8192:256", (256, 256, 64), "work_stealing"),
     "bf16_3000x7000x2048_work_stealing": ("bf16:3000:7000:2048", (256, 256, 64), "work_stealing"),
     "bf16_3000x7000x2048_work_stealing_grid256": ("bf16:3000:7000:2048:256", (256, 256, 64), "work_stealing"),
+    # stream-K (main kernel and fix-up) on the ragged and the under-filled shapes
+    "bf16_5120x5120x4096_stream_k": ("bf16:5120:5120:4096", (256, 256, 64), "stream_k"),
+    "bf16_4864x8000x8192_stream_k": ("bf16:4864:8000:8192", (256, 256, 64), "stream_k"),
+    "bf16_3000x7000x2048_stream_k": ("bf16:3000:7000:2048", (256, 256, 64), "stream_k"),
+    "bf16_8192x1024x8192_stream_k": ("bf16:8192:1024:8192", (256, 256, 64), "stream_k"),
+    "bf16_1024x8192x8192_stream_k": ("bf16:1024:8192:8192", (256, 256, 64), "stream_k"),
+    "bf16_2048x2048x8192_stream_k": ("bf16:2048:2048:8192", (256, 256, 64), "stream_k"),
+    "bf16_8192x1024x8192_work_stealing": ("bf16:8192:1024:8192", (256, 256, 64), "work_stealing"),
+    "bf16_2048x2048x8192_work_stealing": ("bf16:2048:2048:8192", (256, 256, 64), "work_stealing"),
 }
 
 
@@ -374,7 +393,8 @@ def rooflines(flops, head, fp8, add, cfg1):
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "traffic": measured_traffic("bf16_8192cube_work_stealing")}]
     fp8_traffic = {("8192x8192x8192_256x256", "work_stealing"): "fp8_8192cube_work_stealing",
-                   ("256x28672x8192_128x256", "work_stealing"): "fp8_256x28672x8192_128x256_work_stealing"}
+                   ("256x28672x8192_128x256", "work_stealing"): "fp8_256x28672x8192_128x256_work_stealing",
+                   ("256x28672x8192_128x256", "grouped"): "fp8_256x28672x8192_128x256_grouped"}
     for key, sched, bound in [("8192x8192x8192_256x256", "work_stealing", "mfma"),
                               ("256x28672x8192_128x256", "work_stealing", "hbm"),
                               ("256x28672x8192_128x256", "grouped", "hbm"),
@@ -683,16 +703,18 @@ def main():
             dC = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
             f = 2.0 * m * n * k
             nbytes = m * k + k * n + (m + n) * (k // 128) + 2 * m * n
-            # settle the clock, then interleaved rounds of the schedulers
+            # interleaved rounds of the schedulers, each batch right after that
+            # scheduler's own settle (the clock under one kernel's sustained
+            # load differs from another's)
             calls = {}
             for sched in ["grouped", "work_stealing", "stream_k"]:
                 a = pg.make_args(tile=tile, a_scale=dSA, b_scale=dSB)
                 calls[sched] = (a, lambda a=a, sched=sched: pg.pgemm_run(cfg, dA, dB, dC, m, n, k,
                                                                          "fp8_b128_out_bf16", sched, a))
-            settle(calls["grouped"][1], 0.5)
             means = {s_: [] for s_ in calls}
             for _ in range(RAGGED_ROUNDS):
                 for s_, (_, fn) in calls.items():
+                    settle(fn, ROOFLINE_SETTLE_S)
                     means[s_].append(event_batch_ms(fn, args.steps, 3, stream))
             row = {}
             for sched, (a, _) in calls.items():
@@ -717,7 +739,7 @@ def main():
         for tile in [(32, 16), (128, 128)]:
             for sched in ["blocked", "interleaved", "grouped", "work_stealing"]:
                 fn = lambda: pg.padd_run(cfg, X, Y, Z, R, Cc, tile[0], tile[1], sched)  # noqa: E731
-                settle(fn, 0.3)
+                settle(fn, 3 * ROOFLINE_SETTLE_S)
                 ev_mean = float(np.median([event_batch_ms(fn, max(args.steps, 20), 2, stream)
                                            for _ in range(RAGGED_ROUNDS)]))
                 add[f"{tile[0]}x{tile[1]}_{sched}"] = {"gbs": nbytes / (ev_mean * 1e-3) / 1e9,
