@@ -238,7 +238,10 @@ PGEMM_API pgemm_status pgemm_config_destroy(pgemm_config* cfg);
  * or N not a multiple of 8, a tile's panels past 32-bit byte offsets) run
  * on the register-staged kernel, which addresses with 64-bit offsets.
  * A config holds one counter array: calls with the same config on different
- * streams must not overlap.  Errors: NULL pointer, M, N or K < 1,
+ * streams must not overlap.  A config also keeps host-side state between
+ * calls (whether its counters may be dirty, its stream-K workspace, the last
+ * program-numbering decision), so one config serves one host thread at a
+ * time; threads that call concurrently use a config each.  Errors: NULL pointer, M, N or K < 1,
  * group_size < 1, grid < 1 (or < X for work stealing), fp8 without scales or
  * with K % 128 != 0 => PGEMM_ERR_INVALID; a buffer whose byte range (A:
  * M*K, B: K*N elements, C: M*N, scales: (K/128)*M and (K/128)*N bytes) does
