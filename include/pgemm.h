@@ -138,7 +138,9 @@ typedef enum {
 /* Optional per-call arguments; pass NULL for all defaults. */
 typedef struct {
   int tile_m, tile_n, tile_k; /* 0 => default: bf16 256x256x64, fp8 256x256x128 */
-  int group_size;             /* grouped order rows per group; 0 => 8 */
+  int group_size;             /* grouped order rows per group; 0 => 8 for the GEMM, 1 for the
+                                 add (memory order: an add has no operand panels to keep in L2,
+                                 and tiles side by side in a row spread over the memory channels) */
   int grid;                   /* programs; 0 => G0 = number of CUs x workgroups of the selected
                                  kernel one CU holds at once; the GEMM's data-parallel
                                  schedulers then take the balanced grid: the fewest

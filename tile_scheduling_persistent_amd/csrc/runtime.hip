@@ -59,7 +59,15 @@ struct pgemm_config {
 namespace {
 
 constexpr int kDefaultMaxXcds = 16;
-constexpr int kDefaultGroup = 8;
+constexpr int kDefaultGroup = 8;     // GEMM: rows of tiles per group of the grouped order
+// The add: one row of tiles per group, so the grouped order (and the ranges
+// of work stealing) walk the tiles in memory order.  Grouping rows keeps
+// operand panels in L2 for a GEMM; an add reuses nothing, and tiles taken
+// side by side from one row spread over the memory channels, where a group
+// of rows walked column by column puts the tiles in flight in a few narrow
+// column bands (measured at 8192x8192: work stealing 5.6 -> 6.1 TB/s at
+// 128x128 tiles, 4.2 -> 4.8 at 32x16).
+constexpr int kDefaultAddGroup = 1;
 constexpr int kMaxGemmChunk = 64;  // tiles per work-stealing claim, GEMM
 // PGEMM_PIPELINE_DEFAULT takes the ping-pong kernel where it applies.
 constexpr bool kPingPongDefault = false;
@@ -134,12 +142,14 @@ void free_witness(pgemm_config* c) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Common scheduler setup; returns PGEMM_OK or an error (nothing enqueued).
-// balance: GEMM (balanced default grid); the add keeps the full grid.  The
+// balance: GEMM (balanced default grid, group size 8); the add keeps the full
+// grid and takes group size 1 by default.  The
 // program numbering starts as the workgroup order; GEMM paths then call
 // choose_order.
 pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* args,
                         int num_pid_m, int num_pid_n, int default_grid, bool balance,
                         pgk::SchedParams& s) {
+  const int default_group = balance ? kDefaultGroup : kDefaultAddGroup;
   if ((int)sched < 0 || (int)sched > 6) return PGEMM_ERR_INVALID;
   const int64_t T = (int64_t)num_pid_m * num_pid_n;
   if (T > 0x7fffffffLL) return PGEMM_ERR_INVALID;
@@ -151,7 +161,7 @@ pgemm_status make_sched(pgemm_config* cfg, pgemm_sched sched, const pgemm_args* 
   // program: it splits the last round's tiles over all of them).
   if (balance && !(args && args->grid) && sched != PGEMM_SCHED_STREAM_K)
     s.G = pgs::balanced_grid(s.T, s.G, s.X);
-  s.gs = (args && args->group_size) ? args->group_size : kDefaultGroup;
+  s.gs = (args && args->group_size) ? args->group_size : default_group;
   s.num_pid_m = num_pid_m;
   s.num_pid_n = num_pid_n;
   s.counters = cfg->counters;
