@@ -60,6 +60,12 @@ def test_invalid_arguments_enqueue_nothing():
     assert run(a, b, c, 64, 64, 64, 0, 2, ctypes.byref(args), s) == _abi.ERR_INVALID
     args = pg.make_args(grid=cfg.info["num_xcds"] - 1)
     assert run(a, b, c, 64, 64, 64, 0, 3, ctypes.byref(args), s) == _abi.ERR_INVALID
+    for order in (-1, 3):                                                     # program_order
+        args = pg.make_args(program_order=order)
+        assert run(a, b, c, 64, 64, 64, 0, 2, ctypes.byref(args), s) == _abi.ERR_INVALID
+        pl = _abi.pgemm_plan()
+        assert L.pgemm_plan_gemm(cfg.handle, a, b, c, 64, 64, 64, 0, 2, ctypes.byref(args),
+                                 ctypes.byref(pl)) == _abi.ERR_INVALID
     # fp8 without scales, or K not a multiple of 128
     assert run(a, b, c, 64, 64, 128, 2, 0, None, s) == _abi.ERR_INVALID
     sync()
