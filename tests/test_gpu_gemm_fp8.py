@@ -63,6 +63,22 @@ def test_small_shapes(tile):
             assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"{(M, N, K)} {sched} {tile}")
 
 
+@pytest.mark.parametrize("tile", [(128, 128, 128), (256, 256, 128), (128, 256, 128)])
+def test_program_order_keeps_c(tile):
+    """Static walks with their programs numbered XCD-major and in workgroup
+    order: the same tiles per program, so the same bits of C, and both within
+    the oracle's bound."""
+    M, N, K = 1100, 4352, 512
+    qa, sa, qb, sb = make_inputs(M, N, K, 77)
+    Cref, Abs = og.gemm_fp8_b128(qa, sa, qb, sb)
+    for sched in ["blocked", "interleaved", "grouped", "blocked_grouped"]:
+        Cx = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile, program_order="xcd_major")
+        Cd = run_fp8(qa, sa, qb, sb, M, N, K, sched, tile, program_order="dispatch")
+        assert Cx.guards_intact() and Cd.guards_intact()
+        assert np.array_equal(Cx.body_bits(), Cd.body_bits()), (sched, tile)
+        assert_abs_bound(Cx.as_f64().reshape(M, N), Cref, Abs, FP8_TOL, f"{sched} {tile} XCD-major")
+
+
 def test_unsupported_shapes_are_rejected():
     cfg = config()
     qa, sa, qb, sb = make_inputs(64, 24, 128, 3)

@@ -46,6 +46,20 @@ def _run(shapes, ab, out, sched, tile, **kw):
     return outs
 
 
+@pytest.mark.parametrize("si", [0, 3])
+def test_grouped_program_order_keeps_c(si):
+    """Several problems in one launch under both program numberings of the
+    static walks: every problem's C bit-identical."""
+    shapes = SETS[si]
+    ab = _data(shapes, 4500 + 10 * si)
+    for sched in ["blocked", "interleaved", "grouped", "blocked_grouped"]:
+        got = {o: _run(shapes, ab, "bf16_out_bf16", sched, (128, 128, 64), program_order=o)
+               for o in ("xcd_major", "dispatch")}
+        for g, (Cx, Cd) in enumerate(zip(got["xcd_major"], got["dispatch"])):
+            assert Cx.guards_intact() and Cd.guards_intact()
+            assert np.array_equal(Cx.body_bits(), Cd.body_bits()), (si, sched, g)
+
+
 @pytest.mark.parametrize("tile", [(128, 128, 64), (256, 256, 64)])
 @pytest.mark.parametrize("out", ["bf16_out_f32", "bf16_out_bf16"])
 @pytest.mark.parametrize("si", range(len(SETS)))
