@@ -1,5 +1,5 @@
 /* Driver for a sanitizer build of the oracle's C GEMM (oracle/gemm_ref.c,
- * included as is): small shapes, edge sizes among them, each checked element
+ * included as is): small shapes, edge sizes among them (empty ones too), each checked element
  * by element against a plain triple loop over the same definition (fp64 sum
  * over k in ascending order, and the |A|.|B| bound), so that AddressSanitizer
  * and UndefinedBehaviorSanitizer see every index the oracle computes.
@@ -17,13 +17,14 @@ static double draw(uint64_t* s) {
 }
 
 int main(void) {
-  const int64_t sizes[] = {1, 2, 3, 17, 64, 65};
+  const int64_t sizes[] = {0, 1, 2, 3, 17, 64, 65};  /* 0: empty A, B or C; K = 0 gives C = 0 */
+  const int ns = (int)(sizeof(sizes) / sizeof(sizes[0]));
   uint64_t seed = 7;
   int bad = 0;
-  for (int a = 0; a < 6; ++a)
-    for (int b = 0; b < 6; ++b)
-      for (int c = 0; c < 6; ++c) {
-        const int64_t M = sizes[a], N = sizes[b], K = sizes[(a + b + c) % 6];
+  for (int a = 0; a < ns; ++a)
+    for (int b = 0; b < ns; ++b)
+      for (int c = 0; c < ns; ++c) {
+        const int64_t M = sizes[a], N = sizes[b], K = sizes[(a + b + c) % ns];
         double* A = malloc(sizeof(double) * M * K);
         double* B = malloc(sizeof(double) * K * N);
         double* C = malloc(sizeof(double) * M * N);
