@@ -20,11 +20,15 @@
 #include "../../include/pgemm.h"
 #include "common.hpp"
 
-// The program numbering choose_order last made for a single GEMM, by its
-// scheduler parameters and tile.
+// A program numbering choose_order made, by the scheduler parameters, the
+// tile and (several problems per launch) each problem's first tile id and
+// tile grid.
+static_assert(PGEMM_MAX_PROBLEMS == pgk::kMaxGemmProblems, "header states the problem limit");
+constexpr int kOrderKey = 10 + 3 * pgk::kMaxGemmProblems;
+constexpr int kOrderCache = 8;
 struct OrderChoice {
   bool valid = false;
-  int key[10];
+  int key[kOrderKey];
   int xcd_major;
 };
 
@@ -42,7 +46,8 @@ struct pgemm_config {
   float* ws;          // stream-K partial-sum workspace (device), grown on demand
   size_t ws_bytes;
   unsigned char* scratch;  // this device's address of the static `scratch` array
-  OrderChoice order_choice;  // the last single-GEMM numbering decision (choose_order)
+  OrderChoice order_choice[kOrderCache];  // recent numbering decisions (choose_order)
+  int order_next = 0;                     // slot the next new decision replaces
   // witness buffers (device)
   int64_t w_tiles;
   int w_programs;
@@ -258,18 +263,23 @@ void choose_order(pgemm_config* cfg, const pgemm_args* args, pgk::SchedParams& s
     s.xcd_major = 1;
     return;
   }
-  OrderChoice& c = cfg->order_choice;
-  const int key[10] = {s.kind, s.T, s.G, s.X, s.gs, s.num_pid_m, s.num_pid_n, bm, bn, ngemm};
-  if (ngemm == 0 && c.valid && memcmp(c.key, key, sizeof(key)) == 0) {
-    s.xcd_major = c.xcd_major;
-    return;
+  int key[kOrderKey] = {s.kind, s.T, s.G, s.X, s.gs, s.num_pid_m, s.num_pid_n, bm, bn, ngemm};
+  for (int g = 0; g < ngemm; ++g) {
+    key[10 + 3 * g] = gp[g].tile0;
+    key[11 + 3 * g] = gp[g].npm;
+    key[12 + 3 * g] = gp[g].npn;
   }
+  for (const OrderChoice& c : cfg->order_choice)
+    if (c.valid && memcmp(c.key, key, sizeof(key)) == 0) {
+      s.xcd_major = c.xcd_major;
+      return;
+    }
   s.xcd_major = first_round_panels(s, 1, bm, bn, gp, ngemm) < first_round_panels(s, 0, bm, bn, gp, ngemm);
-  if (ngemm == 0) {
-    memcpy(c.key, key, sizeof(key));
-    c.xcd_major = s.xcd_major;
-    c.valid = true;
-  }
+  OrderChoice& c = cfg->order_choice[cfg->order_next];
+  cfg->order_next = (cfg->order_next + 1) % kOrderCache;
+  memcpy(c.key, key, sizeof(key));
+  c.xcd_major = s.xcd_major;
+  c.valid = true;
 }
 
 // Kernel a GEMM call takes, from shapes, formats, tile and pointer alignment
