@@ -55,22 +55,22 @@ BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp
 FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp", "runtime.hip"]
 ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp", "runtime.hip"]
 TRAFFIC = {
-    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "e1e469629e2e7b4e",
-        "read_bytes": 1715144832, "write_bytes": 145547872},
-    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "f29065502952e0d1",
-        "read_bytes": 811824128, "write_bytes": 146922720},
-    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "f29065502952e0d1",
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "d7206a9d76c58585",
+        "read_bytes": 1699993792, "write_bytes": 147780160},
+    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
+        "read_bytes": 811935744, "write_bytes": 146816960},
+    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
         "read_bytes": 253828608, "write_bytes": 14680320},
-    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "f29065502952e0d1",
-        "read_bytes": 253792256, "write_bytes": 14680064},
-    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "a505b3602ea0ca3b",
-        "read_bytes": 536936448, "write_bytes": 268591360},
-    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "a505b3602ea0ca3b",
-        "read_bytes": 536964608, "write_bytes": 268566400},
-    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "a505b3602ea0ca3b",
-        "read_bytes": 1073832960, "write_bytes": 268435456},
-    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "a505b3602ea0ca3b",
-        "read_bytes": 537009408, "write_bytes": 326444992},
+    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
+        "read_bytes": 253793280, "write_bytes": 14680064},
+    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
+        "read_bytes": 536937472, "write_bytes": 268587264},
+    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
+        "read_bytes": 536964608, "write_bytes": 268578048},
+    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
+        "read_bytes": 1073833984, "write_bytes": 268435456},
+    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
+        "read_bytes": 537009472, "write_bytes": 327121344},
 }
 
 
