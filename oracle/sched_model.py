@@ -256,18 +256,20 @@ def _take(chunk, cnt, x, n, G, X):
 
 
 def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
-                chunk=1, seed: int = 0, speeds: Sequence[float] = None):
+                chunk=1, seed: int = 0, speeds: Sequence[float] = None, claims_out=None):
     """One possible work-stealing execution.
 
     Programs run concurrently; the interleaving is drawn at random (or, with
     ``speeds``, the program with the earliest finish time claims next).
-    ``chunk`` is the tiles per claim, or PAIRS.
+    ``chunk`` is the tiles per claim, or PAIRS.  ``claims_out``, a list,
+    receives per program the claims it made on each counter ([G][X]).
     Returns (per-program list of (v, pid_m, pid_n), final counters)."""
     T = num_pid_m * num_pid_n
     if G < X:
         raise ValueError("work stealing needs at least one program per XCD")
     ranges = ws_ranges(T, X)
     cnt = [0] * X
+    made = [[0] * X for _ in range(G)]
     seqs: List[List[Tuple[int, int, int]]] = [[] for _ in range(G)]
     active = list(range(G))
     clock = [0.0] * G
@@ -279,6 +281,7 @@ def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
             p = min(active, key=lambda q: (clock[q], q))
         x = p % X
         s, e = ranges[x]
+        made[p][x] += 1
         got = _take(chunk, cnt, x, e - s, G, X)
         if got is None:
             active.remove(p)
@@ -287,6 +290,8 @@ def ws_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, gs: int = 8,
             seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
         if speeds is not None:
             clock[p] += speeds[p] * (got[1] - got[0])
+    if claims_out is not None:
+        claims_out[:] = made
     return seqs, cnt
 
 
@@ -318,15 +323,18 @@ def wsx_counter_bounds(T: int, G: int, X: int, homes: Sequence[int],
 
 
 def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence[int],
-                 gs: int = 8, chunk=1, seed: int = 0, speeds: Sequence[float] = None):
+                 gs: int = 8, chunk=1, seed: int = 0, speeds: Sequence[float] = None,
+                 claims_out=None):
     """One possible execution of work stealing across XCDs.  ``homes[p]`` is
     the counter program p starts on.  The interleaving is random, or with
     ``speeds`` the program with the earliest clock (then the lowest id)
-    claims next; a failing claim takes no time.  Returns (per-program list
-    of (v, pid_m, pid_n), final counters)."""
+    claims next; a failing claim takes no time.  ``claims_out``, a list,
+    receives per program the claims it made on each counter ([G][X]).
+    Returns (per-program list of (v, pid_m, pid_n), final counters)."""
     T = num_pid_m * num_pid_n
     ranges = ws_ranges(T, X)
     cnt = [0] * X
+    made = [[0] * X for _ in range(G)]
     seqs: List[List[Tuple[int, int, int]]] = [[] for _ in range(G)]
     cur = [homes[p] % X for p in range(G)]
     passed = [0] * G
@@ -340,6 +348,7 @@ def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence
             p = min(active, key=lambda q: (clock[q], q))
         x = cur[p]
         s, e = ranges[x]
+        made[p][x] += 1
         got = _take(chunk, cnt, x, e - s, G, X)
         if got is None:
             passed[p] += 1
@@ -361,15 +370,61 @@ def wsx_simulate(num_pid_m: int, num_pid_n: int, G: int, X: int, homes: Sequence
             seqs[p].append((v,) + grouped_decode(v, num_pid_m, num_pid_n, gs))
         if speeds is not None:
             clock[p] += speeds[p] * (got[1] - got[0])
+    if claims_out is not None:
+        claims_out[:] = made
     return seqs, cnt
+
+
+def claim_of(i: int, n: int, G: int, X: int, chunk=1) -> int:
+    """The claim (counted from 0) that hands out tile i (relative to the
+    start) of a counter range of n tiles: claims of ``chunk`` consecutive
+    tiles, or under PAIRS the pair / single-tile claims of pair_claim."""
+    if chunk == PAIRS:
+        L = pair_span(n, G, X)
+        return i // 2 if i < L else L // 2 + (i - L)
+    return i // chunk
+
+
+def check_claim_counts(claims: Sequence[Sequence[int]], owner: Sequence[int],
+                       counters: Sequence[int], homes: Sequence[int], T: int, G: int, X: int,
+                       chunk=1, across: bool = False) -> None:
+    """Claim accounting of a complete work-stealing launch.  claims[p][c] is
+    the number of claims (counter increments) program p made on counter c;
+    owner[v] the program that computed tile v; homes[p] the counter program p
+    started on.  Every claim adds one step (``chunk`` tiles, one under PAIRS)
+    to its counter, so each final counter is the step times the claims made
+    on it.  The claims of p on c that handed out no tile are its failing
+    claims there: exactly one on its home counter (claims go on there until
+    one fails), and on any other counter none (per-XCD work stealing) or at
+    most one (across XCDs: each counter not yet passed is claimed from at
+    most once more after it was seen not exhausted)."""
+    step = 1 if chunk == PAIRS else chunk
+    got: List[List[set]] = [[set() for _ in range(X)] for _ in range(G)]
+    for x, (s, e) in enumerate(ws_ranges(T, X)):
+        for v in range(s, e):
+            got[owner[v]][x].add(claim_of(v - s, e - s, G, X, chunk))
+    for c in range(X):
+        made = sum(claims[p][c] for p in range(G))
+        if counters[c] != step * made:
+            raise AssertionError(f"counter {c} ended at {counters[c]}, the claims on it add {step * made}")
+    for p in range(G):
+        for c in range(X):
+            fails = claims[p][c] - len(got[p][c])
+            if c == homes[p] % X:
+                if fails != 1:
+                    raise AssertionError(f"program {p}: {fails} failing claims on its home counter {c}")
+            elif fails < 0 or fails > (1 if across else 0):
+                raise AssertionError(f"program {p}: {fails} failing claims on counter {c} (home {homes[p] % X})")
 
 
 def check_wsx_execution(visits: Sequence[int], owner: Sequence[int], local_order: Sequence[int],
                         counters: Sequence[int], homes: Sequence[int], T: int, G: int, X: int,
-                        chunk=1) -> None:
+                        chunk=1, claims=None) -> None:
     """Invariants of every correct launch of work stealing across XCDs.
     visits / owner / local_order are indexed by tile id; homes[p] is the
-    counter program p started on."""
+    counter program p started on; claims[p][c], if given, the claims p made
+    on counter c (check_claim_counts, which fixes each final counter
+    exactly)."""
     for v in range(T):
         if visits[v] != 1:
             raise AssertionError(f"tile {v} visited {visits[v]} times")
@@ -392,6 +447,8 @@ def check_wsx_execution(visits: Sequence[int], owner: Sequence[int], local_order
     for x, (lo, hi) in enumerate(wsx_counter_bounds(T, G, X, homes, chunk)):
         if not (lo <= counters[x] <= hi):
             raise AssertionError(f"counter {x} ended at {counters[x]}, outside [{lo}, {hi}]")
+    if claims is not None:
+        check_claim_counts(claims, owner, counters, homes, T, G, X, chunk, across=True)
 
 
 def check_partition(seqs: Sequence[Sequence[Tuple[int, int, int]]],
@@ -418,11 +475,12 @@ def check_partition(seqs: Sequence[Sequence[Tuple[int, int, int]]],
 
 def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
                        local_order: Sequence[int], counters: Sequence[int],
-                       T: int, G: int, X: int, chunk=1) -> None:
+                       T: int, G: int, X: int, chunk=1, claims=None) -> None:
     """Invariants every correct work-stealing launch satisfies (the exact
     assignment depends on timing).  Arrays are indexed by tile id v:
     visits[v] = times computed, owner[v] = program, local_order[v] = its
-    position in that program's sequence."""
+    position in that program's sequence; claims[p][c], if given, the claims
+    program p made on counter c (check_claim_counts)."""
     ranges = ws_ranges(T, X)
     for v in range(T):
         if visits[v] != 1:
@@ -446,6 +504,8 @@ def check_ws_execution(visits: Sequence[int], owner: Sequence[int],
     want = ws_final_counters(T, G, X, chunk)
     if list(counters[:X]) != want:
         raise AssertionError(f"final counters {list(counters[:X])} != {want}")
+    if claims is not None:
+        check_claim_counts(claims, owner, counters, [p % X for p in range(G)], T, G, X, chunk)
 
 
 def streamk_dp_tiles(T: int, G: int) -> int:

@@ -33,7 +33,11 @@ static int static_walk(int kind, int pm, int pn, int G, int gs) {
 // (pgs::ws_claim), so these threads run the kernels' own claim and sweep code.
 struct HostOps {
   std::atomic<int>* c;
-  int fetch_add(int x, int v) { return c[x].fetch_add(v, std::memory_order_relaxed); }
+  int* made;  // claims this thread made, per counter
+  int fetch_add(int x, int v) {
+    ++made[x];
+    return c[x].fetch_add(v, std::memory_order_relaxed);
+  }
   int load(int x) { return c[x].load(std::memory_order_relaxed); }
   void store(int x, int v) { c[x].store(v, std::memory_order_relaxed); }
 };
@@ -41,8 +45,9 @@ struct HostOps {
 // G threads walk the tiles as a kernel's programs do (Walker::first / next):
 // a claim, the tiles of that claim in order, then the next claim, until a
 // claim returns -1.  Thread p starts on counter homes[p]; `across` is work
-// stealing across XCDs.  Prints the homes, the final counters and, per tile,
-// visits, owner and the tile's position in its owner's sequence.
+// stealing across XCDs.  Prints the homes, the final counters, per tile its
+// visits, owner and position in its owner's sequence, and last the claims
+// each thread made on each counter (thread-major).
 static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
                          const std::vector<int>& homes, bool self_reset = false) {
   const int T = pm * pn;
@@ -51,10 +56,11 @@ static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
   std::vector<std::atomic<int>> visits(T);
   for (auto& v : visits) v.store(0);
   std::vector<int> owner(T, -1), order(T, -1);
+  std::vector<int> made((size_t)G * X, 0);
   std::vector<std::thread> th;
   for (int p = 0; p < G; ++p) {
     th.emplace_back([&, p] {
-      HostOps ops{cnt.data()};
+      HostOps ops{cnt.data(), made.data() + (size_t)p * X};
       pgs::WsWalk w;
       pgs::ws_start(w, homes[p], T, X);
       const int reset_at = self_reset ? pgs::ws_last_claim_value(w.n, chunk, G, X, w.x) : -1;
@@ -77,6 +83,9 @@ static int claim_threads(int pm, int pn, int G, int X, int chunk, bool across,
   for (int x = 0; x < X; ++x) std::printf(" %d", cnt[x].load());
   std::printf("\n");
   for (int v = 0; v < T; ++v) std::printf("%d %d %d %d\n", v, visits[v].load(), owner[v], order[v]);
+  std::printf("claims:");
+  for (int m : made) std::printf(" %d", m);
+  std::printf("\n");
   return 0;
 }
 

@@ -78,17 +78,26 @@ def test_ws_threads_satisfy_model_invariants(harness, pm, pn, G, X, chunk):
     _check_ws(out, pm, pn, G, X, chunk)
 
 
+def _claims(out, G, X):
+    """The harness's last line: the claims each thread made on each counter."""
+    assert out[-1].startswith("claims:")
+    made = list(map(int, out[-1].split(":")[1].split()))
+    assert len(made) == G * X
+    return [made[p * X:(p + 1) * X] for p in range(G)]
+
+
 def _check_ws(out, pm, pn, G, X, chunk):
     homes = list(map(int, out[0].split(":")[1].split()))
     assert homes == [p % X for p in range(G)]
     counters = list(map(int, out[1].split(":")[1].split()))
     T = pm * pn
-    rows = [tuple(map(int, l.split())) for l in out[2:]]
+    rows = [tuple(map(int, l.split())) for l in out[2:-1]]
     assert len(rows) == T
     visits = [r[1] for r in rows]
     owner = [r[2] for r in rows]
     order = [r[3] for r in rows]
-    sm.check_ws_execution(visits, owner, order, counters, T, G, X, sm.PAIRS if chunk < 0 else chunk)
+    sm.check_ws_execution(visits, owner, order, counters, T, G, X, sm.PAIRS if chunk < 0 else chunk,
+                          claims=_claims(out, G, X))
 
 
 @pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (19, 32, 256, 8, 1),
@@ -105,10 +114,11 @@ def _check_wsx(out, pm, pn, G, X, chunk):
     homes = list(map(int, out[0].split(":")[1].split()))
     counters = list(map(int, out[1].split(":")[1].split()))
     T = pm * pn
-    rows = [tuple(map(int, l.split())) for l in out[2:]]
+    rows = [tuple(map(int, l.split())) for l in out[2:-1]]
     assert len(rows) == T and len(homes) == G
     sm.check_wsx_execution([r[1] for r in rows], [r[2] for r in rows], [r[3] for r in rows],
-                           counters, homes, T, G, X, sm.PAIRS if chunk < 0 else chunk)
+                           counters, homes, T, G, X, sm.PAIRS if chunk < 0 else chunk,
+                           claims=_claims(out, G, X))
 
 
 @pytest.mark.parametrize("T,nk,G", [(10, 4, 4), (16, 3, 4), (1, 7, 8), (7, 1, 8), (608, 128, 256),
@@ -231,9 +241,9 @@ def _check_wsr(out, pm, pn, G, X, chunk):
     assert reset_at == [f - step for f in final], (reset_at, final)
     counters = list(map(int, out[2].split(":")[1].split()))
     assert counters == [0] * X
-    rows = [tuple(map(int, l.split())) for l in out[3:]]
+    rows = [tuple(map(int, l.split())) for l in out[3:-1]]
     sm.check_ws_execution([r[1] for r in rows], [r[2] for r in rows], [r[3] for r in rows],
-                          final, T, G, X, c)
+                          final, T, G, X, c, claims=_claims(out, G, X))
 
 
 @pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (32, 32, 256, 8, 1), (19, 32, 256, 8, 1),

@@ -449,3 +449,83 @@ def test_balanced_grid_planted_mistake():
     rounding) takes an extra round on a wave-quantised shape."""
     T, G, X = 608, 256, 8
     assert sm.ws_rounds(T, sm.balanced_grid(T, G, X) - X, X) == sm.ws_rounds(T, G, X) + 1
+
+
+def test_claim_counts_hand_worked():
+    """One counter (X = 1), T = 4, G = 2, single claims: program 0 takes tiles
+    0 and 2, program 1 tiles 1 and 3, then each makes its failing claim:
+    three claims each, and the counter ends at 6."""
+    owner = [0, 1, 0, 1]
+    sm.check_claim_counts([[3], [3]], owner, [6], [0, 0], 4, 2, 1)
+    with pytest.raises(AssertionError):             # a claim left out of the count
+        sm.check_claim_counts([[3], [2]], owner, [6], [0, 0], 4, 2, 1)
+    with pytest.raises(AssertionError):             # two failing claims by program 1
+        sm.check_claim_counts([[2], [4]], owner, [6], [0, 0], 4, 2, 1)
+    # chunk 2: program 0 takes [0, 2), program 1 [2, 4): two claims each, counter 8
+    sm.check_claim_counts([[2], [2]], [0, 0, 1, 1], [8], [0, 0], 4, 2, 1, chunk=2)
+    # pairs with P = 2 programs: L = 2 * min(2, 2 * (2 // 2)) = 4, claims 0 and 1
+    # are the pairs (0, 1) and (2, 3); with one each, the counter ends at 4
+    sm.check_claim_counts([[2], [2]], [1, 1, 0, 0], [4], [0, 0], 4, 2, 1, chunk=sm.PAIRS)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(5, 2, 8, 4, 1), (19, 32, 256, 8, 1), (9, 7, 11, 8, 1),
+                                             (33, 5, 16, 8, 4), (20, 20, 256, 8, "pairs"),
+                                             (13, 11, 24, 8, "pairs")])
+def test_ws_claim_counts_of_simulated_runs(pm, pn, G, X, chunk):
+    chunk = sm.PAIRS if chunk == "pairs" else chunk
+    T = pm * pn
+    for seed in range(3):
+        claims = []
+        seqs, cnt = sm.ws_simulate(pm, pn, G, X, chunk=chunk, seed=seed, claims_out=claims)
+        v, o, r = _witness(seqs, T)
+        sm.check_ws_execution(v, o, r, cnt, T, G, X, chunk, claims=claims)
+        assert all(claims[p][c] == 0 for p in range(G) for c in range(X) if c != p % X)
+
+
+@pytest.mark.parametrize("pm,pn,G,X,chunk", [(4, 4, 8, 4, 1), (5, 7, 3, 8, 1), (16, 16, 256, 8, 1),
+                                             (13, 23, 64, 8, 2), (32, 4, 12, 8, 4), (13, 11, 24, 8, "pairs")])
+def test_wsx_claim_counts_of_simulated_runs(pm, pn, G, X, chunk):
+    chunk = sm.PAIRS if chunk == "pairs" else chunk
+    T = pm * pn
+    rng = random.Random(G * 17 + X)
+    for homes in ([p % X for p in range(G)], [0] * G, [rng.randrange(X) for _ in range(G)]):
+        for seed in range(3):
+            claims = []
+            seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, chunk=chunk, seed=seed, claims_out=claims)
+            v, o, r = _wsx_arrays(seqs, T)
+            sm.check_wsx_execution(v, o, r, cnt, homes, T, G, X, chunk, claims=claims)
+
+
+def test_claim_count_checker_catches_planted_mistakes():
+    pm, pn, G, X = 6, 6, 8, 4
+    T = pm * pn
+    homes = [0, 0, 0, 1, 1, 2, 3, 3]
+    claims = []
+    seqs, cnt = sm.wsx_simulate(pm, pn, G, X, homes, seed=3, claims_out=claims)
+    v, o, r = _wsx_arrays(seqs, T)
+    sm.check_claim_counts(claims, o, cnt, homes, T, G, X, across=True)
+    # an extra failing claim on a home counter, the counter raised to match
+    bad = [list(row) for row in claims]
+    bad[0][0] += 1
+    with pytest.raises(AssertionError):
+        sm.check_claim_counts(bad, o, [cnt[0] + 1] + list(cnt[1:]), homes, T, G, X, across=True)
+    # a claim booked on the wrong counter
+    bad = [list(row) for row in claims]
+    bad[3][1] -= 1
+    bad[3][2] += 1
+    with pytest.raises(AssertionError):
+        sm.check_claim_counts(bad, o, cnt, homes, T, G, X, across=True)
+    # a program that never failed at home (its failing claim unrecorded)
+    bad = [list(row) for row in claims]
+    bad[5][2] -= 1
+    with pytest.raises(AssertionError):
+        sm.check_claim_counts(bad, o, [cnt[0], cnt[1], cnt[2] - 1, cnt[3]], homes, T, G, X, across=True)
+    # per-XCD work stealing allows no claim away from home
+    ws_claims = []
+    seqs, cnt = sm.ws_simulate(pm, pn, G, X, seed=1, claims_out=ws_claims)
+    v, o, r = _witness(seqs, T)
+    bad = [list(row) for row in ws_claims]
+    bad[1][2] += 1
+    with pytest.raises(AssertionError):
+        sm.check_claim_counts(bad, o, [cnt[0], cnt[1], cnt[2] + 1, cnt[3]], [p % X for p in range(G)],
+                              T, G, X)
