@@ -347,7 +347,8 @@ PGEMM_API pgemm_status padd_run_multi(pgemm_config* cfg, const padd_problem* pro
 /* Witness buffers for PGEMM_DEBUG_WITNESS launches: per tile (up to
  * max_tiles) visit count, owner program and position in the owner's
  * sequence; per program (up to max_programs) start / end wall-clock ticks,
- * shader clock cycles, hardware id and tile count.  Allocated on device by this call and owned by
+ * shader clock cycles, hardware id, tile count and, under work stealing, the
+ * claims it made on each counter.  Allocated on device by this call and owned by
  * the config. */
 PGEMM_API pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_programs);
 
@@ -364,6 +365,8 @@ typedef struct {      /* host arrays supplied by the caller */
   int32_t* counters;  /* [counter_capacity] work-stealing counters after the launch */
   int64_t* cycles;    /* [programs] shader clock cycles from program start to end; divided by
                          (t_end - t_start) / wall_clock_khz it is the clock the program ran at */
+  int32_t* claims;    /* [programs][8] work-stealing claims (counter increments) each program made
+                         on counters 0..7, failing ones included; zero for the static kinds */
 } pgemm_witness;
 
 /* Synchronise `hip_stream` and copy the witness of the last launch into the

@@ -168,7 +168,7 @@ def test_slow_xcc_rebalanced_by_stealing_across_xccs():
         if sched == "work_stealing_xcc":
             homes = [int(h) % X for h in xcc]
             sm.check_wsx_execution(w["visits"][:T].tolist(), owner.tolist(), w["order"][:T].tolist(),
-                                   w["counters"].tolist(), homes, T, G, X)
+                                   w["counters"].tolist(), homes, T, G, X, claims=w["claims"][:G, :X].tolist())
     note(f"tiles of range 0 computed off XCC 0: {stolen}")
     assert stolen["work_stealing_xcc"] > (e0 - s0) // 4, stolen
 

@@ -111,11 +111,11 @@ def test_grouped_schedule(sched):
                 assert owner[v] == p and order[v] == i, (sched, v)
     elif sched == "work_stealing":
         sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                              T, G, X)
+                              T, G, X, claims=w["claims"][:G, :X].tolist())
     else:
         homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
         sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                               homes, T, G, X)
+                               homes, T, G, X, claims=w["claims"][:G, :X].tolist())
 
 
 def test_grouped_errors():

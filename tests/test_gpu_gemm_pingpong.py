@@ -101,11 +101,11 @@ def test_pingpong_schedule_exactly_once(sched, shape):
                 assert owner[v] == p and order[v] == i, (sched, v)
     elif sched == "work_stealing":
         sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                              T, G, X, 1)
+                              T, G, X, 1, claims=w["claims"][:G, :X].tolist())
     else:
         homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
         sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                               homes, T, G, X, 1)
+                               homes, T, G, X, 1, claims=w["claims"][:G, :X].tolist())
     # the witness build computes the same bits as the timed build
     C2 = torch.empty_like(C)
     pg.pgemm_run(cfg, A, B, C2, M, N, K, "bf16_out_bf16", sched, args)

@@ -82,11 +82,11 @@ def test_multi_add_schedule(sched, tile):
                 assert owner[v] == p and order[v] == i, (sched, v)
     elif sched == "work_stealing":
         sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                              T, G, X, chunk)
+                              T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
     else:
         homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
         sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
-                               homes, T, G, X, chunk)
+                               homes, T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
 
 
 def test_multi_add_one_problem_equals_single_call():

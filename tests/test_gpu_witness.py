@@ -32,11 +32,11 @@ def _check(w, kind, pm, pn, G, X, gs, chunk=1):
             assert w["n_tiles"][p] == len(seq)
     elif kind == "work_stealing":
         sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(),
-                              w["counters"].tolist(), T, G, X, chunk)
+                              w["counters"].tolist(), T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
     else:
         homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
         sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(),
-                               w["counters"].tolist(), homes, T, G, X, chunk)
+                               w["counters"].tolist(), homes, T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
 
 
 def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0, order="default"):

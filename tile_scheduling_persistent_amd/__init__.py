@@ -202,10 +202,11 @@ class Config:
             "n_tiles": np.zeros(programs, np.int32),
             "counters": np.zeros(self.info["counter_capacity"], np.int32),
             "cycles": np.zeros(programs, np.int64),
+            "claims": np.zeros((programs, _abi.MAX_STEAL_COUNTERS), np.int32),
         }
         w = _abi.pgemm_witness()
         for k in ("visits", "owner", "order", "t_start", "t_end", "hw_id", "n_tiles", "counters",
-                  "cycles"):
+                  "cycles", "claims"):
             setattr(w, k, out[k].ctypes.data)
         w.tiles = tiles
         w.programs = programs

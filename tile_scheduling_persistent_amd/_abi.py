@@ -59,8 +59,11 @@ class pgemm_witness(ctypes.Structure):
         ("t_start", ctypes.c_void_p), ("t_end", ctypes.c_void_p),
         ("hw_id", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("programs", ctypes.c_int32), ("counters", ctypes.c_void_p),
-        ("cycles", ctypes.c_void_p),
+        ("cycles", ctypes.c_void_p), ("claims", ctypes.c_void_p),
     ]
+
+
+MAX_STEAL_COUNTERS = 8  # columns of pgemm_witness.claims
 
 
 class pgemm_plan(ctypes.Structure):

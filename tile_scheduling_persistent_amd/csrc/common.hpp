@@ -20,6 +20,7 @@ struct Witness {
   long long* cycles;  // [G] shader clock cycles from program start to end
   int* hw_id;         // [G] hardware placement of the program
   int* n_tiles;       // [G] tiles the program computed
+  int* claims;        // [G][kMaxStealCounters] claims the program made on each counter
 };
 
 // Work-stealing counter x lives at counters[x * kCounterStride]: one 256-byte
@@ -208,7 +209,9 @@ __device__ __forceinline__ void spin_ns(int ns, int wall_khz) {
 // broadcast, so the claim's state stays uniform (scalar registers).
 struct ThreadOps {
   int* counters;
+  int* made = nullptr;  // witness launches: claims per counter (kMaxStealCounters), counted by the claiming thread
   __device__ __forceinline__ int fetch_add(int c, int v) {
+    if (made && c < kMaxStealCounters) made[c] += 1;
     return __hip_atomic_fetch_add(counters + c * kCounterStride, v, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -222,10 +225,13 @@ struct ThreadOps {
 
 struct WaveOps {
   int* counters;
+  int* made = nullptr;  // witness launches: claims per counter, counted by lane 0
   __device__ __forceinline__ int fetch_add(int c, int v) {
     int r = 0;
-    if ((threadIdx.x & 63) == 0)
+    if ((threadIdx.x & 63) == 0) {
+      if (made && c < kMaxStealCounters) made[c] += 1;
       r = __hip_atomic_fetch_add(counters + c * kCounterStride, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return __builtin_amdgcn_readfirstlane(r);
   }
   __device__ __forceinline__ int load(int c) {
@@ -253,6 +259,7 @@ struct Walker {
   int end;         // static: end of the walk
   pgs::WsWalk ws;  // work stealing: the walk over the counters
   int reset_at;    // per-XCD work stealing with self_reset: see pgs::ws_claim
+  int* claim_row = nullptr;  // witness launches: this program's claims per counter
 
   __device__ __forceinline__ int nx() const { return s.X > 0 ? s.X : 1; }
 
@@ -272,7 +279,7 @@ struct Walker {
 
   // One claim (s.chunk tiles, or a pair / single under paired claims);
   // returns the first claimed id or -1, and sets ws.cend to the claim's end.
-  __device__ __forceinline__ int claim() { return claim_with(ThreadOps{s.counters}); }
+  __device__ __forceinline__ int claim() { return claim_with(ThreadOps{s.counters, claim_row}); }
 
   // End (exclusive) of the claim that starts at tile v (any thread may call it).
   __device__ __forceinline__ int claim_end(int v) const { return pgs::ws_claim_end(v, s.chunk, s.T, nx()); }
@@ -304,11 +311,11 @@ struct Walker {
   // first() / next() called by every lane of one wave (the result and the
   // walk's state are the same in every lane).
   __device__ __forceinline__ int first_wave() {
-    if (pgs::work_stealing(s.kind)) return claim_with(WaveOps{s.counters});
+    if (pgs::work_stealing(s.kind)) return claim_with(WaveOps{s.counters, claim_row});
     return first_static();
   }
   __device__ __forceinline__ int next_wave(int v) {
-    if (pgs::work_stealing(s.kind)) return v + 1 < ws.cend ? v + 1 : claim_with(WaveOps{s.counters});
+    if (pgs::work_stealing(s.kind)) return v + 1 < ws.cend ? v + 1 : claim_with(WaveOps{s.counters, claim_row});
     return next_static(v);
   }
 

@@ -129,6 +129,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmParams P) {
   const unsigned short* __restrict__ B = static_cast<const unsigned short*>(P.B);
 
   Walker walker(P.s, prog);
+  if (WITNESS) walker.claim_row = P.w.claims + (size_t)prog * kMaxStealCounters;
   long long t_start = 0, c_start = 0;
   if (WITNESS && tid == 0) {
     t_start = wall_ticks();

@@ -136,6 +136,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_kernel(GemmParams P) {
   void* Cc = P.C;
 
   Walker walker(P.s, prog);
+  if (WITNESS) walker.claim_row = P.w.claims + (size_t)prog * kMaxStealCounters;
   long long t_start = 0, c_start = 0;
   if (WITNESS && tid == 0) {
     t_start = wall_ticks();

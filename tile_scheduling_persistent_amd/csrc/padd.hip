@@ -54,6 +54,7 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   const int rows = P.rows, cols = P.cols;
   const bool ws = pgs::work_stealing(P.s.kind);
   Walker walker(P.s, prog);
+  if (WITNESS) walker.claim_row = P.w.claims + (size_t)prog * kMaxStealCounters;
   long long t_start = 0, c_start = 0;
   if (WITNESS && tid == 0) {
     t_start = wall_ticks();

@@ -59,6 +59,7 @@ struct pgemm_config {
   long long* w_cycles;
   int* w_hw_id;
   int* w_n_tiles;
+  int* w_claims;  // [w_programs][kMaxStealCounters]
 };
 
 namespace {
@@ -135,10 +136,10 @@ struct DeviceGuard {
 
 void free_witness(pgemm_config* c) {
   void* ptrs[] = {c->w_visits, c->w_owner, c->w_order, c->w_t_start,
-                  c->w_t_end, c->w_cycles, c->w_hw_id, c->w_n_tiles};
+                  c->w_t_end, c->w_cycles, c->w_hw_id, c->w_n_tiles, c->w_claims};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
-  c->w_visits = c->w_owner = c->w_order = c->w_hw_id = c->w_n_tiles = nullptr;
+  c->w_visits = c->w_owner = c->w_order = c->w_hw_id = c->w_n_tiles = c->w_claims = nullptr;
   c->w_t_start = c->w_t_end = c->w_cycles = nullptr;
   c->w_tiles = 0;
   c->w_programs = 0;
@@ -376,8 +377,10 @@ pgemm_status make_witness(pgemm_config* cfg, const pgemm_args* args, const pgk::
   w.cycles = cfg->w_cycles;
   w.hw_id = cfg->w_hw_id;
   w.n_tiles = cfg->w_n_tiles;
-  // visits start at 0, owner / order at -1 (fill kernels, no memset nodes)
+  w.claims = cfg->w_claims;
+  // visits and claims start at 0, owner / order at -1 (fill kernels, no memset nodes)
   hipError_t e = pgk::launch_fill_i32(w.visits, s.T, 0, stream);
+  if (e == hipSuccess) e = pgk::launch_fill_i32(w.claims, s.G * pgk::kMaxStealCounters, 0, stream);
   if (e == hipSuccess) e = pgk::launch_fill_i32(w.owner, s.T, -1, stream);
   if (e == hipSuccess) e = pgk::launch_fill_i32(w.order, s.T, -1, stream);
   if (e == hipSuccess) e = pgk::launch_fill_i32(w.n_tiles, s.G, 0, stream);
@@ -802,6 +805,7 @@ pgemm_status pgemm_witness_enable(pgemm_config* cfg, int64_t max_tiles, int max_
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_cycles, sizeof(long long) * p);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_hw_id, sizeof(int) * p);
   if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_n_tiles, sizeof(int) * p);
+  if (e == hipSuccess) e = hipMalloc((void**)&cfg->w_claims, sizeof(int) * p * pgk::kMaxStealCounters);
   if (e != hipSuccess) {
     free_witness(cfg);
     return from_hip(e);
@@ -829,6 +833,7 @@ pgemm_status pgemm_witness_read(pgemm_config* cfg, pgemm_witness* out, void* hip
       {out->t_end, cfg->w_t_end, 8 * p},        {out->hw_id, cfg->w_hw_id, 4 * p},
       {out->cycles, cfg->w_cycles, 8 * p},
       {out->n_tiles, cfg->w_n_tiles, 4 * p},
+      {out->claims, cfg->w_claims, 4 * p * pgk::kMaxStealCounters},
   };
   for (const Copy& c : cps) {
     if (!c.dst || c.bytes == 0) continue;
