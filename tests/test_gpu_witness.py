@@ -1,9 +1,10 @@
 """GPU schedule witness: every tile computed exactly once under every scheduler;
 static schedules equal the oracle's model tile for tile; work-stealing runs
 satisfy the model's invariants (owner on the right XCD, increasing claims,
-final counters); work stealing across XCDs satisfies its own (each program
-starts on the counter of the hardware XCC it ran on, recorded by the
-witness)."""
+final counters, and each counter equal to the claims the programs recorded
+on it with one failing claim per program at home); work stealing across
+XCDs satisfies its own (each program starts on the counter of the hardware
+XCC it ran on, recorded by the witness)."""
 import numpy as np
 import pytest
 import torch
@@ -30,13 +31,14 @@ def _check(w, kind, pm, pn, G, X, gs, chunk=1):
             for i, (v, _, _) in enumerate(seq):
                 assert owner[v] == p and order[v] == i, (kind, v, owner[v], p, order[v], i)
             assert w["n_tiles"][p] == len(seq)
+        assert not w["claims"][:G].any(), f"{kind}: a static walk recorded claims"
     elif kind == "work_stealing":
-        sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(),
-                              w["counters"].tolist(), T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
+        sm.check_ws_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
+                              T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
     else:
         homes = [((int(h) >> 16) & 0xF) % X for h in w["hw_id"][:G]]
-        sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(),
-                               w["counters"].tolist(), homes, T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
+        sm.check_wsx_execution(visits.tolist(), owner.tolist(), order.tolist(), w["counters"].tolist(),
+                               homes, T, G, X, chunk, claims=w["claims"][:G, :X].tolist())
 
 
 def _gemm_witness(M, N, K, tile, sched, gs=8, grid=0, order="default"):
