@@ -44,7 +44,7 @@ ROOFLINE_SETTLE_S = 0.4  # untimed repeats of a short kernel before each of its 
 # from rocprofv3 counter passes over `bench.py --profile-only <target>`:
 # TCC_EA0_RDREQ_DRAM_32B_sum and TCC_EA0_WRREQ_WRITE_DRAM_32B_sum (32-byte
 # units of read and write requests bound for the memory controllers, a
-# 128-byte request counting 4; median of the last 4 dispatches) x 32 bytes.
+# 128-byte request counting 4; median of the 9 dispatches of a pass) x 32 bytes.
 # On a plain 256 MiB device copy (`bench.py --copy-calibration`) they read
 # exactly 256 MiB each way, so no calibration factor applies.  Hits in the
 # Infinity Cache, which sits on the memory side, are included: no counter
@@ -55,22 +55,22 @@ BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp
 FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp", "runtime.hip"]
 ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp", "runtime.hip"]
 TRAFFIC = {
-    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "d7206a9d76c58585",
-        "read_bytes": 1699993792, "write_bytes": 147780160},
-    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
-        "read_bytes": 811935744, "write_bytes": 146816960},
-    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "139fb94531a09f99",
+        "read_bytes": 1721012608, "write_bytes": 147854592},
+    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
+        "read_bytes": 811835008, "write_bytes": 144877184},
+    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
         "read_bytes": 253828608, "write_bytes": 14680320},
-    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "2ff8f451dd893be3",
-        "read_bytes": 253793280, "write_bytes": 14680064},
-    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
-        "read_bytes": 536937472, "write_bytes": 268587264},
-    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
-        "read_bytes": 536964608, "write_bytes": 268578048},
-    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
-        "read_bytes": 1073833984, "write_bytes": 268435456},
-    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "350f841657d4eb79",
-        "read_bytes": 537009472, "write_bytes": 327121344},
+    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
+        "read_bytes": 253792256, "write_bytes": 14680064},
+    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
+        "read_bytes": 536939520, "write_bytes": 268593920},
+    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
+        "read_bytes": 536969216, "write_bytes": 268715776},
+    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
+        "read_bytes": 1073832960, "write_bytes": 268435456},
+    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
+        "read_bytes": 537005952, "write_bytes": 329532672},
 }
 
 
