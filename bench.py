@@ -119,6 +119,12 @@ PROFILE_TARGETS = {
     "bf16_4864x8000x8192_work_stealing_grid256": ("bf16:4864:8000:8192:256", (256, 256, 64), "work_stealing"),
     "bf16_3000x7000x2048_work_stealing": ("bf16:3000:7000:2048", (256, 256, 64), "work_stealing"),
     "bf16_3000x7000x2048_work_stealing_grid256": ("bf16:3000:7000:2048:256", (256, 256, 64), "work_stealing"),
+    "bf16_4864x8000x8192_grouped": ("bf16:4864:8000:8192", (256, 256, 64), "grouped"),
+    "bf16_4864x8000x8192_blocked_grid256": ("bf16:4864:8000:8192:256", (256, 256, 64), "blocked"),
+    "bf16_4864x8000x8192_grouped_grid256": ("bf16:4864:8000:8192:256", (256, 256, 64), "grouped"),
+    "bf16_3000x7000x2048_blocked": ("bf16:3000:7000:2048", (256, 256, 64), "blocked"),
+    "bf16_3000x7000x2048_blocked_grid256": ("bf16:3000:7000:2048:256", (256, 256, 64), "blocked"),
+    "bf16_3000x7000x2048_interleaved_grid256": ("bf16:3000:7000:2048:256", (256, 256, 64), "interleaved"),
     # stream-K (main kernel and fix-up) on the ragged and the under-filled shapes
     "bf16_5120x5120x4096_stream_k": ("bf16:5120:5120:4096", (256, 256, 64), "stream_k"),
     "bf16_4864x8000x8192_stream_k": ("bf16:4864:8000:8192", (256, 256, 64), "stream_k"),
