@@ -57,12 +57,12 @@ ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp", "runtime.hip"]
 TRAFFIC = {
     "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "139fb94531a09f99",
         "read_bytes": 1721012608, "write_bytes": 147854592},
-    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
-        "read_bytes": 811835008, "write_bytes": 144877184},
-    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
-        "read_bytes": 253828608, "write_bytes": 14680320},
-    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "396806f02519ff37",
-        "read_bytes": 253792256, "write_bytes": 14680064},
+    "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
+        "read_bytes": 811933376, "write_bytes": 144911136},
+    "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
+        "read_bytes": 253829248, "write_bytes": 14680320},
+    "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
+        "read_bytes": 253793792, "write_bytes": 14680064},
     "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
         "read_bytes": 536939520, "write_bytes": 268593920},
     "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
