@@ -55,8 +55,8 @@ BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp
 FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp", "runtime.hip"]
 ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp", "runtime.hip"]
 TRAFFIC = {
-    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "139fb94531a09f99",
-        "read_bytes": 1721012608, "write_bytes": 147854592},
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "2fb5ac13df11ac3c",
+        "read_bytes": 1771079680, "write_bytes": 145744864},
     "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
         "read_bytes": 811933376, "write_bytes": 144911136},
     "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
@@ -99,6 +99,14 @@ PROFILE_TARGETS = {
     "bf16_8192cube_work_stealing": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing"),
     "bf16_8192cube_work_stealing_pingpong": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing", "pingpong"),
     "bf16_8192cube_work_stealing_four_wave": ("bf16n:8192:8192:8192", (256, 256, 64), "work_stealing", "four_wave"),
+    "bf16_8192cube_grouped": ("bf16n:8192:8192:8192", (256, 256, 64), "grouped"),
+    "bf16_8192cube_interleaved": ("bf16n:8192:8192:8192", (256, 256, 64), "interleaved"),
+    "torch_bf16_8192cube": ("bf16n:8192:8192:8192", None, "torch"),
+    # the same shape on separate all-zero A and B: operands that draw little
+    # power, so the chip holds its full clock (the kernel's own ceiling)
+    "bf16_8192cube_zeros_work_stealing": ("bf16z:8192:8192:8192", (256, 256, 64), "work_stealing"),
+    "bf16_8192cube_zeros_grouped": ("bf16z:8192:8192:8192", (256, 256, 64), "grouped"),
+    "torch_bf16_8192cube_zeros": ("bf16z:8192:8192:8192", None, "torch"),
     "bf16_512cube_fp32_blocked": ("bf16f:512:512:512", (128, 128, 64), "blocked"),
     "add_8192sq_128x128_blocked": ("add", (128, 128), "blocked"),
     "add_8192sq_128x128_work_stealing": ("add", (128, 128), "work_stealing"),
@@ -149,13 +157,15 @@ def profile_only(name, steps, warmup, settle_s):
     pipeline = PROFILE_TARGETS[name][3] if len(PROFILE_TARGETS[name]) > 3 else "default"
     cfg = pg.Config(0)
     stream = torch.cuda.current_stream()
-    if kind.split(":")[0] in ("bf16", "bf16n", "bf16f"):
+    if kind.split(":")[0] in ("bf16", "bf16n", "bf16f", "bf16z"):
         from synthetic import bf16_bits_normal, bf16_bits_uniform
         dims = [int(x) for x in kind.split(":")[1:]]
         m, n, k = dims[:3]
         grid = dims[3] if len(dims) > 3 else 0
         if kind.startswith("bf16n:"):
             ab = bf16_bits_normal((m, k), 1030), bf16_bits_normal((k, n), 1031)
+        elif kind.startswith("bf16z:"):
+            ab = np.zeros((m, k), np.uint16), np.zeros((k, n), np.uint16)
         elif kind.startswith("bf16f:"):
             ab = bf16_bits_uniform((m, k), 1010), bf16_bits_uniform((k, n), 1011)
         else:
@@ -164,9 +174,13 @@ def profile_only(name, steps, warmup, settle_s):
         rb = torch.from_numpy(ab[1].view(np.int16)).to("cuda:0").view(torch.bfloat16)
         out = "bf16_out_f32" if kind.startswith("bf16f:") else "bf16_out_bf16"
         rc = torch.empty((m, n), dtype=torch.float32 if out == "bf16_out_f32" else torch.bfloat16, device="cuda:0")
-        a = pg.make_args(tile=tile, grid=grid, pipeline=pipeline)
         nbytes, work = 2 * (m * k + k * n) + rc.element_size() * m * n, 2.0 * m * n * k
-        fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, out, sched, a)  # noqa: E731
+        if sched == "torch":  # hipBLASLt on the same operands, for comparison
+            a = None
+            fn = lambda: torch.matmul(ra, rb, out=rc)  # noqa: E731
+        else:
+            a = pg.make_args(tile=tile, grid=grid, pipeline=pipeline)
+            fn = lambda: pg.pgemm_run(cfg, ra, rb, rc, m, n, k, out, sched, a)  # noqa: E731
     elif kind == "add":
         R = Cc = 8192
         X = torch.from_numpy(f32_normal((R, Cc), 2001)).to("cuda:0")
@@ -191,7 +205,8 @@ def profile_only(name, steps, warmup, settle_s):
     out = {"profile_only": name, "event_ms_mean": round(ev_mean, 5), "event_ms_median": round(float(np.median(d)), 5),
            "batch_ms_per_call": round(batch, 5),
            "plan": (pg.plan_gemm(cfg, m, n, k, "bf16_out_f32" if kind.startswith("bf16f:") else "bf16_out_bf16",
-                                 sched, a) if kind.split(":")[0] in ("bf16", "bf16n", "bf16f") else None),
+                                 sched, a) if kind.split(":")[0] in ("bf16", "bf16n", "bf16f", "bf16z")
+                   and sched != "torch" else None),
            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ev_mean * 1e-3) / 1e9, 1)}
     if work:
         out["tflops"] = round(work / (ev_mean * 1e-3) / 1e12, 2)

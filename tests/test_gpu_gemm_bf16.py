@@ -137,25 +137,31 @@ def test_ragged_all_schedulers(shape):
 
 def test_8192_all_schedulers():
     """Workload 3: 8192^3, normal(0,1) bf16, bf16 C, 256x256x64, every scheduler and
-    group sizes 8 / 16; the first scheduler's C against the oracle on every
-    element, bitwise equality across schedulers."""
+    group sizes 8 / 16 on the direct-to-LDS kernel: the first scheduler's C against the
+    oracle on every element, bitwise equality across schedulers.  The register-staged
+    kernel (32x32 MFMA blocks, so its own rounding order) is checked against the
+    oracle on every element as well."""
     M = N = K = 8192
     a = bf16_bits_normal((M, K), 1030)
     b = bf16_bits_normal((K, N), 1031)
+    note("oracle on all of C (8192x8192)")
+    Cref, Abs = og.gemm_bf16(a, b)
     ref_bits = None
-    for sched, gs, fl in [("blocked", 0, 0), ("interleaved", 0, 0), ("grouped", 8, 0), ("grouped", 16, 0),
-                          ("work_stealing", 8, 0), ("work_stealing", 16, 0), ("blocked_grouped", 8, 0),
-                          ("work_stealing_xcc", 8, 0),
-                          ("work_stealing", 8, pg._abi.DEBUG_REGISTER_STAGED)]:
-        C = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, (256, 256, 64), group_size=gs,
-                     debug_flags=fl)
+    for sched, gs in [("blocked", 0), ("interleaved", 0), ("grouped", 8), ("grouped", 16),
+                      ("work_stealing", 8), ("work_stealing", 16), ("blocked_grouped", 8),
+                      ("work_stealing_xcc", 8)]:
+        C = run_gemm(a, b, M, N, K, "bf16_out_bf16", sched, (256, 256, 64), group_size=gs)
         assert C.guards_intact()
         bits = C.body_bits()
         if ref_bits is None:
-            _full_check(a, b, C, M, N, BF16_TOL, f"8192^3 {sched}")
+            assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, f"8192^3 {sched}")
             ref_bits = bits
         else:
             assert np.array_equal(bits, ref_bits), f"8192^3: {sched}/{gs} differs"
+    C = run_gemm(a, b, M, N, K, "bf16_out_bf16", "work_stealing", (256, 256, 64), group_size=8,
+                 debug_flags=pg._abi.DEBUG_REGISTER_STAGED)
+    assert C.guards_intact()
+    assert_abs_bound(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, "8192^3 register-staged")
 
 
 @pytest.mark.parametrize("tile", [(128, 128, 64), (256, 256, 64)])

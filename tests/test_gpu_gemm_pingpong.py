@@ -1,8 +1,10 @@
 """GPU parity of the eight-wave ping-pong bf16 kernel (PGEMM_PIPELINE_PINGPONG)
 through the C ABI: against the oracle on ragged and K-tail shapes under every
-scheduler, bit-identical to the four-wave kernel (the per-tile K order is the
-same) on those shapes and at full size, every tile computed exactly once
-(witness), and graph replays equal to the eager call."""
+scheduler and at full size (sampled rows), bit-identical across schedulers (the
+per-tile K order does not depend on who computes the tile), every tile
+computed exactly once (witness), and graph replays equal to the eager call.
+It multiplies 32x32 MFMA blocks while the four-wave kernel uses 16x16 ones, so
+the two round differently and are compared through the oracle only."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,8 @@ import tile_scheduling_persistent_amd as pg
 from oracle import gemm as og
 from oracle import sched_model as sm
 from synthetic import bf16_bits_normal, bf16_bits_uniform
-from tests.gpu_util import BF16_TOL, Guarded, assert_within, config, dev_bf16, note, sync
+from oracle.codecs import bf16_to_f64
+from tests.gpu_util import BF16_TOL, Guarded, assert_abs_bound, assert_within, config, dev_bf16, note, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -49,26 +52,38 @@ def test_pingpong_against_oracle(out):
         a = bf16_bits_uniform((M, K), 6000 + si)
         b = bf16_bits_uniform((K, N), 6100 + si)
         Cref, Abs = og.gemm_bf16(a, b)
-        four = _run(a, b, M, N, K, out, "work_stealing", "four_wave").body_bits()
+        first = None
         for sched in SCHEDS:
             C = _run(a, b, M, N, K, out, sched, "pingpong")
             assert_within(C.as_f64().reshape(M, N), Cref, Abs, BF16_TOL, out == "bf16_out_bf16",
                           f"pingpong {(M, N, K)} {sched} {out}")
-            assert np.array_equal(C.body_bits(), four), f"pingpong {(M, N, K)} {sched} differs from four-wave"
+            if first is None:
+                first = C.body_bits()
+            else:
+                assert np.array_equal(C.body_bits(), first), f"pingpong {(M, N, K)} {sched} differs from {SCHEDS[0]}"
 
 
 @pytest.mark.parametrize("shape", [(8192, 8192, 8192), (5120, 5120, 4096), (4864, 8000, 8192),
                                    (3000, 7000, 2048)])
 def test_pingpong_full_size_bit_identical(shape):
-    """Full-size workloads: every scheduler (and paired claims) on the
-    ping-pong kernel gives the bits of the four-wave kernel, whose C the bf16
-    parity tests check against the oracle on every element."""
+    """Full-size workloads: the ping-pong kernel's C under grouped against the
+    oracle on sampled rows (both edges of every tile row, random rows), and
+    every other scheduler (and paired claims) bit-identical to it."""
     M, N, K = shape
     if shape == (8192, 8192, 8192):
         a, b = bf16_bits_normal((M, K), 1030), bf16_bits_normal((K, N), 1031)
     else:
         a, b = bf16_bits_uniform((M, K), 1040 + M), bf16_bits_uniform((K, N), 1041 + N)
-    ref = _run(a, b, M, N, K, "bf16_out_bf16", "grouped", "four_wave").body_bits()
+    C = _run(a, b, M, N, K, "bf16_out_bf16", "grouped", "pingpong")
+    rows = {0, M - 1}
+    for t in range(0, M, 256):
+        rows |= {t, min(t + 255, M - 1)}
+    rows |= set(np.random.default_rng(M).integers(0, M, size=16).tolist())
+    rows = np.array(sorted(rows))
+    note(f"oracle on {len(rows)} rows of C ({shape})")
+    Cref, Abs = og.gemm_f64_sampled(bf16_to_f64(a), bf16_to_f64(b), rows, np.arange(N))
+    assert_abs_bound(C.as_f64().reshape(M, N)[rows, :], Cref, Abs, BF16_TOL, f"pingpong {shape} grouped")
+    ref = C.body_bits()
     for sched, chunk in [(s, 0) for s in SCHEDS] + [("work_stealing", pg._abi.CLAIM_PAIRS)]:
         got = _run(a, b, M, N, K, "bf16_out_bf16", sched, "pingpong", claim_chunk=chunk).body_bits()
         assert np.array_equal(got, ref), f"{shape} {sched} chunk={chunk}"

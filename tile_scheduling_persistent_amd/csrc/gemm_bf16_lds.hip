@@ -14,30 +14,39 @@
 //    on across tiles, like the scheduler's iteration counter of "[Feature]
 //    Introduce tile scheduler", TileLang PR #2441).  The next tile is
 //    claimed when the loader sets up the last slab of the current one.
-//  * One barrier per slab, after its third k-step: each wave has waited for
-//    its own loads of slab g+1 (vmcnt) and finished every read of slab g, so
-//    after the barrier slab g+1 is complete and slab g's stage is free.  The
-//    last k-step then reads slab g+1's first fragments and starts slab g+2's
-//    loads; the loads are issued by hand and the barrier carries no memory
-//    fence (gemm_device.hpp), so the compiler adds no wait for loads in
-//    flight before LDS reads.
-//  * The issue order inside a k-step is fixed by hand (scheduling
-//    barriers): after each MFMA come its share of the next k-step's fragment
-//    reads and, in k-steps 0 and 3, a load, so LDS reads, global loads and
+//  * A slab is two 32-deep k-steps, run as four phases of half a k-step
+//    each (one half of the B^T blocks).  One barrier per slab, after its
+//    third phase: each wave has waited for its own loads of slab g+1 (vmcnt)
+//    and finished every read of slab g, so after the barrier slab g+1 is
+//    complete and slab g's stage is free.  The last phase then reads slab
+//    g+1's first fragments and starts slab g+2's loads; the loads are issued
+//    by hand and the barrier carries no memory fence (gemm_device.hpp), so
+//    the compiler adds no wait for loads in flight before LDS reads.
+//  * The issue order inside a phase is fixed by hand (scheduling barriers):
+//    after each MFMA come its share of the fragment reads the next phase
+//    needs and, in phases 0 and 3, a load, so LDS reads, global loads and
 //    their latencies hide behind the MFMA pipeline instead of stalling the
-//    wave in bursts; each load has at least two k-steps to land.  The
+//    wave in bursts; each load has at least two phases to land.  The
 //    loader's bookkeeping (tile switch, claim, buffer resources) is scalar
 //    pointer arithmetic except on edge slabs.
 //  * A stays [m][k] in LDS; its 16-byte chunks are XOR-swizzled by the row
 //    so that the ds_read_b128 operand reads hit distinct banks (see bf16_swz_a).
 //  * B stays [k][n] in LDS, as it is in memory (chunk c of row k stored at
-//    c ^ 4*(k & 3)); the k-contiguous operand the MFMA needs is produced by
-//    ds_read_b64_tr_b16: within each 16-lane group, lane i points at row
-//    K0 + i/4, columns N0 + 4*(i%4) .. +3, and lane j receives rows
-//    K0 .. K0+3 of column N0 + j.  Two such reads give a lane its 8 k-values.
-//  * Each wave owns a (BM/2) x (BN/2) sub-tile as 32x32 MFMA blocks
-//    (v_mfma_f32_32x32x16_bf16) with the B^T block as the first operand, so
-//    a lane's 4 consecutive accumulators are 4 consecutive columns of C.
+//    c ^ 4*(k & 3) ^ 2*((k >> 3) & 1), see swz_b16); the k-contiguous
+//    operand the MFMA needs is produced by ds_read_b64_tr_b16: within each
+//    16-lane group, lane i points at row K0 + i/4, columns N0 + 4*(i%4) ..
+//    +3, and lane j receives rows K0 .. K0+3 of column N0 + j.  Two such
+//    reads give a lane its 8 k-values; the four 16-lane groups take k rows
+//    8g .. 8g+7 of the 32-deep step.
+//  * Each wave owns a (BM/2) x (BN/2) sub-tile as 16x16 MFMA blocks
+//    (v_mfma_f32_16x16x32_bf16) with the B^T block as the first operand, so
+//    lane l holds row l % 16 of a block and its 4 accumulators are 4
+//    consecutive columns of C (4*(l/16) .. +3).  Against 32x32x16 blocks
+//    the 16x16x32 form moves half the fp32 accumulator bytes through the
+//    register file per product; on this chip, whose clock is held down by
+//    its power limit under these GEMMs, that buys clock: register-only MFMA
+//    loops on random bf16 data ran 11% more flops at the same board power,
+//    and this kernel 3-5% more TFLOP/s on normal(0,1) operands.
 //  * Rows past M (A) and past K (B) read as zero through the buffer range
 //    check; the K tail and columns past N are masked per lane, only on the
 //    slabs / tiles that need it; C stores outside the matrix are dropped by
@@ -49,9 +58,14 @@
 namespace pgk {
 namespace {
 
+// Physical chunk of logical chunk c in row k of B for the 16x16 fragment
+// reads: 32 lanes of a transposing read touch rows k0..k0+3 and k0+8..k0+11
+// at two adjacent chunks; bits 2-3 from k & 3 and bit 1 from bit 3 of k put
+// those 16 chunks in 16 distinct slots of a 256-byte window.
+__device__ __forceinline__ int swz_b16(int k, int c) { return c ^ (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -64,8 +78,8 @@ template <int BM, int BN, int BK, int NST>
 struct Shape {
   static constexpr int WM = 2, WN = 2;
   static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int SM = TM / 32, SN = TN / 32;
-  static constexpr int KK = BK / 16;                  // MFMA k-steps per slab
+  static constexpr int SM = TM / 16, SN = TN / 16;   // 16x16 MFMA blocks
+  static constexpr int KK = BK / 32;                  // MFMA k-steps per slab
   static constexpr int A_ROW = BK * 2;                // bytes per LDS row of A
   static constexpr int A_BYTES = BM * A_ROW;          // one stage of A
   static constexpr int B_ROW = BN * 2;                // bytes per LDS row of B
@@ -94,9 +108,9 @@ template <int BM, int BN, int BK, int NST, bool OUT_BF16, bool WITNESS, bool SK,
 __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   using S = Shape<BM, BN, BK, NST>;
   static_assert(NST == 2, "two LDS stages: the loads of slab g+1 run during slab g");
+  static_assert(S::KK == 2 && S::SN % 2 == 0, "two 32-deep k-steps per slab, B blocks in two halves");
   constexpr int NA = S::A_INSTR, NB = S::B_INSTR, NL = NA + NB;  // loads per wave per slab
   constexpr int NMF = S::SN * S::SM;                             // MFMAs per k-step
-  constexpr int NRD = 2 * S::SN + S::SM;                         // LDS reads per k-step
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* s_first = reinterpret_cast<int*>(smem + NST * S::STAGE);
@@ -143,7 +157,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     for (int i = 0; i < NB; ++i) {
       const int q = wave * NB + i;
       const int row = q * S::B_RPI + lane / S::B_CPR;
-      bchk[i] = bf16_swz_b(row, lane % S::B_CPR);
+      bchk[i] = swz_b16(row, lane % S::B_CPR);
       boff[i] = (unsigned)row * (unsigned)Nx * 2u + (unsigned)bchk[i] * 16u;
     }
   };
@@ -151,21 +165,21 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   // ---- LDS read offsets ----
-  const int l32 = lane & 31;
+  const int l16 = lane & 15;
   unsigned rd_a[S::KK];
 #pragma unroll
   for (int kk = 0; kk < S::KK; ++kk) {
-    const int row = wm * S::TM + l32;
-    rd_a[kk] = (unsigned)(row * S::A_ROW + bf16_swz_a<BK>(row, kk * 2 + (lane >> 5)) * 16);
+    const int row = wm * S::TM + l16;  // + sm*16: swizzle unchanged
+    rd_a[kk] = (unsigned)(row * S::A_ROW + bf16_swz_a<BK>(row, kk * 4 + (lane >> 4)) * 16);
   }
   unsigned rd_b[S::SN];
   {
     const int g = lane >> 4, i16 = lane & 15, a = i16 & 3, e = i16 >> 2;
-    const int krow = (g >> 1) * 8 + e;  // + kk*16 + h*4 (multiples of 4: swizzle unchanged)
+    const int krow = g * 8 + e;  // + kk*32 + h*4: k & 3 and bit 3 of k unchanged
 #pragma unroll
     for (int sn = 0; sn < S::SN; ++sn) {
-      const int n = wn * S::TN + sn * 32 + (g & 1) * 16 + 4 * a;
-      const int c = bf16_swz_b(krow, n >> 3);
+      const int n = wn * S::TN + sn * 16 + 4 * a;
+      const int c = swz_b16(krow, n >> 3);
       rd_b[sn] = (unsigned)(S::A_BYTES + krow * S::B_ROW + c * 16 + 8 * (a & 1));
     }
   }
@@ -303,32 +317,39 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
       load_lds16(rB, sb + (unsigned)(S::A_BYTES + (wave * NB + d - NA) * 1024), bo[d - NA]);
   };
 
-  f32x16 acc[S::SN][S::SM];
+  f32x4 acc[S::SN][S::SM];
   // MFMA operand fragments, double-buffered by k-step; B^T fragments arrive
   // as two halves (4 k-values each).
   i16x4 bh[2][S::SN][2];
   bf16x8 af[2][S::SM];
 
-  // LDS read r of k-step kk into slot: B^T block 0 first, then the A
-  // blocks, then the other B^T blocks (the order the MFMAs consume them).
-  auto read = [&](int st, int kk, int slot, int r) {
+  // LDS reads of k-step kk into slot: A block sm (one ds_read_b128), half h
+  // of B^T block sn (one transposing read).
+  auto read_a = [&](int st, int kk, int slot, int sm) {
     const unsigned char* sbase = smem + st * S::STAGE;
-    if (r >= 2 && r < 2 + S::SM) {
-      const int sm = r - 2;
-      af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 32 * S::A_ROW);
-    } else {
-      const int b = r < 2 ? r : r - S::SM;
-      const int sn = b >> 1, h = b & 1;
-      const unsigned char* p = sbase + rd_b[sn] + kk * 16 * S::B_ROW + h * 4 * S::B_ROW;
-      bh[slot][sn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-    }
+    af[slot][sm] = *reinterpret_cast<const bf16x8*>(sbase + rd_a[kk] + sm * 16 * S::A_ROW);
+  };
+  auto read_b = [&](int st, int kk, int slot, int sn, int h) {
+    const unsigned char* sbase = smem + st * S::STAGE;
+    const unsigned char* p = sbase + rd_b[sn] + kk * 32 * S::B_ROW + h * 4 * S::B_ROW;
+    bh[slot][sn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
   };
 
+  // MFMA j of k-step `slot`: B^T block j / SM against A block j % SM.  The
+  // instruction is written out so that its accumulator operand is an AGPR
+  // tuple (left to itself the register allocator moved accumulators between
+  // AGPRs and VGPRs around every slab).  The compiler's hazard logic does not
+  // see into it, so the code around it keeps the hazards away: a block's
+  // accumulator is next read as SrcC NMF MFMAs later, the operand fragments
+  // come straight from LDS reads (the compiler waits for those reads before
+  // the asm, its inputs), the accumulators are zeroed at the start of a tile
+  // with padding after them, and the epilogue reads them only after
+  // mfma_results_ready.  tests/test_kernel_hazards.py checks the built code.
   auto mfma = [&](int slot, int j) {
     const int sn = j / S::SM, sm = j % S::SM;
     const bf16x8 b = __builtin_bit_cast(
         bf16x8, __builtin_shufflevector(bh[slot][sn][0], bh[slot][sn][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, af[slot][sm], acc[sn][sm], 0, 0, 0);
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[sn][sm]) : "v"(b), "v"(af[slot][sm]));
   };
 
   auto epilogue = [&](int m0, int n0) {
@@ -338,32 +359,25 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     rows = rows < 0 ? 0 : rows;  // never negative: an empty range drops the stores
     const auto rC = rsrc(static_cast<unsigned char*>(Cc) + ((size_t)m0 * N + n0) * esz,
                          (unsigned)((size_t)rows * N - n0) * esz);
-    const int r0 = wm * S::TM + l32;
-    const int c0 = wn * S::TN + 4 * (lane >> 5);
+    // lane l holds row l % 16 of a block, columns 4*(l/16) .. +3
+    const int r0 = wm * S::TM + l16;
+    const int c0 = wn * S::TN + 4 * (lane >> 4);
     const unsigned eb = (unsigned)(r0 * N + c0) * esz;
-    const unsigned rstep = 32u * (unsigned)N * esz;
+    const unsigned rstep = 16u * (unsigned)N * esz;
     const int ncols = N - n0;
-    if (OUT_BF16) {
-      const int hi = lane >> 5;
-      const unsigned eb2 = (unsigned)(r0 * N) * 2u;
 #pragma unroll
-      for (int sm = 0; sm < S::SM; ++sm)
+    for (int sm = 0; sm < S::SM; ++sm) {
 #pragma unroll
-        for (int sn = 0; sn < S::SN; ++sn)
-          store_block_bf16(acc[sn][sm], rC, eb2 + sm * rstep, wn * S::TN + sn * 32, ncols, hi);
-    } else {
-#pragma unroll
-      for (int sm = 0; sm < S::SM; ++sm) {
-#pragma unroll
-        for (int sn = 0; sn < S::SN; ++sn) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int cc = sn * 32 + 8 * g;
-            const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
-            const f32x16& a = acc[sn][sm];
-            const f32x4 v = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off, 0, 0);
-          }
+      for (int sn = 0; sn < S::SN; ++sn) {
+        const int cc = sn * 16;
+        const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
+        const f32x4& a = acc[sn][sm];
+        if (OUT_BF16) {
+          const u32x2 v = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
+        } else {
+          const f32x4 v = a;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off, 0, 0);
         }
       }
     }
@@ -373,18 +387,15 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   // of this program's workspace ([BM][BN], tile-relative).
   auto store_partial = [&](int slot) {
     float* wsb = P.ws + ((size_t)prog * 2 + slot) * (size_t)(BM * BN);
-    const int r0 = wm * S::TM + l32;
-    const int c0 = wn * S::TN + 4 * (lane >> 5);
+    const int r0 = wm * S::TM + l16;
+    const int c0 = wn * S::TN + 4 * (lane >> 4);
 #pragma unroll
     for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
-      for (int sn = 0; sn < S::SN; ++sn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& a = acc[sn][sm];
-          *reinterpret_cast<f32x4*>(wsb + (r0 + sm * 32) * BN + c0 + sn * 32 + 8 * g) =
-              f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-        }
+      for (int sn = 0; sn < S::SN; ++sn) {
+        const f32x4& a = acc[sn][sm];
+        *reinterpret_cast<f32x4*>(wsb + (r0 + sm * 16) * BN + c0 + sn * 16) = f32x4{a[0], a[1], a[2], a[3]};
+      }
   };
 
   int ct = -1;               // tile on the matrix cores
@@ -408,20 +419,41 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
   // so the next slab's first fragments and the loads' latency hide behind
   // MFMAs, and each load has at least two k-steps to land.
   constexpr int HALF = NL / 2;
-  static_assert(NL % 2 == 0 && HALF <= NMF, "half a slab's loads per k-step");
-  static_assert(S::KK % 2 == 0, "the next slab's first k-step lands in slot 0");
-  auto kstep = [&](int st_rd, int kk_rd, int slot, int st_dma, int d0) {
+  constexpr int NMH = NMF / 2;  // MFMAs per phase (half a k-step: half the B blocks)
+  static_assert(NL % 2 == 0 && HALF <= NMH, "half a slab's loads per phase");
+  // Reads of phase ph from stage st_rd, r-th of the phase:
+  //   ph 0, 2: the second half of the B^T blocks of k-step ph/2 (slot ph/2),
+  //            block SN/2 + r/2, half r&1;
+  //   ph 1, 3: k-step 1 (ph 1) or the next slab's k-step 0 (ph 3): B^T block
+  //            0, the A blocks, then B^T blocks 1 .. SN/2-1.
+  auto phase_read = [&](int ph, int st_rd, int r) {
+    if (ph == 0 || ph == 2) {
+      const int kk = ph >> 1;
+      read_b(st_rd, kk, kk, S::SN / 2 + (r >> 1), r & 1);
+    } else {
+      const int kk = ph == 1 ? 1 : 0;
+      if (r < 2)
+        read_b(st_rd, kk, kk, 0, r);
+      else if (r < 2 + S::SM)
+        read_a(st_rd, kk, kk, r - 2);
+      else
+        read_b(st_rd, kk, kk, 1 + ((r - 2 - S::SM) >> 1), (r - 2 - S::SM) & 1);
+    }
+  };
+  // Phase ph of a slab: the MFMAs of half (ph & 1) of k-step (ph >> 1), after
+  // each its share of the phase's reads and (d0 >= 0) of half a slab's loads.
+  auto phase = [&](int ph, int st_rd, int st_dma, int d0) {
+    const int kk = ph >> 1, hh = ph & 1;
+    const int nrd = (ph == 0 || ph == 2) ? S::SN : S::SM + S::SN;
 #pragma unroll
-    for (int j = 0; j < NMF; ++j) {
-      mfma(slot, j);
-      if (kk_rd >= 0) {
+    for (int jl = 0; jl < NMH; ++jl) {
+      mfma(kk, hh * NMH + jl);
 #pragma unroll
-        for (int r = j * NRD / NMF; r < (j + 1) * NRD / NMF; ++r) read(st_rd, kk_rd, slot ^ 1, r);
-      }
+      for (int r = jl * nrd / NMH; r < (jl + 1) * nrd / NMH; ++r) phase_read(ph, st_rd, r);
       if (d0 >= 0) {
 #pragma unroll
         for (int d = 0; d < HALF; ++d)
-          if (d * NMF / HALF == j) dma(st_dma, d0 + d);
+          if (d * NMH / HALF == jl) dma(st_dma, d0 + d);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -441,8 +473,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     wait_vm<0>();
     slab_barrier();
 #pragma unroll
-    for (int r = 0; r < NRD; ++r) read(0, 0, 0, r);
-    prep();  // slab 1: its first half now, the second half in slab 0's k-step 0
+    for (int r = 0; r < S::SM + S::SN; ++r) phase_read(3, 0, r);
+    prep();  // slab 1: its first half now, the second half in slab 0's phase 0
 #pragma unroll
     for (int d = 0; d < HALF; ++d) dma(1, d);
   }
@@ -477,18 +509,20 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
 #pragma unroll
       for (int sm = 0; sm < S::SM; ++sm)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[sn][sm][e] = 0.0f;
+        for (int e = 0; e < 4; ++e) acc[sn][sm][e] = 0.0f;
+    // wait states between the zeroing writes and the first MFMAs reading them
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     for (int ck = 0; ck < cnsl; ++ck) {
       const int st = g & 1;
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk + 1 < S::KK; ++kk)
-        kstep(st, kk + 1, kk & 1, st ^ 1, kk == 0 ? HALF : -1);
+      phase(0, st, st ^ 1, HALF);
+      phase(1, st, 0, -1);
+      phase(2, st, 0, -1);
       wait_vm<0>();
       slab_barrier();
       prep();  // slab g+2
       __builtin_amdgcn_sched_barrier(0);
-      kstep(st ^ 1, 0, (S::KK - 1) & 1, st, 0);
+      phase(3, st ^ 1, st, 0);
       ++g;
     }
     mfma_results_ready();  // the epilogue reads the accumulators with acc_read
