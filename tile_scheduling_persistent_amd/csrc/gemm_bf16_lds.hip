@@ -365,20 +365,36 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_lds_kernel(GemmParams P) {
     const unsigned eb = (unsigned)(r0 * N + c0) * esz;
     const unsigned rstep = 16u * (unsigned)N * esz;
     const int ncols = N - n0;
+    if (OUT_BF16) {
+      // Two neighbouring blocks at a time: v_permlane16_swap trades the odd
+      // 16-lane rows of the first block's packed columns with the even rows
+      // of the second's, so lane l holds 8 consecutive columns, (l/32)*8 ..
+      // +7, of row l % 16 of block 2*sn2 + (l/16) % 2: one 16-byte store.
+      const unsigned eb16 = (unsigned)(r0 * N) * 2u;
+      const int cl = wn * S::TN + ((lane >> 4) & 1) * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int sm = 0; sm < S::SM; ++sm) {
+#pragma unroll
+        for (int sn2 = 0; sn2 < S::SN / 2; ++sn2) {
+          const f32x4& a = acc[2 * sn2][sm];
+          const f32x4& b = acc[2 * sn2 + 1][sm];
+          const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(a[2], a[3]), pack_bf16x2(b[2], b[3]), false, false);
+          const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
+          const int col = cl + sn2 * 32;
+          const unsigned off = col < ncols ? eb16 + sm * rstep + (unsigned)col * 2u : kOob;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int sm = 0; sm < S::SM; ++sm) {
 #pragma unroll
       for (int sn = 0; sn < S::SN; ++sn) {
         const int cc = sn * 16;
         const unsigned off = (c0 + cc < ncols) ? eb + sm * rstep + (unsigned)cc * esz : kOob;
-        const f32x4& a = acc[sn][sm];
-        if (OUT_BF16) {
-          const u32x2 v = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
-        } else {
-          const f32x4 v = a;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off, 0, 0);
-        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[sn][sm]), rC, off, 0, 0);
       }
     }
   };
