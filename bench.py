@@ -55,8 +55,8 @@ BF16_SOURCES = ["gemm_bf16_lds.hip", "gemm_device.hpp", "common.hpp", "sched.hpp
 FP8_SOURCES = ["gemm_fp8.hip", "gemm_device.hpp", "common.hpp", "sched.hpp", "runtime.hip"]
 ADD_SOURCES = ["padd.hip", "common.hpp", "sched.hpp", "runtime.hip"]
 TRAFFIC = {
-    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "97a1639da0192861",
-        "read_bytes": 1822177088, "write_bytes": 137889856},
+    "bf16_8192cube_work_stealing": {"sources": BF16_SOURCES, "sha256_16": "6ad34d738c399914",
+        "read_bytes": 1610946752, "write_bytes": 186131840},
     "fp8_8192cube_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
         "read_bytes": 811933376, "write_bytes": 144911136},
     "fp8_256x28672x8192_128x256_work_stealing": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
