@@ -13,8 +13,8 @@
 // compute unit about 128 KiB of outstanding reads.  Stores stream past the
 // caches (nontemporal).  The tiles of a step are the next U tiles the
 // scheduler gives the program (for work stealing: one claim of U tiles, and
-// the claim for the following step is issued before the current step's
-// loads so its latency is hidden).
+// the claim for the following step is made once the current step's loads
+// are issued, so its latency overlaps theirs).
 //
 // Several problems in one launch (the multi-loop listings of the same
 // page): the problems' tiles share one virtual id space, problem g's ids
@@ -45,14 +45,16 @@ struct AddShape {
   static_assert(TC % 4 == 0, "tile columns must be a multiple of 4");
 };
 
-template <int TR, int TC, bool VEC, bool WITNESS, bool MULTI>
+// WS: the scheduler is a work-stealing kind (a separate instance, so the
+// static walks carry no claim code between their loads and adds).
+template <int TR, int TC, bool VEC, bool WITNESS, bool MULTI, bool WS>
 __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   using S = AddShape<TR, TC>;
   __shared__ int s_claim[2];
   const int tid = threadIdx.x;
   const int prog = blockIdx.x;
   const int rows = P.rows, cols = P.cols;
-  const bool ws = pgs::work_stealing(P.s.kind);
+  constexpr bool ws = WS;
   Walker walker(P.s, prog);
   if (WITNESS) walker.claim_row = P.w.claims + (size_t)prog * kMaxStealCounters;
   long long t_start = 0, c_start = 0;
@@ -78,7 +80,6 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
     int vt[S::U];
     int next_v0 = -1;
     if (ws) {
-      if (tid == 0) s_claim[(step + 1) & 1] = walker.claim();
       const int e = walker.claim_end(v0);
 #pragma unroll
       for (int u = 0; u < S::U; ++u) vt[u] = (v0 + u < e) ? v0 + u : -1;
@@ -164,6 +165,12 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
         }
       }
     }
+    // Work stealing: the claim for the next step, made after this step's
+    // loads are issued.  The returning atomic and the loads share one wait
+    // counter, so thread 0's wait for the claim is the wait the adds need
+    // anyway and its latency overlaps theirs; before the stores, whose
+    // completion the same counter would also wait for.
+    if (ws && tid == 0) s_claim[(step + 1) & 1] = walker.claim();
 #pragma unroll
     for (int j = 0; j < S::SLOTS; ++j) {
       if (cnt[j] <= 0) continue;
@@ -198,18 +205,26 @@ __global__ void __launch_bounds__(kThreads) padd_kernel(AddParams P) {
   }
 }
 
+template <int TR, int TC, bool MULTI, bool VEC, bool WITNESS>
+void launch_kind(const AddParams& p, hipStream_t stream) {
+  if (pgs::work_stealing(p.s.kind))
+    hipLaunchKernelGGL((padd_kernel<TR, TC, VEC, WITNESS, MULTI, true>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((padd_kernel<TR, TC, VEC, WITNESS, MULTI, false>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+}
+
 template <int TR, int TC, bool MULTI>
 hipError_t launch_tile(const AddParams& p, bool vec, bool witness, hipStream_t stream) {
   if (vec) {
     if (witness)
-      hipLaunchKernelGGL((padd_kernel<TR, TC, true, true, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      launch_kind<TR, TC, MULTI, true, true>(p, stream);
     else
-      hipLaunchKernelGGL((padd_kernel<TR, TC, true, false, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      launch_kind<TR, TC, MULTI, true, false>(p, stream);
   } else {
     if (witness)
-      hipLaunchKernelGGL((padd_kernel<TR, TC, false, true, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      launch_kind<TR, TC, MULTI, false, true>(p, stream);
     else
-      hipLaunchKernelGGL((padd_kernel<TR, TC, false, false, MULTI>), dim3(p.s.G), dim3(kThreads), 0, stream, p);
+      launch_kind<TR, TC, MULTI, false, false>(p, stream);
   }
   return hipGetLastError();
 }
