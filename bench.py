@@ -63,14 +63,14 @@ TRAFFIC = {
         "read_bytes": 253829248, "write_bytes": 14680320},
     "fp8_256x28672x8192_128x256_grouped": {"sources": FP8_SOURCES, "sha256_16": "c29722996871b668",
         "read_bytes": 253793792, "write_bytes": 14680064},
-    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
-        "read_bytes": 536939520, "write_bytes": 268593920},
-    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
-        "read_bytes": 536969216, "write_bytes": 268715776},
-    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
-        "read_bytes": 1073832960, "write_bytes": 268435456},
-    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "9846cfd43537d35b",
-        "read_bytes": 537005952, "write_bytes": 329532672},
+    "add_8192sq_128x128_blocked": {"sources": ADD_SOURCES, "sha256_16": "e9c3685c3537e947",
+        "read_bytes": 536905728, "write_bytes": 268644352},
+    "add_8192sq_128x128_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "e9c3685c3537e947",
+        "read_bytes": 536960000, "write_bytes": 268485120},
+    "add_8192sq_32x16_blocked": {"sources": ADD_SOURCES, "sha256_16": "e9c3685c3537e947",
+        "read_bytes": 1073797120, "write_bytes": 268435456},
+    "add_8192sq_32x16_work_stealing": {"sources": ADD_SOURCES, "sha256_16": "e9c3685c3537e947",
+        "read_bytes": 536980160, "write_bytes": 320627072},
 }
 
 
